@@ -1,0 +1,855 @@
+/*
+ * ada_oracle.c -- plain CPU oracle for Spherical KV's Angle-Domain Attention
+ * (ADA) paged decode and its Rate-Distortion Retention (RDR) packer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant
+ * generator with the HIP library; each side implements the same written
+ * specification on its own.
+ *
+ * Source of the method: "SPHERICAL KV: Angle-Domain Attention and
+ * Rate-Distortion Retention for Efficient Long-Context Inference"
+ * (arXiv 2605.18856), Abstract, as printed on the newx.sg paper page, the
+ * Semantic-Scholar-style page and the searcharxiv.org abstract page.  The
+ * abstract says keys are stored as a scalar radius plus compact angle codes,
+ * that attention logits are computed from the codes without rebuilding dense
+ * keys, and that RDR picks keep/drop and a precision tier per token and head
+ * under a fixed budget, producing tier-homogeneous pages.  It gives no bit
+ * layout, formula or rounding rule; the readings used below (pairing of
+ * dimensions, codebooks, rounding, tie rules, page byte layout, the rate and
+ * distortion model of the packer) are this library's specification and are
+ * listed one by one in the design notes that ship with the repository.
+ *
+ * Arithmetic: fp64 throughout.  The two integer decisions that depend on real
+ * numbers (nearest angle code, nearest magnitude code) are taken *exactly*:
+ * the magnitude code by exact products in binary128 (every product fits in
+ * 71 bits), the angle code by an fp64 estimate that is accepted only outside
+ * a 2^-30 guard band around a rounding boundary and is otherwise recomputed
+ * in binary128 (libquadmath), where an exact tie can only arise for 2-bit
+ * angle codes on the diagonals |x| = |y| and is resolved by comparing |x| and
+ * |y| directly.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared ... -lquadmath -lm -lpthread
+ */
+#include <math.h>
+#include <pthread.h>
+#include <quadmath.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Status codes returned by the oracle (same meaning as the library's).      */
+enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_ENOSPC = 2, ORC_EUNSUPPORTED = 3,
+       ORC_EUNDECIDABLE = 99 };
+
+#define ORC_D 128          /* head dimension                      */
+#define ORC_NP 64          /* pairs per key: head dimension / 2   */
+
+/* Fixed tier table (id order): T8 = 8-bit angle / 8-bit magnitude,
+ * T4 = 4 / 4, T2 = 2-bit angle / 3-bit magnitude. */
+static const int TIER_TB[3] = {8, 4, 2};
+static const int TIER_SB[3] = {8, 4, 3};
+
+int orc_tier_theta_bits(int tier) { return (tier >= 0 && tier < 3) ? TIER_TB[tier] : -1; }
+int orc_tier_s_bits(int tier) { return (tier >= 0 && tier < 3) ? TIER_SB[tier] : -1; }
+
+/* ------------------------------------------------------------------------ */
+/* fp16 conversion: round to nearest, ties to even, straight from fp64 (no
+ * intermediate fp32).  Values that would round to infinity saturate to the
+ * largest finite half, 65504.  Only non-negative finite inputs occur for a
+ * radius, but the sign is handled for completeness. */
+uint16_t orc_f64_to_f16(double x)
+{
+    uint16_t sign = 0;
+    if (signbit(x)) { sign = 0x8000; x = -x; }
+    if (x == 0.0) return sign;
+    int e;                       /* x = f * 2^e, f in [0.5, 1) */
+    frexp(x, &e);
+    int E = e - 1;               /* x in [2^E, 2^(E+1)) */
+    double quantum;
+    if (E < -14) quantum = ldexp(1.0, -24);      /* subnormal spacing */
+    else quantum = ldexp(1.0, E - 10);           /* 10 fraction bits */
+    double n = x / quantum;                      /* exact: power-of-two scale */
+    double r = nearbyint(n);                     /* default mode: ties to even */
+    double v = r * quantum;
+    if (v > 65504.0) return (uint16_t)(sign | 0x7BFF);   /* saturate */
+    if (v < ldexp(1.0, -14)) {                   /* stays subnormal */
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    /* normal: recompute exponent of the rounded value */
+    int e2;
+    frexp(v, &e2);
+    int E2 = e2 - 1;
+    double mant = v / ldexp(1.0, E2 - 10) - 1024.0;   /* 0..1023, exact */
+    return (uint16_t)(sign | (uint16_t)((E2 + 15) << 10) | (uint16_t)mant);
+}
+
+double orc_f16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1, ex = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (ex == 0) v = ldexp((double)m, -24);
+    else if (ex == 31) v = m ? NAN : INFINITY;
+    else v = ldexp(1024.0 + m, ex - 25);
+    return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encoder.  Key k (fp32, exact in fp64) -> radius r16 (fp16 bits), 64 angle
+ * codes, 64 magnitude codes, for angle bits tb and magnitude bits sb.
+ *   pairs:    (x_j, y_j) = (k[2j], k[2j+1])
+ *   energies: e_j = x_j^2 + y_j^2 (each square exact in fp64)
+ *   norm^2:   R2 = fixed pairwise tree over e (strides 32,16,...,1)
+ *   radius:   r = sqrt(R2) correctly rounded, r16 = fp16(r)
+ *   magnitude code: nearest integer to L*sqrt(e_j/R2), ties up, L = 2^sb - 1
+ *   angle code:     nearest integer to (atan2(y,x)+pi)/(2pi/2^tb), ties up,
+ *                   taken mod 2^tb; the zero pair gets code 2^(tb-1).       */
+
+/* exact test of  4 L^2 e >= (2m+1)^2 R2, i.e. L*sqrt(e/R2) >= m + 1/2 */
+static int s_reaches(double e, double R2, int L, int m)
+{
+    __float128 lhs = (__float128)(4.0 * (double)L * (double)L) * (__float128)e;
+    __float128 rhs = (__float128)((double)(2 * m + 1) * (double)(2 * m + 1)) * (__float128)R2;
+    return lhs >= rhs;
+}
+
+static int magnitude_code(double e, double R2, int sb)
+{
+    int L = (1 << sb) - 1;
+    if (R2 == 0.0) return 0;
+    double v = (double)L * sqrt(e / R2);
+    int c = (int)floor(v + 0.5);
+    if (c < 0) c = 0;
+    if (c > L) c = L;
+    while (c > 0 && !s_reaches(e, R2, L, c - 1)) c--;
+    while (c < L && s_reaches(e, R2, L, c)) c++;
+    return c;
+}
+
+static int angle_code(double x, double y, int tb, int *undecidable)
+{
+    int N = 1 << tb;
+    if (x == 0.0 && y == 0.0) return N / 2;
+    double t = (atan2(y, x) + M_PI) / (2.0 * M_PI) * (double)N;
+    double fr = t - floor(t);
+    if (fabs(fr - 0.5) > ldexp(1.0, -30)) {
+        long c = (long)floor(t + 0.5);
+        return (int)(((c % N) + N) % N);
+    }
+    /* near a rounding boundary: redo in binary128 */
+    __float128 tq = (atan2q((__float128)y, (__float128)x) + M_PIq) / (2 * M_PIq) * (__float128)N;
+    __float128 m = floorq(tq);
+    __float128 dq = tq - (m + 0.5Q);
+    long c;
+    if (fabsq(dq) > 0x1p-100Q) {
+        c = (long)m + (dq > 0 ? 1 : 0);
+    } else if (tb == 2 && fabs(x) == fabs(y)) {
+        c = (long)m + 1;                 /* exact tie on a diagonal: half up */
+    } else {
+        *undecidable = 1;
+        c = (long)m;
+    }
+    return (int)(((c % N) + N) % N);
+}
+
+/* Returns ORC_OK, ORC_EINVAL (non-finite key) or ORC_EUNDECIDABLE. */
+int orc_encode_key(const float *k, int tb, int sb, uint16_t *r16,
+                   uint16_t *theta, uint16_t *s, double *r_out)
+{
+    double x[ORC_NP], y[ORC_NP], e[ORC_NP], t[ORC_NP];
+    for (int j = 0; j < ORC_NP; j++) {
+        x[j] = (double)k[2 * j];
+        y[j] = (double)k[2 * j + 1];
+        if (!isfinite(x[j]) || !isfinite(y[j])) return ORC_EINVAL;
+        double xx = x[j] * x[j];
+        double yy = y[j] * y[j];
+        e[j] = xx + yy;
+        t[j] = e[j];
+    }
+    for (int stride = ORC_NP / 2; stride >= 1; stride /= 2)
+        for (int j = 0; j < stride; j++) t[j] = t[j] + t[j + stride];
+    double R2 = t[0];
+    double r = sqrt(R2);
+    if (r_out) *r_out = r;
+    *r16 = orc_f64_to_f16(r);
+    int und = 0;
+    for (int j = 0; j < ORC_NP; j++) {
+        s[j] = (uint16_t)magnitude_code(e[j], R2, sb);
+        theta[j] = (uint16_t)angle_code(x[j], y[j], tb, &und);
+    }
+    return und ? ORC_EUNDECIDABLE : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bit strings: code j of width b occupies bits [j*b, (j+1)*b) of a
+ * little-endian bit string; bit i lives in bit (i mod 8) of byte i/8. */
+void orc_bits_put(uint8_t *dst, int b, const uint16_t *codes, int n)
+{
+    memset(dst, 0, (size_t)(n * b + 7) / 8);
+    for (int j = 0; j < n; j++)
+        for (int q = 0; q < b; q++)
+            if ((codes[j] >> q) & 1) {
+                int i = j * b + q;
+                dst[i / 8] |= (uint8_t)(1u << (i % 8));
+            }
+}
+
+void orc_bits_get(const uint8_t *src, int b, uint16_t *codes, int n)
+{
+    for (int j = 0; j < n; j++) {
+        int c = 0;
+        for (int q = 0; q < b; q++) {
+            int i = j * b + q;
+            if ((src[i / 8] >> (i % 8)) & 1) c |= 1 << q;
+        }
+        codes[j] = (uint16_t)c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Page layout.
+ * Code block of a page (tier tau, page size P), 16-byte aligned at
+ * arena + 16*code_off16:
+ *     [radius: P x u16] [angle component] [magnitude component]
+ * A component with Bc = 8*b bytes per token is cut into floor(Bc/16) units of
+ * 16 bytes, plus one unit of 8 bytes when Bc mod 16 == 8.  Unit u of all P
+ * tokens is stored contiguously (token-minor), units in order.
+ * Value page (fp16) for page id p: element (slot, d) at
+ *     value_pool + p*P*128 + (slot/8)*1024 + d*8 + slot%8.
+ * Page metadata (8 bytes): tier (u8), count (u8), reserved (u16, zero),
+ * code_off16 (u32), little-endian. */
+
+static int comp_bytes(int b) { return 8 * b; }           /* per token */
+
+int64_t orc_block_bytes(int tier, int P)
+{
+    return (int64_t)P * (2 + comp_bytes(TIER_TB[tier]) + comp_bytes(TIER_SB[tier]));
+}
+
+/* byte address (relative to the component start) of byte `byte` of the
+ * component bit string of token `slot` */
+static int64_t comp_addr(int Bc, int P, int slot, int byte)
+{
+    int u = byte / 16, within = byte % 16;
+    int nfull = Bc / 16;
+    if (u < nfull) return (int64_t)u * 16 * P + (int64_t)slot * 16 + within;
+    return (int64_t)nfull * 16 * P + (int64_t)slot * 8 + within;   /* 8-byte unit */
+}
+
+static void write_token_codes(uint8_t *block, int tier, int P, int slot,
+                              uint16_t r16, const uint16_t *th, const uint16_t *sc)
+{
+    int tb = TIER_TB[tier], sb = TIER_SB[tier];
+    int Bt = comp_bytes(tb), Bs = comp_bytes(sb);
+    uint8_t bt[64], bs[64];
+    orc_bits_put(bt, tb, th, ORC_NP);
+    orc_bits_put(bs, sb, sc, ORC_NP);
+    block[2 * slot] = (uint8_t)(r16 & 0xFF);
+    block[2 * slot + 1] = (uint8_t)(r16 >> 8);
+    uint8_t *ct = block + 2 * P;
+    uint8_t *cs = ct + (int64_t)P * Bt;
+    for (int i = 0; i < Bt; i++) ct[comp_addr(Bt, P, slot, i)] = bt[i];
+    for (int i = 0; i < Bs; i++) cs[comp_addr(Bs, P, slot, i)] = bs[i];
+}
+
+static void read_token_codes(const uint8_t *block, int tier, int P, int slot,
+                             uint16_t *r16, uint16_t *th, uint16_t *sc)
+{
+    int tb = TIER_TB[tier], sb = TIER_SB[tier];
+    int Bt = comp_bytes(tb), Bs = comp_bytes(sb);
+    uint8_t bt[64], bs[64];
+    const uint8_t *ct = block + 2 * P;
+    const uint8_t *cs = ct + (int64_t)P * Bt;
+    for (int i = 0; i < Bt; i++) bt[i] = ct[comp_addr(Bt, P, slot, i)];
+    for (int i = 0; i < Bs; i++) bs[i] = cs[comp_addr(Bs, P, slot, i)];
+    *r16 = (uint16_t)(block[2 * slot] | (block[2 * slot + 1] << 8));
+    orc_bits_get(bt, tb, th, ORC_NP);
+    orc_bits_get(bs, sb, sc, ORC_NP);
+}
+
+static int64_t value_index(int64_t page, int P, int slot, int d)
+{
+    return page * P * ORC_D + (int64_t)(slot / 8) * 1024 + (int64_t)d * 8 + slot % 8;
+}
+
+static void meta_write(uint8_t *meta, int64_t page, int tier, int count, uint32_t off16)
+{
+    uint8_t *m = meta + 8 * page;
+    m[0] = (uint8_t)tier;
+    m[1] = (uint8_t)count;
+    m[2] = 0; m[3] = 0;
+    m[4] = (uint8_t)(off16 & 0xFF);
+    m[5] = (uint8_t)((off16 >> 8) & 0xFF);
+    m[6] = (uint8_t)((off16 >> 16) & 0xFF);
+    m[7] = (uint8_t)((off16 >> 24) & 0xFF);
+}
+
+static void meta_read(const uint8_t *meta, int64_t page, int *tier, int *count, uint32_t *off16)
+{
+    const uint8_t *m = meta + 8 * page;
+    *tier = m[0];
+    *count = m[1];
+    *off16 = (uint32_t)m[4] | ((uint32_t)m[5] << 8) | ((uint32_t)m[6] << 16) | ((uint32_t)m[7] << 24);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bulk pack (prefill).  For each sequence b < B, head h, tier id ascending,
+ * the kept tokens of that (b,h,tier) in ascending position are cut into pages
+ * of P; pages get consecutive ids from alloc[0] and consecutive code blocks
+ * from alloc[1] (16-byte units).  The page-table row of (b,h) lists its pages
+ * in that order; open_page[(b,h)][tier] is the last page of that tier when it
+ * is not full, else -1.  Rows of sequences < B are (re)initialised.
+ *
+ * tiers: int8 [B][Hkv][ctx_stride], -1 = drop, else tier id.
+ * keys:  fp32 [B][Hkv][ctx_stride][128]; values: fp16 bits, same shape.
+ * All-or-nothing: on EINVAL / ENOSPC nothing is written.
+ * Encoding each kept key is a pure function of that key, so it is done first
+ * on `nthreads` threads; the page layout pass that follows is sequential. */
+typedef struct {
+    const int8_t *tiers;
+    const float *keys;
+    int64_t n_pos;
+    uint16_t *r16;
+    uint8_t *th, *sc;       /* [n_pos][64] each, codes <= 8 bits */
+    int64_t next;
+    int worst;
+    pthread_mutex_t mu;
+} encode_job_t;
+
+static void *encode_worker(void *arg)
+{
+    encode_job_t *J = arg;
+    const int64_t grain = 1024;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t lo = J->next;
+        J->next += grain;
+        pthread_mutex_unlock(&J->mu);
+        if (lo >= J->n_pos) break;
+        int64_t hi = lo + grain < J->n_pos ? lo + grain : J->n_pos;
+        int worst = ORC_OK;
+        for (int64_t i = lo; i < hi; i++) {
+            int tau = J->tiers[i];
+            if (tau < 0) continue;
+            uint16_t th[ORC_NP], sc[ORC_NP];
+            int st = orc_encode_key(J->keys + i * ORC_D, TIER_TB[tau], TIER_SB[tau], &J->r16[i], th, sc, NULL);
+            if (st > worst) worst = st;
+            for (int j = 0; j < ORC_NP; j++) {
+                J->th[i * ORC_NP + j] = (uint8_t)th[j];
+                J->sc[i * ORC_NP + j] = (uint8_t)sc[j];
+            }
+        }
+        pthread_mutex_lock(&J->mu);
+        if (worst > J->worst) J->worst = worst;
+        pthread_mutex_unlock(&J->mu);
+    }
+    return NULL;
+}
+
+int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
+             const int8_t *tiers, const float *keys, const uint16_t *values,
+             int32_t max_pages_per_head, int64_t page_capacity, int64_t arena_capacity16,
+             int32_t *page_table, int32_t *num_pages, int32_t *open_page,
+             uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc,
+             int nthreads)
+{
+    if (P != 16 && P != 32) return ORC_EINVAL;
+    /* validation pass */
+    int64_t need_pages = 0, need16 = 0;
+    for (int b = 0; b < B; b++) {
+        if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride) return ORC_EINVAL;
+        for (int h = 0; h < Hkv; h++) {
+            int64_t row_pages = 0;
+            int64_t n_tier[3] = {0, 0, 0};
+            for (int t = 0; t < ctx_len[b]; t++) {
+                int64_t idx = ((int64_t)b * Hkv + h) * ctx_stride + t;
+                int tv = tiers[idx];
+                if (tv < -1 || tv > 2) return ORC_EINVAL;
+                if (tv < 0) continue;
+                const float *k = keys + idx * ORC_D;
+                for (int d = 0; d < ORC_D; d++)
+                    if (!isfinite(k[d])) return ORC_EINVAL;
+                n_tier[tv]++;
+            }
+            for (int tau = 0; tau < 3; tau++) {
+                int64_t pages = (n_tier[tau] + P - 1) / P;
+                row_pages += pages;
+                need_pages += pages;
+                need16 += pages * (orc_block_bytes(tau, P) / 16);
+            }
+            if (row_pages > max_pages_per_head) return ORC_ENOSPC;
+        }
+    }
+    if (alloc[0] + need_pages > page_capacity) return ORC_ENOSPC;
+    if (alloc[1] + need16 > arena_capacity16) return ORC_ENOSPC;
+
+    /* encode every kept key (positions beyond ctx_len are treated as dropped) */
+    int64_t n_pos = (int64_t)B * Hkv * ctx_stride;
+    int8_t *tiers_used = malloc((size_t)(n_pos > 0 ? n_pos : 1));
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < Hkv; h++)
+            for (int64_t t = 0; t < ctx_stride; t++) {
+                int64_t idx = ((int64_t)b * Hkv + h) * ctx_stride + t;
+                tiers_used[idx] = t < ctx_len[b] ? tiers[idx] : -1;
+            }
+    encode_job_t E;
+    E.tiers = tiers_used; E.keys = keys; E.n_pos = n_pos;
+    E.r16 = malloc(sizeof(uint16_t) * (n_pos > 0 ? n_pos : 1));
+    E.th = malloc((size_t)(n_pos > 0 ? n_pos : 1) * ORC_NP);
+    E.sc = malloc((size_t)(n_pos > 0 ? n_pos : 1) * ORC_NP);
+    E.next = 0; E.worst = ORC_OK;
+    pthread_mutex_init(&E.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    pthread_t *thr = malloc(sizeof(pthread_t) * nthreads);
+    for (int i = 0; i < nthreads; i++) pthread_create(&thr[i], NULL, encode_worker, &E);
+    for (int i = 0; i < nthreads; i++) pthread_join(thr[i], NULL);
+    free(thr);
+    pthread_mutex_destroy(&E.mu);
+    int status = E.worst;
+
+    /* layout pass */
+    for (int b = 0; b < B && status == ORC_OK; b++) {
+        for (int h = 0; h < Hkv; h++) {
+            int64_t row = (int64_t)b * Hkv + h;
+            int32_t np_row = 0;
+            for (int tau = 0; tau < 3; tau++) {
+                open_page[row * 3 + tau] = -1;
+                int64_t page = -1;
+                int slot = P;
+                uint8_t *block = NULL;
+                uint32_t off16 = 0;
+                for (int t = 0; t < ctx_len[b]; t++) {
+                    int64_t idx = row * ctx_stride + t;
+                    if (tiers[idx] != tau) continue;
+                    if (slot == P) {          /* start a new page */
+                        page = alloc[0]++;
+                        off16 = (uint32_t)alloc[1];
+                        int64_t bb = orc_block_bytes(tau, P);
+                        alloc[1] += bb / 16;
+                        block = arena + (int64_t)off16 * 16;
+                        memset(block, 0, (size_t)bb);
+                        for (int i = 0; i < P * ORC_D; i++) value_pool[page * P * ORC_D + i] = 0;
+                        page_table[row * max_pages_per_head + np_row] = (int32_t)page;
+                        np_row++;
+                        slot = 0;
+                    }
+                    uint16_t th[ORC_NP], sc[ORC_NP];
+                    for (int j = 0; j < ORC_NP; j++) {
+                        th[j] = E.th[idx * ORC_NP + j];
+                        sc[j] = E.sc[idx * ORC_NP + j];
+                    }
+                    write_token_codes(block, tau, P, slot, E.r16[idx], th, sc);
+                    for (int d = 0; d < ORC_D; d++)
+                        value_pool[value_index(page, P, slot, d)] = values[idx * ORC_D + d];
+                    slot++;
+                    meta_write(page_meta, page, tau, slot, off16);
+                }
+                if (page >= 0 && slot < P) open_page[row * 3 + tau] = (int32_t)page;
+            }
+            num_pages[row] = np_row;
+        }
+    }
+    free(tiers_used); free(E.r16); free(E.th); free(E.sc);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Append, with sequential semantics in request order: a request for
+ * (seq, head, tier) fills the open page of that (seq, head, tier) at slot
+ * `count`; when there is none it takes page alloc[0] and the next code block,
+ * appends that page to the (seq, head) row and leaves it open unless it is
+ * full.  If any request would exceed the page capacity, the arena capacity or
+ * the row length, the call returns ENOSPC and writes nothing; a request with
+ * an out-of-range seq/head/tier or a non-finite key gives EINVAL and nothing
+ * is written. */
+int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
+               int64_t page_capacity, int64_t arena_capacity16, int n,
+               const int32_t *seq, const int32_t *head, const uint8_t *tier,
+               const float *keys, const uint16_t *values,
+               int32_t *page_table, int32_t *num_pages, int32_t *open_page,
+               uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc)
+{
+    if (P != 16 && P != 32) return ORC_EINVAL;
+    for (int i = 0; i < n; i++) {
+        if (seq[i] < 0 || seq[i] >= num_seqs || head[i] < 0 || head[i] >= Hkv || tier[i] > 2)
+            return ORC_EINVAL;
+        for (int d = 0; d < ORC_D; d++)
+            if (!isfinite(keys[(int64_t)i * ORC_D + d])) return ORC_EINVAL;
+    }
+    /* dry run on copies of the small state */
+    int64_t rows = (int64_t)num_seqs * Hkv;
+    int32_t *np_copy = malloc(sizeof(int32_t) * rows);
+    int32_t *open_copy = malloc(sizeof(int32_t) * rows * 3);
+    int32_t *cnt_open = malloc(sizeof(int32_t) * rows * 3);
+    memcpy(np_copy, num_pages, sizeof(int32_t) * rows);
+    memcpy(open_copy, open_page, sizeof(int32_t) * rows * 3);
+    for (int64_t i = 0; i < rows * 3; i++) {
+        cnt_open[i] = 0;
+        if (open_copy[i] >= 0) {
+            int tr, c; uint32_t o;
+            meta_read(page_meta, open_copy[i], &tr, &c, &o);
+            cnt_open[i] = c;
+        }
+    }
+    int64_t a0 = alloc[0], a1 = alloc[1];
+    int status = ORC_OK;
+    for (int i = 0; i < n && status == ORC_OK; i++) {
+        int64_t row = (int64_t)seq[i] * Hkv + head[i];
+        int64_t key = row * 3 + tier[i];
+        if (open_copy[key] < 0) {
+            if (a0 + 1 > page_capacity) status = ORC_ENOSPC;
+            else if (a1 + orc_block_bytes(tier[i], P) / 16 > arena_capacity16) status = ORC_ENOSPC;
+            else if (np_copy[row] + 1 > max_pages_per_head) status = ORC_ENOSPC;
+            if (status) break;
+            open_copy[key] = (int32_t)a0;
+            a0++;
+            a1 += orc_block_bytes(tier[i], P) / 16;
+            np_copy[row]++;
+            cnt_open[key] = 0;
+        }
+        cnt_open[key]++;
+        if (cnt_open[key] == P) open_copy[key] = -1;
+    }
+    free(np_copy); free(open_copy); free(cnt_open);
+    if (status) return status;
+
+    /* apply */
+    for (int i = 0; i < n; i++) {
+        int64_t row = (int64_t)seq[i] * Hkv + head[i];
+        int tau = tier[i];
+        int32_t *op = &open_page[row * 3 + tau];
+        int64_t page;
+        int cnt;
+        uint32_t off16;
+        if (*op < 0) {
+            page = alloc[0]++;
+            off16 = (uint32_t)alloc[1];
+            int64_t bb = orc_block_bytes(tau, P);
+            alloc[1] += bb / 16;
+            memset(arena + (int64_t)off16 * 16, 0, (size_t)bb);
+            for (int q = 0; q < P * ORC_D; q++) value_pool[page * P * ORC_D + q] = 0;
+            page_table[row * max_pages_per_head + num_pages[row]] = (int32_t)page;
+            num_pages[row]++;
+            cnt = 0;
+            *op = (int32_t)page;
+        } else {
+            int tr;
+            page = *op;
+            meta_read(page_meta, page, &tr, &cnt, &off16);
+        }
+        uint16_t r16, th[ORC_NP], sc[ORC_NP];
+        if (orc_encode_key(keys + (int64_t)i * ORC_D, TIER_TB[tau], TIER_SB[tau], &r16, th, sc, NULL) != ORC_OK)
+            return ORC_EUNDECIDABLE;
+        write_token_codes(arena + (int64_t)off16 * 16, tau, P, cnt, r16, th, sc);
+        for (int d = 0; d < ORC_D; d++)
+            value_pool[value_index(page, P, cnt, d)] = values[(int64_t)i * ORC_D + d];
+        cnt++;
+        meta_write(page_meta, page, tau, cnt, off16);
+        if (cnt == P) *op = -1;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RDR keep/drop and tier assignment under a byte budget.
+ * Items are (head, position) pairs of one sequence; all heads of a sequence
+ * share its budget.  Rate of tier tau: 2 + 8*(tb+sb) + 256 bytes (radius,
+ * codes, fp16 value row); distortion 2^-(tb+sb); a dropped item has rate 0,
+ * distortion 1.  Enabled tiers sorted by rate give upgrade steps
+ * drop -> first -> second ...; step k costs dR_k bytes and saves dD_k, with
+ * c_k = dD_k / dR_k, which must decrease strictly (else EUNSUPPORTED).
+ * Priority of step k of an item with utility w: p = w * c_k (fp64).
+ * Total order: p descending, then position descending, then head ascending,
+ * then k ascending.  Steps are taken in that order while the running byte
+ * total stays within the budget; the walk stops at the first step that does
+ * not fit.  An item's tier is its highest step taken (none: dropped = -1). */
+typedef struct { double p; int32_t t; int32_t h; int32_t k; } orc_step_t;
+
+static int step_cmp(const void *a, const void *b)
+{
+    const orc_step_t *x = a, *y = b;
+    if (x->p != y->p) return x->p > y->p ? -1 : 1;
+    if (x->t != y->t) return x->t > y->t ? -1 : 1;
+    if (x->h != y->h) return x->h < y->h ? -1 : 1;
+    if (x->k != y->k) return x->k < y->k ? -1 : 1;
+    return 0;
+}
+
+int orc_rdr_steps(uint32_t tier_mask, int *n_steps, int *step_tier, int64_t *dR, double *c)
+{
+    int ids[3], n = 0;
+    for (int tau = 0; tau < 3; tau++)
+        if (tier_mask & (1u << tau)) ids[n++] = tau;
+    if (n == 0) return ORC_EINVAL;
+    /* sort enabled tiers by rate ascending */
+    for (int i = 0; i < n; i++)
+        for (int j = i + 1; j < n; j++) {
+            int64_t ri = 2 + 8 * (TIER_TB[ids[i]] + TIER_SB[ids[i]]) + 256;
+            int64_t rj = 2 + 8 * (TIER_TB[ids[j]] + TIER_SB[ids[j]]) + 256;
+            if (rj < ri) { int tmp = ids[i]; ids[i] = ids[j]; ids[j] = tmp; }
+        }
+    int64_t prevR = 0;
+    double prevD = 1.0;
+    for (int i = 0; i < n; i++) {
+        int tau = ids[i];
+        int64_t R = 2 + 8 * (TIER_TB[tau] + TIER_SB[tau]) + 256;
+        double D = ldexp(1.0, -(TIER_TB[tau] + TIER_SB[tau]));
+        if (R <= prevR || D >= prevD) return ORC_EUNSUPPORTED;
+        dR[i] = R - prevR;
+        c[i] = (prevD - D) / (double)dR[i];
+        if (i > 0 && !(c[i] < c[i - 1])) return ORC_EUNSUPPORTED;
+        step_tier[i] = tau;
+        prevR = R;
+        prevD = D;
+    }
+    *n_steps = n;
+    return ORC_OK;
+}
+
+int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
+                   const float *utility, const int64_t *budget, uint32_t tier_mask,
+                   int8_t *tier_out)
+{
+    int n_steps, step_tier[3];
+    int64_t dR[3];
+    double c[3];
+    int st = orc_rdr_steps(tier_mask, &n_steps, step_tier, dR, c);
+    if (st) return st;
+    for (int b = 0; b < B; b++) {
+        if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride || budget[b] < 0) return ORC_EINVAL;
+        for (int h = 0; h < Hkv; h++)
+            for (int t = 0; t < ctx_len[b]; t++) {
+                float w = utility[((int64_t)b * Hkv + h) * ctx_stride + t];
+                if (!isfinite(w) || w < 0) return ORC_EINVAL;
+            }
+    }
+    for (int b = 0; b < B; b++) {
+        int64_t ctx = ctx_len[b];
+        int64_t ns = (int64_t)Hkv * ctx * n_steps;
+        orc_step_t *steps = malloc(sizeof(orc_step_t) * (ns > 0 ? ns : 1));
+        int64_t q = 0;
+        for (int h = 0; h < Hkv; h++)
+            for (int64_t t = 0; t < ctx; t++) {
+                double w = (double)utility[((int64_t)b * Hkv + h) * ctx_stride + t];
+                for (int k = 0; k < n_steps; k++) {
+                    steps[q].p = w * c[k];
+                    steps[q].t = (int32_t)t;
+                    steps[q].h = h;
+                    steps[q].k = k;
+                    q++;
+                }
+            }
+        qsort(steps, (size_t)ns, sizeof(orc_step_t), step_cmp);
+        for (int h = 0; h < Hkv; h++)
+            for (int64_t t = 0; t < ctx_stride; t++)
+                tier_out[((int64_t)b * Hkv + h) * ctx_stride + t] = -1;
+        int8_t *level = calloc((size_t)(Hkv * ctx > 0 ? Hkv * ctx : 1), 1);
+        int64_t cum = 0;
+        for (int64_t i = 0; i < ns; i++) {
+            if (cum + dR[steps[i].k] > budget[b]) break;
+            cum += dR[steps[i].k];
+            level[(int64_t)steps[i].h * ctx + steps[i].t] = (int8_t)(steps[i].k + 1);
+        }
+        for (int h = 0; h < Hkv; h++)
+            for (int64_t t = 0; t < ctx; t++) {
+                int lv = level[(int64_t)h * ctx + t];
+                tier_out[((int64_t)b * Hkv + h) * ctx_stride + t] = lv ? (int8_t)step_tier[lv - 1] : -1;
+            }
+        free(level);
+        free(steps);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Angle lookup table of one query head for angle bits tb:
+ *   LUT[j][c] = q[2j] cos(th_c) + q[2j+1] sin(th_c),  th_c = -pi + c*2pi/2^tb
+ * (no softmax scale folded in). */
+void orc_lut(const float *q, int tb, double *lut)
+{
+    int N = 1 << tb;
+    for (int j = 0; j < ORC_NP; j++)
+        for (int c = 0; c < N; c++) {
+            double th = -M_PI + (double)c * (2.0 * M_PI / (double)N);
+            lut[j * N + c] = (double)q[2 * j] * cos(th) + (double)q[2 * j + 1] * sin(th);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* ADA paged decode, one query row (b, hq), KV head h = hq / G.
+ *   logit_t = scale * r_t * sum_j (s_code/L) * LUT[j][theta_code]   (j order)
+ *   over the kept tokens of (b,h) as they appear in the page-table row:
+ *   m = max logit, w_t = exp(logit_t - m) / sum exp(logit - m),
+ *   out = sum_t w_t v_t, lse = m + log(sum exp(logit - m)).
+ *   No kept token: out = 0, lse = -inf. */
+typedef struct {
+    int P, Hq, Hkv, B;
+    int32_t max_pages_per_head;
+    const int32_t *page_table, *num_pages;
+    const uint8_t *page_meta, *arena;
+    const uint16_t *value_pool;
+    const float *q;
+    double scale;
+    double *out, *lse;
+    int64_t next_row, n_rows;
+    pthread_mutex_t mu;
+} decode_job_t;
+
+static void decode_row(decode_job_t *J, int64_t row_q, double *lut8, double *lut4, double *lut2,
+                       double *logit, int64_t cap)
+{
+    int b = (int)(row_q / J->Hq), hq = (int)(row_q % J->Hq);
+    int G = J->Hq / J->Hkv;
+    int h = hq / G;
+    const float *q = J->q + row_q * ORC_D;
+    orc_lut(q, 8, lut8);
+    orc_lut(q, 4, lut4);
+    orc_lut(q, 2, lut2);
+    double *luts[3] = {lut8, lut4, lut2};
+    int64_t row = (int64_t)b * J->Hkv + h;
+    int np = J->num_pages[row];
+    int64_t n = 0;
+    double m = -INFINITY;
+    /* pass 1: logits */
+    for (int i = 0; i < np; i++) {
+        int64_t page = J->page_table[row * J->max_pages_per_head + i];
+        int tier, count; uint32_t off16;
+        meta_read(J->page_meta, page, &tier, &count, &off16);
+        const uint8_t *block = J->arena + (int64_t)off16 * 16;
+        int tb = TIER_TB[tier], sb = TIER_SB[tier];
+        int N = 1 << tb;
+        double L = (double)((1 << sb) - 1);
+        for (int slot = 0; slot < count; slot++) {
+            uint16_t r16, th[ORC_NP], sc[ORC_NP];
+            read_token_codes(block, tier, J->P, slot, &r16, th, sc);
+            double acc = 0.0;
+            for (int j = 0; j < ORC_NP; j++)
+                acc += ((double)sc[j] / L) * luts[tier][j * N + th[j]];
+            double lg = J->scale * orc_f16_to_f64(r16) * acc;
+            if (n < cap) logit[n] = lg;
+            n++;
+            if (lg > m) m = lg;
+        }
+    }
+    double *o = J->out + row_q * ORC_D;
+    for (int d = 0; d < ORC_D; d++) o[d] = 0.0;
+    if (n == 0) { J->lse[row_q] = -INFINITY; return; }
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; t++) sum += exp(logit[t] - m);
+    /* pass 2: weighted values */
+    int64_t t = 0;
+    for (int i = 0; i < np; i++) {
+        int64_t page = J->page_table[row * J->max_pages_per_head + i];
+        int tier, count; uint32_t off16;
+        meta_read(J->page_meta, page, &tier, &count, &off16);
+        for (int slot = 0; slot < count; slot++, t++) {
+            double w = exp(logit[t] - m) / sum;
+            for (int d = 0; d < ORC_D; d++)
+                o[d] += w * orc_f16_to_f64(J->value_pool[value_index(page, J->P, slot, d)]);
+        }
+    }
+    J->lse[row_q] = m + log(sum);
+}
+
+static void *decode_worker(void *arg)
+{
+    decode_job_t *J = arg;
+    double *lut8 = malloc(sizeof(double) * ORC_NP * 256);
+    double *lut4 = malloc(sizeof(double) * ORC_NP * 16);
+    double *lut2 = malloc(sizeof(double) * ORC_NP * 4);
+    int64_t cap = (int64_t)J->max_pages_per_head * J->P;
+    double *logit = malloc(sizeof(double) * (cap > 0 ? cap : 1));
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t r = J->next_row++;
+        pthread_mutex_unlock(&J->mu);
+        if (r >= J->n_rows) break;
+        decode_row(J, r, lut8, lut4, lut2, logit, cap);
+    }
+    free(lut8); free(lut4); free(lut2); free(logit);
+    return NULL;
+}
+
+/* rows: optional list of (b*Hq + hq) rows to compute (n_rows entries); when
+ * rows == NULL all B*Hq rows are computed.  out/lse are indexed by row. */
+int orc_decode(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
+               const int32_t *page_table, const int32_t *num_pages,
+               const uint8_t *page_meta, const uint8_t *arena, const uint16_t *value_pool,
+               const float *q, double scale, double *out, double *lse, int nthreads)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || (P != 16 && P != 32)) return ORC_EINVAL;
+    decode_job_t J;
+    J.P = P; J.Hq = Hq; J.Hkv = Hkv; J.B = B;
+    J.max_pages_per_head = max_pages_per_head;
+    J.page_table = page_table; J.num_pages = num_pages;
+    J.page_meta = page_meta; J.arena = arena; J.value_pool = value_pool;
+    J.q = q; J.scale = scale; J.out = out; J.lse = lse;
+    J.next_row = 0; J.n_rows = (int64_t)B * Hq;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    pthread_t *th = malloc(sizeof(pthread_t) * nthreads);
+    for (int i = 0; i < nthreads; i++) pthread_create(&th[i], NULL, decode_worker, &J);
+    for (int i = 0; i < nthreads; i++) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Unquantised angle-domain logits (oracle only): r, s_j and theta_j kept as
+ * exact fp64 reals, logit = r * sum_j s_j (q_{2j} cos th_j + q_{2j+1} sin th_j).
+ * This equals the plain dot product q.k up to rounding. */
+void orc_identity_logits(const float *keys, int64_t n, const float *q, double *logits)
+{
+    for (int64_t i = 0; i < n; i++) {
+        const float *k = keys + i * ORC_D;
+        double e[ORC_NP], t[ORC_NP];
+        for (int j = 0; j < ORC_NP; j++) {
+            double x = k[2 * j], y = k[2 * j + 1];
+            e[j] = x * x + y * y;
+            t[j] = e[j];
+        }
+        for (int stride = ORC_NP / 2; stride >= 1; stride /= 2)
+            for (int j = 0; j < stride; j++) t[j] = t[j] + t[j + stride];
+        double r = sqrt(t[0]);
+        double acc = 0.0;
+        if (r > 0)
+            for (int j = 0; j < ORC_NP; j++) {
+                double x = k[2 * j], y = k[2 * j + 1];
+                double s = sqrt(e[j]) / r;
+                double th = atan2(y, x);
+                acc += s * ((double)q[2 * j] * cos(th) + (double)q[2 * j + 1] * sin(th));
+            }
+        logits[i] = r * acc;
+    }
+}
+
+/* encode many keys at once (threads not needed; used by tests) */
+int orc_encode_many(const float *keys, int64_t n, int tb, int sb, uint16_t *r16,
+                    uint16_t *theta, uint16_t *s)
+{
+    int worst = ORC_OK;
+    for (int64_t i = 0; i < n; i++) {
+        int st = orc_encode_key(keys + i * ORC_D, tb, sb, r16 + i, theta + i * ORC_NP, s + i * ORC_NP, NULL);
+        if (st > worst) worst = st;
+    }
+    return worst;
+}
+
+int64_t orc_value_index(int64_t page, int P, int slot, int d) { return value_index(page, P, slot, d); }
+
+void orc_read_token(const uint8_t *arena, const uint8_t *page_meta, int P, int64_t page, int slot,
+                    uint16_t *r16, uint16_t *theta, uint16_t *s, int *tier_out)
+{
+    int tier, count; uint32_t off16;
+    meta_read(page_meta, page, &tier, &count, &off16);
+    read_token_codes(arena + (int64_t)off16 * 16, tier, P, slot, r16, theta, s);
+    *tier_out = tier;
+}
+
+void orc_f64_to_f16_many(const double *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_f64_to_f16(x[i]);
+}

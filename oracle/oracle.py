@@ -1,0 +1,240 @@
+"""ctypes binding of the CPU oracle in ``ada_oracle.c``.
+
+Test infrastructure only: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module; the product path never does.
+Every function here only marshals numpy arrays into the C oracle and back.
+The method follows the abstract of "SPHERICAL KV: Angle-Domain Attention and
+Rate-Distortion Retention for Efficient Long-Context Inference"
+(arXiv 2605.18856, Abstract); the byte layout and rounding rules it leaves
+open are fixed by this library's specification (see ``ada_oracle.c``).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ada_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+OK, EINVAL, ENOSPC, EUNSUPPORTED, EUNDECIDABLE = 0, 1, 2, 3, 99
+TIER_BITS = {0: (8, 8), 1: (4, 4), 2: (2, 3)}   # tier id -> (angle bits, magnitude bits)
+D = 128
+NP_PAIRS = 64
+
+
+def build():
+    """Compile the oracle with gcc (plain C, fp64, no FP contraction)."""
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o", LIB, SRC,
+                           "-lquadmath", "-lm", "-lpthread"])
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _lib = ctypes.CDLL(LIB)
+        _declare(_lib)
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _declare(L):
+    vp, i32, i64, u32, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_double
+    L.orc_f64_to_f16.restype = ctypes.c_uint16
+    L.orc_f64_to_f16.argtypes = [dbl]
+    L.orc_f64_to_f16_many.argtypes = [vp, i64, vp]
+    L.orc_f16_to_f64.restype = dbl
+    L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
+    L.orc_encode_key.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    L.orc_encode_many.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    L.orc_bits_put.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
+    L.orc_bits_get.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
+    L.orc_block_bytes.restype = i64
+    L.orc_block_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.orc_pack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp,
+                           i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+    L.orc_append.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i64, i64, ctypes.c_int,
+                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.orc_rdr_steps.argtypes = [u32, vp, vp, vp, vp]
+    L.orc_rdr_assign.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, u32, vp]
+    L.orc_lut.argtypes = [vp, ctypes.c_int, vp]
+    L.orc_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
+                             vp, vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int]
+    L.orc_identity_logits.argtypes = [vp, i64, vp, vp]
+    L.orc_read_token.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp]
+    L.orc_value_index.restype = i64
+    L.orc_value_index.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+
+
+def f64_to_f16(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f64_to_f16_many(_p(x), x.size, _p(out))
+    return out
+
+
+def f16_to_f64(h):
+    return lib().orc_f16_to_f64(int(h))
+
+
+def encode(keys, tb, sb):
+    """keys [n,128] fp32 -> (r16 [n] u16 fp16 bits, theta [n,64] u16, s [n,64] u16, status)."""
+    keys = np.ascontiguousarray(keys, dtype=np.float32).reshape(-1, D)
+    n = keys.shape[0]
+    r16 = np.zeros(n, np.uint16)
+    th = np.zeros((n, NP_PAIRS), np.uint16)
+    s = np.zeros((n, NP_PAIRS), np.uint16)
+    st = lib().orc_encode_many(_p(keys), n, tb, sb, _p(r16), _p(th), _p(s))
+    return r16, th, s, st
+
+
+def bits_put(codes, b):
+    codes = np.ascontiguousarray(codes, dtype=np.uint16)
+    out = np.zeros((codes.size * b + 7) // 8, np.uint8)
+    lib().orc_bits_put(_p(out), b, _p(codes), codes.size)
+    return out
+
+
+def bits_get(buf, b, n):
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    out = np.zeros(n, np.uint16)
+    lib().orc_bits_get(_p(buf), b, _p(out), n)
+    return out
+
+
+def block_bytes(tier, P):
+    return lib().orc_block_bytes(tier, P)
+
+
+class Cache:
+    """Host copy of a paged ADA cache (the same buffers the library keeps on
+    the device): page table, page counts, open pages, page metadata, code
+    arena, fp16 value pool and the two allocation counters."""
+
+    def __init__(self, P, Hq, Hkv, num_seqs, max_pages_per_head, page_capacity, arena_capacity16):
+        self.P, self.Hq, self.Hkv = P, Hq, Hkv
+        self.num_seqs = num_seqs
+        self.max_pages_per_head = max_pages_per_head
+        self.page_capacity = page_capacity
+        self.arena_capacity16 = arena_capacity16
+        rows = num_seqs * Hkv
+        self.page_table = np.zeros((rows, max_pages_per_head), np.int32)
+        self.num_pages = np.zeros(rows, np.int32)
+        self.open_page = np.full((rows, 3), -1, np.int32)
+        self.page_meta = np.zeros((page_capacity, 8), np.uint8)
+        self.arena = np.zeros(arena_capacity16 * 16, np.uint8)
+        self.value_pool = np.zeros((page_capacity, P * D), np.uint16)
+        self.alloc = np.zeros(2, np.int64)
+
+    def copy(self):
+        c = Cache.__new__(Cache)
+        c.__dict__.update({k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in self.__dict__.items()})
+        return c
+
+    def meta(self, page):
+        m = self.page_meta[page]
+        return int(m[0]), int(m[1]), int(m[4]) | (int(m[5]) << 8) | (int(m[6]) << 16) | (int(m[7]) << 24)
+
+
+def pack(cache, ctx_len, tiers, keys, values, nthreads=None):
+    """Bulk pack sequences 0..B-1 into `cache` (in place). Returns status."""
+    ctx_len = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    tiers = np.ascontiguousarray(tiers, dtype=np.int8)
+    keys = np.ascontiguousarray(keys, dtype=np.float32)
+    values = np.ascontiguousarray(values, dtype=np.uint16)
+    B, Hkv, stride = tiers.shape
+    assert Hkv == cache.Hkv and keys.shape == (B, Hkv, stride, D) and values.shape == keys.shape
+    nthreads = nthreads or max(1, len(os.sched_getaffinity(0)))
+    return lib().orc_pack(cache.P, cache.Hkv, B, _p(ctx_len), stride, _p(tiers), _p(keys), _p(values),
+                          cache.max_pages_per_head, cache.page_capacity, cache.arena_capacity16,
+                          _p(cache.page_table), _p(cache.num_pages), _p(cache.open_page),
+                          _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc),
+                          nthreads)
+
+
+def append(cache, seq, head, tier, keys, values):
+    seq = np.ascontiguousarray(seq, dtype=np.int32)
+    head = np.ascontiguousarray(head, dtype=np.int32)
+    tier = np.ascontiguousarray(tier, dtype=np.uint8)
+    keys = np.ascontiguousarray(keys, dtype=np.float32).reshape(-1, D)
+    values = np.ascontiguousarray(values, dtype=np.uint16).reshape(-1, D)
+    n = seq.size
+    return lib().orc_append(cache.P, cache.Hkv, cache.num_seqs, cache.max_pages_per_head,
+                            cache.page_capacity, cache.arena_capacity16, n,
+                            _p(seq), _p(head), _p(tier), _p(keys), _p(values),
+                            _p(cache.page_table), _p(cache.num_pages), _p(cache.open_page),
+                            _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc))
+
+
+def rdr_steps(tier_mask):
+    n = ctypes.c_int(0)
+    st_tier = np.zeros(3, np.int32)
+    dR = np.zeros(3, np.int64)
+    c = np.zeros(3, np.float64)
+    st = lib().orc_rdr_steps(tier_mask, ctypes.byref(n), _p(st_tier), _p(dR), _p(c))
+    return st, st_tier[:n.value], dR[:n.value], c[:n.value]
+
+
+def rdr_assign(ctx_len, utility, budget, tier_mask=0b111):
+    """utility fp32 [B][Hkv][stride] -> (status, tiers int8 same shape)."""
+    ctx_len = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    utility = np.ascontiguousarray(utility, dtype=np.float32)
+    budget = np.ascontiguousarray(budget, dtype=np.int64)
+    B, Hkv, stride = utility.shape
+    out = np.full(utility.shape, -1, np.int8)
+    st = lib().orc_rdr_assign(Hkv, B, _p(ctx_len), stride, _p(utility), _p(budget), tier_mask, _p(out))
+    return st, out
+
+
+def lut(q, tb):
+    q = np.ascontiguousarray(q, dtype=np.float32).reshape(D)
+    out = np.zeros((NP_PAIRS, 1 << tb), np.float64)
+    lib().orc_lut(_p(q), tb, _p(out))
+    return out
+
+
+def decode(cache, q, scale, nthreads=None):
+    """q fp32 [B][Hq][128] -> (out fp64 [B][Hq][128], lse fp64 [B][Hq])."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, Hq, _ = q.shape
+    assert Hq == cache.Hq
+    out = np.zeros((B, Hq, D), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    nthreads = nthreads or max(1, len(os.sched_getaffinity(0)))
+    st = lib().orc_decode(cache.P, cache.Hq, cache.Hkv, B, cache.max_pages_per_head,
+                          _p(cache.page_table), _p(cache.num_pages), _p(cache.page_meta),
+                          _p(cache.arena), _p(cache.value_pool), _p(q), float(scale),
+                          _p(out), _p(lse), nthreads)
+    assert st == OK, st
+    return out, lse
+
+
+def identity_logits(keys, q):
+    keys = np.ascontiguousarray(keys, dtype=np.float32).reshape(-1, D)
+    q = np.ascontiguousarray(q, dtype=np.float32).reshape(D)
+    out = np.zeros(keys.shape[0], np.float64)
+    lib().orc_identity_logits(_p(keys), keys.shape[0], _p(q), _p(out))
+    return out
+
+
+def read_token(cache, page, slot):
+    r16 = np.zeros(1, np.uint16)
+    th = np.zeros(NP_PAIRS, np.uint16)
+    s = np.zeros(NP_PAIRS, np.uint16)
+    tier = ctypes.c_int(0)
+    lib().orc_read_token(_p(cache.arena), _p(cache.page_meta), cache.P, page, slot,
+                         _p(r16), _p(th), _p(s), ctypes.byref(tier))
+    return int(r16[0]), th, s, tier.value
+
+
+def value_index(page, P, slot, d):
+    return lib().orc_value_index(page, P, slot, d)

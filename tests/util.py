@@ -1,0 +1,53 @@
+"""Helpers shared by the tests: cache sizing and numpy reference pieces that
+are *not* the method (dense softmax attention, fp64 dequantised keys)."""
+import numpy as np
+
+D = 128
+TIER_BITS = {0: (8, 8), 1: (4, 4), 2: (2, 3)}
+
+
+def dense_attention(keys, values, q, scale):
+    """Plain softmax attention in fp64: keys [n,128], values [n,128], q [128]."""
+    keys = np.asarray(keys, np.float64)
+    values = np.asarray(values, np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros(D), -np.inf
+    lg = scale * (keys @ np.asarray(q, np.float64))
+    m = lg.max()
+    e = np.exp(lg - m)
+    return (e[:, None] * values).sum(0) / e.sum(), m + np.log(e.sum())
+
+
+def dequantize(r16, theta, s, tb, sb):
+    """fp64 key from codes: k[2j] = r s_j cos th_j, k[2j+1] = r s_j sin th_j,
+    th_c = -pi + c 2pi/2^tb, s = code/(2^sb - 1)."""
+    r = np.asarray(r16, np.uint16).view(np.float16).astype(np.float64)
+    N = 1 << tb
+    L = (1 << sb) - 1
+    th = -np.pi + np.asarray(theta, np.float64) * (2 * np.pi / N)
+    sv = np.asarray(s, np.float64) / L
+    k = np.zeros(np.shape(theta)[:-1] + (D,))
+    k[..., 0::2] = r[..., None] * sv * np.cos(th)
+    k[..., 1::2] = r[..., None] * sv * np.sin(th)
+    return k
+
+
+def upper_capacity(w, block16_max, extra_pages_per_row=3):
+    """Generous cache dimensions for a workload: every row may hold
+    ceil(ctx/P) + 3 pages (one partial page per tier)."""
+    P = w["P"]
+    rows = w["B"] * w["Hkv"]
+    per_row = -(-int(w["stride"]) // P) + extra_pages_per_row
+    pages = rows * per_row
+    return per_row, pages, pages * block16_max
+
+
+def kept_tokens(w, b, h):
+    """positions and tiers of the kept tokens of (b, h), in page order
+    (tier id ascending, then position ascending)."""
+    t = w["tiers"][b, h, : int(w["ctx_len"][b])]
+    out = []
+    for tau in (0, 1, 2):
+        pos = np.nonzero(t == tau)[0]
+        out.extend((int(p), tau) for p in pos)
+    return out
