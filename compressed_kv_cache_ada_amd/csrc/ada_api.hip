@@ -1,0 +1,526 @@
+// ada_api.hip -- host side of the C ABI declared in include/ada.h:
+// argument validation, workspace layout and kernel launches.  No memory is
+// allocated here; nothing throws across the boundary.
+#include <string.h>
+
+#include "ada_internal.h"
+
+using namespace ada;
+
+namespace {
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// carve typed arrays out of a workspace
+struct Carver {
+    char *base;
+    size_t off = 0;
+    explicit Carver(void *p) : base(static_cast<char *>(p)) {}
+    template <typename T>
+    T *take(size_t n) {
+        T *p = reinterpret_cast<T *>(base ? base + off : nullptr);
+        off = align_up(off + n * sizeof(T));
+        return p;
+    }
+};
+
+ada_status_t check_cfg(const ada_config_t *cfg) {
+    if (!cfg) return ADA_EINVAL;
+    if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads != 0)
+        return ADA_EINVAL;
+    if (cfg->head_dim != kD) return ADA_EUNSUPPORTED;
+    if (cfg->page_size != 16 && cfg->page_size != 32) return ADA_EUNSUPPORTED;
+    const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return ADA_EUNSUPPORTED;
+    if (cfg->decode_chunk_pages < 0) return ADA_EINVAL;
+    if (cfg->rdr_tier_mask > 7u) return ADA_EINVAL;
+    return ADA_OK;
+}
+
+ada_status_t check_cache(const ada_cache_t *c) {
+    if (!c) return ADA_EINVAL;
+    if (c->num_seqs <= 0 || c->max_pages_per_head <= 0 || c->page_capacity <= 0 || c->arena_capacity16 <= 0)
+        return ADA_EINVAL;
+    if (c->page_capacity > INT32_MAX || c->arena_capacity16 > (int64_t)UINT32_MAX) return ADA_EUNSUPPORTED;
+    if (!c->page_table || !c->num_pages || !c->open_page || !c->page_meta || !c->code_arena || !c->value_pool ||
+        !c->alloc || !c->status)
+        return ADA_EINVAL;
+    if (((uintptr_t)c->code_arena & 15) || ((uintptr_t)c->value_pool & 15) || ((uintptr_t)c->page_meta & 7))
+        return ADA_EINVAL;
+    return ADA_OK;
+}
+
+inline ada_status_t hip_status(hipError_t e) { return e == hipSuccess ? ADA_OK : ADA_EHIP; }
+
+int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp) {
+    const int tpg = 64 / cfg->page_size;
+    int cp = cfg->decode_chunk_pages;
+    if (cp <= 0) {
+        const int64_t units = (int64_t)B * cfg->num_kv_heads * maxp;
+        const int64_t target_wgs = 2048;
+        cp = (int)((units + target_wgs - 1) / target_wgs);
+    }
+    cp = (cp + tpg - 1) / tpg * tpg;
+    if (cp < tpg) cp = tpg;
+    return cp;
+}
+
+struct DecodeWs {
+    float *pm, *pl, *pacc;
+    size_t bytes;
+    int S, cp;
+};
+
+DecodeWs decode_layout(const ada_config_t *cfg, int32_t B, int32_t maxp, void *ws) {
+    DecodeWs d;
+    d.cp = decode_chunk_pages(cfg, B, maxp);
+    d.S = (maxp + d.cp - 1) / d.cp;
+    const size_t rows = (size_t)B * cfg->num_q_heads * d.S;
+    Carver c(ws);
+    d.pm = c.take<float>(rows);
+    d.pl = c.take<float>(rows);
+    d.pacc = c.take<float>(rows * kD);
+    d.bytes = c.off;
+    return d;
+}
+
+DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B, float scale,
+                         float *out, float *lse, const DecodeWs &w) {
+    DecodeLaunch a;
+    a.page_table = cache->page_table;
+    a.num_pages = cache->num_pages;
+    a.page_meta = cache->page_meta;
+    a.arena = cache->code_arena;
+    a.value_pool = cache->value_pool;
+    a.q = q;
+    a.pm = w.pm;
+    a.pl = w.pl;
+    a.pacc = w.pacc;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = cfg->num_q_heads;
+    a.Hkv = cfg->num_kv_heads;
+    a.P = cfg->page_size;
+    a.maxp = cache->max_pages_per_head;
+    a.chunk_pages = w.cp;
+    a.S = w.S;
+    a.scale = scale;
+    return a;
+}
+
+struct AppendWs {
+    int32_t *key_cnt, *key_c0, *key_done, *key_page_and_off;
+    int64_t *totals;
+    int32_t *dest_page, *dest_slot, *new_pages, *n_new;
+    size_t bytes;
+};
+
+AppendWs append_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, void *ws) {
+    AppendWs w;
+    const size_t nkeys = (size_t)cache->num_seqs * cfg->num_kv_heads * 3;
+    Carver c(ws);
+    w.key_cnt = c.take<int32_t>(nkeys);
+    w.key_c0 = c.take<int32_t>(nkeys);
+    w.key_done = c.take<int32_t>(nkeys);
+    w.key_page_and_off = c.take<int32_t>(2 * nkeys);
+    w.totals = c.take<int64_t>(2);
+    w.dest_page = c.take<int32_t>(n > 0 ? n : 1);
+    w.dest_slot = c.take<int32_t>(n > 0 ? n : 1);
+    w.new_pages = c.take<int32_t>(n > 0 ? n : 1);
+    w.n_new = c.take<int32_t>(2);
+    w.bytes = c.off;
+    return w;
+}
+
+struct PackWs {
+    int32_t *tile_counts, *row_counts, *row_base, *dest_page, *dest_slot, *range, *ctx;
+    int64_t *row_unit;
+    int n_tiles;
+    size_t bytes;
+};
+
+PackWs pack_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
+    PackWs w;
+    const size_t rows = (size_t)B * cfg->num_kv_heads;
+    w.n_tiles = (int)((stride + 1023) / 1024);
+    Carver c(ws);
+    w.tile_counts = c.take<int32_t>(rows * w.n_tiles * 3);
+    w.row_counts = c.take<int32_t>(rows * 3);
+    w.row_base = c.take<int32_t>(rows * 3);
+    w.row_unit = c.take<int64_t>(rows * 3);
+    w.dest_page = c.take<int32_t>(rows * stride);
+    w.dest_slot = c.take<int32_t>(rows * stride);
+    w.range = c.take<int32_t>(2);
+    w.ctx = c.take<int32_t>(B);
+    w.bytes = c.off;
+    return w;
+}
+
+struct RdrWs {
+    unsigned long long *hist, *prefix;
+    long long *above;
+    int32_t *all_fit, *ctx;
+    int64_t *budget;
+    uint8_t *tie_sel;
+    size_t bytes;
+};
+
+RdrWs rdr_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
+    RdrWs w;
+    Carver c(ws);
+    w.hist = c.take<unsigned long long>((size_t)B * 256);
+    w.prefix = c.take<unsigned long long>(B);
+    w.above = c.take<long long>(B);
+    w.all_fit = c.take<int32_t>(B);
+    w.ctx = c.take<int32_t>(B);
+    w.budget = c.take<int64_t>(B);
+    w.tie_sel = c.take<uint8_t>((size_t)B * cfg->num_kv_heads * stride);
+    w.bytes = c.off;
+    return w;
+}
+
+// RDR upgrade steps of the enabled tiers (rate order); EUNSUPPORTED when the
+// savings per byte do not strictly decrease.
+ada_status_t rdr_steps(uint32_t mask, int *n_steps, int32_t *step_tier, int64_t *dR, double *c) {
+    int ids[3], n = 0;
+    for (int t = 0; t < 3; ++t)
+        if (mask & (1u << t)) ids[n++] = t;
+    auto rate = [](int t) { return (int64_t)(2 + 8 * (tier_tb(t) + tier_sb(t)) + 256); };
+    for (int i = 1; i < n; ++i)   // insertion sort by rate
+        for (int j = i; j > 0 && rate(ids[j]) < rate(ids[j - 1]); --j) {
+            const int tmp = ids[j];
+            ids[j] = ids[j - 1];
+            ids[j - 1] = tmp;
+        }
+    int64_t prevR = 0;
+    double prevD = 1.0;
+    for (int i = 0; i < n; ++i) {
+        const int t = ids[i];
+        const int64_t R = rate(t);
+        const double D = ldexp(1.0, -(tier_tb(t) + tier_sb(t)));
+        if (R <= prevR || D >= prevD) return ADA_EUNSUPPORTED;
+        dR[i] = R - prevR;
+        c[i] = (prevD - D) / (double)dR[i];
+        if (i > 0 && !(c[i] < c[i - 1])) return ADA_EUNSUPPORTED;
+        step_tier[i] = t;
+        prevR = R;
+        prevD = D;
+    }
+    *n_steps = n;
+    return n ? ADA_OK : ADA_EINVAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ada_status_str(ada_status_t s) {
+    switch (s) {
+        case ADA_OK: return "ADA_OK";
+        case ADA_EINVAL: return "ADA_EINVAL: invalid argument or input";
+        case ADA_ENOSPC: return "ADA_ENOSPC: cache capacity exceeded";
+        case ADA_EUNSUPPORTED: return "ADA_EUNSUPPORTED: unsupported shape";
+        case ADA_EHIP: return "ADA_EHIP: HIP runtime error";
+        case ADA_EINTERNAL: return "ADA_EINTERNAL: undecidable code";
+        default: return "ADA_UNKNOWN";
+    }
+}
+
+int64_t ada_block_bytes(int32_t tier, int32_t page_size) {
+    if (tier < 0 || tier > 2 || (page_size != 16 && page_size != 32)) return -1;
+    return (int64_t)block16(tier, page_size) * 16;
+}
+
+size_t ada_lut_floats(const ada_config_t *cfg) {
+    (void)cfg;
+    return 64 * (256 + 16 + 4);
+}
+
+ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cache))) return st;
+    return hip_status(launch_cache_init(cache->num_seqs * cfg->num_kv_heads, cache->num_pages, cache->open_page,
+                                        cache->alloc, cache->status, (hipStream_t)stream));
+}
+
+ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, float *lut, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (B < 0 || (B > 0 && (!q || !lut))) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    return hip_status(launch_build_lut(q, B * cfg->num_q_heads, lut, (hipStream_t)stream));
+}
+
+ada_status_t ada_decode_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0) return ADA_EINVAL;
+    *bytes = decode_layout(cfg, B, cache->max_pages_per_head, nullptr).bytes;
+    return ADA_OK;
+}
+
+static ada_status_t decode_common(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *ws,
+                                  size_t ws_bytes, DecodeWs *w) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cache))) return st;
+    if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
+    *w = decode_layout(cfg, B, cache->max_pages_per_head, ws);
+    if (B > 0 && (!ws || ws_bytes < w->bytes)) return ADA_EINVAL;
+    return ADA_OK;
+}
+
+ada_status_t ada_decode_partials(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                                 float scale, void *ws, size_t ws_bytes, void *stream) {
+    DecodeWs w;
+    ada_status_t st = decode_common(cfg, cache, B, ws, ws_bytes, &w);
+    if (st) return st;
+    if (B == 0) return ADA_OK;
+    if (!q) return ADA_EINVAL;
+    DecodeLaunch a = make_decode(cfg, cache, q, B, scale, nullptr, nullptr, w);
+    return hip_status(launch_decode_partials(a, (hipStream_t)stream));
+}
+
+ada_status_t ada_decode_reduce(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, float *out, float *lse,
+                               void *ws, size_t ws_bytes, void *stream) {
+    DecodeWs w;
+    ada_status_t st = decode_common(cfg, cache, B, ws, ws_bytes, &w);
+    if (st) return st;
+    if (B == 0) return ADA_OK;
+    if (!out) return ADA_EINVAL;
+    DecodeLaunch a = make_decode(cfg, cache, nullptr, B, 0.f, out, lse, w);
+    return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
+}
+
+ada_status_t ada_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B, float scale,
+                        float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    DecodeWs w;
+    ada_status_t st = decode_common(cfg, cache, B, ws, ws_bytes, &w);
+    if (st) return st;
+    if (B == 0) return ADA_OK;
+    if (!q || !out) return ADA_EINVAL;
+    DecodeLaunch a = make_decode(cfg, cache, q, B, scale, out, lse, w);
+    hipError_t e = launch_decode_partials(a, (hipStream_t)stream);
+    if (e != hipSuccess) return ADA_EHIP;
+    return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
+}
+
+ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!cache || !bytes || n < 0 || cache->num_seqs <= 0) return ADA_EINVAL;
+    *bytes = append_layout(cfg, cache, n, nullptr).bytes;
+    return ADA_OK;
+}
+
+ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, const int32_t *seq,
+                               const int32_t *kv_head, const uint8_t *tier, const float *keys, const uint16_t *values,
+                               void *ws, size_t ws_bytes, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cache))) return st;
+    if (n < 0) return ADA_EINVAL;
+    if (n == 0) return ADA_OK;
+    if (!seq || !kv_head || !tier || !keys || !values) return ADA_EINVAL;
+    AppendWs w = append_layout(cfg, cache, n, ws);
+    if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
+    AppendLaunch a;
+    a.n = n;
+    a.Hkv = cfg->num_kv_heads;
+    a.P = cfg->page_size;
+    a.num_seqs = cache->num_seqs;
+    a.maxp = cache->max_pages_per_head;
+    a.page_capacity = cache->page_capacity;
+    a.arena_capacity16 = cache->arena_capacity16;
+    a.seq = seq;
+    a.head = kv_head;
+    a.tier = tier;
+    a.keys = keys;
+    a.values = values;
+    a.page_table = cache->page_table;
+    a.num_pages = cache->num_pages;
+    a.open_page = cache->open_page;
+    a.page_meta = cache->page_meta;
+    a.arena = cache->code_arena;
+    a.value_pool = cache->value_pool;
+    a.alloc = cache->alloc;
+    a.status = cache->status;
+    a.key_cnt = w.key_cnt;
+    a.key_c0 = w.key_c0;
+    a.key_done = w.key_done;
+    a.key_page = w.key_page_and_off;
+    a.totals = w.totals;
+    a.dest_page = w.dest_page;
+    a.dest_slot = w.dest_slot;
+    a.new_pages = w.new_pages;
+    a.n_new = w.n_new;
+    return hip_status(launch_append(a, (hipStream_t)stream));
+}
+
+ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_stride, size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!bytes || B < 0 || ctx_stride < 0) return ADA_EINVAL;
+    *bytes = rdr_layout(cfg, B, ctx_stride, nullptr).bytes;
+    return ADA_OK;
+}
+
+ada_status_t ada_rdr_assign(const ada_config_t *cfg, int32_t B, const int32_t *ctx_len, int64_t ctx_stride,
+                            const float *utility, const int64_t *budget, int8_t *tier_out, int32_t *status, void *ws,
+                            size_t ws_bytes, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (B < 0 || ctx_stride <= 0) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!ctx_len || !utility || !budget || !tier_out || !status) return ADA_EINVAL;
+    if ((int64_t)cfg->num_kv_heads * ctx_stride > INT32_MAX) return ADA_EUNSUPPORTED;
+    for (int b = 0; b < B; ++b)
+        if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride || budget[b] < 0) return ADA_EINVAL;
+    RdrLaunch a;
+    const uint32_t mask = cfg->rdr_tier_mask ? cfg->rdr_tier_mask : 7u;
+    if ((st = rdr_steps(mask, &a.n_steps, a.step_tier, a.dR, a.c))) return st;
+    RdrWs w = rdr_layout(cfg, B, ctx_stride, ws);
+    if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(w.ctx, ctx_len, sizeof(int32_t) * B, hipMemcpyHostToDevice, s) != hipSuccess) return ADA_EHIP;
+    if (hipMemcpyAsync(w.budget, budget, sizeof(int64_t) * B, hipMemcpyHostToDevice, s) != hipSuccess)
+        return ADA_EHIP;
+    a.B = B;
+    a.Hkv = cfg->num_kv_heads;
+    a.stride = ctx_stride;
+    a.ctx_len_dev = w.ctx;
+    a.budget_dev = w.budget;
+    a.utility = utility;
+    a.tier_out = tier_out;
+    a.status = status;
+    a.hist = w.hist;
+    a.prefix = w.prefix;
+    a.above = w.above;
+    a.all_fit = w.all_fit;
+    a.tie_sel = w.tie_sel;
+    return hip_status(launch_rdr(a, s));
+}
+
+ada_status_t ada_pack_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, int64_t ctx_stride,
+                                size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!cache || !bytes || B < 0 || ctx_stride < 0) return ADA_EINVAL;
+    *bytes = pack_layout(cfg, B, ctx_stride, nullptr).bytes;
+    return ADA_OK;
+}
+
+ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, const int32_t *ctx_len,
+                      int64_t ctx_stride, const int8_t *tier, const float *keys, const uint16_t *values, void *ws,
+                      size_t ws_bytes, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cache))) return st;
+    if (B < 0 || B > cache->num_seqs || ctx_stride <= 0) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!ctx_len || !tier || !keys || !values) return ADA_EINVAL;
+    if (ctx_stride > INT32_MAX) return ADA_EUNSUPPORTED;
+    for (int b = 0; b < B; ++b)
+        if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride) return ADA_EINVAL;
+    PackWs w = pack_layout(cfg, B, ctx_stride, ws);
+    if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(w.ctx, ctx_len, sizeof(int32_t) * B, hipMemcpyHostToDevice, s) != hipSuccess) return ADA_EHIP;
+    PackLaunch a;
+    a.B = B;
+    a.Hkv = cfg->num_kv_heads;
+    a.P = cfg->page_size;
+    a.maxp = cache->max_pages_per_head;
+    a.stride = ctx_stride;
+    a.page_capacity = cache->page_capacity;
+    a.arena_capacity16 = cache->arena_capacity16;
+    a.ctx_len_dev = w.ctx;
+    a.tier = tier;
+    a.keys = keys;
+    a.values = values;
+    a.page_table = cache->page_table;
+    a.num_pages = cache->num_pages;
+    a.open_page = cache->open_page;
+    a.page_meta = cache->page_meta;
+    a.arena = cache->code_arena;
+    a.value_pool = cache->value_pool;
+    a.alloc = cache->alloc;
+    a.status = cache->status;
+    a.tile_counts = w.tile_counts;
+    a.row_counts = w.row_counts;
+    a.row_base = w.row_base;
+    a.row_unit = w.row_unit;
+    a.dest_page = w.dest_page;
+    a.dest_slot = w.dest_slot;
+    a.new_pages = nullptr;
+    a.n_new = w.range;
+    a.n_tiles = w.n_tiles;
+    return hip_status(launch_pack(a, s));
+}
+
+ada_status_t ada_read_status(const int32_t *status, void *stream) {
+    if (!status) return ADA_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return ADA_EHIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return ADA_EHIP;
+    const int32_t zero = 0;
+    if (hipMemcpy(const_cast<int32_t *>(status), &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+        return ADA_EHIP;
+    return (ada_status_t)v;
+}
+
+ada_status_t ada_dense_workspace(const ada_config_t *cfg, int32_t B, int32_t max_pages_per_head, size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!bytes || B < 0 || max_pages_per_head <= 0) return ADA_EINVAL;
+    *bytes = decode_layout(cfg, B, max_pages_per_head, nullptr).bytes;
+    return ADA_OK;
+}
+
+ada_status_t ada_dense_decode(const ada_config_t *cfg, int32_t B, int32_t max_pages_per_head,
+                              const int32_t *page_table, const int32_t *ctx_len, const uint16_t *k_pool,
+                              const uint16_t *v_pool, const float *q, float scale, float *out, float *lse, void *ws,
+                              size_t ws_bytes, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (B < 0 || max_pages_per_head <= 0) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!page_table || !ctx_len || !k_pool || !v_pool || !q || !out) return ADA_EINVAL;
+    DecodeWs w = decode_layout(cfg, B, max_pages_per_head, ws);
+    if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
+    DenseLaunch a;
+    a.page_table = page_table;
+    a.ctx_len = ctx_len;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.q = q;
+    a.pm = w.pm;
+    a.pl = w.pl;
+    a.pacc = w.pacc;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = cfg->num_q_heads;
+    a.Hkv = cfg->num_kv_heads;
+    a.P = cfg->page_size;
+    a.maxp = max_pages_per_head;
+    a.chunk_pages = w.cp;
+    a.S = w.S;
+    a.scale = scale;
+    hipError_t e = launch_dense_partials(a, (hipStream_t)stream);
+    if (e != hipSuccess) return ADA_EHIP;
+    return hip_status(launch_dense_reduce(a, (hipStream_t)stream));
+}
+
+ada_status_t ada_probe_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (!src || !dst || (bytes & 15)) return ADA_EINVAL;
+    if (bytes == 0) return ADA_OK;
+    return hip_status(launch_probe_copy(src, dst, bytes, (hipStream_t)stream));
+}
+
+uint16_t ada_host_f64_to_f16(double x) { return host_f64_to_f16(x); }
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// ada_internal.h -- shared definitions of the HIP library (not installed).
+// Layout rules follow include/ada.h; the method is the angle-domain key
+// representation of "SPHERICAL KV" (arXiv 2605.18856, Abstract).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ada.h"
+
+namespace ada {
+
+constexpr int kD = 128;       // head dimension
+constexpr int kPairs = 64;    // 2-D pairs per key
+
+// Tier table in id order: angle bits, magnitude bits.
+__host__ __device__ constexpr int tier_tb(int t) { return t == 0 ? 8 : (t == 1 ? 4 : 2); }
+__host__ __device__ constexpr int tier_sb(int t) { return t == 0 ? 8 : (t == 1 ? 4 : 3); }
+// code block of one page in 16-byte units: P * (2 + 8 tb + 8 sb) / 16
+__host__ __device__ constexpr int block16(int t, int P) { return P * (2 + 8 * tier_tb(t) + 8 * tier_sb(t)) / 16; }
+
+// fp16 bits -> float
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// One angle-LUT entry: q-pair projected on the grid direction (cos, sin).
+// Shared by the stand-alone LUT builder and the decode's on-chip staging so
+// that both produce identical values.
+__device__ __forceinline__ float lut_entry(float qx, float qy, float2 cs) {
+    return fmaf(qx, cs.x, qy * cs.y);
+}
+
+// cos / sin of the 8-bit angle grid point c: th = -pi + c * 2pi / 256.
+// The 4- and 2-bit grids are the sub-grids c = 16 c4 and c = 64 c2.
+__device__ __forceinline__ float2 grid_dir(int c) {
+    float s, co;
+    sincospif(-1.0f + (float)c * (1.0f / 128.0f), &s, &co);
+    return make_float2(co, s);
+}
+
+// ---- launchers (defined in the .hip files; called by ada_api.cpp) ------
+struct DecodeLaunch {
+    const int32_t *page_table;
+    const int32_t *num_pages;
+    const ada_page_meta_t *page_meta;
+    const uint8_t *arena;
+    const uint16_t *value_pool;
+    const float *q;
+    float *pm, *pl, *pacc;     // split-K partials
+    float *out, *lse;
+    int32_t B, Hq, Hkv, P, maxp, chunk_pages, S;
+    float scale;
+};
+hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s);
+hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, hipStream_t s);
+
+struct DenseLaunch {
+    const int32_t *page_table;
+    const int32_t *ctx_len;
+    const uint16_t *k_pool, *v_pool;
+    const float *q;
+    float *pm, *pl, *pacc;
+    float *out, *lse;
+    int32_t B, Hq, Hkv, P, maxp, chunk_pages, S;
+    float scale;
+};
+hipError_t launch_dense_partials(const DenseLaunch &a, hipStream_t s);
+hipError_t launch_dense_reduce(const DenseLaunch &a, hipStream_t s);
+
+// Encoder / page writer shared by pack and append.
+struct EncodeLaunch {
+    const float *keys;          // [n][128]
+    const uint16_t *values;     // [n][128]
+    int64_t n;
+    const int32_t *dest_page;   // [n], -1 = skip
+    const int32_t *dest_slot;   // [n]
+    const ada_page_meta_t *page_meta;
+    uint8_t *arena;
+    uint16_t *value_pool;
+    int32_t P;
+    int32_t *status;
+};
+hipError_t launch_encode_write(const EncodeLaunch &a, hipStream_t s);
+// Zero the code blocks and value pages of new pages listed as
+// (page id) in pages[0..*n_pages), upper bound max_n.
+hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64_t max_n,
+                             const ada_page_meta_t *page_meta, uint8_t *arena, uint16_t *value_pool,
+                             int32_t P, const int32_t *status, hipStream_t s);
+// Host-callable copies of device helpers, for CPU tests of the library.
+uint16_t host_f64_to_f16(double x);
+
+struct PackLaunch {
+    int32_t B, Hkv, P, maxp;
+    int64_t stride, page_capacity, arena_capacity16;
+    const int32_t *ctx_len_dev;     // [B]
+    const int8_t *tier;             // [B][Hkv][stride]
+    const float *keys;
+    const uint16_t *values;
+    int32_t *page_table, *num_pages, *open_page;
+    ada_page_meta_t *page_meta;
+    uint8_t *arena;
+    uint16_t *value_pool;
+    int64_t *alloc;
+    int32_t *status;
+    // workspace
+    int32_t *tile_counts;   // [rows][n_tiles][3]
+    int32_t *row_counts;    // [rows][3]
+    int32_t *row_base;      // [rows][3] first page id of (row, tier)
+    int64_t *row_unit;      // [rows][3] first code unit of (row, tier)
+    int32_t *dest_page, *dest_slot;   // [B*Hkv*stride]
+    int32_t *new_pages;     // [page upper bound] list of allocated pages
+    int32_t *n_new;         // [1]
+    int32_t n_tiles;
+};
+hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
+
+struct AppendLaunch {
+    int32_t n, Hkv, P, num_seqs, maxp;
+    int64_t page_capacity, arena_capacity16;
+    const int32_t *seq, *head;
+    const uint8_t *tier;
+    const float *keys;
+    const uint16_t *values;
+    int32_t *page_table, *num_pages, *open_page;
+    ada_page_meta_t *page_meta;
+    uint8_t *arena;
+    uint16_t *value_pool;
+    int64_t *alloc;
+    int32_t *status;
+    // workspace
+    int32_t *key_cnt;    // [keys] requests per (row, tier)
+    int32_t *key_c0;     // [keys] initial fill of the open page
+    int32_t *key_done;   // [keys] requests already placed
+    int32_t *key_page;   // [keys] current page
+    int64_t *totals;     // [2] pages, units needed
+    int32_t *dest_page, *dest_slot;   // [n]
+    int32_t *new_pages;  // [n]
+    int32_t *n_new;      // [1]
+};
+hipError_t launch_append(const AppendLaunch &a, hipStream_t s);
+
+struct RdrLaunch {
+    int32_t B, Hkv, n_steps;
+    int64_t stride;
+    const int32_t *ctx_len_dev;
+    const int64_t *budget_dev;
+    const float *utility;
+    int8_t *tier_out;
+    int32_t *status;
+    int32_t step_tier[3];
+    int64_t dR[3];
+    double c[3];
+    // workspace
+    unsigned long long *hist;   // [B][256]
+    unsigned long long *prefix; // [B]
+    long long *above;           // [B]
+    int32_t *all_fit;           // [B]
+    uint8_t *tie_sel;           // [B][Hkv][stride]
+};
+hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s);
+
+hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
+                             int32_t *status, hipStream_t s);
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+}  // namespace ada

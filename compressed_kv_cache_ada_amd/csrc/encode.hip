@@ -1,0 +1,799 @@
+// encode.hip -- key encoder and page writers for gfx950: bulk pack from a
+// tier map, sequential-semantics append, page zeroing, cache reset.
+// Compiled with -ffp-contract=off: every rounding below is the one written.
+//
+// Method: "SPHERICAL KV" (arXiv 2605.18856), Abstract: keys are stored as a
+// scalar radius plus compact angle codes in tier-homogeneous pages with
+// lightweight metadata.  Code decisions are exact: a code is the nearest
+// grid point of the real-valued angle / magnitude, not of a rounded estimate.
+//
+// Encoder (one wavefront per key, lane j = pair j):
+//   e_j = x_j^2 + y_j^2 (squares of fp32 values are exact in fp64),
+//   R2  = pairwise tree over the wavefront, strides 32,16,...,1,
+//   r   = sqrt(R2) (correctly rounded fp64), stored as fp16 (RNE, saturating),
+//   magnitude code: exact test 4 L^2 e >= (2m+1)^2 R2 with TwoProduct (fma)
+//                   around an fp64 estimate,
+//   angle code:     fp64 atan2 estimate accepted outside a 2^-30 band around a
+//                   rounding boundary; inside it the side of the boundary
+//                   direction beta is decided by the sign of
+//                   y cos(beta) - x sin(beta) in double-double arithmetic
+//                   (cos/sin of beta from a double-double Taylor series);
+//                   2-bit codes use exact comparisons on the diagonals.
+#include "ada_internal.h"
+
+namespace ada {
+namespace {
+
+// ---------------------------------------------------------------- fp16
+__host__ __device__ inline uint16_t f64_to_f16_rne_sat(double x) {
+    uint64_t u;
+    __builtin_memcpy(&u, &x, 8);
+    const uint16_t sign = (uint16_t)((u >> 63) << 15);
+    u &= 0x7FFFFFFFFFFFFFFFull;
+    if (u == 0) return sign;
+    if (u >= 0x7FF0000000000000ull) return (uint16_t)(sign | 0x7BFF);   // inf / nan: saturate
+    const int e = (int)(u >> 52) - 1023;                               // x in [2^e, 2^(e+1))
+    if (e > 15) return (uint16_t)(sign | 0x7BFF);
+    if (e < -25) return sign;                                          // below half the smallest subnormal
+    const uint64_t m = (u & ((1ull << 52) - 1)) | (1ull << 52);       // x = m 2^(e-52)
+    const int qexp = (e >= -14) ? e - 10 : -24;                        // fp16 spacing 2^qexp
+    const int shift = 52 + qexp - e;                                   // 42..53
+    uint64_t n = m >> shift;
+    const uint64_t rem = m & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (n & 1))) ++n;
+    if (e >= -14) {
+        int ee = e;
+        if (n == 2048) { n = 1024; ++ee; }
+        if (ee > 15) return (uint16_t)(sign | 0x7BFF);
+        return (uint16_t)(sign | ((ee + 15) << 10) | (uint16_t)(n - 1024));
+    }
+    return (uint16_t)(sign | (uint16_t)n);   // subnormal (n == 1024 is the smallest normal)
+}
+
+// ------------------------------------------------------- double-double
+struct dd {
+    double hi, lo;
+};
+__device__ inline dd two_sum(double a, double b) {
+    const double s = a + b;
+    const double bb = s - a;
+    return {s, (a - (s - bb)) + (b - bb)};
+}
+__device__ inline dd quick_two_sum(double a, double b) {
+    const double s = a + b;
+    return {s, b - (s - a)};
+}
+__device__ inline dd two_prod(double a, double b) {
+    const double p = a * b;
+    return {p, __builtin_fma(a, b, -p)};
+}
+__device__ inline dd dd_add(dd a, dd b) {
+    dd s = two_sum(a.hi, b.hi);
+    const dd t = two_sum(a.lo, b.lo);
+    s.lo += t.hi;
+    s = quick_two_sum(s.hi, s.lo);
+    s.lo += t.lo;
+    return quick_two_sum(s.hi, s.lo);
+}
+__device__ inline dd dd_mul(dd a, dd b) {
+    dd p = two_prod(a.hi, b.hi);
+    p.lo += a.hi * b.lo + a.lo * b.hi;
+    return quick_two_sum(p.hi, p.lo);
+}
+__device__ inline dd dd_mul_d(dd a, double b) {
+    dd p = two_prod(a.hi, b);
+    p.lo += a.lo * b;
+    return quick_two_sum(p.hi, p.lo);
+}
+__device__ inline dd dd_div_d(dd a, double b) {
+    const double q1 = a.hi / b;
+    const dd p = two_prod(q1, b);
+    const double r = ((a.hi - p.hi) - p.lo) + a.lo;
+    return quick_two_sum(q1, r / b);
+}
+__device__ inline dd dd_neg(dd a) { return {-a.hi, -a.lo}; }
+
+// sin and cos of pi * n / N for 0 <= n <= N/4 (angle in [0, pi/4]) by Taylor
+// series in double-double; 16 terms leave a truncation error below 2^-110.
+__device__ void dd_sincos_pi_frac(int n, int N, dd *s_out, dd *c_out) {
+    const dd pi = {3.141592653589793116e+00, 1.224646799147353207e-16};
+    dd x = dd_mul_d(pi, (double)n);
+    x.hi = ldexp(x.hi, -__builtin_ctz((unsigned)N));
+    x.lo = ldexp(x.lo, -__builtin_ctz((unsigned)N));
+    const dd x2n = dd_neg(dd_mul(x, x));
+    dd ts = x, ss = x;
+    dd tc = {1.0, 0.0}, sc = {1.0, 0.0};
+    for (int k = 1; k <= 16; ++k) {
+        ts = dd_div_d(dd_mul(ts, x2n), (double)((2 * k) * (2 * k + 1)));
+        ss = dd_add(ss, ts);
+        tc = dd_div_d(dd_mul(tc, x2n), (double)((2 * k - 1) * (2 * k)));
+        sc = dd_add(sc, tc);
+    }
+    *s_out = ss;
+    *c_out = sc;
+}
+
+// direction of the boundary between angle codes m and m+1 (N = 2^tb):
+// beta = -pi + (m + 1/2) 2pi / N = pi (2m + 1 - N) / N
+__device__ void boundary_dir(int m, int N, dd *c, dd *s) {
+    int n = 2 * m + 1 - N;
+    const double sgn_s = n < 0 ? -1.0 : 1.0;
+    int an = n < 0 ? -n : n;          // angle pi*an/N in (0, pi)
+    double sgn_c = 1.0;
+    if (2 * an > N) {                 // beyond pi/2: reflect to pi - a
+        an = N - an;
+        sgn_c = -1.0;
+    }
+    bool swap = false;
+    if (4 * an > N) {                 // beyond pi/4: use pi/2 - a
+        an = N / 2 - an;
+        swap = true;
+    }
+    dd s0, c0;
+    dd_sincos_pi_frac(an, N, &s0, &c0);
+    dd cc = swap ? s0 : c0, ss = swap ? c0 : s0;
+    cc.hi *= sgn_c; cc.lo *= sgn_c;
+    ss.hi *= sgn_s; ss.lo *= sgn_s;
+    *c = cc;
+    *s = ss;
+}
+
+__device__ int angle_code(double x, double y, int tb, int *undecidable) {
+    const int N = 1 << tb;
+    if (x == 0.0 && y == 0.0) return N / 2;
+    const double pi = 3.141592653589793116e+00;
+    const double t = (atan2(y, x) + pi) / (2.0 * pi) * (double)N;
+    const double fl = floor(t);
+    if (fabs((t - fl) - 0.5) > 0x1p-30) {
+        const int c = (int)floor(t + 0.5);
+        return ((c % N) + N) % N;
+    }
+    const int m = (int)fl;   // boundary between codes m and m+1
+    int c;
+    if (tb == 2) {
+        // boundary directions are the diagonals: decide with exact sums
+        double v;
+        switch (m & 3) {
+            case 0: v = x - y; break;     // beta = -3pi/4
+            case 1: v = x + y; break;     // beta = -pi/4
+            case 2: v = y - x; break;     // beta =  pi/4
+            default: v = -x - y; break;   // beta =  3pi/4
+        }
+        c = (v >= 0.0) ? m + 1 : m;       // exact tie: half up
+    } else {
+        dd cb, sb;
+        boundary_dir(m, N, &cb, &sb);
+        const dd v = dd_add(dd_mul_d(cb, y), dd_neg(dd_mul_d(sb, x)));
+        if (fabs(v.hi) <= 0x1p-90 * (fabs(x) + fabs(y))) *undecidable = 1;
+        c = (v.hi > 0.0) ? m + 1 : m;
+    }
+    return ((c % N) + N) % N;
+}
+
+// exact: 4 L^2 e >= (2m+1)^2 R2
+__device__ inline bool magnitude_reaches(double e, double R2, int L, int m) {
+    const double A = 4.0 * (double)L * (double)L;
+    const double Bc = (double)(2 * m + 1) * (double)(2 * m + 1);
+    const dd p1 = two_prod(A, e), p2 = two_prod(Bc, R2);
+    return (p1.hi > p2.hi) || (p1.hi == p2.hi && p1.lo >= p2.lo);
+}
+
+__device__ int magnitude_code(double e, double R2, int sb) {
+    const int L = (1 << sb) - 1;
+    if (R2 == 0.0) return 0;
+    int c = (int)floor((double)L * sqrt(e / R2) + 0.5);
+    c = c < 0 ? 0 : (c > L ? L : c);
+    while (c > 0 && !magnitude_reaches(e, R2, L, c - 1)) --c;
+    while (c < L && magnitude_reaches(e, R2, L, c)) ++c;
+    return c;
+}
+
+__device__ inline void set_status(int32_t *status, int code) { atomicCAS(status, 0, code); }
+
+__device__ inline int read_status(const int32_t *status) {
+    return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------ encode + write one key
+// One wavefront per item; 4 wavefronts per work-group; grid-stride.
+__global__ __launch_bounds__(256) void encode_write_kernel(EncodeLaunch a) {
+    __shared__ uint32_t words[4][2][16];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (read_status(a.status) != 0) return;
+    const int P = a.P;
+    for (int64_t item = (int64_t)blockIdx.x * 4 + wv; item < a.n; item += (int64_t)gridDim.x * 4) {
+        const int page = a.dest_page[item];
+        if (page < 0) continue;
+        const int slot = a.dest_slot[item];
+        const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + page);
+        const int tier = meta.x & 0xFF;
+        const int tb = tier_tb(tier), sb = tier_sb(tier);
+        const float2 kk = *reinterpret_cast<const float2 *>(a.keys + item * kD + 2 * lane);
+        const double x = kk.x, y = kk.y;
+        const double xx = x * x;
+        const double yy = y * y;
+        const double e = xx + yy;
+        double t = e;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+            const double o = __shfl_down(t, s, 64);
+            if (lane < s) t = t + o;
+        }
+        const double R2 = __shfl(t, 0, 64);
+        const double r = sqrt(R2);
+        int und = 0;
+        const uint32_t sc = (uint32_t)magnitude_code(e, R2, sb);
+        const uint32_t tc = (uint32_t)angle_code(x, y, tb, &und);
+        if (__any(und)) {
+            if (lane == 0) set_status(a.status, ADA_EINTERNAL);
+            continue;
+        }
+        uint32_t *wt = words[wv][0], *ws = words[wv][1];
+        if (lane < 16) {
+            wt[lane] = 0u;
+            ws[lane] = 0u;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        {
+            const int bit = lane * tb;
+            atomicOr(&wt[bit >> 5], tc << (bit & 31));
+            const int bs = lane * sb, sh = bs & 31;
+            atomicOr(&ws[bs >> 5], sc << sh);
+            if (sh + sb > 32) atomicOr(&ws[(bs >> 5) + 1], sc >> (32 - sh));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint8_t *blk = a.arena + (size_t)meta.y * 16;
+        const int nwt = 2 * tb, nws = 2 * sb;             // 32-bit words per component
+        if (lane < nwt) {
+            const int w = lane;
+            uint8_t *dst = blk + 2 * P + (w >> 2) * 16 * P + slot * 16 + (w & 3) * 4;
+            *reinterpret_cast<uint32_t *>(dst) = wt[w];
+        } else if (lane >= 32 && lane < 32 + nws) {
+            const int w = lane - 32;
+            const int nfull = (8 * sb) / 16;
+            uint8_t *sbase = blk + 2 * P + 8 * tb * P;
+            uint8_t *dst = (w >> 2) < nfull ? sbase + (w >> 2) * 16 * P + slot * 16 + (w & 3) * 4
+                                            : sbase + nfull * 16 * P + slot * 8 + (w - 4 * nfull) * 4;
+            *reinterpret_cast<uint32_t *>(dst) = ws[w];
+        }
+        if (lane == 0) *reinterpret_cast<uint16_t *>(blk + 2 * slot) = f64_to_f16_rne_sat(r);
+        const uint32_t vv = *reinterpret_cast<const uint32_t *>(a.values + item * kD + 2 * lane);
+        uint16_t *vp = a.value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);
+        vp[(2 * lane) * 8] = (uint16_t)(vv & 0xFFFF);
+        vp[(2 * lane + 1) * 8] = (uint16_t)(vv >> 16);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ------------------------------------------------------- zero new pages
+// pages: explicit list, or (when list == nullptr) the range [first, first+n)
+__global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, const int32_t *first_and_n,
+                                                         const ada_page_meta_t *page_meta, uint8_t *arena,
+                                                         uint16_t *value_pool, int32_t P, const int32_t *status) {
+    if (read_status(status) != 0) return;
+    const int n = first_and_n[1];
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+        const int page = list ? list[i] : first_and_n[0] + i;
+        const uint2 meta = *reinterpret_cast<const uint2 *>(page_meta + page);
+        const int tier = meta.x & 0xFF;
+        uint4 *cb = reinterpret_cast<uint4 *>(arena + (size_t)meta.y * 16);
+        const int nb = block16(tier, P);
+        for (int k = threadIdx.x; k < nb; k += blockDim.x) cb[k] = make_uint4(0u, 0u, 0u, 0u);
+        uint4 *vp = reinterpret_cast<uint4 *>(value_pool + (size_t)page * P * kD);
+        for (int k = threadIdx.x; k < P * kD / 8; k += blockDim.x) vp[k] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// ------------------------------------------------------------- pack
+constexpr int kTile = 1024;
+
+// per (row, tile): validate tiers, check kept keys are finite, count per tier
+__global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
+    __shared__ int cnt[3];
+    const int tile = blockIdx.x, row = blockIdx.y;
+    const int b = row / a.Hkv;
+    const int ctx = a.ctx_len_dev[b];
+    if (threadIdx.x < 3) cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t rbase = (int64_t)row * a.stride;
+    const int t0 = tile * kTile;
+    for (int i = threadIdx.x; i < kTile; i += 256) {
+        const int t = t0 + i;
+        if (t >= ctx) break;
+        const int tv = a.tier[rbase + t];
+        if (tv < -1 || tv > 2) set_status(a.status, ADA_EINVAL);
+        else if (tv >= 0) atomicAdd(&cnt[tv], 1);
+    }
+    // finiteness of kept keys: one wavefront per position
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    bool bad = false;
+    for (int i = wv; i < kTile; i += 4) {
+        const int t = t0 + i;
+        if (t >= ctx) break;
+        if (a.tier[rbase + t] < 0) continue;
+        const float2 kk = *reinterpret_cast<const float2 *>(a.keys + (rbase + t) * kD + 2 * lane);
+        bad |= !(isfinite(kk.x) && isfinite(kk.y));
+    }
+    if (__any(bad) && lane == 0) set_status(a.status, ADA_EINVAL);
+    __syncthreads();
+    if (threadIdx.x < 3) a.tile_counts[((size_t)row * a.n_tiles + tile) * 3 + threadIdx.x] = cnt[threadIdx.x];
+}
+
+// per row: exclusive scan of tile counts (in place) and row totals
+__global__ __launch_bounds__(256) void pack_rowscan_kernel(PackLaunch a) {
+    const int row = blockIdx.x;
+    if (threadIdx.x >= 3) return;
+    const int tau = threadIdx.x;
+    int run = 0;
+    int32_t *tc = a.tile_counts + (size_t)row * a.n_tiles * 3;
+    for (int tl = 0; tl < a.n_tiles; ++tl) {
+        const int c = tc[tl * 3 + tau];
+        tc[tl * 3 + tau] = run;
+        run += c;
+    }
+    a.row_counts[row * 3 + tau] = run;
+}
+
+// single work-group: page and code-unit bases of every (row, tier), capacity
+// checks, row metadata and the allocation counters
+__global__ __launch_bounds__(1024) void pack_plan_kernel(PackLaunch a, int32_t *range /* [2] first, n */) {
+    __shared__ long long sp[1024], su[1024];
+    __shared__ long long carry_p, carry_u;
+    __shared__ int bad;
+    if (threadIdx.x == 0) {
+        carry_p = 0;
+        carry_u = 0;
+        bad = read_status(a.status);
+    }
+    __syncthreads();
+    if (bad) return;
+    const int rows = a.B * a.Hkv;
+    const int n_ent = rows * 3;
+    const int64_t a0 = a.alloc[0], a1 = a.alloc[1];
+    for (int base = 0; base < n_ent; base += 1024) {
+        const int i = base + threadIdx.x;
+        long long pg = 0, un = 0;
+        if (i < n_ent) {
+            const int n = a.row_counts[i];
+            pg = (n + a.P - 1) / a.P;
+            un = pg * block16(i % 3, a.P);
+        }
+        sp[threadIdx.x] = pg;
+        su[threadIdx.x] = un;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan
+            long long vp = 0, vu = 0;
+            if (threadIdx.x >= off) {
+                vp = sp[threadIdx.x - off];
+                vu = su[threadIdx.x - off];
+            }
+            __syncthreads();
+            sp[threadIdx.x] += vp;
+            su[threadIdx.x] += vu;
+            __syncthreads();
+        }
+        if (i < n_ent) {
+            a.row_base[i] = (int32_t)(a0 + carry_p + sp[threadIdx.x] - pg);
+            a.row_unit[i] = a1 + carry_u + su[threadIdx.x] - un;
+        }
+        __syncthreads();
+        if (threadIdx.x == 1023) {
+            carry_p += sp[1023];
+            carry_u += su[1023];
+        }
+        __syncthreads();
+    }
+    // capacity
+    if (threadIdx.x == 0) {
+        if (a0 + carry_p > a.page_capacity || a1 + carry_u > a.arena_capacity16) set_status(a.status, ADA_ENOSPC);
+    }
+    for (int r = threadIdx.x; r < rows; r += 1024) {
+        int tot = 0;
+        for (int tau = 0; tau < 3; ++tau) tot += (a.row_counts[r * 3 + tau] + a.P - 1) / a.P;
+        if (tot > a.maxp) set_status(a.status, ADA_ENOSPC);
+    }
+    __syncthreads();
+    if (read_status(a.status) != 0) return;
+    for (int r = threadIdx.x; r < rows; r += 1024) {
+        int tot = 0;
+        for (int tau = 0; tau < 3; ++tau) {
+            const int n = a.row_counts[r * 3 + tau];
+            const int pg = (n + a.P - 1) / a.P;
+            tot += pg;
+            a.open_page[r * 3 + tau] = (n % a.P != 0) ? a.row_base[r * 3 + tau] + pg - 1 : -1;
+        }
+        a.num_pages[r] = tot;
+    }
+    if (threadIdx.x == 0) {
+        a.alloc[0] = a0 + carry_p;
+        a.alloc[1] = a1 + carry_u;
+        range[0] = (int32_t)a0;
+        range[1] = (int32_t)carry_p;
+    }
+}
+
+// per row: page-table entries and page metadata of the row's new pages
+__global__ __launch_bounds__(256) void pack_pages_kernel(PackLaunch a) {
+    if (read_status(a.status) != 0) return;
+    const int row = blockIdx.x;
+    int pos = 0;
+    for (int tau = 0; tau < 3; ++tau) {
+        const int n = a.row_counts[row * 3 + tau];
+        const int pg = (n + a.P - 1) / a.P;
+        const int base = a.row_base[row * 3 + tau];
+        const int64_t ubase = a.row_unit[row * 3 + tau];
+        for (int i = threadIdx.x; i < pg; i += 256) {
+            const int page = base + i;
+            a.page_table[(size_t)row * a.maxp + pos + i] = page;
+            ada_page_meta_t m;
+            m.tier = (uint8_t)tau;
+            m.count = (uint8_t)((i == pg - 1) ? n - i * a.P : a.P);
+            m.reserved = 0;
+            m.code_off16 = (uint32_t)(ubase + (int64_t)i * block16(tau, a.P));
+            a.page_meta[page] = m;
+        }
+        pos += pg;
+    }
+}
+
+// per (row, tile): rank of every kept token within its (row, tier) ->
+// destination page and slot
+__global__ __launch_bounds__(256) void pack_dest_kernel(PackLaunch a) {
+    __shared__ int sc[3][256];
+    const int tile = blockIdx.x, row = blockIdx.y;
+    const int b = row / a.Hkv;
+    const int ctx = a.ctx_len_dev[b];
+    const int64_t rbase = (int64_t)row * a.stride;
+    const int t0 = tile * kTile + threadIdx.x * 4;
+    if (read_status(a.status) != 0) return;
+    int tv[4], c[3] = {0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int t = t0 + k;
+        tv[k] = (t < ctx && t < a.stride) ? a.tier[rbase + t] : -1;
+        if (tv[k] >= 0) c[tv[k]]++;
+    }
+    for (int tau = 0; tau < 3; ++tau) sc[tau][threadIdx.x] = c[tau];
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        int v[3] = {0, 0, 0};
+        if (threadIdx.x >= off)
+            for (int tau = 0; tau < 3; ++tau) v[tau] = sc[tau][threadIdx.x - off];
+        __syncthreads();
+        for (int tau = 0; tau < 3; ++tau) sc[tau][threadIdx.x] += v[tau];
+        __syncthreads();
+    }
+    int run[3];
+    for (int tau = 0; tau < 3; ++tau)
+        run[tau] = sc[tau][threadIdx.x] - c[tau] + a.tile_counts[((size_t)row * a.n_tiles + tile) * 3 + tau];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int t = t0 + k;
+        if (t >= a.stride) break;
+        int dp = -1, ds = 0;
+        if (tv[k] >= 0) {
+            const int r = run[tv[k]]++;
+            dp = a.row_base[row * 3 + tv[k]] + r / a.P;
+            ds = r % a.P;
+        }
+        a.dest_page[rbase + t] = dp;
+        a.dest_slot[rbase + t] = ds;
+    }
+}
+
+// ------------------------------------------------------------- append
+struct AppendKernelArgs {
+    AppendLaunch a;
+    int32_t *key_off;   // [keys] code offset of the current page
+};
+
+__global__ __launch_bounds__(256) void append_init_kernel(AppendKernelArgs k) {
+    const AppendLaunch &a = k.a;
+    const int nkeys = a.num_seqs * a.Hkv * 3;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nkeys; i += gridDim.x * 256) {
+        const int op = a.open_page[i];
+        a.key_cnt[i] = 0;
+        a.key_done[i] = 0;
+        a.key_page[i] = op;
+        int c0 = 0, off = 0;
+        if (op >= 0) {
+            const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + op);
+            c0 = (meta.x >> 8) & 0xFF;
+            off = (int)meta.y;
+        }
+        a.key_c0[i] = c0;
+        k.key_off[i] = off;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.totals[0] = 0;
+        a.totals[1] = 0;
+        a.n_new[0] = 0;
+    }
+}
+
+__global__ __launch_bounds__(256) void append_validate_kernel(AppendLaunch a) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int i = blockIdx.x * 4 + wv; i < a.n; i += gridDim.x * 4) {
+        const int s = a.seq[i], h = a.head[i], tau = a.tier[i];
+        const bool in_range = s >= 0 && s < a.num_seqs && h >= 0 && h < a.Hkv && tau < 3;
+        const float2 kk = *reinterpret_cast<const float2 *>(a.keys + (int64_t)i * kD + 2 * lane);
+        const bool bad = __any(!(isfinite(kk.x) && isfinite(kk.y)));
+        if (lane == 0) {
+            if (!in_range || bad) set_status(a.status, ADA_EINVAL);
+            else atomicAdd(&a.key_cnt[(s * a.Hkv + h) * 3 + tau], 1);
+        }
+    }
+}
+
+__device__ inline int floordiv(int x, int P) { return x >= 0 ? x / P : -((-x + P - 1) / P); }
+
+__global__ __launch_bounds__(256) void append_capacity_kernel(AppendLaunch a) {
+    if (read_status(a.status) != 0) return;
+    const int rows = a.num_seqs * a.Hkv;
+    for (int r = blockIdx.x * 256 + threadIdx.x; r < rows; r += gridDim.x * 256) {
+        int row_new = 0;
+        long long units = 0;
+        for (int tau = 0; tau < 3; ++tau) {
+            const int key = r * 3 + tau;
+            const int cnt = a.key_cnt[key];
+            if (cnt == 0) continue;
+            const int c0 = a.key_c0[key];
+            const int allocs = floordiv(c0 + cnt - 1, a.P) - floordiv(c0 - 1, a.P);
+            row_new += allocs;
+            units += (long long)allocs * block16(tau, a.P);
+        }
+        if (row_new == 0) continue;
+        if (a.num_pages[r] + row_new > a.maxp) set_status(a.status, ADA_ENOSPC);
+        atomicAdd((unsigned long long *)&a.totals[0], (unsigned long long)row_new);
+        atomicAdd((unsigned long long *)&a.totals[1], (unsigned long long)units);
+    }
+}
+
+// single work-group: place every request in order (tiles of 1024)
+__global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
+    const AppendLaunch &a = k.a;
+    __shared__ int s_key[1024], s_row[1024], s_rank[1024], s_alloc[1024], s_page[1024], s_off[1024];
+    __shared__ long long s_scan_p[1024], s_scan_u[1024];
+    __shared__ long long base_p, base_u;
+    __shared__ int nnew, bad;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        bad = read_status(a.status);
+        if (!bad && (a.alloc[0] + a.totals[0] > a.page_capacity || a.alloc[1] + a.totals[1] > a.arena_capacity16)) {
+            set_status(a.status, ADA_ENOSPC);
+            bad = 1;
+        }
+        base_p = a.alloc[0];
+        base_u = a.alloc[1];
+        nnew = 0;
+    }
+    __syncthreads();
+    if (bad) return;
+    const int P = a.P;
+    for (int t0 = 0; t0 < a.n; t0 += 1024) {
+        const int nt = min(1024, a.n - t0);
+        const int i = t0 + tid;
+        const bool act = tid < nt;
+        int key = -1, row = -1, tau = 0;
+        if (act) {
+            tau = a.tier[i];
+            row = a.seq[i] * a.Hkv + a.head[i];
+            key = row * 3 + tau;
+        }
+        s_key[tid] = key;
+        s_row[tid] = row;
+        __syncthreads();
+        int rank = 0;
+        bool last_in_tile = true;
+        if (act) {
+            for (int j = 0; j < nt; ++j) {
+                if (s_key[j] != key) continue;
+                if (j < tid) ++rank;
+                else if (j > tid) last_in_tile = false;
+            }
+        }
+        int r = 0, pos = 0, alloc = 0;
+        if (act) {
+            r = a.key_done[key] + rank;
+            pos = a.key_c0[key] + r;
+            alloc = (pos % P) == 0;
+        }
+        s_rank[tid] = rank;
+        s_alloc[tid] = alloc;
+        s_scan_p[tid] = alloc;
+        s_scan_u[tid] = alloc ? block16(tau, P) : 0;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            long long vp = 0, vu = 0;
+            if (tid >= off) {
+                vp = s_scan_p[tid - off];
+                vu = s_scan_u[tid - off];
+            }
+            __syncthreads();
+            s_scan_p[tid] += vp;
+            s_scan_u[tid] += vu;
+            __syncthreads();
+        }
+        const long long ex_p = s_scan_p[tid] - alloc;
+        const long long ex_u = s_scan_u[tid] - (alloc ? block16(tau, P) : 0);
+        s_page[tid] = alloc ? (int)(base_p + ex_p) : -1;
+        s_off[tid] = alloc ? (int)(base_u + ex_u) : -1;
+        __syncthreads();
+        int page = -1, off16 = 0;
+        if (act) {
+            if (alloc) {
+                page = s_page[tid];
+                off16 = s_off[tid];
+            } else {
+                const int want = rank - (pos % P);
+                if (want >= 0) {
+                    for (int j = 0; j < nt; ++j)
+                        if (s_key[j] == key && s_rank[j] == want) {
+                            page = s_page[j];
+                            off16 = s_off[j];
+                            break;
+                        }
+                } else {
+                    page = a.key_page[key];
+                    off16 = k.key_off[key];
+                }
+            }
+        }
+        // row positions of newly opened pages
+        int rowrank = 0;
+        bool last_alloc_of_row = true;
+        if (act && alloc) {
+            for (int j = 0; j < nt; ++j) {
+                if (!s_alloc[j] || s_row[j] != row) continue;
+                if (j < tid) ++rowrank;
+                else if (j > tid) last_alloc_of_row = false;
+            }
+        }
+        const int np_row = act ? a.num_pages[row] : 0;
+        __syncthreads();   // every read of carried state precedes the updates below
+        if (act) {
+            if (alloc) {
+                a.page_table[(size_t)row * a.maxp + np_row + rowrank] = page;
+                a.new_pages[nnew + ex_p] = page;
+            }
+            a.dest_page[i] = page;
+            a.dest_slot[i] = pos % P;
+            const bool last_overall = (r == a.key_cnt[key] - 1);
+            if ((pos + 1) % P == 0 || last_overall) {
+                ada_page_meta_t m;
+                m.tier = (uint8_t)tau;
+                m.count = (uint8_t)(pos % P + 1);
+                m.reserved = 0;
+                m.code_off16 = (uint32_t)off16;
+                a.page_meta[page] = m;
+            }
+            if (last_in_tile) {
+                a.key_done[key] = r + 1;
+                a.key_page[key] = page;
+                k.key_off[key] = off16;
+            }
+            if (last_overall) a.open_page[key] = ((pos + 1) % P == 0) ? -1 : page;
+            if (alloc && last_alloc_of_row) a.num_pages[row] = np_row + rowrank + 1;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            base_p += s_scan_p[1023];
+            base_u += s_scan_u[1023];
+            nnew += (int)s_scan_p[1023];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.alloc[0] = base_p;
+        a.alloc[1] = base_u;
+        a.n_new[0] = 0;          // list start
+        a.n_new[1] = nnew;       // list length
+    }
+}
+
+__global__ void cache_init_kernel(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
+                                  int32_t *status) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < rows * 3; i += gridDim.x * blockDim.x) {
+        open_page[i] = -1;
+        if (i < rows) num_pages[i] = 0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        alloc[0] = 0;
+        alloc[1] = 0;
+        *status = 0;
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+inline int grid_for(int64_t n, int per_block, int cap = 8192) {
+    int64_t g = (n + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    return (int)(g > cap ? cap : g);
+}
+
+}  // namespace
+
+uint16_t host_f64_to_f16(double x) { return f64_to_f16_rne_sat(x); }
+
+hipError_t launch_encode_write(const EncodeLaunch &a, hipStream_t s) {
+    hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(a.n, 4, 16384)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64_t max_n,
+                             const ada_page_meta_t *page_meta, uint8_t *arena, uint16_t *value_pool, int32_t P,
+                             const int32_t *status, hipStream_t s) {
+    hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_n, 1, 4096)), dim3(256), 0, s, pages, n_pages,
+                       page_meta, arena, value_pool, P, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc, int32_t *status,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(cache_init_kernel, dim3(grid_for((int64_t)rows * 3, 256, 1024)), dim3(256), 0, s, rows,
+                       num_pages, open_page, alloc, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
+    const int rows = a.B * a.Hkv;
+    hipLaunchKernelGGL(pack_count_kernel, dim3(a.n_tiles, rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pack_rowscan_kernel, dim3(rows), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(1024), 0, s, a, a.n_new);
+    hipLaunchKernelGGL(pack_pages_kernel, dim3(rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pack_dest_kernel, dim3(a.n_tiles, rows), dim3(256), 0, s, a);
+    const int64_t max_pages = (int64_t)rows * a.maxp;
+    hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_pages, 1, 4096)), dim3(256), 0, s,
+                       (const int32_t *)nullptr, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
+                       a.arena, a.value_pool, a.P, (const int32_t *)a.status);
+    EncodeLaunch e;
+    e.keys = a.keys;
+    e.values = a.values;
+    e.n = (int64_t)rows * a.stride;
+    e.dest_page = a.dest_page;
+    e.dest_slot = a.dest_slot;
+    e.page_meta = a.page_meta;
+    e.arena = a.arena;
+    e.value_pool = a.value_pool;
+    e.P = a.P;
+    e.status = a.status;
+    hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(e.n, 4, 16384)), dim3(256), 0, s, e);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendLaunch &a, hipStream_t s) {
+    AppendKernelArgs k;
+    k.a = a;
+    // key_off lives right after key_page in the workspace (same length)
+    const int nkeys = a.num_seqs * a.Hkv * 3;
+    k.key_off = a.key_page + nkeys;
+    hipLaunchKernelGGL(append_init_kernel, dim3(grid_for(nkeys, 256, 1024)), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(append_validate_kernel, dim3(grid_for(a.n, 4, 4096)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(append_capacity_kernel, dim3(grid_for((int64_t)a.num_seqs * a.Hkv, 256, 1024)), dim3(256),
+                       0, s, a);
+    hipLaunchKernelGGL(append_book_kernel, dim3(1), dim3(1024), 0, s, k);
+    hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(a.n, 1, 4096)), dim3(256), 0, s,
+                       (const int32_t *)a.new_pages, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
+                       a.arena, a.value_pool, a.P, (const int32_t *)a.status);
+    EncodeLaunch e;
+    e.keys = a.keys;
+    e.values = a.values;
+    e.n = a.n;
+    e.dest_page = a.dest_page;
+    e.dest_slot = a.dest_slot;
+    e.page_meta = a.page_meta;
+    e.arena = a.arena;
+    e.value_pool = a.value_pool;
+    e.P = a.P;
+    e.status = a.status;
+    hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(e.n, 4, 16384)), dim3(256), 0, s, e);
+    return hipGetLastError();
+}
+
+}  // namespace ada

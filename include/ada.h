@@ -1,0 +1,257 @@
+/*
+ * ada.h -- C ABI of the ADA (Angle-Domain Attention) paged-decode library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "SPHERICAL KV: Angle-Domain Attention and Rate-Distortion
+ * Retention for Efficient Long-Context Inference" (arXiv 2605.18856),
+ * Abstract (newx.sg paper page; searcharxiv.org abstract page).  The
+ * abstract states that keys are stored as a scalar radius plus compact angle
+ * codes, that attention logits are computed straight from the codes on a
+ * paged, block-local decode path, and that Rate-Distortion Retention (RDR)
+ * picks keep/drop and a precision tier per token and KV head under a fixed
+ * budget, producing tier-homogeneous pages with lightweight metadata.  The
+ * abstract fixes no bit layout; this header fixes one:
+ *
+ *  Key codec (head dim 128 -> 64 adjacent pairs (k[2j], k[2j+1])):
+ *   radius     r = |k| (fp64, correctly rounded), stored as fp16 (round to
+ *              nearest even straight from fp64, saturating at 65504);
+ *   magnitude  s_j = |pair j| / r, code = nearest integer to s_j (2^sb - 1),
+ *              ties up, dequantised s = code / (2^sb - 1);
+ *   angle      th_j = atan2(k[2j+1], k[2j]), code = nearest integer to
+ *              (th_j + pi) / (2 pi / 2^tb), ties up, mod 2^tb; dequantised
+ *              th = -pi + code * 2 pi / 2^tb; a zero pair gets code 2^(tb-1).
+ *   The norm^2 is the fixed pairwise tree sum of the 64 pair energies
+ *   (strides 32, 16, ..., 1); codes are decided exactly (not up to rounding).
+ *  Tiers (fixed table, id order): ADA_TIER_T8 = (tb 8, sb 8),
+ *   ADA_TIER_T4 = (4, 4), ADA_TIER_T2 = (2, 3).
+ *  Logit of a kept token t for query q (per query head):
+ *     l_t = scale * r_t * sum_j s_j * LUT[j][theta_code_j],
+ *     LUT[j][c] = q[2j] cos(th_c) + q[2j+1] sin(th_c),
+ *   followed by softmax over the kept tokens of the (sequence, KV head) and
+ *   a weighted sum of their fp16 values.
+ *
+ *  Page layout (page size P in {16, 32}, head dim 128):
+ *   code block of a page: 16-byte aligned at code_arena + 16 * code_off16,
+ *     [radius: P x u16][angle component][magnitude component]; a component
+ *     of Bc = 8*b bytes per token is cut into floor(Bc/16) units of 16 bytes
+ *     plus one 8-byte unit when Bc mod 16 == 8; unit u of all P tokens is
+ *     stored contiguously (token-minor), units in order; code j of width b
+ *     occupies bits [j*b, (j+1)*b) of the token's little-endian bit string.
+ *     Block bytes: T8 130 P, T4 66 P, T2 42 P.
+ *   value page: fp16, element (slot, d) of page p at
+ *     value_pool + p*P*128 + (slot/8)*1024 + d*8 + slot%8
+ *     (8-token groups, dimension-major inside a group).
+ *   Unused slots of a page (slot >= count) are zero in codes and values.
+ *
+ * Conventions for every call:
+ *  - Pointers documented "device" point to HIP device memory owned by the
+ *    caller; pointers documented "host" point to host memory read before
+ *    the call returns.  The library never allocates or frees memory and
+ *    keeps no global state; scratch comes from a caller workspace whose size
+ *    the matching *_workspace call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *    calls are asynchronous on that stream except ada_read_status.
+ *  - Host-side validation happens before any launch and returns ADA_EINVAL /
+ *    ADA_EUNSUPPORTED without touching memory.  Errors found on the device
+ *    (non-finite key or utility, capacity) are written to a device status
+ *    word; the writing kernels of that call then do nothing (all-or-nothing)
+ *    and the caller reads and clears the word with ada_read_status.  Calls
+ *    made while the status word is non-zero do not modify the cache.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef ADA_H
+#define ADA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ADA_OK = 0,
+    ADA_EINVAL = 1,          /* bad argument, or non-finite / negative input on the device */
+    ADA_ENOSPC = 2,          /* page / arena / row capacity would be exceeded */
+    ADA_EUNSUPPORTED = 3,    /* valid but unsupported shape (head dim, page size, group size) */
+    ADA_EHIP = 4,            /* a HIP runtime call failed */
+    ADA_EINTERNAL = 5        /* an exact code decision could not be made (never expected) */
+} ada_status_t;
+
+enum { ADA_TIER_T8 = 0, ADA_TIER_T4 = 1, ADA_TIER_T2 = 2, ADA_NUM_TIERS = 3 };
+
+/* Shape of one attention layer's cache (host struct). */
+typedef struct {
+    int32_t head_dim;           /* must be 128 */
+    int32_t page_size;          /* P: 16 or 32 */
+    int32_t num_q_heads;        /* Hq */
+    int32_t num_kv_heads;       /* Hkv; Hq / Hkv must be 1, 2, 4 or 8 (query head hq uses KV head hq / (Hq/Hkv)) */
+    uint32_t rdr_tier_mask;     /* tiers RDR may assign (bit i = tier id i); 0 means all three */
+    int32_t decode_chunk_pages; /* split-K chunk length in pages for ada_decode; 0 = automatic */
+} ada_config_t;
+
+/* Metadata of one page, 8 bytes. */
+typedef struct {
+    uint8_t tier;        /* tier id */
+    uint8_t count;       /* filled slots, 1..P */
+    uint16_t reserved;   /* zero */
+    uint32_t code_off16; /* code block offset in 16-byte units */
+} ada_page_meta_t;
+
+/* The cache: every pointer is device memory owned by the caller.  Row r of
+ * the page table belongs to (sequence r / Hkv, KV head r % Hkv). */
+typedef struct {
+    int32_t num_seqs;           /* rows = num_seqs * Hkv */
+    int32_t max_pages_per_head; /* page-table row length */
+    int64_t page_capacity;      /* pages in page_meta / value_pool */
+    int64_t arena_capacity16;   /* code arena size in 16-byte units */
+    int32_t *page_table;        /* [rows][max_pages_per_head] physical page ids */
+    int32_t *num_pages;         /* [rows] pages in use per row */
+    int32_t *open_page;         /* [rows][3] last non-full page per tier, -1 = none */
+    ada_page_meta_t *page_meta; /* [page_capacity] */
+    uint8_t *code_arena;        /* [arena_capacity16 * 16], 16-byte aligned */
+    uint16_t *value_pool;       /* [page_capacity][P * 128] fp16 bits */
+    int64_t *alloc;             /* [2]: next page id, next code unit */
+    int32_t *status;            /* [1] device error word (0 = OK) */
+} ada_cache_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *ada_status_str(ada_status_t s);
+
+/* Bytes of one page's code block for a tier and page size (see layout
+ * above); -1 for an invalid tier or page size.  Pure host function. */
+int64_t ada_block_bytes(int32_t tier, int32_t page_size);
+
+/* Floats of the angle LUT of one query head as written by ada_build_lut:
+ * 64 * (256 + 16 + 4) = 17664 (T8, T4, T2 tables in tier-id order). */
+size_t ada_lut_floats(const ada_config_t *cfg);
+
+/* Reset the rows, counters and status of a cache: num_pages = 0,
+ * open_page = -1, alloc = {0, 0}, status = 0.  Page contents are left as
+ * they are (pages are zeroed when they are allocated). */
+ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, void *stream);
+
+/* Angle lookup table (the per-query table of the abstract's angle-domain
+ * logits): for each query row (b, hq) and each tier, LUT[j][c] =
+ * q[2j] cos(th_c) + q[2j+1] sin(th_c), fp32, no softmax scale.
+ *   q   device fp32 [B][Hq][128]
+ *   lut device fp32 [B][Hq][17664]: T8 [64][256], then T4 [64][16], then T2 [64][4].
+ * ada_decode stages the same values in on-chip memory itself and does not
+ * read this buffer; this call exists for callers that want the table. */
+ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, float *lut, void *stream);
+
+/* Workspace bytes for ada_decode / ada_decode_partials / ada_decode_reduce
+ * on sequences 0..B-1 of `cache` (split-K partials). */
+ada_status_t ada_decode_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, size_t *bytes);
+
+/* ADA paged decode (abstract: logits from the codes, paged block-local
+ * decode path) for sequences 0..B-1: one query per (sequence, query head).
+ *   q     device fp32 [B][Hq][128]
+ *   scale softmax scale applied to the logits (typically 1/sqrt(128))
+ *   out   device fp32 [B][Hq][128]: softmax-weighted sum of kept fp16 values
+ *   lse   device fp32 [B][Hq] natural-log sum-exp of the scaled logits, or NULL
+ *   ws    device workspace of at least ada_decode_workspace() bytes
+ * A row with no kept token gives out = 0 and lse = -inf.  Runs the split-K
+ * pass (LUT staging, logits, online softmax, value accumulation per context
+ * chunk) then the reduction pass.  Page ids are not range-checked. */
+ada_status_t ada_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                        float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* The two passes of ada_decode, callable separately (same arguments). */
+ada_status_t ada_decode_partials(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                                 float scale, void *ws, size_t ws_bytes, void *stream);
+ada_status_t ada_decode_reduce(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
+                               float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for ada_encode_append with n requests. */
+ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, size_t *bytes);
+
+/* Encode n new keys into their tiers and append them with their values
+ * (abstract: keys stored as radius + angle codes in tier-homogeneous pages).
+ * Sequential semantics in request order: request i fills the open page of
+ * (seq[i], kv_head[i], tier[i]) at its next slot, or opens a new page (next
+ * page id, next code block) appended to that row.
+ *   seq, kv_head device int32 [n]; tier device uint8 [n]
+ *   keys   device fp32 [n][128]; values device fp16 bits [n][128]
+ * Device errors: out-of-range seq / head / tier or non-finite key ->
+ * ADA_EINVAL; capacity -> ADA_ENOSPC; in both cases nothing is written. */
+ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n,
+                               const int32_t *seq, const int32_t *kv_head, const uint8_t *tier,
+                               const float *keys, const uint16_t *values, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/* Workspace bytes for ada_rdr_assign over B sequences of stride ctx_stride. */
+ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_stride, size_t *bytes);
+
+/* RDR keep/drop + tier choice under a byte budget (abstract: joint
+ * keep/drop and precision tiers per token and head under a fixed budget).
+ * Items are (KV head, position) of one sequence, all heads sharing the
+ * sequence's budget.  Rate of tier (tb, sb): 2 + 8 (tb + sb) + 256 bytes;
+ * distortion 2^-(tb + sb); drop: rate 0, distortion 1.  Enabled tiers in
+ * rate order form upgrade steps drop -> ... with cost dR_k and priority
+ * w * (dD_k / dR_k) (fp64); steps are taken in order of priority descending,
+ * position descending, head ascending, step ascending, while the byte total
+ * stays within the budget, stopping at the first step that does not fit.
+ *   ctx_len    host int32 [B] (<= ctx_stride)
+ *   utility    device fp32 [B][Hkv][ctx_stride], finite and >= 0
+ *   budget     host int64 [B] bytes
+ *   tier_out   device int8 [B][Hkv][ctx_stride]: tier id or -1 (dropped, or
+ *              position >= ctx_len)
+ *   status     device int32 [1]: set to ADA_EINVAL for a bad utility
+ * Returns ADA_EUNSUPPORTED when the enabled tiers' savings per byte do not
+ * strictly decrease. */
+ada_status_t ada_rdr_assign(const ada_config_t *cfg, int32_t B, const int32_t *ctx_len, int64_t ctx_stride,
+                            const float *utility, const int64_t *budget, int8_t *tier_out, int32_t *status,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for ada_pack over B sequences of stride ctx_stride. */
+ada_status_t ada_pack_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, int64_t ctx_stride,
+                                size_t *bytes);
+
+/* Bulk pack (prefill) of sequences 0..B-1 from a tier map (abstract:
+ * tier-homogeneous pages with lightweight metadata).  For each sequence,
+ * KV head and tier id ascending, the kept tokens in ascending position are
+ * cut into pages of P with consecutive page ids and code blocks taken from
+ * alloc; the rows of sequences 0..B-1 are (re)initialised; open_page holds
+ * each (row, tier)'s last page if it is not full.
+ *   ctx_len host int32 [B]
+ *   tier    device int8 [B][Hkv][ctx_stride] (-1 = drop)
+ *   keys    device fp32 [B][Hkv][ctx_stride][128]; values device fp16 bits, same shape
+ * Device errors (tier out of range, non-finite kept key -> ADA_EINVAL;
+ * capacity -> ADA_ENOSPC) leave the cache unmodified. */
+ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, const int32_t *ctx_len,
+                      int64_t ctx_stride, const int8_t *tier, const float *keys, const uint16_t *values,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Synchronise `stream`, return the device status word of `cache` (or
+ * ADA_EHIP if the copy fails) and reset it to 0. */
+ada_status_t ada_read_status(const int32_t *status, void *stream);
+
+/* ---- Measurement companions (not part of the method) ------------------ */
+
+/* Dense fp16 paged decode over un-compressed keys and values, with the same
+ * split-K skeleton as ada_decode; used as a traffic and footprint reference.
+ *   page_table device int32 [B*Hkv][max_pages_per_head]; ctx_len device int32 [B]
+ *   (every row of sequence b holds ctx_len[b] tokens in its pages, in order)
+ *   k_pool device fp16 [pages][P*128]: element (slot, d) at (d/8)*P*8 + slot*8 + d%8
+ *   v_pool device fp16 [pages][P*128]: same layout as ADA value pages
+ *   other arguments as ada_decode. */
+ada_status_t ada_dense_workspace(const ada_config_t *cfg, int32_t B, int32_t max_pages_per_head, size_t *bytes);
+ada_status_t ada_dense_decode(const ada_config_t *cfg, int32_t B, int32_t max_pages_per_head,
+                              const int32_t *page_table, const int32_t *ctx_len, const uint16_t *k_pool,
+                              const uint16_t *v_pool, const float *q, float scale, float *out, float *lse,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Plain streaming copy of `bytes` (multiple of 16) from src to dst, device
+ * pointers: calibration of memory counters and the stream bandwidth ceiling. */
+ada_status_t ada_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Host-side evaluation of the library's fp64 -> fp16 radius rounding (round
+ * to nearest even straight from fp64, saturating at 65504): the same code the
+ * encoder runs on the device, exported so CPU tests can check it. */
+uint16_t ada_host_f64_to_f16(double x);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ADA_H */

@@ -1,0 +1,81 @@
+"""The C-ABI library loads, exports every function include/ada.h declares,
+and its host-only paths behave as documented (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_kv_cache_ada_amd as ada
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ada.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ada_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ada.lib()
+    names = _declared()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ada.ABI_SYMBOLS)
+
+
+def test_block_bytes_and_lut_floats():
+    assert [ada.block_bytes(t, 16) for t in (0, 1, 2)] == [2080, 1056, 672]
+    assert ada.block_bytes(1, 32) == 2112
+    assert ada.block_bytes(3, 16) == -1 and ada.block_bytes(0, 8) == -1
+    assert ada.lut_floats(ada.make_config(16, 32, 8)) == 64 * (256 + 16 + 4)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert ada.status_str(s).startswith("ADA_")
+
+
+def test_host_fp16_rounding_matches_numpy():
+    rng = np.random.default_rng(7)
+    e = rng.uniform(-30, 16, 20000)
+    x = rng.uniform(1, 2, e.size) * 2.0 ** e
+    x = np.concatenate([x[x < 65504], [0.0, 2 ** -25, 3 * 2 ** -25, 1 + 2 ** -11, 1 + 2 ** -11 + 2 ** -40,
+                                       2 ** -14 - 2 ** -25, 65504.0, 65519.0]])
+    ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([ada.host_f64_to_f16(v) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+    assert ada.host_f64_to_f16(65520.0) == 0x7BFF and ada.host_f64_to_f16(1e300) == 0x7BFF
+
+
+def _size(fn, *args):
+    n = ctypes.c_size_t(0)
+    st = fn(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_host_validation_without_gpu():
+    L = ada.lib()
+    good = ada.make_config(16, 32, 8)
+    desc = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
+    st, n = _size(L.ada_decode_workspace, ctypes.byref(good), ctypes.byref(desc), 2)
+    assert st == ada.OK and n > 0
+    bad = [(ada.make_config(16, 32, 8), None),
+           (ada.Config(64, 16, 32, 8, 0, 0), ada.EUNSUPPORTED),
+           (ada.Config(128, 24, 32, 8, 0, 0), ada.EUNSUPPORTED),
+           (ada.Config(128, 16, 48, 8, 0, 0), ada.EUNSUPPORTED),
+           (ada.Config(128, 16, 30, 8, 0, 0), ada.EINVAL),
+           (ada.Config(128, 16, 32, 0, 0, 0), ada.EINVAL),
+           (ada.Config(128, 16, 32, 8, 9, 0), ada.EINVAL)]
+    for cfg, want in bad[1:]:
+        assert _size(L.ada_decode_workspace, ctypes.byref(cfg), ctypes.byref(desc), 2)[0] == want
+    # decode refuses a cache with null buffers before touching the device
+    null_cache = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
+    assert L.ada_decode(ctypes.byref(good), ctypes.byref(null_cache), None, 2, 1.0, None, None, None, 0, None) \
+        == ada.EINVAL
+    # RDR: unsupported tier set is caught on the host (T8 + T4 only is fine; 0 = all)
+    assert _size(L.ada_rdr_workspace, ctypes.byref(good), 2, 100)[0] == ada.OK
+    assert L.ada_probe_copy(None, None, 16, None) == ada.EINVAL

@@ -1,0 +1,94 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (automatic split-K chunking): bit-exact pages and RDR tier
+maps against the oracle, and decode outputs within 2e-3 per row."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_cache_ada_amd as ada
+import workloads as W
+from oracle import oracle as O
+from tests.gpu_util import check_outputs, compare_caches, gpu_pack, log, oracle_cache, to_dev
+from tests.util import dense_attention, dense_pages
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_pack(w, tiers=None):
+    oc = oracle_cache(w)
+    assert O.pack(oc, w["ctx_len"], w["tiers"] if tiers is None else tiers, w["keys"], w["values"]) == O.OK
+    return oc
+
+
+@pytest.mark.parametrize("name", ["llama8b", "long256k", "ragged"])
+def test_fullsize_pack_and_decode(name):
+    log(f"full {name}: generate")
+    w = W.config(name)
+    log("  gpu pack")
+    gc, dev = gpu_pack(w)
+    log("  oracle pack")
+    oc = _oracle_pack(w)
+    log("  compare pages")
+    compare_caches(gc, oc, w["P"])
+    if name == "ragged":   # shared pool: physical page ids permuted after packing
+        n = int(gc.alloc[0].item())
+        perm = torch.from_numpy(W.page_permutation(w["perm_rng"], n)).cuda().long()
+        gc.page_meta[perm] = gc.page_meta[:n].clone()
+        gc.value_pool[perm] = gc.value_pool[:n].clone()
+        pt = gc.page_table.long()
+        mask = torch.arange(pt.shape[1], device=pt.device)[None, :] < gc.num_pages[:, None]
+        gc.page_table.copy_(torch.where(mask, perm[pt.clamp(0, n - 1)], pt).int())
+    log("  decode")
+    out, lse = ada.decode(gc, dev["q"], w["scale"])
+    o_ref, lse_ref = O.decode(oc, w["q"], w["scale"])
+    worst = check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    log(f"  worst row rel err {worst:.2e}")
+
+
+def test_fullsize_rdr_pack_decode():
+    log("full rdr128k: generate")
+    w = W.config("rdr128k")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cfg = ada.make_config(w["P"], w["Hq"], w["Hkv"])
+    util = torch.from_numpy(w["utility"]).cuda()
+    log("  gpu rdr")
+    t_gpu = ada.rdr_assign(cfg, w["ctx_len"], util, w["budget"], status)
+    assert ada.read_status(status) == ada.OK
+    log("  oracle rdr")
+    st, t_ref = O.rdr_assign(w["ctx_len"], w["utility"], w["budget"])
+    assert st == O.OK
+    t_np = t_gpu.cpu().numpy()
+    assert np.array_equal(t_np, t_ref)
+    fr = {k: float((t_np == k).mean()) for k in (-1, 0, 1, 2)}
+    log(f"  tier fractions drop/T8/T4/T2 = {fr[-1]:.4f}/{fr[0]:.5f}/{fr[1]:.4f}/{fr[2]:.4f}")
+    w["tiers"] = t_ref
+    log("  gpu pack")
+    gc, dev = gpu_pack(w)
+    log("  oracle pack")
+    oc = _oracle_pack(w)
+    compare_caches(gc, oc, w["P"])
+    log("  decode")
+    out, lse = ada.decode(gc, dev["q"], w["scale"])
+    o_ref, lse_ref = O.decode(oc, w["q"], w["scale"])
+    check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("ctx", [1000, 262144])
+def test_dense_reference_parity(ctx):
+    w = W.config("long256k", ctx=ctx)
+    k16 = w["keys"].astype(np.float16).view(np.uint16)
+    kp, vp, pt = dense_pages(k16, w["values"], w["P"])
+    cfg = ada.make_config(w["P"], w["Hq"], w["Hkv"])
+    out, lse = ada.dense_decode(cfg, torch.from_numpy(pt).cuda(),
+                                torch.from_numpy(w["ctx_len"]).cuda(),
+                                torch.from_numpy(kp.view(np.int16)).cuda(), torch.from_numpy(vp.view(np.int16)).cuda(),
+                                torch.from_numpy(w["q"]).cuda(), w["scale"])
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    G = w["Hq"] // w["Hkv"]
+    rows = range(w["Hq"]) if ctx < 10000 else range(0, w["Hq"], 9)
+    for hq in rows:
+        h = hq // G
+        o_ref, l_ref = dense_attention(k16[0, h].view(np.float16), w["values"][0, h].view(np.float16),
+                                       w["q"][0, hq], w["scale"])
+        err = np.max(np.abs(out[0, hq] - o_ref)) / np.max(np.abs(o_ref))
+        assert err <= 2e-3 and abs(lse[0, hq] - l_ref) <= 2e-3, (hq, err)

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
+from tests.util import near_boundary_pairs as _near_boundary_pairs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -103,33 +104,6 @@ def test_theta_random_vs_mpmath(tb):
             c, dist = _mp_theta_code(keys[i, 2 * j], keys[i, 2 * j + 1], tb, prec=120)
             assert dist > 1e-20      # random inputs are never exact ties
             assert th[i, j] == c
-
-
-def _near_boundary_pairs(tb, per_boundary=2):
-    """fp32 pairs whose angle lies extremely close to a rounding boundary of
-    the tb-bit angle grid: for a boundary direction beta in the first octant,
-    search integers M in [2^23, 2^24) for which M tan(beta) is nearly an
-    integer Y; (M, Y) is then exactly representable.  The other octants
-    follow by the exact maps (x,y)->(-y,x) and (x,y)->(y,x)."""
-    N = 1 << tb
-    M = np.arange(2 ** 23, 2 ** 24, dtype=np.float64)
-    out = []
-    for m in range(N):
-        beta = -np.pi + (m + 0.5) * 2 * np.pi / N
-        if not (0 < beta < np.pi / 4):
-            continue
-        y = M * np.tan(beta)
-        frac = np.abs(y - np.round(y))
-        best = np.argsort(frac)[:per_boundary]
-        for i in best:
-            out.append((float(M[i]), float(np.round(y[i]))))
-    pairs = []
-    for x, y in out:
-        for (a, b) in [(x, y), (y, x)]:
-            for _ in range(4):
-                pairs.append((a, b))
-                a, b = -b, a
-    return pairs
 
 
 @pytest.mark.parametrize("tb", [3, 4, 8])

@@ -51,3 +51,46 @@ def kept_tokens(w, b, h):
         pos = np.nonzero(t == tau)[0]
         out.extend((int(p), tau) for p in pos)
     return out
+
+
+def near_boundary_pairs(tb, per_boundary=2):
+    """fp32 pairs whose angle lies extremely close to a rounding boundary of
+    the tb-bit angle grid: for a boundary direction beta in the first octant,
+    search integers M in [2^23, 2^24) for which M tan(beta) is nearly an
+    integer Y; (M, Y) is then exactly representable.  The other octants
+    follow by the exact maps (x,y)->(-y,x) and (x,y)->(y,x)."""
+    N = 1 << tb
+    M = np.arange(2 ** 23, 2 ** 24, dtype=np.float64)
+    out = []
+    for m in range(N):
+        beta = -np.pi + (m + 0.5) * 2 * np.pi / N
+        if not (0 < beta < np.pi / 4):
+            continue
+        y = M * np.tan(beta)
+        frac = np.abs(y - np.round(y))
+        best = np.argsort(frac)[:per_boundary]
+        for i in best:
+            out.append((float(M[i]), float(np.round(y[i]))))
+    pairs = []
+    for x, y in out:
+        for (a, b) in [(x, y), (y, x)]:
+            for _ in range(4):
+                pairs.append((a, b))
+                a, b = -b, a
+    return pairs
+
+
+def dense_pages(keys16, values16, P):
+    """Lay out un-dropped fp16 keys / values [B][Hkv][ctx][128] (uint16 bits)
+    as dense pages: key page [16 dim blocks][P][8], value page [P/8][128][8];
+    row (b, h) owns pages row*npr .. row*npr + npr - 1.  Returns
+    (k_pool [pages][P*128], v_pool [pages][P*128], page_table [rows][npr])."""
+    B, H, ctx, _ = keys16.shape
+    npr = -(-ctx // P)
+    pad = npr * P - ctx
+    k = np.pad(keys16, ((0, 0), (0, 0), (0, pad), (0, 0)))
+    v = np.pad(values16, ((0, 0), (0, 0), (0, pad), (0, 0)))
+    k = k.reshape(B * H * npr, P, 16, 8).transpose(0, 2, 1, 3).reshape(B * H * npr, P * 128)
+    v = v.reshape(B * H * npr, P // 8, 8, 128).transpose(0, 1, 3, 2).reshape(B * H * npr, P * 128)
+    pt = np.arange(B * H * npr, dtype=np.int32).reshape(B * H, npr)
+    return np.ascontiguousarray(k), np.ascontiguousarray(v), pt
