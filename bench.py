@@ -1,0 +1,303 @@
+"""Benchmark: ADA paged decode on one MI355X.
+
+One step = one full decode of the workload: the split-K pass (angle-LUT
+staging, logits from codes, online softmax, value accumulation) followed by
+the reduction pass, for every (sequence, query head), with the packed cache
+already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+Reported value: kept KV token-heads scanned per second (a token-head is one
+(token, KV head) entry of the cache; dropped tokens are absent from the
+pages).  The roofline entry prices the split-K kernel's algorithmic bytes
+(radius + codes + fp16 values per kept token-head, 12 bytes of metadata and
+page-table per page, the queries) against MI355X's 8 TB/s HBM peak.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+TIER_TOKEN_BYTES = {0: 386, 1: 322, 2: 298}       # radius + codes + fp16 values, head dim 128
+DENSE_TOKEN_BYTES = 512
+METRIC = "ADA decode KV-tokens/sec and achieved HBM GB/s (% of peak) at 32k–128k ctx"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "rdr128k", "ragged", "long256k", "tiny"])
+    ap.add_argument("--chunk-pages", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "decode_core.h", "ada_internal.h"):
+        with open(os.path.join(ROOT, "compressed_kv_cache_ada_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per split-K launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"ada_decode_partials_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def build_workload(name, torch, ada, W):
+    w = W.config(name)
+    if w["tiers"] is None:   # RDR workload: the packer decides the tiers first
+        cfg = ada.make_config(w["P"], w["Hq"], w["Hkv"])
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        t = ada.rdr_assign(cfg, w["ctx_len"], torch.from_numpy(w["utility"]).cuda(), w["budget"], status)
+        assert ada.read_status(status) == ada.OK
+        w["tiers"] = t.cpu().numpy()
+    return w
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding of the decode is described, not built)"}))
+        sys.exit(2)
+    import torch
+    import compressed_kv_cache_ada_amd as ada
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    w = build_workload(args.workload, torch, ada, W)
+    P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
+    G = Hq // Hkv
+    tiers = w["tiers"]
+    kept = {t: int((tiers == t).sum()) for t in (0, 1, 2)}
+    kept_total = sum(kept.values())
+    rows = B * Hkv
+    pages_by_tier = {t: 0 for t in (0, 1, 2)}
+    max_row = 0
+    for b in range(B):
+        for h in range(Hkv):
+            rp = 0
+            for t in (0, 1, 2):
+                n = int((tiers[b, h] == t).sum())
+                pages_by_tier[t] += -(-n // P)
+                rp += -(-n // P)
+            max_row = max(max_row, rp)
+    n_pages = sum(pages_by_tier.values())
+    units = sum(pages_by_tier[t] * ada.block_bytes(t, P) // 16 for t in (0, 1, 2))
+
+    cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages)
+    cache = ada.Cache(cfg, B, max_row, n_pages, units)
+    ada.cache_init(cache)
+    keys = torch.from_numpy(w["keys"]).cuda()
+    vals = torch.from_numpy(w["values"].view(np.int16)).cuda()
+    ada.pack(cache, w["ctx_len"], torch.from_numpy(tiers).cuda(), keys, vals)
+    st = ada.read_status(cache.status)
+    assert st == ada.OK, ada.status_str(st)
+    del keys, vals
+    torch.cuda.empty_cache()
+
+    q = torch.from_numpy(w["q"]).cuda()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ws = ada.decode_workspace(cache, B)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ada.decode_partials(cache, q, w["scale"], ws)
+        if ev is not None:
+            ev[1].record()
+        ada.decode_reduce(cache, B, out, lse, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K back-to-back steps; events bracket every split-K launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    k_ms_each = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # dominant kernel alone: K back-to-back split-K launches between two events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        ada.decode_partials(cache, q, w["scale"], ws)
+    e1.record()
+    torch.cuda.synchronize()
+    k_ms = e0.elapsed_time(e1) / args.steps
+
+    # cold steps: the 256 MB last-level cache is flushed (1 GB of writes) before each
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(args.cold_steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ada.decode_partials(cache, q, w["scale"], ws)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+
+    # copy probe: streaming ceiling of this machine (read + write bytes)
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        ada.probe_copy(src, dst, nb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        ada.probe_copy(src, dst, nb)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # read ceiling: best of the streaming-read variants over 1 GiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    read_gbps = {}
+    for variant in range(5):
+        for _ in range(2):
+            ada.probe_read(src, nb, variant, sink)
+        e0.record()
+        for _ in range(10):
+            ada.probe_read(src, nb, variant, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        read_gbps[variant] = nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in (0, 1, 2)) + 12 * n_pages + B * Hq * 128 * 4
+    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    value = kept_total / (ms_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
+            "context": int(w["ctx_len"].max()), "page_size": P, "kept_token_heads": kept_total,
+            "kept_by_tier_T8_T4_T2": [kept[0], kept[1], kept[2]],
+            "pages_by_tier_T8_T4_T2": [pages_by_tier[0], pages_by_tier[1], pages_by_tier[2]],
+            "decode_chunk_pages": cfg.decode_chunk_pages,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "kernel": "decode_partials_kernel", "kernel_ms": k_ms, "kernel_ms_event_per_launch": k_ms_each,
+            "algorithmic_bytes": alg_bytes,
+        },
+        "step_hbm_gbps": (alg_bytes + B * Hq * 512) / (ms_step * 1e-3) / 1e9,
+        "context_tokens_per_s": float(w["ctx_len"].sum()) * Hkv / (ms_step * 1e-3),
+        "cold_kernel_ms_median": float(np.median(cold)) if cold else None,
+        "cold_gbps": alg_bytes / (np.median(cold) * 1e-3) / 1e9 if cold else None,
+        "copy_probe_gbps": copy_gbps,
+        "read_probe_gbps": max(read_gbps[v] for v in range(4)),
+        "read_probe_variants_gbps": read_gbps,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+
+    if not args.no_dense:
+        result["dense_fp16_reference"] = dense_reference(w, ada, torch, cfg)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, kept_total, max_row, n_pages, units)
+    print(json.dumps(result), flush=True)
+
+
+def dense_reference(w, ada, torch, cfg):
+    """Same-box dense fp16 paged decode over the un-dropped keys and values
+    (every context token kept, keys rounded to fp16)."""
+    from workloads import dense_pages
+    B, Hq = w["B"], w["Hq"]
+    k16 = w["keys"].astype(np.float16).view(np.uint16)
+    kp, vp, pt = dense_pages(k16, w["values"], w["P"])
+    del k16
+    kp_d = torch.from_numpy(kp.view(np.int16)).cuda()
+    vp_d = torch.from_numpy(vp.view(np.int16)).cuda()
+    del kp, vp
+    pt_d = torch.from_numpy(pt).cuda()
+    ctx_d = torch.from_numpy(w["ctx_len"]).cuda()
+    q = torch.from_numpy(w["q"]).cuda()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ws = ada.dense_workspace(cfg, B, pt.shape[1])
+    for _ in range(5):
+        ada.dense_decode(cfg, pt_d, ctx_d, kp_d, vp_d, q, w["scale"], out, lse, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    e0.record()
+    for _ in range(n):
+        ada.dense_decode(cfg, pt_d, ctx_d, kp_d, vp_d, q, w["scale"], out, lse, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    token_heads = int(w["ctx_len"].sum()) * w["Hkv"]
+    dbytes = token_heads * DENSE_TOKEN_BYTES + B * Hq * 1024
+    del kp_d, vp_d
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "token_heads": token_heads, "bytes_per_token_head": DENSE_TOKEN_BYTES,
+            "algorithmic_bytes": dbytes, "gbps": dbytes / (ms * 1e-3) / 1e9,
+            "token_heads_per_s": token_heads / (ms * 1e-3)}
+
+
+def cpu_baseline(w, kept_total, max_row, n_pages, units):
+    """The fp64 CPU oracle, as it stands, decoding the same workload on the
+    host's cores (pages built by the oracle's own pack, untimed)."""
+    from oracle import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    B = w["B"]
+    # bounded sample: whole sequences of the workload, about 10-30 s of CPU work
+    b_s = B
+    oc = O.Cache(w["P"], w["Hq"], w["Hkv"], b_s, max_row, n_pages, units)
+    assert O.pack(oc, w["ctx_len"][:b_s], w["tiers"][:b_s], w["keys"][:b_s], w["values"][:b_s]) == O.OK
+    t0 = time.perf_counter()
+    O.decode(oc, w["q"][:b_s], w["scale"], nthreads=cores)
+    dt = time.perf_counter() - t0
+    kept = int((w["tiers"][:b_s] >= 0).sum())
+    return {"value": kept / dt, "unit": "KV token-heads/s", "cores": cores, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{b_s} of {B} sequences (all heads, all kept tokens): {kept} token-heads, one decode step"}
+
+
+if __name__ == "__main__":
+    main()

@@ -84,6 +84,7 @@ def _declare(L):
         "ada_dense_workspace": (st, [cfgp, i32, i32, ctypes.POINTER(sz)]),
         "ada_dense_decode": (st, [cfgp, i32, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
         "ada_probe_copy": (st, [vp, vp, sz, vp]),
+        "ada_probe_read": (st, [vp, sz, i32, vp, vp]),
         "ada_host_f64_to_f16": (ctypes.c_uint16, [ctypes.c_double]),
     }
     for name, (res, args) in sig.items():
@@ -96,7 +97,7 @@ ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache
                "ada_decode_workspace", "ada_decode", "ada_decode_partials", "ada_decode_reduce",
                "ada_append_workspace", "ada_encode_append", "ada_rdr_workspace", "ada_rdr_assign",
                "ada_pack_workspace", "ada_pack", "ada_read_status", "ada_dense_workspace",
-               "ada_dense_decode", "ada_probe_copy", "ada_host_f64_to_f16")
+               "ada_dense_decode", "ada_probe_copy", "ada_probe_read", "ada_host_f64_to_f16")
 
 
 def status_str(s):
@@ -289,6 +290,10 @@ def dense_decode(cfg, page_table, ctx_len, k_pool, v_pool, q, scale, out=None, l
 
 def probe_copy(src, dst, nbytes):
     _check(lib().ada_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream()), "ada_probe_copy")
+
+
+def probe_read(src, nbytes, variant, out):
+    _check(lib().ada_probe_read(_ptr(src), nbytes, variant, _ptr(out), _stream()), "ada_probe_read")
 
 
 def host_f64_to_f16(x):

@@ -62,6 +62,7 @@ int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp) {
     }
     cp = (cp + tpg - 1) / tpg * tpg;
     if (cp < tpg) cp = tpg;
+    if (cp > 256) cp = 256;   // page list of a work-group lives in LDS
     return cp;
 }
 
@@ -519,6 +520,12 @@ ada_status_t ada_probe_copy(const void *src, void *dst, size_t bytes, void *stre
     if (!src || !dst || (bytes & 15)) return ADA_EINVAL;
     if (bytes == 0) return ADA_OK;
     return hip_status(launch_probe_copy(src, dst, bytes, (hipStream_t)stream));
+}
+
+ada_status_t ada_probe_read(const void *src, size_t bytes, int32_t variant, uint32_t *out, void *stream) {
+    if (!src || !out || (bytes & 15) || variant < 0 || variant > 4) return ADA_EINVAL;
+    if (bytes == 0) return ADA_OK;
+    return hip_status(launch_probe_read(src, bytes, variant, out, (hipStream_t)stream));
 }
 
 uint16_t ada_host_f64_to_f16(double x) { return host_f64_to_f16(x); }

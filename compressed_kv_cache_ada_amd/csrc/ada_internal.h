@@ -164,5 +164,6 @@ hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s);
 hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
                              int32_t *status, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
+hipError_t launch_probe_read(const void *src, size_t bytes, int variant, uint32_t *out, hipStream_t s);
 
 }  // namespace ada

@@ -6,9 +6,10 @@
 // from the radius + angle codes (no dense key is rebuilt) on a paged,
 // block-local decode path that streams tier-homogeneous pages.
 //
-// Work decomposition: one work-group per (context chunk, KV head, sequence).
-// The G = Hq/Hkv query heads of a KV head share every code and value read.
-// A wavefront takes 64 tokens at a time (4 pages of 16 or 2 pages of 32):
+// The split-K skeleton (page staging, value prefetch, online softmax, value
+// accumulation on the matrix cores, chunk partials) is decode_core.h; this
+// file supplies the ADA logits.  The G = Hq/Hkv query heads of a KV head
+// share every code and value read.
 //   logits:  lane = token; the token's 16-byte code units are read with one
 //            128-bit load per unit (units are token-minor, so the 64 lanes
 //            read contiguous memory); per pair j the lane gathers
@@ -16,366 +17,334 @@
 //            s_code * entry.  T8 uses the factorised form
 //            s (cos th, sin th) . (q[2j], q[2j+1]) with a 256-entry cos/sin
 //            table in LDS instead of a 64 KB-per-head table.
-//   softmax: per head, running max over the wavefront (butterfly), exp2 of
-//            the base-2 scaled logits, per-lane running sums.
-//   values:  lane = head dimension (lane and lane+64); each 128-bit load
-//            brings 8 consecutive tokens of one dimension (value pages are
-//            stored in 8-token groups, dimension-major), fp32 accumulation.
 // There is no matrix-core work in the logit path: it is a gather-reduce over
 // small per-pair tables, not a dense contraction.
-#include "ada_internal.h"
+#include "decode_core.h"
 
 namespace ada {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-// LDS writes by one lane become visible to other lanes of the same wave.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <typename T>
-__device__ __forceinline__ T ldg(const void *p) {
-    return *reinterpret_cast<const T *>(p);
-}
+using core::ldg;
 
 // ---- logits per tier (lane = token) --------------------------------------
 // Each returns base-2 scaled logits: scale * log2(e) * r * sum_j s_j LUT[j][c].
 
-template <int G, int P>
-__device__ __forceinline__ void logits_t4(const uint8_t *blk, int slot, const float *lut4, float mul,
-                                          float (&lg)[G]) {
-    const float r = h2f(ldg<uint16_t>(blk + 2 * slot));
-    const uint8_t *tb = blk + 2 * P + slot * 16;
-    const uint8_t *sbp = blk + 2 * P + 32 * P + slot * 16;
+// Raw code units of one token, fetched before the group's value loads so that
+// the logit arithmetic waits only for them.  Unit use per tier:
+//   T4: u[0..1] angle units, u[2..3] magnitude units
+//   T2: u[0] angle unit, u[1] magnitude unit, h the 8-byte magnitude unit
+//   T8: u[0..3] angle units, u[4..7] magnitude units
+// At most 16 LUT gathers in flight: a compiler barrier every JB pairs stops
+// the scheduler from hoisting all gathers of an unrolled unit into registers.
+template <int G>
+__device__ __forceinline__ void pair_fence(int j) {
+    constexpr int JB = 16 / G;
+    if ((j + 1) % JB == 0) asm volatile("" ::: "memory");
+}
+
+// Makes a code word opaque at this point of the program, so the field
+// extractions that use it cannot be hoisted above the preceding pairs.
+__device__ __forceinline__ uint32_t pin(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+struct CodeRegs {
+    uint4 u[4];
+    uint2 h;
+    uint32_t r;
+    const uint8_t *c;   // the token's first angle unit
+};
+
+// Raw code units of one token, fetched before the group's value loads so that
+// the logit arithmetic waits only for them.  Unit use per tier:
+//   T4: u[0..1] angle units, u[2..3] magnitude units
+//   T2: u[0] angle unit, u[1] magnitude unit, h the 8-byte magnitude unit
+//       (u[2], u[3] repeat u[1])
+//   T8: u[0..1] angle units 0-1, u[2..3] magnitude units 0-1 (pairs 0-31);
+//       units 2-3 (pairs 32-63) are read by the T8 logit routine itself
+template <int P>
+__device__ __forceinline__ CodeRegs fetch_codes(const uint8_t *blk, int tier, int slot) {
+    // Branch-free: every lane issues the same five loads; the offsets are
+    // chosen by tier and always stay inside the lane's own code block.
+    CodeRegs k;
+    k.c = blk + 2 * P + slot * 16;
+    const bool t2 = tier == ADA_TIER_T2;
+    const int so = (tier == ADA_TIER_T4) ? 32 * P : 64 * P;    // first magnitude unit
+    const int o1 = 16 * P;
+    const int o2 = t2 ? 16 * P : so;
+    const int o3 = t2 ? 16 * P : so + 16 * P;
+    k.r = ldg<uint16_t>(blk + 2 * slot);
+    k.u[0] = ldg<uint4>(k.c);
+    k.u[1] = ldg<uint4>(k.c + o1);
+    k.u[2] = ldg<uint4>(k.c + o2);
+    k.u[3] = ldg<uint4>(k.c + o3);
+    k.h = ldg<uint2>(t2 ? blk + 2 * P + 32 * P + slot * 8 : k.c);
+    return k;
+}
+
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+
+// LUT entries of one (pair, code) for all G heads are contiguous
+// ([pair][code][head]): one 64-lane gather of 16 bytes serves 4 heads.
+template <int G>
+__device__ __forceinline__ void lut_fma(const float *e, float s, float (&acc)[G]) {
+    if constexpr (G >= 4) {
+#pragma unroll
+        for (int g4 = 0; g4 < G; g4 += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(e + g4);
+            acc[g4] = fmaf(s, v.x, acc[g4]);
+            acc[g4 + 1] = fmaf(s, v.y, acc[g4 + 1]);
+            acc[g4 + 2] = fmaf(s, v.z, acc[g4 + 2]);
+            acc[g4 + 3] = fmaf(s, v.w, acc[g4 + 3]);
+        }
+    } else if constexpr (G == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(e);
+        acc[0] = fmaf(s, v.x, acc[0]);
+        acc[1] = fmaf(s, v.y, acc[1]);
+    } else {
+        acc[0] = fmaf(s, e[0], acc[0]);
+    }
+}
+
+// Gathers the LUT entries of one (pair, code) for the G heads into e[].
+template <int G>
+__device__ __forceinline__ void lut_load(const float *src, float (&e)[G]) {
+    if constexpr (G >= 4) {
+#pragma unroll
+        for (int g4 = 0; g4 < G; g4 += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + g4);
+            e[g4] = v.x;
+            e[g4 + 1] = v.y;
+            e[g4 + 2] = v.z;
+            e[g4 + 3] = v.w;
+        }
+    } else if constexpr (G == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(src);
+        e[0] = v.x;
+        e[1] = v.y;
+    } else {
+        e[0] = src[0];
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void logits_t4(const CodeRegs &k, const float *lut4, float mul, float (&lg)[G]) {
+    const uint32_t tw[8] = {k.u[0].x, k.u[0].y, k.u[0].z, k.u[0].w, k.u[1].x, k.u[1].y, k.u[1].z, k.u[1].w};
+    const uint32_t sw[8] = {k.u[2].x, k.u[2].y, k.u[2].z, k.u[2].w, k.u[3].x, k.u[3].y, k.u[3].z, k.u[3].w};
     float acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    // one 16-byte unit = 32 pairs of 4-bit angle and magnitude codes
-#pragma unroll 1
-    for (int u = 0; u < 2; ++u) {
-        const uint4 t = ldg<uint4>(tb + u * 16 * P);
-        const uint4 sv = ldg<uint4>(sbp + u * 16 * P);
-        const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-        const float *lu = lut4 + u * 32 * G * 16;
+    // word by word (8 pairs): the 8 gathers are issued together, then the
+    // FMAs; a compiler fence keeps the next word's work after this one.
+    // Magnitude nibbles are split into even / odd bytes so each converts
+    // to float with a single byte-select conversion.
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const uint32_t c = (tw[j >> 3] >> ((j & 7) * 4)) & 15u;
-            const float s = (float)((sw[j >> 3] >> ((j & 7) * 4)) & 15u);
-            const float *e = lu + j * G * 16 + c;
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t t = tw[w];
+        const uint32_t se = sw[w] & 0x0F0F0F0Fu, so = (sw[w] >> 4) & 0x0F0F0F0Fu;
+        const float *lu = lut4 + w * 8 * 16 * G;
+        float e[8][G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = fmaf(s, e[g * 16], acc[g]);
+        for (int j = 0; j < 8; ++j) lut_load<G>(lu + (j * 16 + ((t >> (4 * j)) & 15u)) * G, e[j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sb = (j & 1) ? so : se;
+            const float s = (float)((sb >> (8 * (j >> 1))) & 0xFFu);
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = fmaf(s, e[j][g], acc[g]);
         }
-    }
-    const float m = r * mul * (1.0f / 15.0f);
-#pragma unroll
-    for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
-}
-
-template <int G, int P>
-__device__ __forceinline__ void logits_t2(const uint8_t *blk, int slot, const float *lut2, float mul,
-                                          float (&lg)[G]) {
-    const float r = h2f(ldg<uint16_t>(blk + 2 * slot));
-    const uint8_t *tb = blk + 2 * P;
-    const uint8_t *sbp = tb + 16 * P;
-    const uint4 t0 = ldg<uint4>(tb + slot * 16);
-    const uint4 s0 = ldg<uint4>(sbp + slot * 16);
-    const uint2 s1 = ldg<uint2>(sbp + 16 * P + slot * 8);
-    // half h covers pairs 32h..32h+31: angle words 2h, 2h+1 (2-bit codes),
-    // magnitude words 3h..3h+2 (3-bit codes, 96 bits)
-    uint32_t tw[4] = {t0.x, t0.y, t0.z, t0.w};
-    uint32_t sw[6] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y};
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    const float *lu = lut2;
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const uint32_t c = (tw[j >> 4] >> ((j & 15) * 2)) & 3u;
-            const int bit = 3 * j, wd = bit >> 5, sh = bit & 31;
-            uint32_t sv;
-            if (sh <= 29)
-                sv = (sw[wd] >> sh) & 7u;
-            else   // the code straddles two words
-                sv = ((sw[wd] >> sh) | (sw[wd + 1] << (32 - sh))) & 7u;
-            const float s = (float)sv;
-            const float *e = lu + j * G * 4 + c;
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = fmaf(s, e[g * 4], acc[g]);
-        }
-        tw[0] = tw[2];
-        tw[1] = tw[3];
-        sw[0] = sw[3];
-        sw[1] = sw[4];
-        sw[2] = sw[5];
-        lu += 32 * G * 4;
-    }
-    const float m = r * mul * (1.0f / 7.0f);
-#pragma unroll
-    for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
-}
-
-template <int G, int P>
-__device__ __forceinline__ void logits_t8(const uint8_t *blk, int slot, const float2 *cs8, const float *q8,
-                                          float mul, float (&lg)[G]) {
-    const float r = h2f(ldg<uint16_t>(blk + 2 * slot));
-    const uint8_t *tb = blk + 2 * P + slot * 16;
-    const uint8_t *sbp = blk + 2 * P + 64 * P + slot * 16;
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    // one 16-byte unit = 16 pairs of 8-bit codes
-#pragma unroll 1
-    for (int u = 0; u < 4; ++u) {
-        const uint4 t = ldg<uint4>(tb + u * 16 * P);
-        const uint4 sv = ldg<uint4>(sbp + u * 16 * P);
-        const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-        const float *qu = q8 + u * 16 * G * 2;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint32_t c = (tw[j >> 2] >> ((j & 3) * 8)) & 255u;
-            const float s = (float)((sw[j >> 2] >> ((j & 3) * 8)) & 255u);
-            const float2 cs = cs8[c];
-            const float ux = s * cs.x, uy = s * cs.y;
-            const float *qq = qu + j * G * 2;
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = fmaf(ux, qq[2 * g], fmaf(uy, qq[2 * g + 1], acc[g]));
-        }
-    }
-    const float m = r * mul * (1.0f / 255.0f);
-#pragma unroll
-    for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
-}
-
-// ---- split-K pass ----------------------------------------------------------
-template <int G, int P, int NW, int WPE>
-__global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
-    constexpr int TPG = 64 / P;       // pages per 64-token group
-    constexpr int KB = P / 8;         // 8-token value blocks per page
-    constexpr int NBLK = TPG * KB;    // value blocks per group (8)
-    constexpr int RED = NW * G * 130;
-    constexpr int LUTF = 64 * G * 16 + 64 * G * 4;
-    __shared__ float lut[(LUTF > RED) ? LUTF : RED];   // T4 then T2 tables; reused for the wave merge
-    __shared__ float2 cs8[256];
-    __shared__ float q8[64 * G * 2];                     // [j][g][x|y]
-    __shared__ float pbuf[NW][64 * G];                   // [wave][token][g]
-    float *lut4 = lut;
-    float *lut2 = lut + 64 * G * 16;
-
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int row = b * a.Hkv + h;
-    const int np = a.num_pages[row];
-    const int p0 = chunk * a.chunk_pages;
-    if (p0 >= np) return;
-    const int p1 = min(p0 + a.chunk_pages, np);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    constexpr int NT = NW * 64;
-
-    // -- stage the angle LUTs of the G query heads --------------------------
-    const float *qrow = a.q + ((size_t)b * a.Hq + (size_t)h * G) * kD;
-    for (int i = tid; i < G * kD; i += NT) {
-        const int g = i >> 7, d = i & 127;
-        q8[((d >> 1) * G + g) * 2 + (d & 1)] = qrow[i];
-    }
-    for (int c = tid; c < 256; c += NT) cs8[c] = grid_dir(c);
-    __syncthreads();
-    for (int i = tid; i < 64 * G * 16; i += NT) {
-        const int c = i & 15, jg = i >> 4;
-        lut4[i] = lut_entry(q8[jg * 2], q8[jg * 2 + 1], cs8[c * 16]);
-    }
-    for (int i = tid; i < 64 * G * 4; i += NT) {
-        const int c = i & 3, jg = i >> 2;
-        lut2[i] = lut_entry(q8[jg * 2], q8[jg * 2 + 1], cs8[c * 64]);
-    }
-    __syncthreads();
-
-    const float mul = a.scale * kLog2e;
-    float m_run[G], l_run[G], acc0[G], acc1[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m_run[g] = -INFINITY;
-        l_run[g] = 0.f;
-        acc0[g] = 0.f;
-        acc1[g] = 0.f;
-    }
-
-    const int n_groups = (p1 - p0 + TPG - 1) / TPG;
-    const int pg = lane / P, slot = lane % P;
-    const int32_t *ptab = a.page_table + (size_t)row * a.maxp;
-    for (int grp = w; grp < n_groups; grp += NW) {
-        // Opaque to the optimiser: keeps loop-invariant LDS reads (query
-        // pairs, tables) inside the loop instead of hoisting them into
-        // registers for the whole loop.
         asm volatile("" ::: "memory");
-        const int pbase = p0 + grp * TPG;
-        const int npg = __builtin_amdgcn_readfirstlane(min(TPG, p1 - pbase));   // pages in this group
-        const int nblk = npg * KB;
-        const bool pvalid = pg < npg;
-        const int page = pvalid ? ptab[pbase + pg] : 0;
-        int pk[TPG];
+    }
+    const float m = h2f(k.r) * mul * (1.0f / 15.0f);
 #pragma unroll
-        for (int k = 0; k < TPG; ++k) pk[k] = __builtin_amdgcn_readlane(page, k * P);
+    for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
+}
 
-        // value block `blk` (8 tokens): dimension `lane` and `lane + 64`
-        auto vaddr = [&](int blk) -> const uint16_t * {
-            return a.value_pool + (size_t)pk[blk / KB] * P * kD + (blk % KB) * 1024 + lane * 8;
-        };
-        uint4 vb0[2], vb1[2];
+template <int G>
+__device__ __forceinline__ void logits_t2(const CodeRegs &k, const float *lut2, float mul, float (&lg)[G]) {
+    // quarter q covers pairs 16q..16q+15: angle word q (2-bit codes) and
+    // magnitude bits [48q, 48q+48) (3-bit codes)
+    const uint32_t tw[4] = {k.u[0].x, k.u[0].y, k.u[0].z, k.u[0].w};
+    const uint32_t sw[7] = {k.u[1].x, k.u[1].y, k.u[1].z, k.u[1].w, k.h.x, k.h.y, 0u};
+    float acc[G];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            vb0[i] = make_uint4(0u, 0u, 0u, 0u);
-            vb1[i] = vb0[i];
-            if (i < nblk) {
-                vb0[i] = ldg<uint4>(vaddr(i));
-                vb1[i] = ldg<uint4>(vaddr(i) + 64 * 8);
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t t = tw[q];
+        const int wd = (48 * q) >> 5, sh = (48 * q) & 31;
+        const uint64_t win = ((((uint64_t)sw[wd + 1]) << 32) | sw[wd]) >> sh;
+        const float *lu = lut2 + q * 16 * 4 * G;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {   // 8 pairs at a time
+            float e[8][G];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int jj = 8 * h8 + j;
+                lut_load<G>(lu + (jj * 4 + ((t >> (2 * jj)) & 3u)) * G, e[j]);
             }
-        }
-
-        uint2 meta = make_uint2(0u, 0u);
-        if (pvalid) meta = ldg<uint2>(a.page_meta + page);
-        const int tier = meta.x & 0xFF;
-        const int count = (meta.x >> 8) & 0xFF;
-        const bool valid = pvalid && slot < count;
-
-        float lg[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
-        const uint8_t *blkp = a.arena + (size_t)meta.y * 16;
+            for (int j = 0; j < 8; ++j) {
+                const int jj = 8 * h8 + j;
+                const float s = (float)((uint32_t)(win >> (3 * jj)) & 7u);
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g] = fmaf(s, e[j][g], acc[g]);
+            }
+            asm volatile("" ::: "memory");
+        }
+    }
+    const float m = h2f(k.r) * mul * (1.0f / 7.0f);
+#pragma unroll
+    for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
+}
+
+// 16 pairs of 8-bit codes: angle word array tw[4], magnitude word array sw[4]
+template <int G>
+__device__ __forceinline__ void t8_unit(const uint32_t (&tw)[4], const uint32_t (&sw)[4], const float2 *cs8,
+                                        const float *qu, float (&acc)[G]) {
+    uint32_t tcur = 0, scur = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if ((j & 3) == 0) {
+            tcur = pin(tw[j >> 2]);
+            scur = pin(sw[j >> 2]);
+        }
+        const uint32_t c = (tcur >> ((j & 3) * 8)) & 255u;
+        const float s = (float)((scur >> ((j & 3) * 8)) & 255u);
+        const float2 cs = cs8[c];
+        const float ux = s * cs.x, uy = s * cs.y;
+        const float *qq = qu + j * G * 2;
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = fmaf(ux, qq[2 * g], fmaf(uy, qq[2 * g + 1], acc[g]));
+        pair_fence<G>(j);
+    }
+}
+
+template <int G, int P>
+__device__ __forceinline__ void logits_t8(const CodeRegs &k, const float2 *cs8, const float *q8, float mul,
+                                          float (&lg)[G]) {
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint32_t tw[4] = {k.u[u].x, k.u[u].y, k.u[u].z, k.u[u].w};
+        const uint32_t sw[4] = {k.u[2 + u].x, k.u[2 + u].y, k.u[2 + u].z, k.u[2 + u].w};
+        t8_unit<G>(tw, sw, cs8, q8 + u * 16 * G * 2, acc);
+    }
+#pragma unroll
+    for (int u = 2; u < 4; ++u) {
+        const uint4 t = ldg<uint4>(k.c + u * 16 * P);
+        const uint4 v = ldg<uint4>(k.c + (4 + u) * 16 * P);
+        const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+        const uint32_t sw[4] = {v.x, v.y, v.z, v.w};
+        t8_unit<G>(tw, sw, cs8, q8 + u * 16 * G * 2, acc);
+    }
+    const float m = h2f(k.r) * mul * (1.0f / 255.0f);
+#pragma unroll
+    for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
+}
+
+// ---- ADA logit policy for the split-K core -------------------------------
+template <int G, int P>
+struct AdaPolicy {
+    struct Smem {
+        float lut4[64 * 16 * G];   // [j][c][g] 4-bit angle grid
+        float lut2[64 * 4 * G];    // [j][c][g] 2-bit angle grid
+        float2 cs8[256];           // cos / sin of the 8-bit grid
+        float2 cs4[16];            // the 4-bit sub-grid, contiguous (conflict-free reads)
+        float2 cs2[4];             // the 2-bit sub-grid
+        float q8[64 * G * 2];      // [j][g][x|y] query pairs (T8, factorised)
+    };
+    const int32_t *num_pages_;
+    const ada_page_meta_t *page_meta;
+    const uint8_t *arena;
+    const float *q;
+    int32_t Hq;
+    float mul;   // softmax scale * log2(e)
+
+    __device__ int num_pages(int row, int) const { return num_pages_[row]; }
+    __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
+
+    __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
+        const float *qrow = q + ((size_t)b * Hq + (size_t)h * G) * kD;
+        for (int i = tid; i < G * kD; i += nt) {
+            const int g = i >> 7, d = i & 127;
+            s.q8[((d >> 1) * G + g) * 2 + (d & 1)] = qrow[i];
+        }
+        for (int c = tid; c < 256; c += nt) {
+            const float2 d = grid_dir(c);
+            s.cs8[c] = d;
+            if ((c & 15) == 0) s.cs4[c >> 4] = d;
+            if ((c & 63) == 0) s.cs2[c >> 6] = d;
+        }
+        __syncthreads();
+        // [pair][code][head]; consecutive threads take consecutive heads, then codes
+        for (int i = tid; i < 64 * 16 * G; i += nt) {
+            const int g = i % G, c = (i / G) & 15, j = i / (16 * G);
+            s.lut4[i] = lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs4[c]);
+        }
+        for (int i = tid; i < 64 * 4 * G; i += nt) {
+            const int g = i % G, c = (i / G) & 3, j = i / (4 * G);
+            s.lut2[i] = lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs2[c]);
+        }
+    }
+
+    using Codes = CodeRegs;
+    __device__ Codes fetch(int, uint2 meta, int slot, bool valid) const {
+        return fetch_codes<P>(arena + (size_t)meta.y * 16, meta.x & 0xFF, slot);
+    }
+
+    __device__ void logits(const Smem &s, const Codes &k, uint2 meta, bool valid, float (&lg)[G]) const {
+        const int tier = meta.x & 0xFF;
         if (__any(valid && tier == ADA_TIER_T4)) {
-            if (valid && tier == ADA_TIER_T4) logits_t4<G, P>(blkp, slot, lut4, mul, lg);
+            if (valid && tier == ADA_TIER_T4) logits_t4<G>(k, s.lut4, mul, lg);
         }
         if (__any(valid && tier == ADA_TIER_T2)) {
-            if (valid && tier == ADA_TIER_T2) logits_t2<G, P>(blkp, slot, lut2, mul, lg);
+            if (valid && tier == ADA_TIER_T2) logits_t2<G>(k, s.lut2, mul, lg);
         }
         if (__any(valid && tier == ADA_TIER_T8)) {
-            if (valid && tier == ADA_TIER_T8) logits_t8<G, P>(blkp, slot, cs8, q8, mul, lg);
-        }
-
-        // online softmax (base 2)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mx = wave_max(valid ? lg[g] : -INFINITY);
-            const float mnew = fmaxf(m_run[g], mx);
-            const float alpha = (m_run[g] == -INFINITY) ? 0.f : exp2f(m_run[g] - mnew);
-            const float p = valid ? exp2f(lg[g] - mnew) : 0.f;
-            l_run[g] = l_run[g] * alpha + p;
-            acc0[g] *= alpha;
-            acc1[g] *= alpha;
-            m_run[g] = mnew;
-            pbuf[w][lane * G + g] = p;
-        }
-        wave_lds_sync();
-
-        // value accumulation, two blocks in flight
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-            if (blk >= nblk) break;
-            const uint4 x0 = vb0[blk & 1], x1 = vb1[blk & 1];
-            if (blk + 2 < nblk) {
-                vb0[blk & 1] = ldg<uint4>(vaddr(blk + 2));
-                vb1[blk & 1] = ldg<uint4>(vaddr(blk + 2) + 64 * 8);
-            }
-            const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
-            const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int tok = blk * 8 + i;
-                const float f0 = h2f((i & 1) ? (a0[i >> 1] >> 16) : (a0[i >> 1] & 0xFFFFu));
-                const float f1 = h2f((i & 1) ? (a1[i >> 1] >> 16) : (a1[i >> 1] & 0xFFFFu));
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float p = pbuf[w][tok * G + g];
-                    acc0[g] = fmaf(p, f0, acc0[g]);
-                    acc1[g] = fmaf(p, f1, acc1[g]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        wave_lds_sync();
-    }
-
-    // -- merge the waves of the work-group, write the chunk's partial --------
-#pragma unroll
-    for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
-    __syncthreads();
-    float *red = lut;   // [w][g][130]: m, l, acc[128]
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float *rr = red + (w * G + g) * 130;
-        if (lane == 0) {
-            rr[0] = m_run[g];
-            rr[1] = l_run[g];
-        }
-        rr[2 + lane] = acc0[g];
-        rr[2 + 64 + lane] = acc1[g];
-    }
-    __syncthreads();
-    const size_t bq0 = (size_t)b * a.Hq + (size_t)h * G;
-    for (int i = tid; i < G * kD; i += NT) {
-        const int g = i >> 7, d = i & 127;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red[(ww * G + g) * 130]);
-        float o = 0.f, L = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float mw = red[(ww * G + g) * 130];
-            const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-            o = fmaf(red[(ww * G + g) * 130 + 2 + d], f, o);
-            L = fmaf(red[(ww * G + g) * 130 + 1], f, L);
-        }
-        const size_t pidx = (bq0 + g) * a.S + chunk;
-        a.pacc[pidx * kD + d] = o;
-        if (d == 0) {
-            a.pm[pidx] = M;
-            a.pl[pidx] = L;
+            if (valid && tier == ADA_TIER_T8) logits_t8<G, P>(k, s.cs8, s.q8, mul, lg);
         }
     }
+};
+
+template <int G, int P, int NW, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
+    using Pol = AdaPolicy<G, P>;
+    constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
+    constexpr size_t RAW = sizeof(typename Pol::Smem) > RED ? sizeof(typename Pol::Smem) : RED;
+    __shared__ __align__(16) unsigned char raw[RAW];   // policy tables, later the wave-merge buffer
+    __shared__ core::CoreSmem<G, NW> cs;
+    Pol pol;
+    pol.num_pages_ = a.num_pages;
+    pol.page_meta = a.page_meta;
+    pol.arena = a.arena;
+    pol.q = a.q;
+    pol.Hq = a.Hq;
+    pol.mul = a.scale * core::kLog2e;
+    core::CoreArgs c;
+    c.page_table = a.page_table;
+    c.value_pool = a.value_pool;
+    c.pm = a.pm;
+    c.pl = a.pl;
+    c.pacc = a.pacc;
+    c.Hq = a.Hq;
+    c.Hkv = a.Hkv;
+    c.maxp = a.maxp;
+    c.chunk_pages = a.chunk_pages;
+    c.S = a.S;
+    core::split_k<G, P, NW>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
+                            reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// ---- reduction pass: merge the chunks of every (sequence, query head) -------
 __global__ __launch_bounds__(128) void decode_reduce_kernel(DecodeLaunch a) {
     const int bq = blockIdx.x;
     const int b = bq / a.Hq, hq = bq % a.Hq;
     const int G = a.Hq / a.Hkv;
     const int np = a.num_pages[b * a.Hkv + hq / G];
-    const int nc = (np + a.chunk_pages - 1) / a.chunk_pages;
-    const int d = threadIdx.x;
-    const size_t base = (size_t)bq * a.S;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.pm[base + c]);
-    if (nc == 0 || M == -INFINITY) {
-        a.out[(size_t)bq * kD + d] = 0.f;
-        if (a.lse && d == 0) a.lse[bq] = -INFINITY;
-        return;
-    }
-    float L = 0.f, o = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float f = exp2f(a.pm[base + c] - M);
-        L = fmaf(a.pl[base + c], f, L);
-        o = fmaf(a.pacc[(base + c) * kD + d], f, o);
-    }
-    a.out[(size_t)bq * kD + d] = o / L;
-    if (a.lse && d == 0) a.lse[bq] = (M + log2f(L)) * 0.69314718055994531f;
+    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, a.out, a.lse);
 }
 
 // ---- stand-alone LUT builder --------------------------------------------
@@ -406,7 +375,7 @@ __global__ __launch_bounds__(256) void build_lut_kernel(const float *q, float *l
 template <int G, int P>
 hipError_t launch_gp(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
-    constexpr int WPE = (G >= 8) ? 2 : 4;
+    constexpr int WPE = (G >= 8) ? 2 : 3;
     dim3 grid(a.S, a.Hkv, a.B);
     hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE>), grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();

@@ -246,6 +246,15 @@ ada_status_t ada_dense_decode(const ada_config_t *cfg, int32_t B, int32_t max_pa
  * pointers: calibration of memory counters and the stream bandwidth ceiling. */
 ada_status_t ada_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/* Streaming read of `bytes` (multiple of 16) from device memory: the
+ * bandwidth ceiling a read-dominated kernel can reach on this device.
+ * variant 0: one 16-byte load per lane in flight, grid-stride (the active
+ * work-groups read a moving window); 1: four loads; 2: four with the
+ * non-temporal hint; 3: eight with the hint; 4: each work-group reads its
+ * own contiguous region (many distant streams).  `out` (device, 1 word) is only
+ * written when the xor of the data hits a fixed value. */
+ada_status_t ada_probe_read(const void *src, size_t bytes, int32_t variant, uint32_t *out, void *stream);
+
 /* Host-side evaluation of the library's fp64 -> fp16 radius rounding (round
  * to nearest even straight from fp64, saturating at 65504): the same code the
  * encoder runs on the device, exported so CPU tests can check it. */

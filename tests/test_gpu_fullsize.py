@@ -9,7 +9,8 @@ import compressed_kv_cache_ada_amd as ada
 import workloads as W
 from oracle import oracle as O
 from tests.gpu_util import check_outputs, compare_caches, gpu_pack, log, oracle_cache, to_dev
-from tests.util import dense_attention, dense_pages
+from tests.util import dense_attention
+from workloads import dense_pages
 
 pytestmark = pytest.mark.gpu
 

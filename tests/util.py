@@ -79,18 +79,3 @@ def near_boundary_pairs(tb, per_boundary=2):
                 a, b = -b, a
     return pairs
 
-
-def dense_pages(keys16, values16, P):
-    """Lay out un-dropped fp16 keys / values [B][Hkv][ctx][128] (uint16 bits)
-    as dense pages: key page [16 dim blocks][P][8], value page [P/8][128][8];
-    row (b, h) owns pages row*npr .. row*npr + npr - 1.  Returns
-    (k_pool [pages][P*128], v_pool [pages][P*128], page_table [rows][npr])."""
-    B, H, ctx, _ = keys16.shape
-    npr = -(-ctx // P)
-    pad = npr * P - ctx
-    k = np.pad(keys16, ((0, 0), (0, 0), (0, pad), (0, 0)))
-    v = np.pad(values16, ((0, 0), (0, 0), (0, pad), (0, 0)))
-    k = k.reshape(B * H * npr, P, 16, 8).transpose(0, 2, 1, 3).reshape(B * H * npr, P * 128)
-    v = v.reshape(B * H * npr, P // 8, 8, 128).transpose(0, 1, 3, 2).reshape(B * H * npr, P * 128)
-    pt = np.arange(B * H * npr, dtype=np.int32).reshape(B * H, npr)
-    return np.ascontiguousarray(k), np.ascontiguousarray(v), pt
