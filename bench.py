@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--chunk-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=10)
+    ap.add_argument("--cold-steps", type=int, default=0)
     return ap.parse_args()
 
 
@@ -155,18 +155,22 @@ def main():
     torch.cuda.synchronize()
     k_ms = e0.elapsed_time(e1) / args.steps
 
-    # cold steps: the 256 MB last-level cache is flushed (1 GB of writes) before each
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # cold steps: before each, 1 GiB of another buffer is streamed through the
+    # caches with a read kernel (the 256 MB last-level cache then holds clean
+    # lines of that buffer, so no write-back is charged to the decode)
     cold = []
-    for _ in range(args.cold_steps):
-        flush.fill_(1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        ada.decode_partials(cache, q, w["scale"], ws)
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del flush
+    if args.cold_steps:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fsink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(args.cold_steps):
+            ada.probe_read(flush, 1 << 30, 0, fsink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ada.decode_partials(cache, q, w["scale"], ws)
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
 
     # copy probe: streaming ceiling of this machine (read + write bytes)
     nb = 1 << 30
@@ -280,23 +284,27 @@ def dense_reference(w, ada, torch, cfg):
             "token_heads_per_s": token_heads / (ms * 1e-3)}
 
 
-def cpu_baseline(w, kept_total, max_row, n_pages, units):
+def cpu_baseline(w, kept_total, max_row, n_pages, units, min_seconds=10.0, max_steps=20):
     """The fp64 CPU oracle, as it stands, decoding the same workload on the
-    host's cores (pages built by the oracle's own pack, untimed)."""
+    host's cores (pages built by the oracle's own pack, untimed).  Decode
+    steps over the whole batch are repeated until about min_seconds of CPU
+    work have been timed."""
     from oracle import oracle as O
-    cores = len(os.sched_getaffinity(0))
+    # the host share of one GPU is at most 16 cores, whatever the affinity mask shows
+    cores = min(16, len(os.sched_getaffinity(0)))
     B = w["B"]
-    # bounded sample: whole sequences of the workload, about 10-30 s of CPU work
-    b_s = B
-    oc = O.Cache(w["P"], w["Hq"], w["Hkv"], b_s, max_row, n_pages, units)
-    assert O.pack(oc, w["ctx_len"][:b_s], w["tiers"][:b_s], w["keys"][:b_s], w["values"][:b_s]) == O.OK
-    t0 = time.perf_counter()
-    O.decode(oc, w["q"][:b_s], w["scale"], nthreads=cores)
-    dt = time.perf_counter() - t0
-    kept = int((w["tiers"][:b_s] >= 0).sum())
-    return {"value": kept / dt, "unit": "KV token-heads/s", "cores": cores, "kind": "oracle",
+    oc = O.Cache(w["P"], w["Hq"], w["Hkv"], B, max_row, n_pages, units)
+    assert O.pack(oc, w["ctx_len"], w["tiers"], w["keys"], w["values"], nthreads=cores) == O.OK
+    steps, dt = 0, 0.0
+    while steps < max_steps and (steps == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        O.decode(oc, w["q"], w["scale"], nthreads=cores)
+        dt += time.perf_counter() - t0
+        steps += 1
+    return {"value": kept_total * steps / dt, "unit": "KV token-heads/s", "cores": cores, "kind": "oracle",
             "seconds": dt,
-            "sample": f"{b_s} of {B} sequences (all heads, all kept tokens): {kept} token-heads, one decode step"}
+            "sample": f"{steps} decode steps over all {B} sequences (all heads, all kept tokens, "
+                      f"{kept_total} token-heads per step), same queries each step"}
 
 
 if __name__ == "__main__":

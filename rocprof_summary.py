@@ -1,0 +1,146 @@
+"""Turn rocprofv3 result databases of a bench.py run into the short text
+summaries kept under profiles/.
+
+    python rocprof_summary.py stats --db KT.db --workload llama8b --cmd "..."
+    python rocprof_summary.py pmc --fetch-db F.db --write-db W.db --workload llama8b \
+        --cmd-fetch "..." --cmd-write "..." [--bench-json B.json]
+
+`stats` summarises a `--kernel-trace --stats` run: every kernel's call count
+and duration, and the split-K decode kernel's per-dispatch spread.  `pmc`
+turns the FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) into HBM bytes
+per split-K launch, calibrated by the same counters on the copy probe of the
+same run, which moves exactly 1 GiB each way per launch.  The record carries
+the hash of the decode kernel's sources, so bench.py ignores it once the
+kernel has changed.
+"""
+import argparse
+import collections
+import json
+import os
+import sqlite3
+import statistics
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE = "decode_partials_kernel"
+COPY = "probe_copy_kernel"
+COPY_BYTES = 1 << 30
+
+
+def short(name):
+    """Kernel name without namespace, return type and argument list."""
+    name = name.replace("ada::(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    if "(" in name:
+        name = name[: name.index("(")]
+    return name if len(name) < 80 else name[:77] + "..."
+
+
+def per_kernel_durations(db):
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels").fetchall()
+    agg = collections.defaultdict(list)
+    for name, d in rows:
+        agg[name].append(d)
+    return agg
+
+
+def per_kernel_counter(db, counter):
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, dispatch_id, value from counters_collection where counter_name=?",
+                       (counter,)).fetchall()
+    per_dispatch = collections.defaultdict(lambda: collections.defaultdict(float))
+    for name, did, v in rows:
+        per_dispatch[name][did] += v      # a counter may arrive split over dimensions
+    return {k: list(d.values()) for k, d in per_dispatch.items()}
+
+
+def pick(agg, key):
+    hits = [k for k in agg if key in k]
+    if not hits:
+        raise SystemExit(f"no kernel matching {key!r} in the database")
+    return hits
+
+
+def cmd_stats(a):
+    agg = per_kernel_durations(a.db)
+    total = sum(sum(v) for v in agg.values())
+    lines = [f"# rocprofv3 kernel trace: {a.workload}", "", "Command (from the repository root):", "",
+             "```", a.cmd, "```", "",
+             "| kernel | calls | total ms | avg us | % |", "|---|---:|---:|---:|---:|"]
+    for name, d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{short(name)}` | {len(d)} | {sum(d) / 1e6:.3f} | {sum(d) / len(d) / 1e3:.2f} | "
+                     f"{100 * sum(d) / total:.1f} |")
+    lines += ["", "Split-K decode kernel, per dispatch (us):", ""]
+    for name in pick(agg, DECODE):
+        d = agg[name]
+        lines.append(f"- `{short(name)}`: n={len(d)} mean={statistics.mean(d) / 1e3:.2f} "
+                     f"median={statistics.median(d) / 1e3:.2f} min={min(d) / 1e3:.2f} max={max(d) / 1e3:.2f}")
+    out = os.path.join(PROFILES, f"ada_decode_partials_{a.workload}_kernel_stats.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def cmd_pmc(a):
+    import bench
+    fetch = per_kernel_counter(a.fetch_db, "FETCH_SIZE")
+    write = per_kernel_counter(a.write_db, "WRITE_SIZE")
+    cf = statistics.mean(fetch[pick(fetch, COPY)[0]])
+    cw = statistics.mean(write[pick(write, COPY)[0]])
+    f_scale = COPY_BYTES / (cf * 1024)
+    w_scale = COPY_BYTES / (cw * 1024)
+    kn = pick(fetch, DECODE)[0]
+    fk = statistics.mean(fetch[kn])
+    wk = statistics.mean(write[pick(write, DECODE)[0]])
+    rec = {
+        "kernel": short(kn),
+        "workload": a.workload,
+        "kernel_source_hash": bench.kernel_source_hash(),
+        "fetch_kib_per_dispatch": fk,
+        "write_kib_per_dispatch": wk,
+        "dispatches": len(fetch[kn]),
+        "copy_probe_fetch_kib": cf,
+        "copy_probe_write_kib": cw,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "hbm_read_bytes_per_launch": fk * 1024 * f_scale,
+        "hbm_write_bytes_per_launch": wk * 1024 * w_scale,
+        "hbm_bytes_per_launch": (fk * 1024 * f_scale) + (wk * 1024 * w_scale),
+        "cmd_fetch": a.cmd_fetch,
+        "cmd_write": a.cmd_write,
+    }
+    if a.bench_json:
+        with open(a.bench_json) as f:
+            b = json.loads(f.read().strip().splitlines()[-1])
+        rec["algorithmic_bytes_per_launch"] = b["roofline"]["algorithmic_bytes"]
+        rec["traffic_over_algorithmic"] = rec["hbm_bytes_per_launch"] / b["roofline"]["algorithmic_bytes"]
+    out = os.path.join(PROFILES, f"ada_decode_partials_{a.workload}_pmc.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(out)
+    print(json.dumps(rec, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--db", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--cmd", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("--fetch-db", required=True)
+    p.add_argument("--write-db", required=True)
+    p.add_argument("--workload", required=True)
+    p.add_argument("--cmd-fetch", required=True)
+    p.add_argument("--cmd-write", required=True)
+    p.add_argument("--bench-json")
+    a = ap.parse_args()
+    (cmd_stats if a.mode == "stats" else cmd_pmc)(a)
+
+
+if __name__ == "__main__":
+    main()
