@@ -46,10 +46,15 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the split-K kernel's sources with comments and blank lines
+    removed (a comment edit does not change the kernel)."""
     h = hashlib.sha256()
     for f in ("decode.hip", "decode_core.h", "ada_internal.h"):
-        with open(os.path.join(ROOT, "compressed_kv_cache_ada_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_kv_cache_ada_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -154,6 +159,13 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     k_ms = e0.elapsed_time(e1) / args.steps
+    # the reduction pass alone, K back-to-back launches
+    e0.record()
+    for _ in range(args.steps):
+        ada.decode_reduce(cache, B, out, lse, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    r_ms = e0.elapsed_time(e1) / args.steps
 
     # cold steps: before each, 1 GiB of another buffer is streamed through the
     # caches with a read kernel (the 256 MB last-level cache then holds clean
@@ -228,6 +240,7 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "kernel": "decode_partials_kernel", "kernel_ms": k_ms, "kernel_ms_event_per_launch": k_ms_each,
+            "reduce_kernel_ms": r_ms,
             "algorithmic_bytes": alg_bytes,
         },
         "step_hbm_gbps": (alg_bytes + B * Hq * 512) / (ms_step * 1e-3) / 1e9,

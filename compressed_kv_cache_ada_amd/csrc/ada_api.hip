@@ -3,6 +3,8 @@
 // allocated here; nothing throws across the boundary.
 #include <string.h>
 
+#include <algorithm>
+
 #include "ada_internal.h"
 
 using namespace ada;
@@ -52,17 +54,25 @@ ada_status_t check_cache(const ada_cache_t *c) {
 
 inline ada_status_t hip_status(hipError_t e) { return e == hipSuccess ? ADA_OK : ADA_EHIP; }
 
+// Split-K chunk length in pages.  Automatic choice: about one round of
+// resident work-groups over the whole cache (B * Hkv rows of up to maxp
+// pages), so no partial last round idles compute units and each work-group
+// builds its LUTs once for as much work as possible.
 int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp) {
     const int tpg = 64 / cfg->page_size;
     int cp = cfg->decode_chunk_pages;
     if (cp <= 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;   // MI355X
+        const int64_t slots = (int64_t)cus * decode_waves_per_simd(cfg->num_q_heads / cfg->num_kv_heads);
         const int64_t units = (int64_t)B * cfg->num_kv_heads * maxp;
-        const int64_t target_wgs = 2048;
-        cp = (int)((units + target_wgs - 1) / target_wgs);
+        cp = (int)std::min<int64_t>((units + slots - 1) / slots, 1 << 20);
     }
     cp = (cp + tpg - 1) / tpg * tpg;
     if (cp < tpg) cp = tpg;
-    if (cp > 256) cp = 256;   // page list of a work-group lives in LDS
+    if (cp > kMaxChunkPages) cp = kMaxChunkPages;   // page list of a work-group lives in LDS
     return cp;
 }
 

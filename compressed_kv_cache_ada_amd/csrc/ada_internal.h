@@ -12,6 +12,7 @@ namespace ada {
 
 constexpr int kD = 128;       // head dimension
 constexpr int kPairs = 64;    // 2-D pairs per key
+constexpr int kMaxChunkPages = 256;   // page list of a split-K work-group (in LDS)
 
 // Tier table in id order: angle bits, magnitude bits.
 __host__ __device__ constexpr int tier_tb(int t) { return t == 0 ? 8 : (t == 1 ? 4 : 2); }
@@ -38,6 +39,10 @@ __device__ __forceinline__ float2 grid_dir(int c) {
     sincospif(-1.0f + (float)c * (1.0f / 128.0f), &s, &co);
     return make_float2(co, s);
 }
+
+// Split-K decode work-groups are 4 wavefronts (one per SIMD); this many are
+// resident per compute unit (the kernels' launch bounds ask for it).
+__host__ __device__ constexpr int decode_waves_per_simd(int G) { return G >= 8 ? 2 : 3; }
 
 // ---- launchers (defined in the .hip files; called by ada_api.cpp) ------
 struct DecodeLaunch {

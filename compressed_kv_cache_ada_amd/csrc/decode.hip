@@ -107,24 +107,41 @@ __device__ __forceinline__ void lut_fma(const float *e, float s, float (&acc)[G]
     }
 }
 
-// Gathers the LUT entries of one (pair, code) for the G heads into e[].
+// Per-work-group LUT layout, per pair j with NC codes: slices of SW =
+// min(G, 4) heads, [j][slice][code][SW] -- [j][code][head] for G <= 4.  One
+// LDS read per slice returns a lane's SW heads; with at most 16 bytes per
+// code the 16 codes of a slice span 256 contiguous bytes, so the lanes'
+// random codes fall in distinct bank groups.
 template <int G>
-__device__ __forceinline__ void lut_load(const float *src, float (&e)[G]) {
-    if constexpr (G >= 4) {
+constexpr int lut_sw() { return G < 4 ? G : 4; }
+
+template <int G, int NC>
+__device__ __forceinline__ int lut_index(int j, int c, int g) {
+    constexpr int SW = lut_sw<G>();
+    return ((j * (G / SW) + g / SW) * NC + c) * SW + g % SW;
+}
+
+// Gathers the LUT entries of one (pair, code) for the G heads into e[];
+// `pair` points at the pair's NC * G floats.
+template <int G, int NC>
+__device__ __forceinline__ void lut_load(const float *pair, uint32_t c, float (&e)[G]) {
+    constexpr int SW = lut_sw<G>();
 #pragma unroll
-        for (int g4 = 0; g4 < G; g4 += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(src + g4);
-            e[g4] = v.x;
-            e[g4 + 1] = v.y;
-            e[g4 + 2] = v.z;
-            e[g4 + 3] = v.w;
+    for (int sl = 0; sl < G / SW; ++sl) {
+        const float *src = pair + (sl * NC + c) * SW;
+        if constexpr (SW == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(src);
+            e[4 * sl] = v.x;
+            e[4 * sl + 1] = v.y;
+            e[4 * sl + 2] = v.z;
+            e[4 * sl + 3] = v.w;
+        } else if constexpr (SW == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(src);
+            e[0] = v.x;
+            e[1] = v.y;
+        } else {
+            e[0] = src[0];
         }
-    } else if constexpr (G == 2) {
-        const float2 v = *reinterpret_cast<const float2 *>(src);
-        e[0] = v.x;
-        e[1] = v.y;
-    } else {
-        e[0] = src[0];
     }
 }
 
@@ -146,7 +163,7 @@ __device__ __forceinline__ void logits_t4(const CodeRegs &k, const float *lut4, 
         const float *lu = lut4 + w * 8 * 16 * G;
         float e[8][G];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lut_load<G>(lu + (j * 16 + ((t >> (4 * j)) & 15u)) * G, e[j]);
+        for (int j = 0; j < 8; ++j) lut_load<G, 16>(lu + j * 16 * G, (t >> (4 * j)) & 15u, e[j]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t sb = (j & 1) ? so : se;
@@ -182,7 +199,7 @@ __device__ __forceinline__ void logits_t2(const CodeRegs &k, const float *lut2, 
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int jj = 8 * h8 + j;
-                lut_load<G>(lu + (jj * 4 + ((t >> (2 * jj)) & 3u)) * G, e[j]);
+                lut_load<G, 4>(lu + jj * 4 * G, (t >> (2 * jj)) & 3u, e[j]);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -250,8 +267,8 @@ __device__ __forceinline__ void logits_t8(const CodeRegs &k, const float2 *cs8, 
 template <int G, int P>
 struct AdaPolicy {
     struct Smem {
-        float lut4[64 * 16 * G];   // [j][c][g] 4-bit angle grid
-        float lut2[64 * 4 * G];    // [j][c][g] 2-bit angle grid
+        float lut4[64 * 16 * G];   // 4-bit angle grid, lut_index<G, 16> layout
+        float lut2[64 * 4 * G];    // 2-bit angle grid, lut_index<G, 4> layout
         float2 cs8[256];           // cos / sin of the 8-bit grid
         float2 cs4[16];            // the 4-bit sub-grid, contiguous (conflict-free reads)
         float2 cs2[4];             // the 2-bit sub-grid
@@ -280,14 +297,15 @@ struct AdaPolicy {
             if ((c & 63) == 0) s.cs2[c >> 6] = d;
         }
         __syncthreads();
-        // [pair][code][head]; consecutive threads take consecutive heads, then codes
+        // consecutive threads fill consecutive heads, then codes
         for (int i = tid; i < 64 * 16 * G; i += nt) {
             const int g = i % G, c = (i / G) & 15, j = i / (16 * G);
-            s.lut4[i] = lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs4[c]);
+            s.lut4[lut_index<G, 16>(j, c, g)] =
+                lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs4[c]);
         }
         for (int i = tid; i < 64 * 4 * G; i += nt) {
             const int g = i % G, c = (i / G) & 3, j = i / (4 * G);
-            s.lut2[i] = lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs2[c]);
+            s.lut2[lut_index<G, 4>(j, c, g)] = lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs2[c]);
         }
     }
 
@@ -310,7 +328,7 @@ struct AdaPolicy {
     }
 };
 
-template <int G, int P, int NW, int WPE>
+template <int G, int P, int NW, int WPE, int PF>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
     using Pol = AdaPolicy<G, P>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
@@ -335,16 +353,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     c.maxp = a.maxp;
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
-    core::split_k<G, P, NW>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
+    core::split_k<G, P, NW, PF>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-__global__ __launch_bounds__(128) void decode_reduce_kernel(DecodeLaunch a) {
+__global__ __launch_bounds__(core::kReduceThreads) void decode_reduce_kernel(DecodeLaunch a) {
     const int bq = blockIdx.x;
     const int b = bq / a.Hq, hq = bq % a.Hq;
     const int G = a.Hq / a.Hkv;
     const int np = a.num_pages[b * a.Hkv + hq / G];
-    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, a.out, a.lse);
+    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, blockIdx.y, a.out,
+                        a.lse);
 }
 
 // ---- stand-alone LUT builder --------------------------------------------
@@ -375,9 +394,10 @@ __global__ __launch_bounds__(256) void build_lut_kernel(const float *q, float *l
 template <int G, int P>
 hipError_t launch_gp(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
-    constexpr int WPE = (G >= 8) ? 2 : 3;
+    constexpr int WPE = decode_waves_per_simd(G);
+    constexpr int PF = 0;
     dim3 grid(a.S, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, PF>), grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -399,7 +419,7 @@ hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Hq, core::kReduceSlices), dim3(core::kReduceThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -6,15 +6,17 @@
 // critical path has no dependent global loads before the code fetch), and
 // the policy stages its per-query tables.  Then each wavefront walks 64-token
 // groups (4 pages of 16 / 2 pages of 32):
-//   1. issue all value loads of the group (16 x 128-bit per lane): each lane
-//      gets 8 consecutive tokens of one head dimension, which is exactly the
-//      A operand of v_mfma_f32_16x16x32_f16 (value pages are stored in
-//      8-token groups, dimension-major);
+//   1. fetch the tokens' codes (lane = token, policy);
 //   2. logits for the G query heads, lane = token (policy);
-//   3. online softmax per head: wavefront max, exp2, running sums; the
+//   3. issue the group's value loads (16 x 128-bit per lane): each lane gets
+//      8 consecutive tokens of one head dimension, which is exactly the A
+//      operand of v_mfma_f32_16x16x32_f16 (value pages are stored in 8-token
+//      groups, dimension-major).  They are issued after the logit arithmetic
+//      so they are not held in registers through it;
+//   4. online softmax per head: wavefront max, exp2, running sums; the
 //      weights are written to LDS as fp16 hi + lo parts (p ~ hi + lo to
 //      about 2^-22 relative), head-major;
-//   4. value accumulation O^T[dims x heads] += V^T[dims x 32 tokens] .
+//   5. value accumulation O^T[dims x heads] += V^T[dims x 32 tokens] .
 //      P^T[32 tokens x heads] on the matrix cores: 8 dimension tiles of 16,
 //      two 32-token K steps, hi and lo weights -> 32 MFMAs per group.  This
 //      product is a genuine dense contraction; the logit path is not.
@@ -32,7 +34,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxChunkPages = 256;   // LDS page list of a work-group
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -80,7 +81,7 @@ struct CoreSmem {
 //   void prologue(smem, b, h, tid, nthreads)
 //   Codes fetch(page, meta, slot, valid)        issue the token's code loads
 //   void logits(smem, codes, meta, valid, lg[G]) lane = token, base-2 scaled
-template <int G, int P, int NW, class Pol>
+template <int G, int P, int NW, int PF, class Pol>
 __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typename Pol::Smem &ps,
                                         CoreSmem<G, NW> &cs, float *red, int chunk, int h, int b) {
     constexpr int TPG = 64 / P;     // pages per group
@@ -126,20 +127,71 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 
     const int n_groups = (nch + TPG - 1) / TPG;
     const int pg = lane / P, slot = lane % P;
-    for (int grp = w; grp < n_groups; grp += NW) {
-        asm volatile("" ::: "memory");   // keep LDS reads of the tables inside the loop
-        const int gbase = grp * TPG;
-
-        // 1. the tokens' code units (lane = token)
+    struct Tok {
+        typename Pol::Codes codes;
+        uint2 meta;
+        bool valid;
+    };
+    // the tokens' code units of group g (lane = token); lanes past the row's
+    // last page read the group's first page (weight 0)
+    auto stage = [&](int g) {
+        const int gbase = g * TPG;
         const int pidx = gbase + pg;
         const int page_raw = cs.pages[pidx];
         const bool pvalid = page_raw >= 0;
-        // lanes past the row's last page read the group's first page (weight 0)
         const int page = pvalid ? page_raw : cs.pages[gbase];
-        const uint2 meta = cs.meta[pvalid ? pidx : gbase];
-        const int count = (meta.x >> 8) & 0xFF;
-        const bool valid = pvalid && slot < count;
-        const typename Pol::Codes codes = pol.fetch(page, meta, slot, valid);
+        Tok t;
+        t.meta = cs.meta[pvalid ? pidx : gbase];
+        t.valid = pvalid && slot < (int)((t.meta.x >> 8) & 0xFF);
+        t.codes = pol.fetch(page, t.meta, slot, t.valid);
+        return t;
+    };
+    // the group's value blocks -> MFMA A operands; a block past the row's
+    // last page is read from the group's first page instead (weight 0)
+    auto load_values = [&](int g, uint4 (&va)[2][8]) {
+        const int gb = g * TPG;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int blk = 4 * kc + kq;            // 8-token block of the group
+            const int vpage = cs.pages[gb + blk / KB];
+            const uint16_t *base =
+                a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gb]) * P * kD + (blk % KB) * 1024 + n_head * 8;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
+        }
+    };
+    Tok nxt{};
+    uint4 va_nxt[2][8];
+    if (PF >= 1 && w < n_groups) nxt = stage(w);
+    if (PF == 2 && w < n_groups) load_values(w, va_nxt);
+    for (int grp = w; grp < n_groups; grp += NW) {
+        asm volatile("" ::: "memory");   // keep LDS reads of the tables inside the loop
+
+        // 1. the tokens' code units; with PF the next group's codes (and with
+        //    PF = 2 its values) are issued now, this group's one iteration
+        //    earlier
+        Tok cur;
+        uint4 va[2][8];
+        if constexpr (PF >= 1) {
+            cur = nxt;
+            if constexpr (PF == 2) {
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) va[kc][t] = va_nxt[kc][t];
+            }
+            if (grp + NW < n_groups) {
+                nxt = stage(grp + NW);
+                if constexpr (PF == 2) load_values(grp + NW, va_nxt);
+            }
+        } else {
+            cur = stage(grp);
+        }
+        const typename Pol::Codes &codes = cur.codes;
+        const uint2 meta = cur.meta;
+        const bool valid = cur.valid;
+        // PF = 3: this group's values are issued before its logits
+        if constexpr (PF == 3) load_values(grp, va);
 
         // 2. logits, lane = token
         float lg[G];
@@ -147,20 +199,10 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
         pol.logits(ps, codes, meta, valid, lg);
 
-        // 3. values -> MFMA A operands, issued after the logit arithmetic so
+        // 3. values (without PF = 2), issued after the logit arithmetic so
         //    they are not held in registers through it (other wavefronts'
-        //    work covers their latency).  A block past the row's last page
-        //    is read from the group's first page instead: weight 0.
-        uint4 va[2][8];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int blk = 4 * kc + kq;            // 8-token block of the group
-            const int vpage = cs.pages[gbase + blk / KB];
-            const uint16_t *base =
-                a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gbase]) * P * kD + (blk % KB) * 1024 + n_head * 8;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
-        }
+        //    work covers their latency)
+        if constexpr (PF < 2) load_values(grp, va);
 
         // 4. online softmax, weights to LDS as fp16 hi + lo
         float alpha_n = 1.f;
@@ -248,26 +290,70 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 // number of chunks holding data for a row of np pages (page groups of tpg)
 __device__ __forceinline__ int chunks_with_data(int np, int tpg, int S) { return min(S, (np + tpg - 1) / tpg); }
 
-// reduction pass over the chunks of one (sequence, query head)
+// Reduction pass.  One work-group of kReduceThreads per (sequence, query
+// head, 32-dimension slice): the running max and the weighted sum of the
+// chunks' partial sums are block reductions over the chunks; the output
+// slice is summed by 8 chunk lanes x 32 dimensions, each lane taking every
+// 8th chunk, then merged in LDS.  Every order is fixed, so the result is
+// deterministic.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceSlices = 4;   // 128 dimensions / 32
+
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float *scratch) {
+    v = MAX ? wave_max(v) : wave_sum(v);
+    const int wv = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[wv] = v;
+    __syncthreads();
+    float r = scratch[0];
+#pragma unroll
+    for (int i = 1; i < kReduceThreads / 64; ++i) r = MAX ? fmaxf(r, scratch[i]) : r + scratch[i];
+    return r;
+}
+
 __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, const float *pacc, int S, int nc,
-                                              int bq, float *out, float *lse) {
-    const int d = threadIdx.x;
+                                              int bq, int slice, float *out, float *lse) {
+    __shared__ float scratch[kReduceThreads / 64];
+    __shared__ float part_sum[8][32];
+    const int tid = threadIdx.x;
     const size_t base = (size_t)bq * S;
+    const int d = slice * 32 + (tid & 31), part = tid >> 5;
+    // the first 64 chunks' accumulators are loaded before the reductions
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = part + 8 * i;
+        pv[i] = c < nc ? pacc[(base + c) * kD + d] : 0.f;
+    }
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, pm[base + c]);
-    if (nc == 0 || M == -INFINITY) {
-        out[(size_t)bq * kD + d] = 0.f;
-        if (lse && d == 0) lse[bq] = -INFINITY;
+    for (int c = tid; c < nc; c += kReduceThreads) M = fmaxf(M, pm[base + c]);
+    M = block_reduce<true>(M, scratch);
+    if (M == -INFINITY) {   // no chunk holds a kept token (uniform over the block)
+        if (tid < 32) out[(size_t)bq * kD + d] = 0.f;
+        if (lse && slice == 0 && tid == 0) lse[bq] = -INFINITY;
         return;
     }
-    float L = 0.f, o = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float f = exp2f(pm[base + c] - M);
-        L = fmaf(pl[base + c], f, L);
-        o = fmaf(pacc[(base + c) * kD + d], f, o);
+    float L = 0.f;
+    for (int c = tid; c < nc; c += kReduceThreads) L = fmaf(pl[base + c], exp2f(pm[base + c] - M), L);
+    L = block_reduce<false>(L, scratch);
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = part + 8 * i;
+        if (c < nc) o = fmaf(pv[i], exp2f(pm[base + c] - M), o);
     }
-    out[(size_t)bq * kD + d] = o / L;
-    if (lse && d == 0) lse[bq] = (M + log2f(L)) * 0.69314718055994531f;
+#pragma unroll 4
+    for (int c = part + 64; c < nc; c += 8) o = fmaf(pacc[(base + c) * kD + d], exp2f(pm[base + c] - M), o);
+    part_sum[part][tid & 31] = o;
+    __syncthreads();
+    if (tid < 32) {
+        float t = part_sum[0][tid];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) t += part_sum[i][tid];
+        out[(size_t)bq * kD + d] = t / L;
+    }
+    if (lse && slice == 0 && tid == 0) lse[bq] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 }  // namespace core

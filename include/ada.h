@@ -87,7 +87,11 @@ typedef struct {
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv; Hq / Hkv must be 1, 2, 4 or 8 (query head hq uses KV head hq / (Hq/Hkv)) */
     uint32_t rdr_tier_mask;     /* tiers RDR may assign (bit i = tier id i); 0 means all three */
-    int32_t decode_chunk_pages; /* split-K chunk length in pages for ada_decode; 0 = automatic */
+    int32_t decode_chunk_pages; /* split-K chunk length in pages for ada_decode; 0 = automatic: about
+                                   one round of resident work-groups over B * Hkv rows of
+                                   max_pages_per_head pages on the current device.  Rounded up to
+                                   64 tokens' worth of pages, at most 256.  The same value must be
+                                   in effect for the workspace query and the decode calls. */
 } ada_config_t;
 
 /* Metadata of one page, 8 bytes. */
