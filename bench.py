@@ -1,9 +1,9 @@
 """Benchmark: ADA paged decode on one MI355X.
 
-One step = one full decode of the workload: the split-K pass (angle-LUT
-staging, logits from codes, online softmax, value accumulation) followed by
-the reduction pass, for every (sequence, query head), with the packed cache
-already resident in HBM.  Prints one JSON line.
+One step = one full decode of the workload (`ada_decode`): the split-K pass
+(angle-LUT staging, logits from codes, online softmax, value accumulation)
+followed by the reduction pass, for every (sequence, query head), with the
+packed cache already resident in HBM.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
 
@@ -159,7 +159,8 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     k_ms = e0.elapsed_time(e1) / args.steps
-    # the reduction pass alone, K back-to-back launches
+    # the reduction pass alone, K back-to-back launches (mostly launch cost:
+    # behind a split-K launch it adds about 2 us)
     e0.record()
     for _ in range(args.steps):
         ada.decode_reduce(cache, B, out, lse, ws)

@@ -328,7 +328,7 @@ struct AdaPolicy {
     }
 };
 
-template <int G, int P, int NW, int WPE, int PF>
+template <int G, int P, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
     using Pol = AdaPolicy<G, P>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     c.maxp = a.maxp;
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
-    core::split_k<G, P, NW, PF>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
+    core::split_k<G, P, NW>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(core::kReduceThreads) void decode_reduce_kernel(Dec
     const int b = bq / a.Hq, hq = bq % a.Hq;
     const int G = a.Hq / a.Hkv;
     const int np = a.num_pages[b * a.Hkv + hq / G];
-    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, blockIdx.y, a.out,
+    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, threadIdx.x, a.out,
                         a.lse);
 }
 
@@ -395,9 +395,7 @@ template <int G, int P>
 hipError_t launch_gp(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
     constexpr int WPE = decode_waves_per_simd(G);
-    constexpr int PF = 0;
-    dim3 grid(a.S, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, PF>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE>), dim3(a.S, a.Hkv, a.B), dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -419,7 +417,7 @@ hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Hq, core::kReduceSlices), dim3(core::kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Hq), dim3(core::kReduceThreads), 0, s, a);
     return hipGetLastError();
 }
 

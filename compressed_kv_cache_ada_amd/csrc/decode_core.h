@@ -35,17 +35,40 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+// DPP lane permutation of a float (row_mask and bank_mask all on)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// Wavefront maximum on the VALU: within each row of 16 lanes by DPP (quad
+// xor 1, quad xor 2, half-row mirror, row mirror), then across the four
+// rows by reading one lane of each.  The result is wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm(1, 0, 3, 2)
+    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm(2, 3, 0, 1)
+    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+
+// Wavefront sum in the same pattern (a fixed order, identical in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 
 // LDS writes by one lane become visible to the other lanes of its wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -74,6 +97,51 @@ struct CoreSmem {
     _Float16 pb[NW][2][G][64];   // [wave][hi|lo][head][token]
 };
 
+// Reduction pass.  One thread per (sequence, query head, dimension): a
+// running merge over the chunks' partials in tiles of kReduceTile chunks
+// whose loads are all issued before any arithmetic, so a tile costs one
+// memory round trip and no barrier.  The order is fixed: deterministic.
+constexpr int kReduceThreads = 128;
+constexpr int kReduceTile = 16;
+
+__device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, const float *pacc, int S, int nc,
+                                              int bq, int d, float *out, float *lse) {
+    const size_t base = (size_t)bq * S;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += kReduceTile) {
+        float mv[kReduceTile], lv[kReduceTile], av[kReduceTile];
+#pragma unroll
+        for (int i = 0; i < kReduceTile; ++i) {
+            const int c = min(c0 + i, nc - 1);   // in range; repeats are masked below
+            mv[i] = pm[base + c];
+            lv[i] = pl[base + c];
+            av[i] = pacc[(base + c) * kD + d];
+        }
+        float Mt = M;
+#pragma unroll
+        for (int i = 0; i < kReduceTile; ++i)
+            if (c0 + i < nc) Mt = fmaxf(Mt, mv[i]);
+        if (Mt == -INFINITY) continue;       // no kept token so far (uniform)
+        const float so = (M == -INFINITY) ? 0.f : exp2f(M - Mt);
+        L *= so;
+        O *= so;
+#pragma unroll
+        for (int i = 0; i < kReduceTile; ++i) {
+            const float f = (c0 + i < nc && mv[i] != -INFINITY) ? exp2f(mv[i] - Mt) : 0.f;
+            L = fmaf(lv[i], f, L);
+            O = fmaf(av[i], f, O);
+        }
+        M = Mt;
+    }
+    if (M == -INFINITY) {
+        out[(size_t)bq * kD + d] = 0.f;
+        if (lse && d == 0) lse[bq] = -INFINITY;
+        return;
+    }
+    out[(size_t)bq * kD + d] = O / L;
+    if (lse && d == 0) lse[bq] = (M + log2f(L)) * 0.69314718055994531f;
+}
+
 // Policy interface (see decode.hip / dense.hip):
 //   Smem                      policy LDS (per-query tables)
 //   int num_pages(row, b)     pages in the row
@@ -81,7 +149,7 @@ struct CoreSmem {
 //   void prologue(smem, b, h, tid, nthreads)
 //   Codes fetch(page, meta, slot, valid)        issue the token's code loads
 //   void logits(smem, codes, meta, valid, lg[G]) lane = token, base-2 scaled
-template <int G, int P, int NW, int PF, class Pol>
+template <int G, int P, int NW, class Pol>
 __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typename Pol::Smem &ps,
                                         CoreSmem<G, NW> &cs, float *red, int chunk, int h, int b) {
     constexpr int TPG = 64 / P;     // pages per group
@@ -127,71 +195,19 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 
     const int n_groups = (nch + TPG - 1) / TPG;
     const int pg = lane / P, slot = lane % P;
-    struct Tok {
-        typename Pol::Codes codes;
-        uint2 meta;
-        bool valid;
-    };
-    // the tokens' code units of group g (lane = token); lanes past the row's
-    // last page read the group's first page (weight 0)
-    auto stage = [&](int g) {
-        const int gbase = g * TPG;
+    for (int grp = w; grp < n_groups; grp += NW) {
+        asm volatile("" ::: "memory");   // keep LDS reads of the tables inside the loop
+        const int gbase = grp * TPG;
+
+        // 1. the tokens' code units (lane = token); lanes past the row's last
+        //    page read the group's first page (weight 0)
         const int pidx = gbase + pg;
         const int page_raw = cs.pages[pidx];
         const bool pvalid = page_raw >= 0;
         const int page = pvalid ? page_raw : cs.pages[gbase];
-        Tok t;
-        t.meta = cs.meta[pvalid ? pidx : gbase];
-        t.valid = pvalid && slot < (int)((t.meta.x >> 8) & 0xFF);
-        t.codes = pol.fetch(page, t.meta, slot, t.valid);
-        return t;
-    };
-    // the group's value blocks -> MFMA A operands; a block past the row's
-    // last page is read from the group's first page instead (weight 0)
-    auto load_values = [&](int g, uint4 (&va)[2][8]) {
-        const int gb = g * TPG;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int blk = 4 * kc + kq;            // 8-token block of the group
-            const int vpage = cs.pages[gb + blk / KB];
-            const uint16_t *base =
-                a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gb]) * P * kD + (blk % KB) * 1024 + n_head * 8;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
-        }
-    };
-    Tok nxt{};
-    uint4 va_nxt[2][8];
-    if (PF >= 1 && w < n_groups) nxt = stage(w);
-    if (PF == 2 && w < n_groups) load_values(w, va_nxt);
-    for (int grp = w; grp < n_groups; grp += NW) {
-        asm volatile("" ::: "memory");   // keep LDS reads of the tables inside the loop
-
-        // 1. the tokens' code units; with PF the next group's codes (and with
-        //    PF = 2 its values) are issued now, this group's one iteration
-        //    earlier
-        Tok cur;
-        uint4 va[2][8];
-        if constexpr (PF >= 1) {
-            cur = nxt;
-            if constexpr (PF == 2) {
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) va[kc][t] = va_nxt[kc][t];
-            }
-            if (grp + NW < n_groups) {
-                nxt = stage(grp + NW);
-                if constexpr (PF == 2) load_values(grp + NW, va_nxt);
-            }
-        } else {
-            cur = stage(grp);
-        }
-        const typename Pol::Codes &codes = cur.codes;
-        const uint2 meta = cur.meta;
-        const bool valid = cur.valid;
-        // PF = 3: this group's values are issued before its logits
-        if constexpr (PF == 3) load_values(grp, va);
+        const uint2 meta = cs.meta[pvalid ? pidx : gbase];
+        const bool valid = pvalid && slot < (int)((meta.x >> 8) & 0xFF);
+        const typename Pol::Codes codes = pol.fetch(page, meta, slot, valid);
 
         // 2. logits, lane = token
         float lg[G];
@@ -199,10 +215,20 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
         pol.logits(ps, codes, meta, valid, lg);
 
-        // 3. values (without PF = 2), issued after the logit arithmetic so
+        // 3. values -> MFMA A operands, issued after the logit arithmetic so
         //    they are not held in registers through it (other wavefronts'
-        //    work covers their latency)
-        if constexpr (PF < 2) load_values(grp, va);
+        //    work covers their latency).  A block past the row's last page is
+        //    read from the group's first page instead: weight 0.
+        uint4 va[2][8];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int blk = 4 * kc + kq;            // 8-token block of the group
+            const int vpage = cs.pages[gbase + blk / KB];
+            const uint16_t *base =
+                a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gbase]) * P * kD + (blk % KB) * 1024 + n_head * 8;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
+        }
 
         // 4. online softmax, weights to LDS as fp16 hi + lo
         float alpha_n = 1.f;
@@ -210,8 +236,10 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         for (int g = 0; g < G; ++g) {
             const float mx = wave_max(valid ? lg[g] : -INFINITY);
             const float mnew = fmaxf(m_run[g], mx);
-            const float alpha = (m_run[g] == -INFINITY) ? 0.f : exp2f(m_run[g] - mnew);
-            const float p = valid ? exp2f(lg[g] - mnew) : 0.f;
+            // v_exp_f32 directly: arguments are <= 0, results below 2^-126
+            // flush to zero, far below the weights' resolution
+            const float alpha = (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - mnew);
+            const float p = valid ? __builtin_amdgcn_exp2f(lg[g] - mnew) : 0.f;
             l_run[g] = l_run[g] * alpha + p;
             m_run[g] = mnew;
             const _Float16 hi = (_Float16)p;
@@ -234,12 +262,10 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, va[kc][t]), bh, acc[t],
-                                                                0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, va[kc][t]), bh, acc[t], 0, 0, 0);
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, va[kc][t]), bl, acc[t],
-                                                                0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, va[kc][t]), bl, acc[t], 0, 0, 0);
         }
         wave_lds_sync();
     }
@@ -289,72 +315,6 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 
 // number of chunks holding data for a row of np pages (page groups of tpg)
 __device__ __forceinline__ int chunks_with_data(int np, int tpg, int S) { return min(S, (np + tpg - 1) / tpg); }
-
-// Reduction pass.  One work-group of kReduceThreads per (sequence, query
-// head, 32-dimension slice): the running max and the weighted sum of the
-// chunks' partial sums are block reductions over the chunks; the output
-// slice is summed by 8 chunk lanes x 32 dimensions, each lane taking every
-// 8th chunk, then merged in LDS.  Every order is fixed, so the result is
-// deterministic.
-constexpr int kReduceThreads = 256;
-constexpr int kReduceSlices = 4;   // 128 dimensions / 32
-
-template <bool MAX>
-__device__ __forceinline__ float block_reduce(float v, float *scratch) {
-    v = MAX ? wave_max(v) : wave_sum(v);
-    const int wv = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[wv] = v;
-    __syncthreads();
-    float r = scratch[0];
-#pragma unroll
-    for (int i = 1; i < kReduceThreads / 64; ++i) r = MAX ? fmaxf(r, scratch[i]) : r + scratch[i];
-    return r;
-}
-
-__device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, const float *pacc, int S, int nc,
-                                              int bq, int slice, float *out, float *lse) {
-    __shared__ float scratch[kReduceThreads / 64];
-    __shared__ float part_sum[8][32];
-    const int tid = threadIdx.x;
-    const size_t base = (size_t)bq * S;
-    const int d = slice * 32 + (tid & 31), part = tid >> 5;
-    // the first 64 chunks' accumulators are loaded before the reductions
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = part + 8 * i;
-        pv[i] = c < nc ? pacc[(base + c) * kD + d] : 0.f;
-    }
-    float M = -INFINITY;
-    for (int c = tid; c < nc; c += kReduceThreads) M = fmaxf(M, pm[base + c]);
-    M = block_reduce<true>(M, scratch);
-    if (M == -INFINITY) {   // no chunk holds a kept token (uniform over the block)
-        if (tid < 32) out[(size_t)bq * kD + d] = 0.f;
-        if (lse && slice == 0 && tid == 0) lse[bq] = -INFINITY;
-        return;
-    }
-    float L = 0.f;
-    for (int c = tid; c < nc; c += kReduceThreads) L = fmaf(pl[base + c], exp2f(pm[base + c] - M), L);
-    L = block_reduce<false>(L, scratch);
-    float o = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = part + 8 * i;
-        if (c < nc) o = fmaf(pv[i], exp2f(pm[base + c] - M), o);
-    }
-#pragma unroll 4
-    for (int c = part + 64; c < nc; c += 8) o = fmaf(pacc[(base + c) * kD + d], exp2f(pm[base + c] - M), o);
-    part_sum[part][tid & 31] = o;
-    __syncthreads();
-    if (tid < 32) {
-        float t = part_sum[0][tid];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) t += part_sum[i][tid];
-        out[(size_t)bq * kD + d] = t / L;
-    }
-    if (lse && slice == 0 && tid == 0) lse[bq] = (M + log2f(L)) * 0.69314718055994531f;
-}
 
 }  // namespace core
 }  // namespace ada

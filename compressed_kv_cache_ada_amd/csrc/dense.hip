@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void dense_partials_kernel(DenseLaunc
     c.maxp = a.maxp;
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
-    core::split_k<G, P, NW, 0>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
+    core::split_k<G, P, NW>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(core::kReduceThreads) void dense_reduce_kernel(Dens
     const int bq = blockIdx.x;
     const int b = bq / a.Hq;
     const int np = (a.ctx_len[b] + a.P - 1) / a.P;
-    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, blockIdx.y, a.out,
+    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, threadIdx.x, a.out,
                         a.lse);
 }
 
@@ -173,7 +173,7 @@ hipError_t launch_dense_partials(const DenseLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_dense_reduce(const DenseLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(dense_reduce_kernel, dim3(a.B * a.Hq, core::kReduceSlices), dim3(core::kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(dense_reduce_kernel, dim3(a.B * a.Hq), dim3(core::kReduceThreads), 0, s, a);
     return hipGetLastError();
 }
 
