@@ -6,12 +6,13 @@
 // from the radius + angle codes (no dense key is rebuilt) on a paged,
 // block-local decode path that streams tier-homogeneous pages.
 //
-// The split-K skeleton (page staging, value prefetch, online softmax, value
+// The split-K skeleton (page staging, value loads, online softmax, value
 // accumulation on the matrix cores, chunk partials) is decode_core.h; this
 // file supplies the ADA logits.  The G = Hq/Hkv query heads of a KV head
 // share every code and value read.
-//   logits:  lane = token; the token's 16-byte code units are read with one
-//            128-bit load per unit (units are token-minor, so the 64 lanes
+//   logits:  lane = token; the token's 16-byte code units arrive through a
+//            per-wavefront LDS stage filled by direct global-to-LDS 128-bit
+//            loads one group ahead (units are token-minor, so the 64 lanes
 //            read contiguous memory); per pair j the lane gathers
 //            LUT_g[j][theta_code] from LDS for every head g and accumulates
 //            s_code * entry.  T8 uses the factorised form
@@ -29,13 +30,9 @@ using core::ldg;
 // ---- logits per tier (lane = token) --------------------------------------
 // Each returns base-2 scaled logits: scale * log2(e) * r * sum_j s_j LUT[j][c].
 
-// Raw code units of one token, fetched before the group's value loads so that
-// the logit arithmetic waits only for them.  Unit use per tier:
-//   T4: u[0..1] angle units, u[2..3] magnitude units
-//   T2: u[0] angle unit, u[1] magnitude unit, h the 8-byte magnitude unit
-//   T8: u[0..3] angle units, u[4..7] magnitude units
-// At most 16 LUT gathers in flight: a compiler barrier every JB pairs stops
-// the scheduler from hoisting all gathers of an unrolled unit into registers.
+// T8: at most 16 table reads in flight -- a compiler barrier every JB pairs
+// stops the scheduler from hoisting all reads of an unrolled unit into
+// registers.
 template <int G>
 __device__ __forceinline__ void pair_fence(int j) {
     constexpr int JB = 16 / G;
@@ -49,63 +46,18 @@ __device__ __forceinline__ uint32_t pin(uint32_t x) {
     return x;
 }
 
-struct CodeRegs {
-    uint4 u[4];
-    uint2 h;
-    uint32_t r;
-    const uint8_t *c;   // the token's first angle unit
-};
-
-// Raw code units of one token, fetched before the group's value loads so that
-// the logit arithmetic waits only for them.  Unit use per tier:
+// Code units of one token in registers.  Unit use per tier:
 //   T4: u[0..1] angle units, u[2..3] magnitude units
 //   T2: u[0] angle unit, u[1] magnitude unit, h the 8-byte magnitude unit
 //       (u[2], u[3] repeat u[1])
 //   T8: u[0..1] angle units 0-1, u[2..3] magnitude units 0-1 (pairs 0-31);
 //       units 2-3 (pairs 32-63) are read by the T8 logit routine itself
-template <int P>
-__device__ __forceinline__ CodeRegs fetch_codes(const uint8_t *blk, int tier, int slot) {
-    // Branch-free: every lane issues the same five loads; the offsets are
-    // chosen by tier and always stay inside the lane's own code block.
-    CodeRegs k;
-    k.c = blk + 2 * P + slot * 16;
-    const bool t2 = tier == ADA_TIER_T2;
-    const int so = (tier == ADA_TIER_T4) ? 32 * P : 64 * P;    // first magnitude unit
-    const int o1 = 16 * P;
-    const int o2 = t2 ? 16 * P : so;
-    const int o3 = t2 ? 16 * P : so + 16 * P;
-    k.r = ldg<uint16_t>(blk + 2 * slot);
-    k.u[0] = ldg<uint4>(k.c);
-    k.u[1] = ldg<uint4>(k.c + o1);
-    k.u[2] = ldg<uint4>(k.c + o2);
-    k.u[3] = ldg<uint4>(k.c + o3);
-    k.h = ldg<uint2>(t2 ? blk + 2 * P + 32 * P + slot * 8 : k.c);
-    return k;
-}
-
-typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
-
-// LUT entries of one (pair, code) for all G heads are contiguous
-// ([pair][code][head]): one 64-lane gather of 16 bytes serves 4 heads.
-template <int G>
-__device__ __forceinline__ void lut_fma(const float *e, float s, float (&acc)[G]) {
-    if constexpr (G >= 4) {
-#pragma unroll
-        for (int g4 = 0; g4 < G; g4 += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(e + g4);
-            acc[g4] = fmaf(s, v.x, acc[g4]);
-            acc[g4 + 1] = fmaf(s, v.y, acc[g4 + 1]);
-            acc[g4 + 2] = fmaf(s, v.z, acc[g4 + 2]);
-            acc[g4 + 3] = fmaf(s, v.w, acc[g4 + 3]);
-        }
-    } else if constexpr (G == 2) {
-        const float2 v = *reinterpret_cast<const float2 *>(e);
-        acc[0] = fmaf(s, v.x, acc[0]);
-        acc[1] = fmaf(s, v.y, acc[1]);
-    } else {
-        acc[0] = fmaf(s, e[0], acc[0]);
-    }
-}
+struct CodeRegs {
+    uint4 u[4];
+    uint2 h;
+    uint32_t r;         // fp16 radius bits
+    const uint8_t *c;   // the token's first angle unit
+};
 
 // Per-work-group LUT layout, per pair j with NC codes: slices of SW =
 // min(G, 4) heads, [j][slice][code][SW] -- [j][code][head] for G <= 4.  One
@@ -183,15 +135,21 @@ __device__ __forceinline__ void logits_t2(const CodeRegs &k, const float *lut2, 
     // quarter q covers pairs 16q..16q+15: angle word q (2-bit codes) and
     // magnitude bits [48q, 48q+48) (3-bit codes)
     const uint32_t tw[4] = {k.u[0].x, k.u[0].y, k.u[0].z, k.u[0].w};
-    const uint32_t sw[7] = {k.u[1].x, k.u[1].y, k.u[1].z, k.u[1].w, k.h.x, k.h.y, 0u};
+    // the 192 magnitude bits are words u[1].x..w, h.x, h.y; quarter q
+    // starts at bit 48q: windows at bits 0, 48, 96 and 144
+    const uint64_t win4[4] = {
+        ((uint64_t)k.u[1].y << 32) | k.u[1].x,
+        (((uint64_t)k.u[1].z << 32) | k.u[1].y) >> 16,
+        ((uint64_t)k.h.x << 32) | k.u[1].w,
+        (((uint64_t)k.h.y << 32) | k.h.x) >> 16,
+    };
     float acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t t = tw[q];
-        const int wd = (48 * q) >> 5, sh = (48 * q) & 31;
-        const uint64_t win = ((((uint64_t)sw[wd + 1]) << 32) | sw[wd]) >> sh;
+        const uint64_t win = win4[q];
         const float *lu = lut2 + q * 16 * 4 * G;
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {   // 8 pairs at a time
@@ -264,8 +222,19 @@ __device__ __forceinline__ void logits_t8(const CodeRegs &k, const float2 *cs8, 
 }
 
 // ---- ADA logit policy for the split-K core -------------------------------
-template <int G, int P>
+// Per-wavefront LDS staging of one 64-token group's code units, filled by
+// direct global-to-LDS loads (lane = token): units 0-3 as in CodeRegs, the
+// aligned 16 bytes holding the token's 8-byte T2 unit, and the aligned
+// dword holding its fp16 radius.
+struct CodeStage {
+    uint4 u[4][64];
+    uint4 h[64];
+    uint32_t r[64];
+};
+
+template <int G, int P, int NW>
 struct AdaPolicy {
+    static constexpr bool kStaged = true;
     struct Smem {
         float lut4[64 * 16 * G];   // 4-bit angle grid, lut_index<G, 16> layout
         float lut2[64 * 4 * G];    // 2-bit angle grid, lut_index<G, 4> layout
@@ -273,6 +242,7 @@ struct AdaPolicy {
         float2 cs4[16];            // the 4-bit sub-grid, contiguous (conflict-free reads)
         float2 cs2[4];             // the 2-bit sub-grid
         float q8[64 * G * 2];      // [j][g][x|y] query pairs (T8, factorised)
+        CodeStage st[NW];          // the next group's code units, per wavefront
     };
     const int32_t *num_pages_;
     const ada_page_meta_t *page_meta;
@@ -284,6 +254,7 @@ struct AdaPolicy {
     __device__ int num_pages(int row, int) const { return num_pages_[row]; }
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
 
+    // phase 1: query pairs and the grid directions
     __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
         const float *qrow = q + ((size_t)b * Hq + (size_t)h * G) * kD;
         for (int i = tid; i < G * kD; i += nt) {
@@ -296,7 +267,10 @@ struct AdaPolicy {
             if ((c & 15) == 0) s.cs4[c >> 4] = d;
             if ((c & 63) == 0) s.cs2[c >> 6] = d;
         }
-        __syncthreads();
+    }
+
+    // phase 2 (after a barrier): the T4 / T2 tables
+    __device__ void build(Smem &s, int tid, int nt) const {
         // consecutive threads fill consecutive heads, then codes
         for (int i = tid; i < 64 * 16 * G; i += nt) {
             const int g = i % G, c = (i / G) & 15, j = i / (16 * G);
@@ -310,8 +284,39 @@ struct AdaPolicy {
     }
 
     using Codes = CodeRegs;
-    __device__ Codes fetch(int, uint2 meta, int slot, bool valid) const {
-        return fetch_codes<P>(arena + (size_t)meta.y * 16, meta.x & 0xFF, slot);
+
+    // Issues the direct-to-LDS loads of a group's code units into wavefront
+    // w's stage (lane = token, wave-uniform destinations).  Branch-free:
+    // every address stays inside the lane's own code block.
+    __device__ void stage(Smem &s, int w, uint2 meta, int slot) const {
+        const uint8_t *blk = arena + (size_t)meta.y * 16;
+        const int tier = meta.x & 0xFF;
+        const uint8_t *c = blk + 2 * P + slot * 16;
+        const bool t2 = tier == ADA_TIER_T2;
+        const int so = (tier == ADA_TIER_T4) ? 32 * P : 64 * P;   // first magnitude unit
+        const int o2 = t2 ? 16 * P : so;
+        const int o3 = t2 ? 16 * P : so + 16 * P;
+        CodeStage &st = s.st[w];
+        __builtin_amdgcn_global_load_lds(c, &st.u[0][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(c + 16 * P, &st.u[1][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(c + o2, &st.u[2][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(c + o3, &st.u[3][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(t2 ? blk + 34 * P + (slot & ~1) * 8 : c, &st.h[0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(blk + 4 * (slot >> 1), &st.r[0], 4, 0, 0);
+    }
+
+    // The lane's code units from wavefront w's stage (after its loads landed).
+    __device__ Codes unstage(const Smem &s, int w, uint2 meta, int slot, int lane) const {
+        const CodeStage &st = s.st[w];
+        CodeRegs k;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) k.u[u] = st.u[u][lane];
+        const uint4 hh = st.h[lane];
+        k.h = (slot & 1) ? make_uint2(hh.z, hh.w) : make_uint2(hh.x, hh.y);
+        const uint32_t rr = st.r[lane];
+        k.r = (slot & 1) ? rr >> 16 : rr & 0xFFFFu;
+        k.c = arena + (size_t)meta.y * 16 + 2 * P + slot * 16;
+        return k;
     }
 
     __device__ void logits(const Smem &s, const Codes &k, uint2 meta, bool valid, float (&lg)[G]) const {
@@ -330,7 +335,7 @@ struct AdaPolicy {
 
 template <int G, int P, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
-    using Pol = AdaPolicy<G, P>;
+    using Pol = AdaPolicy<G, P, NW>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
     constexpr size_t RAW = sizeof(typename Pol::Smem) > RED ? sizeof(typename Pol::Smem) : RED;
     __shared__ __align__(16) unsigned char raw[RAW];   // policy tables, later the wave-merge buffer

@@ -6,7 +6,8 @@
 // critical path has no dependent global loads before the code fetch), and
 // the policy stages its per-query tables.  Then each wavefront walks 64-token
 // groups (4 pages of 16 / 2 pages of 32):
-//   1. fetch the tokens' codes (lane = token, policy);
+//   1. the tokens' codes (lane = token, policy); a staged policy has them
+//      requested into LDS one group ahead;
 //   2. logits for the G query heads, lane = token (policy);
 //   3. issue the group's value loads (16 x 128-bit per lane): each lane gets
 //      8 consecutive tokens of one head dimension, which is exactly the A
@@ -146,8 +147,14 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //   Smem                      policy LDS (per-query tables)
 //   int num_pages(row, b)     pages in the row
 //   uint2 meta(page, idx, b)  x = tier | count << 8, y = policy data
-//   void prologue(smem, b, h, tid, nthreads)
-//   Codes fetch(page, meta, slot, valid)        issue the token's code loads
+//   void prologue(smem, b, h, tid, nthreads)   stores before a barrier
+//   void build(smem, tid, nthreads)            tables after that barrier
+//   kStaged = true:
+//     void stage(smem, w, meta, slot)          request a group's codes into
+//                                              wavefront w's LDS stage
+//     Codes unstage(smem, w, meta, slot, lane) read them (after they landed)
+//   kStaged = false:
+//     Codes fetch(page, meta, slot, valid)     issue the token's code loads
 //   void logits(smem, codes, meta, valid, lg[G]) lane = token, base-2 scaled
 template <int G, int P, int NW, class Pol>
 __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typename Pol::Smem &ps,
@@ -180,6 +187,29 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
     }
     pol.prologue(ps, b, h, tid, NT);
     __syncthreads();
+    const int n_groups = (nch + TPG - 1) / TPG;
+    const int pg = lane / P, slot = lane % P;
+    // the group's page for this lane (lane = token); lanes past the row's
+    // last page use the group's first page (weight 0)
+    auto group_meta = [&](int g, bool &valid) {
+        const int gbase = g * TPG;
+        const int pidx = gbase + pg;
+        const bool pvalid = cs.pages[pidx] >= 0;
+        const uint2 meta = cs.meta[pvalid ? pidx : gbase];
+        valid = pvalid && slot < (int)((meta.x >> 8) & 0xFF);
+        return meta;
+    };
+    // staged policies: the first group's code units are requested before
+    // the tables are built
+    if constexpr (Pol::kStaged) {
+        if (w < n_groups) {
+            bool v;
+            const uint2 m0 = group_meta(w, v);
+            pol.stage(ps, w, m0, slot);
+        }
+    }
+    pol.build(ps, tid, NT);
+    __syncthreads();
 
     float m_run[G], l_run[G];
 #pragma unroll
@@ -193,21 +223,31 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
     const int n_head = lane & 15;       // MFMA column = query head of this lane
     const int kq = lane >> 4;           // MFMA K quarter: tokens 8*kq .. 8*kq + 7 of a 32-token step
 
-    const int n_groups = (nch + TPG - 1) / TPG;
-    const int pg = lane / P, slot = lane % P;
     for (int grp = w; grp < n_groups; grp += NW) {
         asm volatile("" ::: "memory");   // keep LDS reads of the tables inside the loop
         const int gbase = grp * TPG;
 
-        // 1. the tokens' code units (lane = token); lanes past the row's last
-        //    page read the group's first page (weight 0)
-        const int pidx = gbase + pg;
-        const int page_raw = cs.pages[pidx];
-        const bool pvalid = page_raw >= 0;
-        const int page = pvalid ? page_raw : cs.pages[gbase];
-        const uint2 meta = cs.meta[pvalid ? pidx : gbase];
-        const bool valid = pvalid && slot < (int)((meta.x >> 8) & 0xFF);
-        const typename Pol::Codes codes = pol.fetch(page, meta, slot, valid);
+        // 1. the tokens' code units (lane = token).  Staged: this group's were
+        //    requested into LDS one iteration earlier; once copied to
+        //    registers the next group's are requested, so their latency
+        //    overlaps this group's logits, values and softmax.
+        bool valid;
+        const uint2 meta = group_meta(grp, valid);
+        typename Pol::Codes codes;
+        if constexpr (Pol::kStaged) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the stage has landed
+            codes = pol.unstage(ps, w, meta, slot, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before it is refilled
+            if (grp + NW < n_groups) {
+                bool vn;
+                const uint2 mn = group_meta(grp + NW, vn);
+                pol.stage(ps, w, mn, slot);
+            }
+        } else {
+            const int pidx = gbase + pg;
+            const int page = cs.pages[pidx] >= 0 ? cs.pages[pidx] : cs.pages[gbase];
+            codes = pol.fetch(page, meta, slot, valid);
+        }
 
         // 2. logits, lane = token
         float lg[G];

@@ -17,6 +17,7 @@ using core::ldg;
 
 template <int G, int P>
 struct DensePolicy {
+    static constexpr bool kStaged = false;
     struct Smem {
         float qd[kD * G];   // [d][g], pre-multiplied by scale * log2(e)
     };
@@ -35,6 +36,7 @@ struct DensePolicy {
         const float *qrow = q + ((size_t)b * Hq + (size_t)h * G) * kD;
         for (int i = tid; i < G * kD; i += nt) s.qd[(i & 127) * G + (i >> 7)] = qrow[i] * mul;
     }
+    __device__ void build(Smem &, int, int) const {}
     // keys are read inside the logit loop: fetch only records the address
     struct Codes {
         const uint16_t *kp;
