@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "rdr128k", "ragged", "long256k", "tiny"])
     ap.add_argument("--chunk-pages", type=int, default=0)
+    ap.add_argument("--queries", type=int, default=1,
+                    help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=0)
@@ -124,18 +126,33 @@ def main():
     del keys, vals
     torch.cuda.empty_cache()
 
-    q = torch.from_numpy(w["q"]).cuda()
-    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    ws = ada.decode_workspace(cache, B)
+    Q = args.queries
+    if Q == 1:
+        q = torch.from_numpy(w["q"]).cuda()
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        ws = ada.decode_workspace(cache, B)
+    else:   # multi-query decode: Q seeded N(0,1) queries per sequence
+        qm = np.random.default_rng(4242).standard_normal((B, Q, Hq, 128), dtype=np.float32)
+        q = torch.from_numpy(qm).cuda()
+        out = torch.empty((B, Q, Hq, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda")
+        ws = ada.decode_multi_workspace(cache, B, Q)
+
+    def split_k():
+        if Q == 1:
+            ada.decode_partials(cache, q, w["scale"], ws)
+        else:   # the multi-query call includes its reduction pass
+            ada.decode_multi(cache, q, w["scale"], out, lse, ws)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        ada.decode_partials(cache, q, w["scale"], ws)
+        split_k()
         if ev is not None:
             ev[1].record()
-        ada.decode_reduce(cache, B, out, lse, ws)
+        if Q == 1:
+            ada.decode_reduce(cache, B, out, lse, ws)
 
     for _ in range(args.warmup):
         step()
@@ -155,18 +172,20 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        ada.decode_partials(cache, q, w["scale"], ws)
+        split_k()
     e1.record()
     torch.cuda.synchronize()
     k_ms = e0.elapsed_time(e1) / args.steps
     # the reduction pass alone, K back-to-back launches (mostly launch cost:
     # behind a split-K launch it adds about 2 us)
-    e0.record()
-    for _ in range(args.steps):
-        ada.decode_reduce(cache, B, out, lse, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    r_ms = e0.elapsed_time(e1) / args.steps
+    r_ms = None
+    if Q == 1:
+        e0.record()
+        for _ in range(args.steps):
+            ada.decode_reduce(cache, B, out, lse, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        r_ms = e0.elapsed_time(e1) / args.steps
 
     # cold steps: before each, 1 GiB of another buffer is streamed through the
     # caches with a read kernel (the 256 MB last-level cache then holds clean
@@ -179,7 +198,7 @@ def main():
             ada.probe_read(flush, 1 << 30, 0, fsink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            ada.decode_partials(cache, q, w["scale"], ws)
+            split_k()
             e1.record()
             torch.cuda.synchronize()
             cold.append(e0.elapsed_time(e1))
@@ -212,9 +231,9 @@ def main():
         read_gbps[variant] = nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
-    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in (0, 1, 2)) + 12 * n_pages + B * Hq * 128 * 4
+    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in (0, 1, 2)) + 12 * n_pages + B * Q * Hq * 128 * 4
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload) if Q == 1 else None
     value = kept_total / (ms_step * 1e-3)
 
     result = {
@@ -235,16 +254,17 @@ def main():
             "context": int(w["ctx_len"].max()), "page_size": P, "kept_token_heads": kept_total,
             "kept_by_tier_T8_T4_T2": [kept[0], kept[1], kept[2]],
             "pages_by_tier_T8_T4_T2": [pages_by_tier[0], pages_by_tier[1], pages_by_tier[2]],
-            "decode_chunk_pages": cfg.decode_chunk_pages,
+            "decode_chunk_pages": cfg.decode_chunk_pages, "queries_per_sequence": Q,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-            "kernel": "decode_partials_kernel", "kernel_ms": k_ms, "kernel_ms_event_per_launch": k_ms_each,
+            "kernel": "decode_partials_kernel" if Q == 1 else "decode_partials_kernel + decode_reduce_kernel",
+            "kernel_ms": k_ms, "kernel_ms_event_per_launch": k_ms_each,
             "reduce_kernel_ms": r_ms,
             "algorithmic_bytes": alg_bytes,
         },
-        "step_hbm_gbps": (alg_bytes + B * Hq * 512) / (ms_step * 1e-3) / 1e9,
+        "step_hbm_gbps": (alg_bytes + B * Q * Hq * 512) / (ms_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w["ctx_len"].sum()) * Hkv / (ms_step * 1e-3),
         "cold_kernel_ms_median": float(np.median(cold)) if cold else None,
         "cold_gbps": alg_bytes / (np.median(cold) * 1e-3) / 1e9 if cold else None,
@@ -254,9 +274,11 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
 
-    if not args.no_dense:
+    if Q > 1:
+        result["query_token_heads_per_s"] = value * Q   # (query, kept token-head) pairs scored per second
+    if not args.no_dense and Q == 1:
         result["dense_fp16_reference"] = dense_reference(w, ada, torch, cfg)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and Q == 1:
         result["cpu_baseline"] = cpu_baseline(w, kept_total, max_row, n_pages, units)
     print(json.dumps(result), flush=True)
 

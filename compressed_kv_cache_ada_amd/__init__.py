@@ -74,6 +74,8 @@ def _declare(L):
         "ada_decode": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, sz, vp]),
         "ada_decode_partials": (st, [cfgp, cachep, vp, i32, f32, vp, sz, vp]),
         "ada_decode_reduce": (st, [cfgp, cachep, i32, vp, vp, vp, sz, vp]),
+        "ada_decode_multi_workspace": (st, [cfgp, cachep, i32, i32, ctypes.POINTER(sz)]),
+        "ada_decode_multi": (st, [cfgp, cachep, vp, i32, i32, f32, vp, vp, vp, sz, vp]),
         "ada_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_encode_append": (st, [cfgp, cachep, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ada_rdr_workspace": (st, [cfgp, i32, i64, ctypes.POINTER(sz)]),
@@ -95,6 +97,7 @@ def _declare(L):
 
 ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_build_lut",
                "ada_decode_workspace", "ada_decode", "ada_decode_partials", "ada_decode_reduce",
+               "ada_decode_multi_workspace", "ada_decode_multi",
                "ada_append_workspace", "ada_encode_append", "ada_rdr_workspace", "ada_rdr_assign",
                "ada_pack_workspace", "ada_pack", "ada_read_status", "ada_dense_workspace",
                "ada_dense_decode", "ada_probe_copy", "ada_probe_read", "ada_host_f64_to_f16")
@@ -198,6 +201,27 @@ def decode(cache, q, scale, out=None, lse=None, ws=None):
     ws = decode_workspace(cache, B) if ws is None else ws
     _check(lib().ada_decode(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _ptr(q), B, float(scale),
                             _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()), "ada_decode")
+    return out, lse
+
+
+def decode_multi_workspace(cache, B, Q):
+    n = ctypes.c_size_t(0)
+    _check(lib().ada_decode_multi_workspace(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), B, Q,
+                                            ctypes.byref(n)), "ada_decode_multi_workspace")
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=cache.page_table.device)
+
+
+def decode_multi(cache, q, scale, out=None, lse=None, ws=None):
+    """q: fp32 [B][Q][Hq][128] -> out [B][Q][Hq][128], lse [B][Q][Hq]."""
+    q = _dev(q, torch.float32, "q")
+    B, Q = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, Q, cache.cfg.num_q_heads, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Q, cache.cfg.num_q_heads), dtype=torch.float32, device=q.device)
+    ws = decode_multi_workspace(cache, B, Q) if ws is None else ws
+    _check(lib().ada_decode_multi(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _ptr(q), B, Q, float(scale),
+                                  _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()), "ada_decode_multi")
     return out, lse
 
 

@@ -58,7 +58,7 @@ inline ada_status_t hip_status(hipError_t e) { return e == hipSuccess ? ADA_OK :
 // resident work-groups over the whole cache (B * Hkv rows of up to maxp
 // pages), so no partial last round idles compute units and each work-group
 // builds its LUTs once for as much work as possible.
-int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp) {
+int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp, int gv) {
     const int tpg = 64 / cfg->page_size;
     int cp = cfg->decode_chunk_pages;
     if (cp <= 0) {
@@ -66,7 +66,7 @@ int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp) {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;   // MI355X
-        const int64_t slots = (int64_t)cus * decode_waves_per_simd(cfg->num_q_heads / cfg->num_kv_heads);
+        const int64_t slots = (int64_t)cus * decode_waves_per_simd(gv);
         const int64_t units = (int64_t)B * cfg->num_kv_heads * maxp;
         cp = (int)std::min<int64_t>((units + slots - 1) / slots, 1 << 20);
     }
@@ -82,11 +82,12 @@ struct DecodeWs {
     int S, cp;
 };
 
-DecodeWs decode_layout(const ada_config_t *cfg, int32_t B, int32_t maxp, void *ws) {
+// Q queries per sequence; partial rows are (sequence, query, query head)
+DecodeWs decode_layout(const ada_config_t *cfg, int32_t B, int32_t Q, int32_t maxp, void *ws) {
     DecodeWs d;
-    d.cp = decode_chunk_pages(cfg, B, maxp);
+    d.cp = decode_chunk_pages(cfg, B, maxp, Q * (cfg->num_q_heads / cfg->num_kv_heads));
     d.S = (maxp + d.cp - 1) / d.cp;
-    const size_t rows = (size_t)B * cfg->num_q_heads * d.S;
+    const size_t rows = (size_t)B * Q * cfg->num_q_heads * d.S;
     Carver c(ws);
     d.pm = c.take<float>(rows);
     d.pl = c.take<float>(rows);
@@ -95,9 +96,10 @@ DecodeWs decode_layout(const ada_config_t *cfg, int32_t B, int32_t maxp, void *w
     return d;
 }
 
-DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B, float scale,
-                         float *out, float *lse, const DecodeWs &w) {
+DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B, int32_t Q,
+                         float scale, float *out, float *lse, const DecodeWs &w) {
     DecodeLaunch a;
+    a.Q = Q;
     a.page_table = cache->page_table;
     a.num_pages = cache->num_pages;
     a.page_meta = cache->page_meta;
@@ -264,21 +266,36 @@ ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, f
     return hip_status(launch_build_lut(q, B * cfg->num_q_heads, lut, (hipStream_t)stream));
 }
 
-ada_status_t ada_decode_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, size_t *bytes) {
-    ada_status_t st = check_cfg(cfg);
-    if (st) return st;
-    if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0) return ADA_EINVAL;
-    *bytes = decode_layout(cfg, B, cache->max_pages_per_head, nullptr).bytes;
+// queries per sequence: a power of two with Q * (Hq / Hkv) <= 8
+static ada_status_t check_queries(const ada_config_t *cfg, int32_t Q) {
+    if (Q < 1) return ADA_EINVAL;
+    const int gv = Q * (cfg->num_q_heads / cfg->num_kv_heads);
+    if ((Q & (Q - 1)) || gv > 8) return ADA_EUNSUPPORTED;
     return ADA_OK;
 }
 
-static ada_status_t decode_common(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *ws,
+ada_status_t ada_decode_multi_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, int32_t Q,
+                                        size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_queries(cfg, Q))) return st;
+    if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0) return ADA_EINVAL;
+    *bytes = decode_layout(cfg, B, Q, cache->max_pages_per_head, nullptr).bytes;
+    return ADA_OK;
+}
+
+ada_status_t ada_decode_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, size_t *bytes) {
+    return ada_decode_multi_workspace(cfg, cache, B, 1, bytes);
+}
+
+static ada_status_t decode_common(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, int32_t Q, void *ws,
                                   size_t ws_bytes, DecodeWs *w) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
+    if ((st = check_queries(cfg, Q))) return st;
     if ((st = check_cache(cache))) return st;
     if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
-    *w = decode_layout(cfg, B, cache->max_pages_per_head, ws);
+    *w = decode_layout(cfg, B, Q, cache->max_pages_per_head, ws);
     if (B > 0 && (!ws || ws_bytes < w->bytes)) return ADA_EINVAL;
     return ADA_OK;
 }
@@ -286,36 +303,41 @@ static ada_status_t decode_common(const ada_config_t *cfg, const ada_cache_t *ca
 ada_status_t ada_decode_partials(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
                                  float scale, void *ws, size_t ws_bytes, void *stream) {
     DecodeWs w;
-    ada_status_t st = decode_common(cfg, cache, B, ws, ws_bytes, &w);
+    ada_status_t st = decode_common(cfg, cache, B, 1, ws, ws_bytes, &w);
     if (st) return st;
     if (B == 0) return ADA_OK;
     if (!q) return ADA_EINVAL;
-    DecodeLaunch a = make_decode(cfg, cache, q, B, scale, nullptr, nullptr, w);
+    DecodeLaunch a = make_decode(cfg, cache, q, B, 1, scale, nullptr, nullptr, w);
     return hip_status(launch_decode_partials(a, (hipStream_t)stream));
 }
 
 ada_status_t ada_decode_reduce(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, float *out, float *lse,
                                void *ws, size_t ws_bytes, void *stream) {
     DecodeWs w;
-    ada_status_t st = decode_common(cfg, cache, B, ws, ws_bytes, &w);
+    ada_status_t st = decode_common(cfg, cache, B, 1, ws, ws_bytes, &w);
     if (st) return st;
     if (B == 0) return ADA_OK;
     if (!out) return ADA_EINVAL;
-    DecodeLaunch a = make_decode(cfg, cache, nullptr, B, 0.f, out, lse, w);
+    DecodeLaunch a = make_decode(cfg, cache, nullptr, B, 1, 0.f, out, lse, w);
+    return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
+}
+
+ada_status_t ada_decode_multi(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                              int32_t Q, float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    DecodeWs w;
+    ada_status_t st = decode_common(cfg, cache, B, Q, ws, ws_bytes, &w);
+    if (st) return st;
+    if (B == 0) return ADA_OK;
+    if (!q || !out) return ADA_EINVAL;
+    DecodeLaunch a = make_decode(cfg, cache, q, B, Q, scale, out, lse, w);
+    hipError_t e = launch_decode_partials(a, (hipStream_t)stream);
+    if (e != hipSuccess) return ADA_EHIP;
     return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
 }
 
 ada_status_t ada_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B, float scale,
                         float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
-    DecodeWs w;
-    ada_status_t st = decode_common(cfg, cache, B, ws, ws_bytes, &w);
-    if (st) return st;
-    if (B == 0) return ADA_OK;
-    if (!q || !out) return ADA_EINVAL;
-    DecodeLaunch a = make_decode(cfg, cache, q, B, scale, out, lse, w);
-    hipError_t e = launch_decode_partials(a, (hipStream_t)stream);
-    if (e != hipSuccess) return ADA_EHIP;
-    return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
+    return ada_decode_multi(cfg, cache, q, B, 1, scale, out, lse, ws, ws_bytes, stream);
 }
 
 ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, size_t *bytes) {
@@ -487,7 +509,7 @@ ada_status_t ada_dense_workspace(const ada_config_t *cfg, int32_t B, int32_t max
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!bytes || B < 0 || max_pages_per_head <= 0) return ADA_EINVAL;
-    *bytes = decode_layout(cfg, B, max_pages_per_head, nullptr).bytes;
+    *bytes = decode_layout(cfg, B, 1, max_pages_per_head, nullptr).bytes;
     return ADA_OK;
 }
 
@@ -500,7 +522,7 @@ ada_status_t ada_dense_decode(const ada_config_t *cfg, int32_t B, int32_t max_pa
     if (B < 0 || max_pages_per_head <= 0) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
     if (!page_table || !ctx_len || !k_pool || !v_pool || !q || !out) return ADA_EINVAL;
-    DecodeWs w = decode_layout(cfg, B, max_pages_per_head, ws);
+    DecodeWs w = decode_layout(cfg, B, 1, max_pages_per_head, ws);
     if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
     DenseLaunch a;
     a.page_table = page_table;

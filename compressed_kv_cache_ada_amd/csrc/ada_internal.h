@@ -45,6 +45,10 @@ __device__ __forceinline__ float2 grid_dir(int c) {
 __host__ __device__ constexpr int decode_waves_per_simd(int G) { return G >= 8 ? 2 : 3; }
 
 // ---- launchers (defined in the .hip files; called by ada_api.cpp) ------
+// Q queries per sequence (multi-query decode): q, out are [B][Q][Hq][128].
+// The split-K pass treats the Q * G queries of a KV head as G' = Q * G
+// "virtual heads" v = qi * G + g; its partials are indexed by the virtual
+// row (b * Hkv + h) * G' + v.
 struct DecodeLaunch {
     const int32_t *page_table;
     const int32_t *num_pages;
@@ -54,7 +58,7 @@ struct DecodeLaunch {
     const float *q;
     float *pm, *pl, *pacc;     // split-K partials
     float *out, *lse;
-    int32_t B, Hq, Hkv, P, maxp, chunk_pages, S;
+    int32_t B, Q, Hq, Hkv, P, maxp, chunk_pages, S;
     float scale;
 };
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);

@@ -248,18 +248,19 @@ struct AdaPolicy {
     const ada_page_meta_t *page_meta;
     const uint8_t *arena;
     const float *q;
-    int32_t Hq;
+    int32_t Q, Hq, Gr;   // queries per sequence, query heads, query heads per KV head
     float mul;   // softmax scale * log2(e)
 
     __device__ int num_pages(int row, int) const { return num_pages_[row]; }
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
 
-    // phase 1: query pairs and the grid directions
+    // phase 1: query pairs and the grid directions.  Virtual head v of the
+    // KV head is query qi = v / Gr, head h * Gr + v % Gr of q [B][Q][Hq][128].
     __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
-        const float *qrow = q + ((size_t)b * Hq + (size_t)h * G) * kD;
         for (int i = tid; i < G * kD; i += nt) {
-            const int g = i >> 7, d = i & 127;
-            s.q8[((d >> 1) * G + g) * 2 + (d & 1)] = qrow[i];
+            const int v = i >> 7, d = i & 127;
+            const int qi = v / Gr, g = v % Gr;
+            s.q8[((d >> 1) * G + v) * 2 + (d & 1)] = q[(((size_t)b * Q + qi) * Hq + (size_t)h * Gr + g) * kD + d];
         }
         for (int c = tid; c < 256; c += nt) {
             const float2 d = grid_dir(c);
@@ -345,7 +346,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.page_meta = a.page_meta;
     pol.arena = a.arena;
     pol.q = a.q;
+    pol.Q = a.Q;
     pol.Hq = a.Hq;
+    pol.Gr = a.Hq / a.Hkv;
     pol.mul = a.scale * core::kLog2e;
     core::CoreArgs c;
     c.page_table = a.page_table;
@@ -362,13 +365,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// one work-group per virtual row (b, h, v); writes query qi = v / Gr, head
+// h * Gr + v % Gr
 __global__ __launch_bounds__(core::kReduceThreads) void decode_reduce_kernel(DecodeLaunch a) {
-    const int bq = blockIdx.x;
-    const int b = bq / a.Hq, hq = bq % a.Hq;
-    const int G = a.Hq / a.Hkv;
-    const int np = a.num_pages[b * a.Hkv + hq / G];
-    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, threadIdx.x, a.out,
-                        a.lse);
+    const int vr = blockIdx.x;
+    const int Gr = a.Hq / a.Hkv, GV = a.Q * Gr;
+    const int b = vr / (a.Hkv * GV), rem = vr % (a.Hkv * GV);
+    const int h = rem / GV, v = rem % GV;
+    const size_t orow = ((size_t)b * a.Q + v / Gr) * a.Hq + (size_t)h * Gr + v % Gr;
+    const int np = a.num_pages[b * a.Hkv + h];
+    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), (size_t)vr, orow,
+                        threadIdx.x, a.out, a.lse);
 }
 
 // ---- stand-alone LUT builder --------------------------------------------
@@ -412,7 +419,7 @@ hipError_t launch_g(const DecodeLaunch &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
-    switch (a.Hq / a.Hkv) {
+    switch (a.Q * (a.Hq / a.Hkv)) {   // virtual heads per KV head
         case 1: return launch_g<1>(a, s);
         case 2: return launch_g<2>(a, s);
         case 4: return launch_g<4>(a, s);
@@ -422,7 +429,7 @@ hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Hq), dim3(core::kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Q * a.Hq), dim3(core::kReduceThreads), 0, s, a);
     return hipGetLastError();
 }
 

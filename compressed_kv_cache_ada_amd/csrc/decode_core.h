@@ -105,9 +105,10 @@ struct CoreSmem {
 constexpr int kReduceThreads = 128;
 constexpr int kReduceTile = 16;
 
+// prow: partial row, orow: output row
 __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, const float *pacc, int S, int nc,
-                                              int bq, int d, float *out, float *lse) {
-    const size_t base = (size_t)bq * S;
+                                              size_t prow, size_t orow, int d, float *out, float *lse) {
+    const size_t base = prow * S;
     float M = -INFINITY, L = 0.f, O = 0.f;
     for (int c0 = 0; c0 < nc; c0 += kReduceTile) {
         float mv[kReduceTile], lv[kReduceTile], av[kReduceTile];
@@ -135,12 +136,12 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
         M = Mt;
     }
     if (M == -INFINITY) {
-        out[(size_t)bq * kD + d] = 0.f;
-        if (lse && d == 0) lse[bq] = -INFINITY;
+        out[orow * kD + d] = 0.f;
+        if (lse && d == 0) lse[orow] = -INFINITY;
         return;
     }
-    out[(size_t)bq * kD + d] = O / L;
-    if (lse && d == 0) lse[bq] = (M + log2f(L)) * 0.69314718055994531f;
+    out[orow * kD + d] = O / L;
+    if (lse && d == 0) lse[orow] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 // Policy interface (see decode.hip / dense.hip):
@@ -330,7 +331,7 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         }
     }
     __syncthreads();
-    const size_t bq0 = (size_t)b * a.Hq + (size_t)h * G;
+    const size_t bq0 = ((size_t)b * a.Hkv + h) * G;   // first partial row of this KV head
     for (int i = tid; i < G * kD; i += NT) {
         const int g = i >> 7, d = i & 127;
         float M = -INFINITY;

@@ -100,8 +100,8 @@ __global__ __launch_bounds__(core::kReduceThreads) void dense_reduce_kernel(Dens
     const int bq = blockIdx.x;
     const int b = bq / a.Hq;
     const int np = (a.ctx_len[b] + a.P - 1) / a.P;
-    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, threadIdx.x, a.out,
-                        a.lse);
+    core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), bq, bq, threadIdx.x,
+                        a.out, a.lse);
 }
 
 template <int G, int P>

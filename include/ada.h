@@ -167,6 +167,22 @@ ada_status_t ada_decode_partials(const ada_config_t *cfg, const ada_cache_t *cac
 ada_status_t ada_decode_reduce(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
                                float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* Multi-query decode: Q queries per sequence (speculative drafts, beams,
+ * several positions' queries), all attending to the same cached tokens.
+ * One pass over the cache serves every query: the Q * G queries of a KV head
+ * share each code and value read (G = Hq / Hkv).  Q must be a power of two
+ * with Q * G <= 8, else ADA_EUNSUPPORTED.
+ *   q     device fp32 [B][Q][Hq][128]
+ *   out   device fp32 [B][Q][Hq][128]; lse device fp32 [B][Q][Hq] or NULL
+ *   ws    device workspace of at least ada_decode_multi_workspace() bytes
+ * Query (b, i) gives exactly what ada_decode gives for the query q[b][i]
+ * (up to rounding: the split-K chunking may differ).  ada_decode is this
+ * call with Q = 1. */
+ada_status_t ada_decode_multi_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, int32_t Q,
+                                        size_t *bytes);
+ada_status_t ada_decode_multi(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                              int32_t Q, float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes for ada_encode_append with n requests. */
 ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, size_t *bytes);
 

@@ -76,6 +76,18 @@ def test_host_validation_without_gpu():
     null_cache = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
     assert L.ada_decode(ctypes.byref(good), ctypes.byref(null_cache), None, 2, 1.0, None, None, None, 0, None) \
         == ada.EINVAL
+    # multi-query: Q must be a power of two with Q * (Hq / Hkv) <= 8
+    L_ws = L.ada_decode_multi_workspace
+    st2, n2 = _size(L_ws, ctypes.byref(good), ctypes.byref(desc), 2, 2)
+    assert st2 == ada.OK and n2 > n   # twice the partial rows
+    assert _size(L_ws, ctypes.byref(good), ctypes.byref(desc), 2, 1) == (ada.OK, n)
+    for Q, want in [(0, ada.EINVAL), (-1, ada.EINVAL), (3, ada.EUNSUPPORTED), (4, ada.EUNSUPPORTED)]:
+        assert _size(L_ws, ctypes.byref(good), ctypes.byref(desc), 2, Q)[0] == want
+    g1 = ada.make_config(16, 8, 8)
+    assert _size(L_ws, ctypes.byref(g1), ctypes.byref(desc), 2, 8)[0] == ada.OK
+    assert _size(L_ws, ctypes.byref(g1), ctypes.byref(desc), 2, 16)[0] == ada.EUNSUPPORTED
+    assert L.ada_decode_multi(ctypes.byref(good), ctypes.byref(desc), None, 2, 3, 1.0, None, None, None, 0,
+                              None) == ada.EUNSUPPORTED
     # RDR: unsupported tier set is caught on the host (T8 + T4 only is fine; 0 = all)
     assert _size(L.ada_rdr_workspace, ctypes.byref(good), 2, 100)[0] == ada.OK
     assert L.ada_probe_copy(None, None, 16, None) == ada.EINVAL
