@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "rdr128k", "ragged", "long256k", "tiny"])
     ap.add_argument("--chunk-pages", type=int, default=0)
+    ap.add_argument("--append", action="store_true",
+                    help="time the fused append + decode step against append then decode")
     ap.add_argument("--queries", type=int, default=1,
                     help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -116,6 +118,9 @@ def main():
     units = sum(pages_by_tier[t] * ada.block_bytes(t, P) // 16 for t in (0, 1, 2))
 
     cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages)
+    if args.append:
+        append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
+        return
     cache = ada.Cache(cfg, B, max_row, n_pages, units)
     ada.cache_init(cache)
     keys = torch.from_numpy(w["keys"]).cuda()
@@ -281,6 +286,76 @@ def main():
     if not args.no_cpu_baseline and Q == 1:
         result["cpu_baseline"] = cpu_baseline(w, kept_total, max_row, n_pages, units)
     print(json.dumps(result), flush=True)
+
+
+def append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
+    """One decode step with one new token per (sequence, KV head): the fused
+    ada_decode_append against ada_encode_append followed by ada_decode, each
+    on its own copy of the packed cache with room for the appended tokens.
+    The new tokens go to the 4-bit tier; keys, values and queries are seeded
+    N(0,1) draws."""
+    P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
+    rows = B * Hkv
+    n_steps = args.warmup + args.steps
+    extra = rows * (-(-n_steps // P) + 1)               # new pages the appends may open
+    caches = []
+    keys = torch.from_numpy(w["keys"]).cuda()
+    vals = torch.from_numpy(w["values"].view(np.int16)).cuda()
+    for _ in range(2):
+        c = ada.Cache(cfg, B, max_row + extra // rows, n_pages + extra, units + extra * ada.block_bytes(0, P) // 16)
+        ada.cache_init(c)
+        ada.pack(c, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), keys, vals)
+        assert ada.read_status(c.status) == ada.OK
+        caches.append(c)
+    del keys, vals
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(77)
+    nk = torch.from_numpy(rng.standard_normal((n_steps, B, Hkv, 128), dtype=np.float32)).cuda()
+    nv = torch.from_numpy(rng.standard_normal((n_steps, B, Hkv, 128)).astype(np.float16).view(np.int16)).cuda()
+    nt = torch.ones((B, Hkv), dtype=torch.uint8, device="cuda")
+    qs = torch.from_numpy(rng.standard_normal((n_steps, B, Hq, 128), dtype=np.float32)).cuda()
+    seq = torch.arange(B, dtype=torch.int32, device="cuda").repeat_interleave(Hkv)
+    head = torch.arange(Hkv, dtype=torch.int32, device="cuda").repeat(B)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    wsf = ada.decode_append_workspace(caches[0], B)
+    wsd = ada.decode_workspace(caches[1], B)
+    sz = ada.append_workspace_bytes(caches[1], rows)
+    wsa = torch.empty(max(1, sz), dtype=torch.uint8, device="cuda")
+
+    def fused(i):
+        ada.decode_append(caches[0], qs[i], w["scale"], nk[i], nv[i], nt, out, lse, wsf)
+
+    def separate(i):
+        ada.encode_append(caches[1], seq, head, nt.reshape(-1), nk[i].reshape(-1, 128), nv[i].reshape(-1, 128), wsa)
+        ada.decode(caches[1], qs[i], w["scale"], out, lse, wsd)
+
+    timing = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.warmup, n_steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        timing[name] = e0.elapsed_time(e1) / args.steps
+    for c in caches:
+        assert ada.read_status(c.status) == ada.OK
+    kept_total = sum(kept.values())
+    print(json.dumps({
+        "metric": "ADA decode step with append (one new token per sequence and KV head)",
+        "value": (kept_total + rows) / (timing["fused"] * 1e-3), "unit": "KV token-heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": timing["fused"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "page_size": P,
+                   "kept_token_heads_before": kept_total, "new_tier": "T4"},
+        "fused_ms_per_step": timing["fused"],
+        "append_then_decode_ms_per_step": timing["separate"],
+        "speedup": timing["separate"] / timing["fused"],
+    }), flush=True)
 
 
 def dense_reference(w, ada, torch, cfg):

@@ -76,6 +76,8 @@ def _declare(L):
         "ada_decode_reduce": (st, [cfgp, cachep, i32, vp, vp, vp, sz, vp]),
         "ada_decode_multi_workspace": (st, [cfgp, cachep, i32, i32, ctypes.POINTER(sz)]),
         "ada_decode_multi": (st, [cfgp, cachep, vp, i32, i32, f32, vp, vp, vp, sz, vp]),
+        "ada_decode_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
+        "ada_decode_append": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ada_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_encode_append": (st, [cfgp, cachep, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ada_rdr_workspace": (st, [cfgp, i32, i64, ctypes.POINTER(sz)]),
@@ -97,7 +99,8 @@ def _declare(L):
 
 ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_build_lut",
                "ada_decode_workspace", "ada_decode", "ada_decode_partials", "ada_decode_reduce",
-               "ada_decode_multi_workspace", "ada_decode_multi",
+               "ada_decode_multi_workspace", "ada_decode_multi", "ada_decode_append_workspace",
+               "ada_decode_append",
                "ada_append_workspace", "ada_encode_append", "ada_rdr_workspace", "ada_rdr_assign",
                "ada_pack_workspace", "ada_pack", "ada_read_status", "ada_dense_workspace",
                "ada_dense_decode", "ada_probe_copy", "ada_probe_read", "ada_host_f64_to_f16")
@@ -236,6 +239,13 @@ def decode_reduce(cache, B, out, lse, ws):
                                    _ptr(ws), ws.numel(), _stream()), "ada_decode_reduce")
 
 
+def append_workspace_bytes(cache, n):
+    sz = ctypes.c_size_t(0)
+    _check(lib().ada_append_workspace(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), n, ctypes.byref(sz)),
+           "ada_append_workspace")
+    return sz.value
+
+
 def encode_append(cache, seq, kv_head, tier, keys, values, ws=None):
     seq = _dev(seq, torch.int32, "seq")
     kv_head = _dev(kv_head, torch.int32, "kv_head")
@@ -251,6 +261,33 @@ def encode_append(cache, seq, kv_head, tier, keys, values, ws=None):
     _check(lib().ada_encode_append(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), n, _ptr(seq), _ptr(kv_head),
                                    _ptr(tier), _ptr(keys), _ptr(values), _ptr(ws), ws.numel(), _stream()),
            "ada_encode_append")
+
+
+def decode_append_workspace(cache, B):
+    n = ctypes.c_size_t(0)
+    _check(lib().ada_decode_append_workspace(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), B, ctypes.byref(n)),
+           "ada_decode_append_workspace")
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=cache.page_table.device)
+
+
+def decode_append(cache, q, scale, new_keys, new_values, new_tier, out=None, lse=None, ws=None):
+    """One decode step: append new_keys / new_values ([B][Hkv][128]) at
+    new_tier ([B][Hkv]) and decode q ([B][Hq][128]) over the cache including
+    them.  Device errors land in cache.status (read with read_status)."""
+    q = _dev(q, torch.float32, "q")
+    new_keys = _dev(new_keys, torch.float32, "new_keys")
+    new_values = _dev(new_values, torch.int16, "new_values")
+    new_tier = _dev(new_tier, torch.uint8, "new_tier")
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, cache.cfg.num_q_heads, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, cache.cfg.num_q_heads), dtype=torch.float32, device=q.device)
+    ws = decode_append_workspace(cache, B) if ws is None else ws
+    _check(lib().ada_decode_append(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _ptr(q), B, float(scale),
+                                   _ptr(new_keys), _ptr(new_values), _ptr(new_tier), _ptr(out), _ptr(lse),
+                                   _ptr(ws), ws.numel(), _stream()), "ada_decode_append")
+    return out, lse
 
 
 def rdr_assign(cfg, ctx_len, utility, budget, status, tier_out=None):

@@ -119,6 +119,13 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.chunk_pages = w.cp;
     a.S = w.S;
     a.scale = scale;
+    a.app_page = nullptr;
+    a.app_slot = nullptr;
+    a.app_keys = nullptr;
+    a.app_values = nullptr;
+    a.arena_w = nullptr;
+    a.value_pool_w = nullptr;
+    a.status = cache->status;
     return a;
 }
 
@@ -144,6 +151,42 @@ AppendWs append_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_
     w.n_new = c.take<int32_t>(2);
     w.bytes = c.off;
     return w;
+}
+
+AppendLaunch make_append(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, const int32_t *seq,
+                         const int32_t *kv_head, const uint8_t *tier, const float *keys, const uint16_t *values,
+                         const AppendWs &w) {
+    AppendLaunch a;
+    a.n = n;
+    a.Hkv = cfg->num_kv_heads;
+    a.P = cfg->page_size;
+    a.num_seqs = cache->num_seqs;
+    a.maxp = cache->max_pages_per_head;
+    a.page_capacity = cache->page_capacity;
+    a.arena_capacity16 = cache->arena_capacity16;
+    a.seq = seq;
+    a.head = kv_head;
+    a.tier = tier;
+    a.keys = keys;
+    a.values = values;
+    a.page_table = cache->page_table;
+    a.num_pages = cache->num_pages;
+    a.open_page = cache->open_page;
+    a.page_meta = cache->page_meta;
+    a.arena = cache->code_arena;
+    a.value_pool = cache->value_pool;
+    a.alloc = cache->alloc;
+    a.status = cache->status;
+    a.key_cnt = w.key_cnt;
+    a.key_c0 = w.key_c0;
+    a.key_done = w.key_done;
+    a.key_page = w.key_page_and_off;
+    a.totals = w.totals;
+    a.dest_page = w.dest_page;
+    a.dest_slot = w.dest_slot;
+    a.new_pages = w.new_pages;
+    a.n_new = w.n_new;
+    return a;
 }
 
 struct PackWs {
@@ -359,37 +402,60 @@ ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache
     if (!seq || !kv_head || !tier || !keys || !values) return ADA_EINVAL;
     AppendWs w = append_layout(cfg, cache, n, ws);
     if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
-    AppendLaunch a;
-    a.n = n;
-    a.Hkv = cfg->num_kv_heads;
-    a.P = cfg->page_size;
-    a.num_seqs = cache->num_seqs;
-    a.maxp = cache->max_pages_per_head;
-    a.page_capacity = cache->page_capacity;
-    a.arena_capacity16 = cache->arena_capacity16;
-    a.seq = seq;
-    a.head = kv_head;
-    a.tier = tier;
-    a.keys = keys;
-    a.values = values;
-    a.page_table = cache->page_table;
-    a.num_pages = cache->num_pages;
-    a.open_page = cache->open_page;
-    a.page_meta = cache->page_meta;
-    a.arena = cache->code_arena;
-    a.value_pool = cache->value_pool;
-    a.alloc = cache->alloc;
-    a.status = cache->status;
-    a.key_cnt = w.key_cnt;
-    a.key_c0 = w.key_c0;
-    a.key_done = w.key_done;
-    a.key_page = w.key_page_and_off;
-    a.totals = w.totals;
-    a.dest_page = w.dest_page;
-    a.dest_slot = w.dest_slot;
-    a.new_pages = w.new_pages;
-    a.n_new = w.n_new;
-    return hip_status(launch_append(a, (hipStream_t)stream));
+    AppendLaunch a = make_append(cfg, cache, n, seq, kv_head, tier, keys, values, w);
+    return hip_status(launch_append(a, true, (hipStream_t)stream));
+}
+
+// Fused append + decode: workspace = decode partials, then the append's
+// booking arrays for B * Hkv requests.
+static size_t decode_append_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *ws,
+                                   DecodeWs *dw, AppendWs *aw) {
+    *dw = decode_layout(cfg, B, 1, cache->max_pages_per_head, ws);
+    char *ab = ws ? static_cast<char *>(ws) + dw->bytes : nullptr;
+    *aw = append_layout(cfg, cache, B * cfg->num_kv_heads, ab);
+    return dw->bytes + aw->bytes;
+}
+
+ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
+                                         size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0 || cache->num_seqs <= 0) return ADA_EINVAL;
+    DecodeWs dw;
+    AppendWs aw;
+    *bytes = decode_append_layout(cfg, cache, B, nullptr, &dw, &aw);
+    return ADA_OK;
+}
+
+ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                               float scale, const float *new_keys, const uint16_t *new_values,
+                               const uint8_t *new_tier, float *out, float *lse, void *ws, size_t ws_bytes,
+                               void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cache))) return st;
+    if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!q || !out || !new_keys || !new_values || !new_tier || !ws) return ADA_EINVAL;
+    DecodeWs dw;
+    AppendWs aw;
+    if (ws_bytes < decode_append_layout(cfg, cache, B, ws, &dw, &aw)) return ADA_EINVAL;
+    const int32_t n = B * cfg->num_kv_heads;
+    // 1. book one request per row (row order), update metadata, zero new pages
+    AppendLaunch ap = make_append(cfg, cache, n, nullptr, nullptr, new_tier, new_keys, new_values, aw);
+    hipError_t e = launch_append(ap, false, (hipStream_t)stream);
+    if (e != hipSuccess) return ADA_EHIP;
+    // 2. split-K pass; the owner of each booked slot encodes and writes it first
+    DecodeLaunch a = make_decode(cfg, cache, q, B, 1, scale, out, lse, dw);
+    a.app_page = aw.dest_page;
+    a.app_slot = aw.dest_slot;
+    a.app_keys = new_keys;
+    a.app_values = new_values;
+    a.arena_w = cache->code_arena;
+    a.value_pool_w = cache->value_pool;
+    if ((e = launch_decode_partials(a, (hipStream_t)stream)) != hipSuccess) return ADA_EHIP;
+    // 3. reduction over the chunks
+    return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
 }
 
 ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_stride, size_t *bytes) {

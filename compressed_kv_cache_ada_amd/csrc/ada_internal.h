@@ -60,6 +60,15 @@ struct DecodeLaunch {
     float *out, *lse;
     int32_t B, Q, Hq, Hkv, P, maxp, chunk_pages, S;
     float scale;
+    // fused append (app_page != nullptr): row r's new token, already booked
+    // at (app_page[r], app_slot[r]) with its page zeroed, is encoded and
+    // written by the work-group whose chunk holds that page
+    const int32_t *app_page, *app_slot;
+    const float *app_keys;        // [B * Hkv][128] fp32
+    const uint16_t *app_values;   // [B * Hkv][128] fp16 bits
+    uint8_t *arena_w;
+    uint16_t *value_pool_w;
+    int32_t *status;
 };
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s);
@@ -128,7 +137,7 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
 struct AppendLaunch {
     int32_t n, Hkv, P, num_seqs, maxp;
     int64_t page_capacity, arena_capacity16;
-    const int32_t *seq, *head;
+    const int32_t *seq, *head;   // nullptr: request i is row i (sequence i / Hkv, head i % Hkv)
     const uint8_t *tier;
     const float *keys;
     const uint16_t *values;
@@ -148,7 +157,9 @@ struct AppendLaunch {
     int32_t *new_pages;  // [n]
     int32_t *n_new;      // [1]
 };
-hipError_t launch_append(const AppendLaunch &a, hipStream_t s);
+// append: book destinations, update metadata, zero new pages, then (with
+// encode) encode and write the keys; without encode the caller encodes
+hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s);
 
 struct RdrLaunch {
     int32_t B, Hkv, n_steps;

@@ -21,6 +21,7 @@
 // There is no matrix-core work in the logit path: it is a gather-reduce over
 // small per-pair tables, not a dense contraction.
 #include "decode_core.h"
+#include "encode_core.h"
 
 namespace ada {
 namespace {
@@ -232,7 +233,7 @@ struct CodeStage {
     uint32_t r[64];
 };
 
-template <int G, int P, int NW>
+template <int G, int P, int NW, bool APPEND>
 struct AdaPolicy {
     static constexpr bool kStaged = true;
     struct Smem {
@@ -243,6 +244,7 @@ struct AdaPolicy {
         float2 cs2[4];             // the 2-bit sub-grid
         float q8[64 * G * 2];      // [j][g][x|y] query pairs (T8, factorised)
         CodeStage st[NW];          // the next group's code units, per wavefront
+        uint32_t enc_words[2][16]; // bit-string packing of the fused append's key
     };
     const int32_t *num_pages_;
     const ada_page_meta_t *page_meta;
@@ -250,6 +252,36 @@ struct AdaPolicy {
     const float *q;
     int32_t Q, Hq, Gr;   // queries per sequence, query heads, query heads per KV head
     float mul;   // softmax scale * log2(e)
+    // fused append (APPEND)
+    const int32_t *app_page, *app_slot;
+    const float *app_keys;
+    const uint16_t *app_values;
+    uint8_t *arena_w;
+    uint16_t *value_pool_w;
+    int32_t *status;
+
+    // Fused append: the work-group whose chunk holds the page booked for the
+    // row's new token encodes it (wavefront 0) and writes radius, codes and
+    // value into its slot before any wavefront reads the chunk's pages.  No
+    // other work-group reads that page.  Skipped when the booking failed.
+    __device__ bool after_pages(Smem &s, const int *pages, int nch, int row, int w, int lane) const {
+        if constexpr (!APPEND) {
+            return false;
+        } else {
+            if (enc::read_status(status) != 0) return false;
+            const int dp = app_page[row];
+            bool own = false;
+            for (int i = lane; i < nch; i += 64) own |= pages[i] == dp;
+            own = __any(own);   // the same in every wavefront
+            if (own && w == 0) {
+                const uint2 m = ldg<uint2>(page_meta + dp);
+                enc::encode_write_one(app_keys + (size_t)row * kD, app_values + (size_t)row * kD, dp, app_slot[row], m,
+                                      arena_w, value_pool_w, P, status, s.enc_words);
+                __threadfence_block();
+            }
+            return own;
+        }
+    }
 
     __device__ int num_pages(int row, int) const { return num_pages_[row]; }
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
@@ -334,9 +366,9 @@ struct AdaPolicy {
     }
 };
 
-template <int G, int P, int NW, int WPE>
+template <int G, int P, int NW, int WPE, bool APPEND>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
-    using Pol = AdaPolicy<G, P, NW>;
+    using Pol = AdaPolicy<G, P, NW, APPEND>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
     constexpr size_t RAW = sizeof(typename Pol::Smem) > RED ? sizeof(typename Pol::Smem) : RED;
     __shared__ __align__(16) unsigned char raw[RAW];   // policy tables, later the wave-merge buffer
@@ -349,6 +381,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.Q = a.Q;
     pol.Hq = a.Hq;
     pol.Gr = a.Hq / a.Hkv;
+    pol.app_page = a.app_page;
+    pol.app_slot = a.app_slot;
+    pol.app_keys = a.app_keys;
+    pol.app_values = a.app_values;
+    pol.arena_w = a.arena_w;
+    pol.value_pool_w = a.value_pool_w;
+    pol.status = a.status;
     pol.mul = a.scale * core::kLog2e;
     core::CoreArgs c;
     c.page_table = a.page_table;
@@ -407,7 +446,12 @@ template <int G, int P>
 hipError_t launch_gp(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
     constexpr int WPE = decode_waves_per_simd(G);
-    hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE>), dim3(a.S, a.Hkv, a.B), dim3(NW * 64), 0, s, a);
+    if (a.app_page)
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, true>), dim3(a.S, a.Hkv, a.B), dim3(NW * 64), 0, s,
+                           a);
+    else
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, false>), dim3(a.S, a.Hkv, a.B), dim3(NW * 64), 0, s,
+                           a);
     return hipGetLastError();
 }
 

@@ -150,6 +150,10 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //   uint2 meta(page, idx, b)  x = tier | count << 8, y = policy data
 //   void prologue(smem, b, h, tid, nthreads)   stores before a barrier
 //   void build(smem, tid, nthreads)            tables after that barrier
+//   bool after_pages(smem, pages, n, row, w, lane)  work before any page of
+//                                              the chunk is read; returns
+//                                              (uniformly) whether a barrier
+//                                              must follow
 //   kStaged = true:
 //     void stage(smem, w, meta, slot)          request a group's codes into
 //                                              wavefront w's LDS stage
@@ -188,6 +192,9 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
     }
     pol.prologue(ps, b, h, tid, NT);
     __syncthreads();
+    // policy work that must precede every code / value read of the chunk
+    // (the fused append writes the row's new token into its slot)
+    if (pol.after_pages(ps, cs.pages, nch, row, w, lane)) __syncthreads();
     const int n_groups = (nch + TPG - 1) / TPG;
     const int pg = lane / P, slot = lane % P;
     // the group's page for this lane (lane = token); lanes past the row's

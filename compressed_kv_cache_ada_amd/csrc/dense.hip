@@ -37,6 +37,7 @@ struct DensePolicy {
         for (int i = tid; i < G * kD; i += nt) s.qd[(i & 127) * G + (i >> 7)] = qrow[i] * mul;
     }
     __device__ void build(Smem &, int, int) const {}
+    __device__ bool after_pages(Smem &, const int *, int, int, int, int) const { return false; }
     // keys are read inside the logit loop: fetch only records the address
     struct Codes {
         const uint16_t *kp;

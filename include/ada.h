@@ -200,6 +200,33 @@ ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache
                                const float *keys, const uint16_t *values, void *ws, size_t ws_bytes,
                                void *stream);
 
+/* Workspace bytes for ada_decode_append on sequences 0..B-1. */
+ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
+                                         size_t *bytes);
+
+/* Fused append + decode for one decode step: each (sequence b < B, KV
+ * head h) gets one new token, which is encoded into its tier's open page
+ * (abstract: keys stored as radius + angle codes in tier-homogeneous pages)
+ * and attended to in the same split-K launch.  The result equals
+ * ada_encode_append of the B * Hkv requests in row order (b, h ascending)
+ * followed by ada_decode(q): the same pages, bytes and metadata, and the
+ * same outputs.
+ *   q          device fp32 [B][Hq][128]
+ *   new_keys   device fp32 [B][Hkv][128]; new_values device fp16 bits [B][Hkv][128]
+ *   new_tier   device uint8 [B][Hkv] (tier id)
+ *   out, lse   as for ada_decode
+ *   ws         device workspace of at least ada_decode_append_workspace() bytes
+ * The new slots are booked first (metadata updated, new pages zeroed); in the
+ * split-K launch the work-group whose context chunk holds a booked slot
+ * encodes the key and writes the slot before reading any of its pages.
+ * Device errors are the append's (bad tier or non-finite key -> ADA_EINVAL,
+ * capacity -> ADA_ENOSPC, in the status word): then nothing is written and
+ * out / lse cover the tokens cached before the call. */
+ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                               float scale, const float *new_keys, const uint16_t *new_values,
+                               const uint8_t *new_tier, float *out, float *lse, void *ws, size_t ws_bytes,
+                               void *stream);
+
 /* Workspace bytes for ada_rdr_assign over B sequences of stride ctx_stride. */
 ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_stride, size_t *bytes);
 
