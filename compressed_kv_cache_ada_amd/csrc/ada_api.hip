@@ -441,9 +441,9 @@ ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache
     AppendWs aw;
     if (ws_bytes < decode_append_layout(cfg, cache, B, ws, &dw, &aw)) return ADA_EINVAL;
     const int32_t n = B * cfg->num_kv_heads;
-    // 1. book one request per row (row order), update metadata, zero new pages
+    // 1. book one request per row (row order) and update the metadata
     AppendLaunch ap = make_append(cfg, cache, n, nullptr, nullptr, new_tier, new_keys, new_values, aw);
-    hipError_t e = launch_append(ap, false, (hipStream_t)stream);
+    hipError_t e = launch_append_rows(ap, (hipStream_t)stream);
     if (e != hipSuccess) return ADA_EHIP;
     // 2. split-K pass; the owner of each booked slot encodes and writes it first
     DecodeLaunch a = make_decode(cfg, cache, q, B, 1, scale, out, lse, dw);

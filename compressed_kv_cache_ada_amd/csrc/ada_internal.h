@@ -61,8 +61,9 @@ struct DecodeLaunch {
     int32_t B, Q, Hq, Hkv, P, maxp, chunk_pages, S;
     float scale;
     // fused append (app_page != nullptr): row r's new token, already booked
-    // at (app_page[r], app_slot[r]) with its page zeroed, is encoded and
-    // written by the work-group whose chunk holds that page
+    // at (app_page[r], app_slot[r]), is encoded and written by the
+    // work-group whose chunk holds that page; a booked slot 0 is a new page,
+    // which that work-group zeroes first
     const int32_t *app_page, *app_slot;
     const float *app_keys;        // [B * Hkv][128] fp32
     const uint16_t *app_values;   // [B * Hkv][128] fp16 bits
@@ -160,6 +161,10 @@ struct AppendLaunch {
 // append: book destinations, update metadata, zero new pages, then (with
 // encode) encode and write the keys; without encode the caller encodes
 hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s);
+// one request per row (request r = row r, seq / head unused): book, check
+// and update metadata in one launch; dest_page / dest_slot get the slots,
+// new pages (slot 0) are not zeroed and new_pages[r] holds their code offset
+hipError_t launch_append_rows(const AppendLaunch &a, hipStream_t s);
 
 struct RdrLaunch {
     int32_t B, Hkv, n_steps;

@@ -273,13 +273,24 @@ struct AdaPolicy {
             bool own = false;
             for (int i = lane; i < nch; i += 64) own |= pages[i] == dp;
             own = __any(own);   // the same in every wavefront
-            if (own && w == 0) {
-                const uint2 m = ldg<uint2>(page_meta + dp);
-                enc::encode_write_one(app_keys + (size_t)row * kD, app_values + (size_t)row * kD, dp, app_slot[row], m,
-                                      arena_w, value_pool_w, P, status, s.enc_words);
+            if (!own) return false;
+            const int slot = app_slot[row];
+            const uint2 m = ldg<uint2>(page_meta + dp);
+            if (slot == 0) {   // a new page: zero its code block and value page
+                const int tid = threadIdx.x;
+                uint4 *cb = reinterpret_cast<uint4 *>(arena_w + (size_t)m.y * 16);
+                for (int k = tid; k < block16(m.x & 0xFF, P); k += NW * 64) cb[k] = make_uint4(0u, 0u, 0u, 0u);
+                uint4 *vp = reinterpret_cast<uint4 *>(value_pool_w + (size_t)dp * P * kD);
+                for (int k = tid; k < P * kD / 8; k += NW * 64) vp[k] = make_uint4(0u, 0u, 0u, 0u);
+                __threadfence_block();
+                __syncthreads();
+            }
+            if (w == 0) {
+                enc::encode_write_one(app_keys + (size_t)row * kD, app_values + (size_t)row * kD, dp, slot, m, arena_w,
+                                      value_pool_w, P, status, s.enc_words);
                 __threadfence_block();
             }
-            return own;
+            return true;
         }
     }
 

@@ -319,6 +319,118 @@ __global__ __launch_bounds__(256) void append_capacity_kernel(AppendLaunch a) {
     }
 }
 
+// One request per row (request r = row r), single work-group: validates the
+// tiers and keys, books each row's slot -- the next slot of its tier's open
+// page, or a new page, new pages numbered in row order -- checks every
+// capacity, and only if everything fits updates the metadata and the
+// allocation counters (the same result as the general append of the same
+// requests).  New pages are left to the caller to zero: their booked slot
+// is 0, and new_pages[r] holds their code block offset (16-byte units).
+__global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
+    __shared__ int s_need[1024];
+    __shared__ long long s_units[1024];
+    __shared__ int s_bad, s_nospace, c_pages;
+    __shared__ long long c_units;
+    const int tid = threadIdx.x;
+    if (read_status(a.status) != 0) return;
+    if (tid == 0) {
+        s_bad = 0;
+        s_nospace = 0;
+        c_pages = 0;
+        c_units = 0;
+    }
+    __syncthreads();
+    const int P = a.P, rows = a.n;
+    // tiers and keys, coalesced: one thread per 16 bytes of key
+    const float4 *k4 = reinterpret_cast<const float4 *>(a.keys);
+    bool ok = true;
+    for (int i = tid; i < rows * (kD / 4); i += 1024) {
+        const float4 v = k4[i];
+        ok &= isfinite(v.x) & isfinite(v.y) & isfinite(v.z) & isfinite(v.w);
+        if ((i & 31) == 0) ok &= a.tier[i >> 5] < 3;
+    }
+    if (!ok) atomicOr(&s_bad, 1);
+    __syncthreads();
+    if (s_bad) {
+        if (tid == 0) set_status(a.status, ADA_EINVAL);
+        return;
+    }
+    const long long base_p = a.alloc[0], base_u = a.alloc[1];
+    for (int t0 = 0; t0 < rows; t0 += 1024) {
+        const int r = t0 + tid;
+        int need = 0, page = -1, slot = 0;
+        long long units = 0;
+        if (r < rows) {
+            const int tau = a.tier[r];
+            const int open = a.open_page[r * 3 + tau];
+            const int cnt = open >= 0 ? (int)a.page_meta[open].count : P;
+            if (cnt < P) {
+                page = open;
+                slot = cnt;
+            } else {
+                need = 1;
+                units = block16(tau, P);
+                if (a.num_pages[r] >= a.maxp) atomicOr(&s_nospace, 1);
+            }
+        }
+        // inclusive scans of new pages and code units over the tile
+        s_need[tid] = need;
+        s_units[tid] = units;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int v = tid >= off ? s_need[tid - off] : 0;
+            const long long u = tid >= off ? s_units[tid - off] : 0;
+            __syncthreads();
+            s_need[tid] += v;
+            s_units[tid] += u;
+            __syncthreads();
+        }
+        if (r < rows) {
+            if (need) {
+                a.dest_page[r] = (int)(base_p + c_pages + s_need[tid] - 1);
+                a.dest_slot[r] = 0;
+                a.new_pages[r] = (int32_t)(uint32_t)(base_u + c_units + s_units[tid] - units);
+            } else {
+                a.dest_page[r] = page;
+                a.dest_slot[r] = slot;
+            }
+        }
+        __syncthreads();
+        if (tid == 1023) {
+            c_pages += s_need[1023];
+            c_units += s_units[1023];
+        }
+        __syncthreads();
+    }
+    if (tid == 0 && (base_p + c_pages > a.page_capacity || base_u + c_units > a.arena_capacity16)) s_nospace = 1;
+    __syncthreads();
+    if (s_nospace) {
+        if (tid == 0) set_status(a.status, ADA_ENOSPC);
+        return;
+    }
+    for (int r = tid; r < rows; r += 1024) {
+        const int tau = a.tier[r], page = a.dest_page[r], slot = a.dest_slot[r];
+        if (slot == 0) {   // a new page (an open page always holds at least one token)
+            ada_page_meta_t m;
+            m.tier = (uint8_t)tau;
+            m.count = 1;
+            m.reserved = 0;
+            m.code_off16 = (uint32_t)a.new_pages[r];
+            a.page_meta[page] = m;
+            a.page_table[(size_t)r * a.maxp + a.num_pages[r]] = page;
+            a.num_pages[r] += 1;
+            a.open_page[r * 3 + tau] = P > 1 ? page : -1;
+        } else {
+            a.page_meta[page].count = (uint8_t)(slot + 1);
+            if (slot + 1 == P) a.open_page[r * 3 + tau] = -1;
+        }
+    }
+    if (tid == 0) {
+        a.alloc[0] = base_p + c_pages;
+        a.alloc[1] = base_u + c_units;
+    }
+}
+
 // single work-group: place every request in order (tiles of 1024)
 __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
     const AppendLaunch &a = k.a;
@@ -532,6 +644,11 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     e.P = a.P;
     e.status = a.status;
     hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(e.n, 4, 16384)), dim3(256), 0, s, e);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_rows(const AppendLaunch &a, hipStream_t s) {
+    hipLaunchKernelGGL(append_rows_kernel, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 

@@ -1,7 +1,7 @@
 """Turn rocprofv3 result databases of a bench.py run into the short text
 summaries kept under profiles/.
 
-    python rocprof_summary.py stats --db KT.db --workload llama8b --cmd "..."
+    python rocprof_summary.py stats --db KT.db --workload llama8b --cmd "..." [--out NAME.md]
     python rocprof_summary.py pmc --fetch-db F.db --write-db W.db --workload llama8b \
         --cmd-fetch "..." --cmd-write "..." [--bench-json B.json]
 
@@ -77,7 +77,7 @@ def cmd_stats(a):
         d = agg[name]
         lines.append(f"- `{short(name)}`: n={len(d)} mean={statistics.mean(d) / 1e3:.2f} "
                      f"median={statistics.median(d) / 1e3:.2f} min={min(d) / 1e3:.2f} max={max(d) / 1e3:.2f}")
-    out = os.path.join(PROFILES, f"ada_decode_partials_{a.workload}_kernel_stats.md")
+    out = os.path.join(PROFILES, a.out or f"ada_decode_partials_{a.workload}_kernel_stats.md")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out)
@@ -131,6 +131,7 @@ def main():
     s.add_argument("--db", required=True)
     s.add_argument("--workload", required=True)
     s.add_argument("--cmd", required=True)
+    s.add_argument("--out", help="summary file name under profiles/")
     p = sub.add_parser("pmc")
     p.add_argument("--fetch-db", required=True)
     p.add_argument("--write-db", required=True)
