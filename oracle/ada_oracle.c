@@ -798,6 +798,114 @@ int orc_decode(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Attention mass of every kept token in one decode step (the utility signal
+ * the RDR packer consumes; the abstract names "estimated future utility"
+ * without defining it, and this is the plain reading: the attention the
+ * token receives now).  For KV row (b, h) and each of its G query heads hq,
+ * the logits and lse are exactly those of orc_decode; the token's utility is
+ *     u_t = sum_{hq of h} exp(logit_t(hq) - lse(hq)),
+ * accumulated over hq in ascending order and written to
+ * util[page * P + slot].  Other entries of util are left unchanged.  Over a
+ * row with kept tokens the u_t sum to G.  Threaded over KV rows. */
+typedef struct {
+    decode_job_t d;          /* shared fields; d.out / d.lse unused */
+    double *util;
+    int64_t next_kv, n_kv;
+} util_job_t;
+
+static void *util_worker(void *arg)
+{
+    util_job_t *U = arg;
+    decode_job_t *J = &U->d;
+    int G = J->Hq / J->Hkv;
+    double *lut8 = malloc(sizeof(double) * ORC_NP * 256);
+    double *lut4 = malloc(sizeof(double) * ORC_NP * 16);
+    double *lut2 = malloc(sizeof(double) * ORC_NP * 4);
+    int64_t cap = (int64_t)J->max_pages_per_head * J->P;
+    double *logit = malloc(sizeof(double) * (cap > 0 ? cap : 1));
+    double *u = malloc(sizeof(double) * (cap > 0 ? cap : 1));
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t row = U->next_kv++;
+        pthread_mutex_unlock(&J->mu);
+        if (row >= U->n_kv) break;
+        int b = (int)(row / J->Hkv), h = (int)(row % J->Hkv);
+        int np = J->num_pages[row];
+        int64_t n = 0;
+        for (int g = 0; g < G; g++) {
+            const float *q = J->q + ((int64_t)b * J->Hq + (int64_t)h * G + g) * ORC_D;
+            orc_lut(q, 8, lut8);
+            orc_lut(q, 4, lut4);
+            orc_lut(q, 2, lut2);
+            double *luts[3] = {lut8, lut4, lut2};
+            double m = -INFINITY;
+            n = 0;
+            for (int i = 0; i < np; i++) {
+                int64_t page = J->page_table[row * J->max_pages_per_head + i];
+                int tier, count; uint32_t off16;
+                meta_read(J->page_meta, page, &tier, &count, &off16);
+                const uint8_t *block = J->arena + (int64_t)off16 * 16;
+                int N = 1 << TIER_TB[tier];
+                double L = (double)((1 << TIER_SB[tier]) - 1);
+                for (int slot = 0; slot < count; slot++) {
+                    uint16_t r16, th[ORC_NP], sc[ORC_NP];
+                    read_token_codes(block, tier, J->P, slot, &r16, th, sc);
+                    double acc = 0.0;
+                    for (int j = 0; j < ORC_NP; j++)
+                        acc += ((double)sc[j] / L) * luts[tier][j * N + th[j]];
+                    double lg = J->scale * orc_f16_to_f64(r16) * acc;
+                    logit[n++] = lg;
+                    if (lg > m) m = lg;
+                }
+            }
+            if (n == 0) break;
+            double sum = 0.0;
+            for (int64_t t = 0; t < n; t++) sum += exp(logit[t] - m);
+            double lse = m + log(sum);
+            for (int64_t t = 0; t < n; t++) {
+                double w = exp(logit[t] - lse);
+                u[t] = (g == 0) ? w : u[t] + w;
+            }
+        }
+        int64_t t = 0;
+        for (int i = 0; i < np && n > 0; i++) {
+            int64_t page = J->page_table[row * J->max_pages_per_head + i];
+            int tier, count; uint32_t off16;
+            meta_read(J->page_meta, page, &tier, &count, &off16);
+            for (int slot = 0; slot < count; slot++, t++) U->util[page * J->P + slot] = u[t];
+        }
+    }
+    free(lut8); free(lut4); free(lut2); free(logit); free(u);
+    return NULL;
+}
+
+int orc_decode_utility(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
+                       const int32_t *page_table, const int32_t *num_pages,
+                       const uint8_t *page_meta, const uint8_t *arena,
+                       const float *q, double scale, double *util, int nthreads)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || (P != 16 && P != 32)) return ORC_EINVAL;
+    util_job_t U;
+    memset(&U, 0, sizeof(U));
+    decode_job_t *J = &U.d;
+    J->P = P; J->Hq = Hq; J->Hkv = Hkv; J->B = B;
+    J->max_pages_per_head = max_pages_per_head;
+    J->page_table = page_table; J->num_pages = num_pages;
+    J->page_meta = page_meta; J->arena = arena;
+    J->q = q; J->scale = scale;
+    U.util = util;
+    U.next_kv = 0; U.n_kv = (int64_t)B * Hkv;
+    pthread_mutex_init(&J->mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    pthread_t *th = malloc(sizeof(pthread_t) * nthreads);
+    for (int i = 0; i < nthreads; i++) pthread_create(&th[i], NULL, util_worker, &U);
+    for (int i = 0; i < nthreads; i++) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&J->mu);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Unquantised angle-domain logits (oracle only): r, s_j and theta_j kept as
  * exact fp64 reals, logit = r * sum_j s_j (q_{2j} cos th_j + q_{2j+1} sin th_j).
  * This equals the plain dot product q.k up to rounding. */

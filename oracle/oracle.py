@@ -69,6 +69,8 @@ def _declare(L):
     L.orc_lut.argtypes = [vp, ctypes.c_int, vp]
     L.orc_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
                              vp, vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int]
+    L.orc_decode_utility.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
+                                     vp, vp, vp, vp, vp, dbl, vp, ctypes.c_int]
     L.orc_identity_logits.argtypes = [vp, i64, vp, vp]
     L.orc_read_token.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp]
     L.orc_value_index.restype = i64
@@ -216,6 +218,24 @@ def decode(cache, q, scale, nthreads=None):
                           _p(out), _p(lse), nthreads)
     assert st == OK, st
     return out, lse
+
+
+def decode_utility(cache, q, scale, util=None, nthreads=None):
+    """Attention mass of every kept token for q fp32 [B][Hq][128]: returns
+    util fp64 [page_capacity][P], util[page][slot] = sum over the KV head's
+    query heads of the token's softmax weight; entries of slots holding no
+    kept token of sequences 0..B-1 keep their input value (NaN by default)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, Hq, _ = q.shape
+    assert Hq == cache.Hq
+    if util is None:
+        util = np.full((cache.page_capacity, cache.P), np.nan, np.float64)
+    nthreads = nthreads or max(1, len(os.sched_getaffinity(0)))
+    st = lib().orc_decode_utility(cache.P, cache.Hq, cache.Hkv, B, cache.max_pages_per_head,
+                                  _p(cache.page_table), _p(cache.num_pages), _p(cache.page_meta),
+                                  _p(cache.arena), _p(q), float(scale), _p(util), nthreads)
+    assert st == OK, st
+    return util
 
 
 def identity_logits(keys, q):
