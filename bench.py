@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "rdr128k", "ragged", "long256k", "tiny"])
     ap.add_argument("--chunk-pages", type=int, default=0)
+    ap.add_argument("--utility", action="store_true",
+                    help="time decode with per-token utility emission against plain decode")
     ap.add_argument("--append", action="store_true",
                     help="time the fused append + decode step against append then decode")
     ap.add_argument("--queries", type=int, default=1,
@@ -120,6 +122,9 @@ def main():
     cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages)
     if args.append:
         append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
+        return
+    if args.utility:
+        utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
         return
     cache = ada.Cache(cfg, B, max_row, n_pages, units)
     ada.cache_init(cache)
@@ -286,6 +291,49 @@ def main():
     if not args.no_cpu_baseline and Q == 1:
         result["cpu_baseline"] = cpu_baseline(w, kept_total, max_row, n_pages, units)
     print(json.dumps(result), flush=True)
+
+
+def utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
+    """ada_decode_utility (decode + every kept token's attention mass) against
+    ada_decode on the same packed cache."""
+    P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
+    cache = ada.Cache(cfg, B, max_row, n_pages, units)
+    ada.cache_init(cache)
+    ada.pack(cache, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), torch.from_numpy(w["keys"]).cuda(),
+             torch.from_numpy(w["values"].view(np.int16)).cuda())
+    assert ada.read_status(cache.status) == ada.OK
+    torch.cuda.empty_cache()
+    q = torch.from_numpy(w["q"]).cuda()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    util = torch.zeros((n_pages, P), dtype=torch.float32, device="cuda")
+    wsu = ada.decode_utility_workspace(cache, B)
+    wsd = ada.decode_workspace(cache, B)
+    runs = {"utility": lambda: ada.decode_utility(cache, q, w["scale"], util, out, lse, wsu),
+            "decode": lambda: ada.decode(cache, q, w["scale"], out, lse, wsd)}
+    timing = {}
+    for name, fn in runs.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        timing[name] = e0.elapsed_time(e1) / args.steps
+    kept_total = sum(kept.values())
+    print(json.dumps({
+        "metric": "ADA decode with per-token utility emission",
+        "value": kept_total / (timing["utility"] * 1e-3), "unit": "KV token-heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": timing["utility"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "page_size": P,
+                   "kept_token_heads": kept_total},
+        "utility_ms_per_step": timing["utility"], "decode_ms_per_step": timing["decode"],
+        "overhead": timing["utility"] / timing["decode"] - 1.0,
+    }), flush=True)
 
 
 def append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):

@@ -76,6 +76,8 @@ def _declare(L):
         "ada_decode_reduce": (st, [cfgp, cachep, i32, vp, vp, vp, sz, vp]),
         "ada_decode_multi_workspace": (st, [cfgp, cachep, i32, i32, ctypes.POINTER(sz)]),
         "ada_decode_multi": (st, [cfgp, cachep, vp, i32, i32, f32, vp, vp, vp, sz, vp]),
+        "ada_decode_utility_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
+        "ada_decode_utility": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "ada_decode_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_decode_append": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ada_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
@@ -100,7 +102,7 @@ def _declare(L):
 ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_build_lut",
                "ada_decode_workspace", "ada_decode", "ada_decode_partials", "ada_decode_reduce",
                "ada_decode_multi_workspace", "ada_decode_multi", "ada_decode_append_workspace",
-               "ada_decode_append",
+               "ada_decode_append", "ada_decode_utility_workspace", "ada_decode_utility",
                "ada_append_workspace", "ada_encode_append", "ada_rdr_workspace", "ada_rdr_assign",
                "ada_pack_workspace", "ada_pack", "ada_read_status", "ada_dense_workspace",
                "ada_dense_decode", "ada_probe_copy", "ada_probe_read", "ada_host_f64_to_f16")
@@ -261,6 +263,32 @@ def encode_append(cache, seq, kv_head, tier, keys, values, ws=None):
     _check(lib().ada_encode_append(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), n, _ptr(seq), _ptr(kv_head),
                                    _ptr(tier), _ptr(keys), _ptr(values), _ptr(ws), ws.numel(), _stream()),
            "ada_encode_append")
+
+
+def decode_utility_workspace(cache, B):
+    n = ctypes.c_size_t(0)
+    _check(lib().ada_decode_utility_workspace(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), B,
+                                              ctypes.byref(n)), "ada_decode_utility_workspace")
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=cache.page_table.device)
+
+
+def decode_utility(cache, q, scale, util=None, out=None, lse=None, ws=None):
+    """Decode q ([B][Hq][128]) and write every kept token's attention mass
+    into util (fp32 [page_capacity][P]; a new NaN-filled tensor if None)."""
+    q = _dev(q, torch.float32, "q")
+    B = q.shape[0]
+    if util is None:
+        util = torch.full((cache.desc.page_capacity, cache.cfg.page_size), float("nan"), dtype=torch.float32,
+                          device=q.device)
+    if out is None:
+        out = torch.empty((B, cache.cfg.num_q_heads, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, cache.cfg.num_q_heads), dtype=torch.float32, device=q.device)
+    ws = decode_utility_workspace(cache, B) if ws is None else ws
+    _check(lib().ada_decode_utility(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _ptr(q), B, float(scale),
+                                    _ptr(out), _ptr(lse), _ptr(util), _ptr(ws), ws.numel(), _stream()),
+           "ada_decode_utility")
+    return out, lse, util
 
 
 def decode_append_workspace(cache, B):

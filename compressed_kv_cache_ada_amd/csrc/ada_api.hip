@@ -126,6 +126,8 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.arena_w = nullptr;
     a.value_pool_w = nullptr;
     a.status = cache->status;
+    a.logit_buf = nullptr;
+    a.util = nullptr;
     return a;
 }
 
@@ -456,6 +458,50 @@ ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache
     if ((e = launch_decode_partials(a, (hipStream_t)stream)) != hipSuccess) return ADA_EHIP;
     // 3. reduction over the chunks
     return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
+}
+
+// Utility emission: workspace = decode partials, then the logit buffer
+// [page_capacity * P][G], then an lse buffer [B][Hq] (used when lse is NULL).
+static size_t decode_utility_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *ws,
+                                    DecodeWs *dw, float **logit_buf, float **lse_buf) {
+    *dw = decode_layout(cfg, B, 1, cache->max_pages_per_head, ws);
+    Carver c(ws ? static_cast<char *>(ws) + dw->bytes : nullptr);
+    const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    *logit_buf = c.take<float>((size_t)cache->page_capacity * cfg->page_size * G);
+    *lse_buf = c.take<float>((size_t)B * cfg->num_q_heads);
+    return dw->bytes + c.off;
+}
+
+ada_status_t ada_decode_utility_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
+                                          size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0 || cache->page_capacity <= 0) return ADA_EINVAL;
+    DecodeWs dw;
+    float *lb, *sb;
+    *bytes = decode_utility_layout(cfg, cache, B, nullptr, &dw, &lb, &sb);
+    return ADA_OK;
+}
+
+ada_status_t ada_decode_utility(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                                float scale, float *out, float *lse, float *util, void *ws, size_t ws_bytes,
+                                void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cache))) return st;
+    if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!q || !out || !util || !ws) return ADA_EINVAL;
+    DecodeWs dw;
+    float *logit_buf, *lse_buf;
+    if (ws_bytes < decode_utility_layout(cfg, cache, B, ws, &dw, &logit_buf, &lse_buf)) return ADA_EINVAL;
+    DecodeLaunch a = make_decode(cfg, cache, q, B, 1, scale, out, lse ? lse : lse_buf, dw);
+    a.logit_buf = logit_buf;
+    a.util = util;
+    hipError_t e = launch_decode_partials(a, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_decode_reduce(a, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_decode_utility(a, (hipStream_t)stream);
+    return hip_status(e);
 }
 
 ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_stride, size_t *bytes) {

@@ -70,10 +70,17 @@ struct DecodeLaunch {
     uint8_t *arena_w;
     uint16_t *value_pool_w;
     int32_t *status;
+    // utility emission (logit_buf != nullptr): the split-K pass stores every
+    // kept token's base-2 logits at [page * P + slot][Hq / Hkv]; the utility
+    // pass turns them into attention mass in util[page * P + slot]
+    float *logit_buf;
+    float *util;
 };
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, hipStream_t s);
+// after the reduction (needs lse): util[page * P + slot] for every kept token
+hipError_t launch_decode_utility(const DecodeLaunch &a, hipStream_t s);
 
 struct DenseLaunch {
     const int32_t *page_table;

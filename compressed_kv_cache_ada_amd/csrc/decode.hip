@@ -359,7 +359,12 @@ struct AdaPolicy {
         k.h = (slot & 1) ? make_uint2(hh.z, hh.w) : make_uint2(hh.x, hh.y);
         const uint32_t rr = st.r[lane];
         k.r = (slot & 1) ? rr >> 16 : rr & 0xFFFFu;
-        k.c = arena + (size_t)meta.y * 16 + 2 * P + slot * 16;
+        // the slot offset is made opaque here so that arena + slot offset (a
+        // 64-bit per-lane value) is not hoisted out of the group loop, where
+        // it would hold two more registers for the whole loop
+        uint32_t soff = 2 * P + slot * 16;
+        asm volatile("" : "+v"(soff));
+        k.c = arena + (size_t)meta.y * 16 + soff;
         return k;
     }
 
@@ -377,9 +382,10 @@ struct AdaPolicy {
     }
 };
 
-template <int G, int P, int NW, int WPE, bool APPEND>
+// MODE: 0 plain, 1 fused append, 2 utility emission
+template <int G, int P, int NW, int WPE, int MODE>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
-    using Pol = AdaPolicy<G, P, NW, APPEND>;
+    using Pol = AdaPolicy<G, P, NW, MODE == 1>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
     constexpr size_t RAW = sizeof(typename Pol::Smem) > RED ? sizeof(typename Pol::Smem) : RED;
     __shared__ __align__(16) unsigned char raw[RAW];   // policy tables, later the wave-merge buffer
@@ -411,7 +417,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     c.maxp = a.maxp;
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
-    core::split_k<G, P, NW>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
+    c.logit_buf = a.logit_buf;
+    core::split_k<G, P, NW, MODE == 2>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
@@ -426,6 +433,43 @@ __global__ __launch_bounds__(core::kReduceThreads) void decode_reduce_kernel(Dec
     const int np = a.num_pages[b * a.Hkv + h];
     core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), (size_t)vr, orow,
                         threadIdx.x, a.out, a.lse);
+}
+
+// ---- utility pass ---------------------------------------------------------
+// Attention mass of every kept token (the signal RDR consumes as "estimated
+// future utility"): u = sum over the KV head's G query heads of
+// exp2(logit2 - lse2), logit2 the stored base-2 logit, lse2 = lse * log2(e)
+// from the reduction.  One work-group per (row, block of 64 pages).
+constexpr int kUtilPages = 64;
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_utility_kernel(DecodeLaunch a) {
+    __shared__ int s_page[kUtilPages], s_count[kUtilPages];
+    const int row = blockIdx.y, b = row / a.Hkv, h = row % a.Hkv;
+    const int np = a.num_pages[row];
+    const int p0 = blockIdx.x * kUtilPages;
+    if (p0 >= np) return;
+    const int npg = min(kUtilPages, np - p0);
+    if (threadIdx.x < npg) {
+        const int page = a.page_table[(size_t)row * a.maxp + p0 + threadIdx.x];
+        s_page[threadIdx.x] = page;
+        s_count[threadIdx.x] = a.page_meta[page].count;
+    }
+    float lse2[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lse2[g] = a.lse[(size_t)b * a.Hq + (size_t)h * G + g] * core::kLog2e;
+    __syncthreads();
+    const int P = a.P, n = npg * P;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int pi = i / P, slot = i % P;
+        if (slot >= s_count[pi]) continue;
+        const size_t tok = (size_t)s_page[pi] * P + slot;
+        const float *lg = a.logit_buf + tok * G;
+        float u = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) u += exp2f(lg[g] - lse2[g]);
+        a.util[tok] = u;
+    }
 }
 
 // ---- stand-alone LUT builder --------------------------------------------
@@ -457,12 +501,13 @@ template <int G, int P>
 hipError_t launch_gp(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
     constexpr int WPE = decode_waves_per_simd(G);
+    const dim3 grid(a.S, a.Hkv, a.B), block(NW * 64);
     if (a.app_page)
-        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, true>), dim3(a.S, a.Hkv, a.B), dim3(NW * 64), 0, s,
-                           a);
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 1>), grid, block, 0, s, a);
+    else if (a.logit_buf)
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 2>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, false>), dim3(a.S, a.Hkv, a.B), dim3(NW * 64), 0, s,
-                           a);
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 0>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -485,6 +530,18 @@ hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
 
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Q * a.Hq), dim3(core::kReduceThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_utility(const DecodeLaunch &a, hipStream_t s) {
+    const dim3 grid((a.maxp + kUtilPages - 1) / kUtilPages, a.B * a.Hkv), block(256);
+    switch (a.Hq / a.Hkv) {
+        case 1: hipLaunchKernelGGL(decode_utility_kernel<1>, grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(decode_utility_kernel<2>, grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL(decode_utility_kernel<4>, grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL(decode_utility_kernel<8>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -89,6 +89,7 @@ struct CoreArgs {
     const uint16_t *value_pool;
     float *pm, *pl, *pacc;
     int32_t Hq, Hkv, maxp, chunk_pages, S;
+    float *logit_buf;   // EMIT: [page * P + slot][G] base-2 logits of every kept token
 };
 
 template <int G, int NW>
@@ -161,7 +162,7 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //   kStaged = false:
 //     Codes fetch(page, meta, slot, valid)     issue the token's code loads
 //   void logits(smem, codes, meta, valid, lg[G]) lane = token, base-2 scaled
-template <int G, int P, int NW, class Pol>
+template <int G, int P, int NW, bool EMIT, class Pol>
 __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typename Pol::Smem &ps,
                                         CoreSmem<G, NW> &cs, float *red, int chunk, int h, int b) {
     constexpr int TPG = 64 / P;     // pages per group
@@ -262,6 +263,18 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 #pragma unroll
         for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
         pol.logits(ps, codes, meta, valid, lg);
+        if constexpr (EMIT) {   // keep the token's logits for the utility pass
+            if (valid) {
+                // a 32-bit element offset formed here: a 64-bit per-lane base
+                // hoisted out of the loop costs registers the loop needs
+                const uint32_t off = ((uint32_t)cs.pages[gbase + pg] * P + slot) * G;
+                float *dst = a.logit_buf + off;
+                // streaming (non-temporal) stores: read back once by the
+                // utility pass, they should not displace cached lines
+#pragma unroll
+                for (int g = 0; g < G; ++g) __builtin_nontemporal_store(lg[g], dst + g);
+            }
+        }
 
         // 3. values -> MFMA A operands, issued after the logit arithmetic so
         //    they are not held in registers through it (other wavefronts'

@@ -93,7 +93,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void dense_partials_kernel(DenseLaunc
     c.maxp = a.maxp;
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
-    core::split_k<G, P, NW>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
+    c.logit_buf = nullptr;
+    core::split_k<G, P, NW, false>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }
 

@@ -200,6 +200,28 @@ ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache
                                const float *keys, const uint16_t *values, void *ws, size_t ws_bytes,
                                void *stream);
 
+/* Workspace bytes for ada_decode_utility on sequences 0..B-1 (grows with
+ * the cache's page_capacity: 4 * P * Hq/Hkv bytes per page). */
+ada_status_t ada_decode_utility_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
+                                          size_t *bytes);
+
+/* ADA decode that also emits each kept token's utility for RDR (abstract:
+ * retention chosen by estimated future utility; the estimator is not
+ * defined there, and this is the attention the token receives in this
+ * step): for every kept token of sequences 0..B-1,
+ *     util[page * P + slot] = sum over the KV head's query heads hq of
+ *                             exp(logit_t(hq) - lse(hq)),
+ * the token's softmax weights in this decode summed over its query heads
+ * (the values over one KV row sum to Hq / Hkv).  Other entries of util are
+ * not written.
+ *   util  device fp32 [page_capacity][P]
+ *   out, lse, q, scale as for ada_decode (lse may be NULL)
+ * Runs the split-K pass (which also stores the kept tokens' logits, 4 bytes
+ * per token and query head), the reduction, and the utility pass. */
+ada_status_t ada_decode_utility(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                                float scale, float *out, float *lse, float *util, void *ws, size_t ws_bytes,
+                                void *stream);
+
 /* Workspace bytes for ada_decode_append on sequences 0..B-1. */
 ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
                                          size_t *bytes);
