@@ -348,6 +348,59 @@ static void *encode_worker(void *arg)
     return NULL;
 }
 
+/* Layout pass of a pack: for each (b, h), tier ascending, the items of
+ * that tier in ascending position are written into consecutive new pages
+ * (item idx carries its radius r16[idx], codes th/sc[idx][64] and value row
+ * values[idx][128]). */
+static void pack_layout(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride, const int8_t *tiers,
+                        const uint16_t *r16, const uint8_t *th_codes, const uint8_t *sc_codes,
+                        const uint16_t *values, int32_t max_pages_per_head, int32_t *page_table,
+                        int32_t *num_pages, int32_t *open_page, uint8_t *page_meta, uint8_t *arena,
+                        uint16_t *value_pool, int64_t *alloc)
+{
+    for (int b = 0; b < B; b++) {
+        for (int h = 0; h < Hkv; h++) {
+            int64_t row = (int64_t)b * Hkv + h;
+            int32_t np_row = 0;
+            for (int tau = 0; tau < 3; tau++) {
+                open_page[row * 3 + tau] = -1;
+                int64_t page = -1;
+                int slot = P;
+                uint8_t *block = NULL;
+                uint32_t off16 = 0;
+                for (int t = 0; t < ctx_len[b]; t++) {
+                    int64_t idx = row * ctx_stride + t;
+                    if (tiers[idx] != tau) continue;
+                    if (slot == P) {          /* start a new page */
+                        page = alloc[0]++;
+                        off16 = (uint32_t)alloc[1];
+                        int64_t bb = orc_block_bytes(tau, P);
+                        alloc[1] += bb / 16;
+                        block = arena + (int64_t)off16 * 16;
+                        memset(block, 0, (size_t)bb);
+                        for (int i = 0; i < P * ORC_D; i++) value_pool[page * P * ORC_D + i] = 0;
+                        page_table[row * max_pages_per_head + np_row] = (int32_t)page;
+                        np_row++;
+                        slot = 0;
+                    }
+                    uint16_t th[ORC_NP], sc[ORC_NP];
+                    for (int j = 0; j < ORC_NP; j++) {
+                        th[j] = th_codes[idx * ORC_NP + j];
+                        sc[j] = sc_codes[idx * ORC_NP + j];
+                    }
+                    write_token_codes(block, tau, P, slot, r16[idx], th, sc);
+                    for (int d = 0; d < ORC_D; d++)
+                        value_pool[value_index(page, P, slot, d)] = values[idx * ORC_D + d];
+                    slot++;
+                    meta_write(page_meta, page, tau, slot, off16);
+                }
+                if (page >= 0 && slot < P) open_page[row * 3 + tau] = (int32_t)page;
+            }
+            num_pages[row] = np_row;
+        }
+    }
+}
+
 int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
              const int8_t *tiers, const float *keys, const uint16_t *values,
              int32_t max_pages_per_head, int64_t page_capacity, int64_t arena_capacity16,
@@ -408,49 +461,9 @@ int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
     free(thr);
     pthread_mutex_destroy(&E.mu);
     int status = E.worst;
-
-    /* layout pass */
-    for (int b = 0; b < B && status == ORC_OK; b++) {
-        for (int h = 0; h < Hkv; h++) {
-            int64_t row = (int64_t)b * Hkv + h;
-            int32_t np_row = 0;
-            for (int tau = 0; tau < 3; tau++) {
-                open_page[row * 3 + tau] = -1;
-                int64_t page = -1;
-                int slot = P;
-                uint8_t *block = NULL;
-                uint32_t off16 = 0;
-                for (int t = 0; t < ctx_len[b]; t++) {
-                    int64_t idx = row * ctx_stride + t;
-                    if (tiers[idx] != tau) continue;
-                    if (slot == P) {          /* start a new page */
-                        page = alloc[0]++;
-                        off16 = (uint32_t)alloc[1];
-                        int64_t bb = orc_block_bytes(tau, P);
-                        alloc[1] += bb / 16;
-                        block = arena + (int64_t)off16 * 16;
-                        memset(block, 0, (size_t)bb);
-                        for (int i = 0; i < P * ORC_D; i++) value_pool[page * P * ORC_D + i] = 0;
-                        page_table[row * max_pages_per_head + np_row] = (int32_t)page;
-                        np_row++;
-                        slot = 0;
-                    }
-                    uint16_t th[ORC_NP], sc[ORC_NP];
-                    for (int j = 0; j < ORC_NP; j++) {
-                        th[j] = E.th[idx * ORC_NP + j];
-                        sc[j] = E.sc[idx * ORC_NP + j];
-                    }
-                    write_token_codes(block, tau, P, slot, E.r16[idx], th, sc);
-                    for (int d = 0; d < ORC_D; d++)
-                        value_pool[value_index(page, P, slot, d)] = values[idx * ORC_D + d];
-                    slot++;
-                    meta_write(page_meta, page, tau, slot, off16);
-                }
-                if (page >= 0 && slot < P) open_page[row * 3 + tau] = (int32_t)page;
-            }
-            num_pages[row] = np_row;
-        }
-    }
+    if (status == ORC_OK)
+        pack_layout(P, Hkv, B, ctx_len, ctx_stride, tiers, E.r16, E.th, E.sc, values, max_pages_per_head,
+                    page_table, num_pages, open_page, page_meta, arena, value_pool, alloc);
     free(tiers_used); free(E.r16); free(E.th); free(E.sc);
     return status;
 }
@@ -608,9 +621,11 @@ int orc_rdr_steps(uint32_t tier_mask, int *n_steps, int *step_tier, int64_t *dR,
     return ORC_OK;
 }
 
+/* cap_level (optional, int8 [B][Hkv][ctx_stride]): an item may take only its
+ * first cap_level steps (0 = it must be dropped); NULL = no cap. */
 int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
                    const float *utility, const int64_t *budget, uint32_t tier_mask,
-                   int8_t *tier_out)
+                   const int8_t *cap_level, int8_t *tier_out)
 {
     int n_steps, step_tier[3];
     int64_t dR[3];
@@ -632,8 +647,10 @@ int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
         int64_t q = 0;
         for (int h = 0; h < Hkv; h++)
             for (int64_t t = 0; t < ctx; t++) {
-                double w = (double)utility[((int64_t)b * Hkv + h) * ctx_stride + t];
-                for (int k = 0; k < n_steps; k++) {
+                int64_t idx = ((int64_t)b * Hkv + h) * ctx_stride + t;
+                double w = (double)utility[idx];
+                int nk = cap_level && cap_level[idx] < n_steps ? cap_level[idx] : n_steps;
+                for (int k = 0; k < nk; k++) {
                     steps[q].p = w * c[k];
                     steps[q].t = (int32_t)t;
                     steps[q].h = h;
@@ -641,6 +658,7 @@ int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
                     q++;
                 }
             }
+        ns = q;
         qsort(steps, (size_t)ns, sizeof(orc_step_t), step_cmp);
         for (int h = 0; h < Hkv; h++)
             for (int64_t t = 0; t < ctx_stride; t++)
@@ -661,6 +679,135 @@ int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
         free(steps);
     }
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Transcoding a token's codes to a tier of no more bits (tb and sb both not
+ * larger), in code space:
+ *   angle:     the grids are nested (grid point c of tb bits is grid point
+ *              c * 2^(tb_old - tb) of tb_old bits), so the new code is the
+ *              nearest new grid point, c_old / 2^d rounded half up, mod 2^tb
+ *              (d = tb_old - tb): the tie rule of the encoder;
+ *   magnitude: the nearest of the new levels c / L to c_old / L_old, i.e.
+ *              round(c_old * L / L_old); for these tiers no exact tie exists;
+ *   radius and value unchanged.
+ * This is re-encoding the dequantised key, decided exactly. */
+void orc_transcode(int tier_old, int tier_new, const uint16_t *th_old, const uint16_t *s_old,
+                   uint16_t *th_new, uint16_t *s_new)
+{
+    int d = TIER_TB[tier_old] - TIER_TB[tier_new];
+    int N = 1 << TIER_TB[tier_new];
+    int64_t L_old = (1 << TIER_SB[tier_old]) - 1, L = (1 << TIER_SB[tier_new]) - 1;
+    for (int j = 0; j < ORC_NP; j++) {
+        int c = d > 0 ? (th_old[j] + (1 << (d - 1))) >> d : th_old[j];
+        th_new[j] = (uint16_t)(c % N);
+        /* floor((2 c L + L_old) / (2 L_old)) = round half up of c L / L_old */
+        s_new[j] = (uint16_t)((2 * (int64_t)s_old[j] * L + L_old) / (2 * L_old));
+    }
+}
+
+/* Re-pack (RDR over the cache's own tokens, downgrade only).  The items of
+ * sequence b are the kept tokens of its rows in the source cache: item
+ * (h, t) is slot t % P of page-list entry t / P of row (b, h), so t orders
+ * the row's tokens as its pages list them (t plays the part of the position
+ * in the RDR order).  Each item's utility is util[page * P + slot]; it may
+ * take only the steps up to its current tier (the codes hold no more), so
+ * RDR assigns drop or a tier no larger than the current one under the
+ * budget.  The kept items are transcoded (orc_transcode) and packed into the
+ * destination cache exactly as orc_pack lays out a tier map over positions
+ * 0 .. max_pages_per_head(src) * P - 1.
+ * tier_v (optional, int8 [B][Hkv][max_pages_src * P]) receives the tier map.
+ * Status: RDR's (EINVAL for a bad utility or budget), then ENOSPC if the
+ * destination is too small (nothing written to it). */
+int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_table,
+               const int32_t *src_num_pages, const uint8_t *src_page_meta, const uint8_t *src_arena,
+               const uint16_t *src_value_pool, const float *util, const int64_t *budget, uint32_t tier_mask,
+               int32_t dst_maxp, int64_t dst_page_capacity, int64_t dst_arena_capacity16,
+               int32_t *page_table, int32_t *num_pages, int32_t *open_page, uint8_t *page_meta,
+               uint8_t *arena, uint16_t *value_pool, int64_t *alloc, int8_t *tier_v_out)
+{
+    if (P != 16 && P != 32) return ORC_EINVAL;
+    if (tier_mask == 0) tier_mask = 7;
+    int n_steps, step_tier[3];
+    int64_t dR[3];
+    double c[3];
+    int st = orc_rdr_steps(tier_mask, &n_steps, step_tier, dR, c);
+    if (st) return st;
+    int64_t S = (int64_t)src_maxp * P;
+    int64_t n = (int64_t)B * Hkv * S;
+    float *uv = calloc((size_t)(n > 0 ? n : 1), sizeof(float));
+    int8_t *cap = calloc((size_t)(n > 0 ? n : 1), 1);
+    int8_t *cur = malloc((size_t)(n > 0 ? n : 1));
+    int8_t *tier_v = malloc((size_t)(n > 0 ? n : 1));
+    int32_t *ctx = malloc(sizeof(int32_t) * (B > 0 ? B : 1));
+    memset(cur, -1, (size_t)(n > 0 ? n : 1));
+    for (int b = 0; b < B; b++) {
+        ctx[b] = (int32_t)S;
+        for (int h = 0; h < Hkv; h++) {
+            int64_t row = (int64_t)b * Hkv + h;
+            for (int i = 0; i < src_num_pages[row]; i++) {
+                int64_t page = src_page_table[row * src_maxp + i];
+                int tier, count; uint32_t off16;
+                meta_read(src_page_meta, page, &tier, &count, &off16);
+                int64_t rate = 2 + 8 * (TIER_TB[tier] + TIER_SB[tier]) + 256;
+                int lv = 0;   /* steps up to the current tier */
+                while (lv < n_steps && 2 + 8 * (TIER_TB[step_tier[lv]] + TIER_SB[step_tier[lv]]) + 256 <= rate) lv++;
+                for (int slot = 0; slot < count; slot++) {
+                    int64_t idx = row * S + (int64_t)i * P + slot;
+                    uv[idx] = util[page * P + slot];
+                    cap[idx] = (int8_t)lv;
+                    cur[idx] = (int8_t)tier;
+                }
+            }
+        }
+    }
+    st = orc_rdr_assign(Hkv, B, ctx, S, uv, budget, tier_mask, cap, tier_v);
+    if (st == ORC_OK) {
+        /* destination capacity (all-or-nothing) */
+        int64_t need_pages = 0, need16 = 0;
+        for (int64_t row = 0; row < (int64_t)B * Hkv && st == ORC_OK; row++) {
+            int64_t cnt[3] = {0, 0, 0}, rp = 0;
+            for (int64_t t = 0; t < S; t++)
+                if (tier_v[row * S + t] >= 0) cnt[tier_v[row * S + t]]++;
+            for (int tau = 0; tau < 3; tau++) {
+                int64_t pg = (cnt[tau] + P - 1) / P;
+                rp += pg;
+                need_pages += pg;
+                need16 += pg * (orc_block_bytes(tau, P) / 16);
+            }
+            if (rp > dst_maxp) st = ORC_ENOSPC;
+        }
+        if (alloc[0] + need_pages > dst_page_capacity || alloc[1] + need16 > dst_arena_capacity16) st = ORC_ENOSPC;
+    }
+    if (st == ORC_OK) {
+        uint16_t *r16 = calloc((size_t)(n > 0 ? n : 1), sizeof(uint16_t));
+        uint8_t *th = calloc((size_t)(n > 0 ? n : 1) * ORC_NP, 1);
+        uint8_t *sc = calloc((size_t)(n > 0 ? n : 1) * ORC_NP, 1);
+        uint16_t *vals = calloc((size_t)(n > 0 ? n : 1) * ORC_D, sizeof(uint16_t));
+        for (int64_t row = 0; row < (int64_t)B * Hkv; row++)
+            for (int64_t t = 0; t < S; t++) {
+                int64_t idx = row * S + t;
+                if (tier_v[idx] < 0) continue;
+                int64_t page = src_page_table[row * src_maxp + t / P];
+                int slot = (int)(t % P), tier, count; uint32_t off16;
+                meta_read(src_page_meta, page, &tier, &count, &off16);
+                uint16_t th_o[ORC_NP], s_o[ORC_NP], th_n[ORC_NP], s_n[ORC_NP];
+                read_token_codes(src_arena + (int64_t)off16 * 16, tier, P, slot, &r16[idx], th_o, s_o);
+                orc_transcode(tier, tier_v[idx], th_o, s_o, th_n, s_n);
+                for (int j = 0; j < ORC_NP; j++) {
+                    th[idx * ORC_NP + j] = (uint8_t)th_n[j];
+                    sc[idx * ORC_NP + j] = (uint8_t)s_n[j];
+                }
+                for (int dd = 0; dd < ORC_D; dd++)
+                    vals[idx * ORC_D + dd] = src_value_pool[value_index(page, P, slot, dd)];
+            }
+        pack_layout(P, Hkv, B, ctx, S, tier_v, r16, th, sc, vals, dst_maxp, page_table, num_pages, open_page,
+                    page_meta, arena, value_pool, alloc);
+        free(r16); free(th); free(sc); free(vals);
+    }
+    if (tier_v_out) memcpy(tier_v_out, tier_v, (size_t)n);
+    free(uv); free(cap); free(cur); free(tier_v); free(ctx);
+    return st;
 }
 
 /* ------------------------------------------------------------------------ */

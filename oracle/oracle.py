@@ -65,7 +65,10 @@ def _declare(L):
     L.orc_append.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i64, i64, ctypes.c_int,
                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.orc_rdr_steps.argtypes = [u32, vp, vp, vp, vp]
-    L.orc_rdr_assign.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, u32, vp]
+    L.orc_rdr_assign.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, u32, vp, vp]
+    L.orc_transcode.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    L.orc_repack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp, vp, u32,
+                             i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.orc_lut.argtypes = [vp, ctypes.c_int, vp]
     L.orc_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
                              vp, vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int]
@@ -186,15 +189,43 @@ def rdr_steps(tier_mask):
     return st, st_tier[:n.value], dR[:n.value], c[:n.value]
 
 
-def rdr_assign(ctx_len, utility, budget, tier_mask=0b111):
-    """utility fp32 [B][Hkv][stride] -> (status, tiers int8 same shape)."""
+def rdr_assign(ctx_len, utility, budget, tier_mask=0b111, cap_level=None):
+    """utility fp32 [B][Hkv][stride] -> (status, tiers int8 same shape).
+    cap_level (optional int8, same shape): steps an item may take."""
     ctx_len = np.ascontiguousarray(ctx_len, dtype=np.int32)
     utility = np.ascontiguousarray(utility, dtype=np.float32)
     budget = np.ascontiguousarray(budget, dtype=np.int64)
     B, Hkv, stride = utility.shape
     out = np.full(utility.shape, -1, np.int8)
-    st = lib().orc_rdr_assign(Hkv, B, _p(ctx_len), stride, _p(utility), _p(budget), tier_mask, _p(out))
+    cap = None if cap_level is None else np.ascontiguousarray(cap_level, dtype=np.int8)
+    st = lib().orc_rdr_assign(Hkv, B, _p(ctx_len), stride, _p(utility), _p(budget), tier_mask,
+                              None if cap is None else _p(cap), _p(out))
     return st, out
+
+
+def transcode(tier_old, tier_new, theta, s):
+    """codes [..., 64] of tier_old -> codes of tier_new (code-space rounding)."""
+    theta = np.ascontiguousarray(theta, dtype=np.uint16).reshape(-1, NP_PAIRS)
+    s = np.ascontiguousarray(s, dtype=np.uint16).reshape(-1, NP_PAIRS)
+    th_n, s_n = np.zeros_like(theta), np.zeros_like(s)
+    for i in range(theta.shape[0]):
+        lib().orc_transcode(tier_old, tier_new, _p(theta[i]), _p(s[i]), _p(th_n[i:i + 1]), _p(s_n[i:i + 1]))
+    return th_n, s_n
+
+
+def repack(src, B, util, budget, dst, tier_mask=0):
+    """RDR re-pack of sequences 0..B-1 of `src` into the empty cache `dst`
+    from per-slot utilities util fp32 [page_capacity][P]; returns
+    (status, tier map int8 [B][Hkv][src.max_pages_per_head * P])."""
+    util = np.ascontiguousarray(util, dtype=np.float32)
+    budget = np.ascontiguousarray(budget, dtype=np.int64)
+    tv = np.full((B, src.Hkv, src.max_pages_per_head * src.P), -1, np.int8)
+    st = lib().orc_repack(src.P, src.Hkv, B, src.max_pages_per_head, _p(src.page_table), _p(src.num_pages),
+                          _p(src.page_meta), _p(src.arena), _p(src.value_pool), _p(util), _p(budget), tier_mask,
+                          dst.max_pages_per_head, dst.page_capacity, dst.arena_capacity16, _p(dst.page_table),
+                          _p(dst.num_pages), _p(dst.open_page), _p(dst.page_meta), _p(dst.arena),
+                          _p(dst.value_pool), _p(dst.alloc), _p(tv))
+    return st, tv
 
 
 def lut(q, tb):
