@@ -78,6 +78,8 @@ def _declare(L):
         "ada_decode_multi": (st, [cfgp, cachep, vp, i32, i32, f32, vp, vp, vp, sz, vp]),
         "ada_decode_utility_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_decode_utility": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "ada_repack_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
+        "ada_repack": (st, [cfgp, cachep, i32, vp, vp, cachep, vp, sz, vp]),
         "ada_decode_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_decode_append": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ada_append_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
@@ -102,7 +104,8 @@ def _declare(L):
 ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_build_lut",
                "ada_decode_workspace", "ada_decode", "ada_decode_partials", "ada_decode_reduce",
                "ada_decode_multi_workspace", "ada_decode_multi", "ada_decode_append_workspace",
-               "ada_decode_append", "ada_decode_utility_workspace", "ada_decode_utility",
+               "ada_decode_append", "ada_decode_utility_workspace", "ada_decode_utility", "ada_repack_workspace",
+               "ada_repack",
                "ada_append_workspace", "ada_encode_append", "ada_rdr_workspace", "ada_rdr_assign",
                "ada_pack_workspace", "ada_pack", "ada_read_status", "ada_dense_workspace",
                "ada_dense_decode", "ada_probe_copy", "ada_probe_read", "ada_host_f64_to_f16")
@@ -289,6 +292,21 @@ def decode_utility(cache, q, scale, util=None, out=None, lse=None, ws=None):
                                     _ptr(out), _ptr(lse), _ptr(util), _ptr(ws), ws.numel(), _stream()),
            "ada_decode_utility")
     return out, lse, util
+
+
+def repack(src, B, util, budget, dst, ws=None):
+    """RDR re-pack of sequences 0..B-1 of `src` into `dst` from per-slot
+    utilities util (device fp32 [page_capacity][P]) under budget (host
+    sequence of B byte counts).  Device errors land in dst.status."""
+    util = _dev(util, torch.float32, "util")
+    bud = (ctypes.c_int64 * B)(*[int(x) for x in budget])
+    if ws is None:
+        n = ctypes.c_size_t(0)
+        _check(lib().ada_repack_workspace(ctypes.byref(src.cfg), ctypes.byref(src.desc), B, ctypes.byref(n)),
+               "ada_repack_workspace")
+        ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=util.device)
+    _check(lib().ada_repack(ctypes.byref(src.cfg), ctypes.byref(src.desc), B, _ptr(util), bud,
+                            ctypes.byref(dst.desc), _ptr(ws), ws.numel(), _stream()), "ada_repack")
 
 
 def decode_append_workspace(cache, B):

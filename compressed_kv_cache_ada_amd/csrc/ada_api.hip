@@ -545,6 +545,7 @@ ada_status_t ada_rdr_assign(const ada_config_t *cfg, int32_t B, const int32_t *c
     a.above = w.above;
     a.all_fit = w.all_fit;
     a.tie_sel = w.tie_sel;
+    a.cap = nullptr;
     return hip_status(launch_rdr(a, s));
 }
 
@@ -602,6 +603,145 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.new_pages = nullptr;
     a.n_new = w.range;
     a.n_tiles = w.n_tiles;
+    a.src_page_table = nullptr;
+    a.src_page_meta = nullptr;
+    a.src_arena = nullptr;
+    a.src_value_pool = nullptr;
+    a.src_maxp = 0;
+    return hip_status(launch_pack(a, s));
+}
+
+// Re-pack workspace: the virtual item arrays (utility, step cap, tier map)
+// over B * Hkv rows of S = max_pages_per_head(src) * P positions, then the
+// RDR and pack workspaces for that stride.
+struct RepackWs {
+    float *util_v;
+    int8_t *cap_v, *tier_v;
+    void *rdr, *pack;
+    size_t bytes;
+};
+
+static RepackWs repack_layout(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, void *ws) {
+    RepackWs r;
+    const int64_t S = (int64_t)src->max_pages_per_head * cfg->page_size;
+    const size_t n = (size_t)B * cfg->num_kv_heads * S;
+    Carver c(ws);
+    r.util_v = c.take<float>(n);
+    r.cap_v = c.take<int8_t>(n);
+    r.tier_v = c.take<int8_t>(n);
+    const size_t rb = rdr_layout(cfg, B, S, nullptr).bytes;
+    r.rdr = c.take<char>(rb);
+    const size_t pb = pack_layout(cfg, B, S, nullptr).bytes;
+    r.pack = c.take<char>(pb);
+    r.bytes = c.off;
+    return r;
+}
+
+ada_status_t ada_repack_workspace(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, size_t *bytes) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if (!src || !bytes || B < 0 || src->max_pages_per_head <= 0) return ADA_EINVAL;
+    *bytes = repack_layout(cfg, src, B, nullptr).bytes;
+    return ADA_OK;
+}
+
+ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, const float *util,
+                        const int64_t *budget, const ada_cache_t *dst, void *ws, size_t ws_bytes, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(src)) || (st = check_cache(dst))) return st;
+    if (B < 0 || B > src->num_seqs || B > dst->num_seqs) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!util || !budget || !ws) return ADA_EINVAL;
+    const int P = cfg->page_size;
+    const int64_t S = (int64_t)src->max_pages_per_head * P;
+    if ((int64_t)cfg->num_kv_heads * S > INT32_MAX) return ADA_EUNSUPPORTED;
+    for (int b = 0; b < B; ++b)
+        if (budget[b] < 0) return ADA_EINVAL;
+    RepackWs r = repack_layout(cfg, src, B, ws);
+    if (ws_bytes < r.bytes) return ADA_EINVAL;
+    RdrLaunch ra;
+    const uint32_t mask = cfg->rdr_tier_mask ? cfg->rdr_tier_mask : 7u;
+    if ((st = rdr_steps(mask, &ra.n_steps, ra.step_tier, ra.dR, ra.c))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    // 1. the source's kept tokens as RDR items with their step caps
+    RepackItemsLaunch it;
+    it.B = B;
+    it.Hkv = cfg->num_kv_heads;
+    it.P = P;
+    it.src_maxp = src->max_pages_per_head;
+    it.page_table = src->page_table;
+    it.num_pages = src->num_pages;
+    it.page_meta = src->page_meta;
+    it.util = util;
+    auto rate = [](int t) { return 2 + 8 * (tier_tb(t) + tier_sb(t)) + 256; };
+    for (int t = 0; t < 3; ++t) {   // steps up to the tier's rate: the tier or cheaper
+        int lv = 0;
+        while (lv < ra.n_steps && rate(ra.step_tier[lv]) <= rate(t)) ++lv;
+        it.level_of_tier[t] = (int8_t)lv;
+    }
+    it.util_v = r.util_v;
+    it.cap_v = r.cap_v;
+    RdrWs rw = rdr_layout(cfg, B, S, r.rdr);
+    it.ctx_v = rw.ctx;
+    hipError_t e = launch_repack_items(it, s);
+    if (e != hipSuccess) return ADA_EHIP;
+    // 2. capped RDR over them (status word: the destination's)
+    if (hipMemcpyAsync(rw.budget, budget, sizeof(int64_t) * B, hipMemcpyHostToDevice, s) != hipSuccess)
+        return ADA_EHIP;
+    ra.B = B;
+    ra.Hkv = cfg->num_kv_heads;
+    ra.stride = S;
+    ra.ctx_len_dev = rw.ctx;
+    ra.budget_dev = rw.budget;
+    ra.utility = r.util_v;
+    ra.tier_out = r.tier_v;
+    ra.status = dst->status;
+    ra.hist = rw.hist;
+    ra.prefix = rw.prefix;
+    ra.above = rw.above;
+    ra.all_fit = rw.all_fit;
+    ra.tie_sel = rw.tie_sel;
+    ra.cap = r.cap_v;
+    if ((e = launch_rdr(ra, s)) != hipSuccess) return ADA_EHIP;
+    // 3. pack the tier map into dst, transcoding each kept token from src
+    PackWs w = pack_layout(cfg, B, S, r.pack);
+    if (hipMemcpyAsync(w.ctx, rw.ctx, sizeof(int32_t) * B, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return ADA_EHIP;
+    PackLaunch a;
+    a.B = B;
+    a.Hkv = cfg->num_kv_heads;
+    a.P = P;
+    a.maxp = dst->max_pages_per_head;
+    a.stride = S;
+    a.page_capacity = dst->page_capacity;
+    a.arena_capacity16 = dst->arena_capacity16;
+    a.ctx_len_dev = w.ctx;
+    a.tier = r.tier_v;
+    a.keys = nullptr;
+    a.values = nullptr;
+    a.page_table = dst->page_table;
+    a.num_pages = dst->num_pages;
+    a.open_page = dst->open_page;
+    a.page_meta = dst->page_meta;
+    a.arena = dst->code_arena;
+    a.value_pool = dst->value_pool;
+    a.alloc = dst->alloc;
+    a.status = dst->status;
+    a.tile_counts = w.tile_counts;
+    a.row_counts = w.row_counts;
+    a.row_base = w.row_base;
+    a.row_unit = w.row_unit;
+    a.dest_page = w.dest_page;
+    a.dest_slot = w.dest_slot;
+    a.new_pages = nullptr;
+    a.n_new = w.range;
+    a.n_tiles = w.n_tiles;
+    a.src_page_table = src->page_table;
+    a.src_page_meta = src->page_meta;
+    a.src_arena = src->code_arena;
+    a.src_value_pool = src->value_pool;
+    a.src_maxp = src->max_pages_per_head;
     return hip_status(launch_pack(a, s));
 }
 

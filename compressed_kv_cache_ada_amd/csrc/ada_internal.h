@@ -139,6 +139,14 @@ struct PackLaunch {
     int32_t *new_pages;     // [page upper bound] list of allocated pages
     int32_t *n_new;         // [1]
     int32_t n_tiles;
+    // re-pack (src_page_table != nullptr): item (row, t) is slot t % P of
+    // page-list entry t / P of the source cache's row; its codes are
+    // transcoded instead of encoding keys (keys / values unused)
+    const int32_t *src_page_table;
+    const ada_page_meta_t *src_page_meta;
+    const uint8_t *src_arena;
+    const uint16_t *src_value_pool;
+    int32_t src_maxp;
 };
 hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
 
@@ -190,8 +198,24 @@ struct RdrLaunch {
     long long *above;           // [B]
     int32_t *all_fit;           // [B]
     uint8_t *tie_sel;           // [B][Hkv][stride]
+    const int8_t *cap;          // optional [B][Hkv][stride]: steps an item may take
 };
 hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s);
+
+// Re-pack items of a source cache: for B * Hkv rows of S = src_maxp * P
+// virtual positions, util_v / cap_v get the kept tokens' utilities and step
+// caps (0 for empty positions), ctx_v[b] = S.
+struct RepackItemsLaunch {
+    int32_t B, Hkv, P, src_maxp;
+    const int32_t *page_table, *num_pages;
+    const ada_page_meta_t *page_meta;
+    const float *util;          // [page_capacity][P]
+    int8_t level_of_tier[3];    // steps up to and including each tier
+    float *util_v;
+    int8_t *cap_v;
+    int32_t *ctx_v;
+};
+hipError_t launch_repack_items(const RepackItemsLaunch &a, hipStream_t s);
 
 hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
                              int32_t *status, hipStream_t s);

@@ -30,6 +30,27 @@ __global__ __launch_bounds__(256) void encode_write_kernel(EncodeLaunch a) {
     }
 }
 
+// ------------------------------------------------- transcode (re-pack)
+// One wavefront per item of the tier map; item (row, t) comes from slot
+// t % P of page-list entry t / P of the source cache's row.
+__global__ __launch_bounds__(256) void transcode_write_kernel(PackLaunch a) {
+    __shared__ uint32_t words[4][2][16];
+    const int wv = threadIdx.x >> 6;
+    if (read_status(a.status) != 0) return;
+    const int64_t n = (int64_t)a.B * a.Hkv * a.stride;
+    for (int64_t item = (int64_t)blockIdx.x * 4 + wv; item < n; item += (int64_t)gridDim.x * 4) {
+        const int page = a.dest_page[item];
+        if (page < 0) continue;
+        const int64_t row = item / a.stride, t = item % a.stride;
+        const int src_page = a.src_page_table[row * a.src_maxp + t / a.P];
+        const ada_page_meta_t sm = a.src_page_meta[src_page];
+        const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + page);
+        enc::transcode_write_one(a.src_arena + (size_t)sm.code_off16 * 16, sm.tier,
+                                 a.src_value_pool + (size_t)src_page * a.P * kD, (int)(t % a.P), page,
+                                 a.dest_slot[item], meta, a.arena, a.value_pool, a.P, words[wv]);
+    }
+}
+
 // ------------------------------------------------------- zero new pages
 // pages: explicit list, or (when list == nullptr) the range [first, first+n)
 __global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, const int32_t *first_and_n,
@@ -69,10 +90,11 @@ __global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
         if (tv < -1 || tv > 2) set_status(a.status, ADA_EINVAL);
         else if (tv >= 0) atomicAdd(&cnt[tv], 1);
     }
-    // finiteness of kept keys: one wavefront per position
+    // finiteness of kept keys: one wavefront per position (no keys when
+    // re-packing from a cache)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     bool bad = false;
-    for (int i = wv; i < kTile; i += 4) {
+    for (int i = wv; a.keys && i < kTile; i += 4) {
         const int t = t0 + i;
         if (t >= ctx) break;
         if (a.tier[rbase + t] < 0) continue;
@@ -632,6 +654,11 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_pages, 1, 4096)), dim3(256), 0, s,
                        (const int32_t *)nullptr, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
                        a.arena, a.value_pool, a.P, (const int32_t *)a.status);
+    if (a.src_page_table) {
+        hipLaunchKernelGGL(transcode_write_kernel, dim3(grid_for((int64_t)rows * a.stride, 4, 16384)), dim3(256), 0,
+                           s, a);
+        return hipGetLastError();
+    }
     EncodeLaunch e;
     e.keys = a.keys;
     e.values = a.values;

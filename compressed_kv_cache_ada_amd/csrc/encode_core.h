@@ -210,6 +210,55 @@ __device__ inline int read_status(const int32_t *status) {
     return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// --------------------------------------------------- write one token
+// Called by all 64 lanes of one wavefront, lane j holding pair j's angle code
+// tc and magnitude code sc and the token's value dims 2j, 2j+1 (fp16 bits):
+// packs the two bit strings (LSB first) in the wavefront's LDS scratch and
+// writes radius r16, codes and value into slot `slot` of page `page` (tier
+// and code block from meta).
+__device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint32_t v2, int page, int slot,
+                                   uint2 meta, uint8_t *arena, uint16_t *value_pool, int P,
+                                   uint32_t (&words)[2][16]) {
+    const int lane = threadIdx.x & 63;
+    const int tier = meta.x & 0xFF;
+    const int tb = tier_tb(tier), sb = tier_sb(tier);
+    uint32_t *wt = words[0], *ws = words[1];
+    if (lane < 16) {
+        wt[lane] = 0u;
+        ws[lane] = 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    {
+        const int bit = lane * tb;
+        atomicOr(&wt[bit >> 5], tc << (bit & 31));
+        const int bs = lane * sb, sh = bs & 31;
+        atomicOr(&ws[bs >> 5], sc << sh);
+        if (sh + sb > 32) atomicOr(&ws[(bs >> 5) + 1], sc >> (32 - sh));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint8_t *blk = arena + (size_t)meta.y * 16;
+    const int nwt = 2 * tb, nws = 2 * sb;             // 32-bit words per component
+    if (lane < nwt) {
+        const int w = lane;
+        uint8_t *dst = blk + 2 * P + (w >> 2) * 16 * P + slot * 16 + (w & 3) * 4;
+        *reinterpret_cast<uint32_t *>(dst) = wt[w];
+    } else if (lane >= 32 && lane < 32 + nws) {
+        const int w = lane - 32;
+        const int nfull = (8 * sb) / 16;
+        uint8_t *sbase = blk + 2 * P + 8 * tb * P;
+        uint8_t *dst = (w >> 2) < nfull ? sbase + (w >> 2) * 16 * P + slot * 16 + (w & 3) * 4
+                                        : sbase + nfull * 16 * P + slot * 8 + (w - 4 * nfull) * 4;
+        *reinterpret_cast<uint32_t *>(dst) = ws[w];
+    }
+    if (lane == 0) *reinterpret_cast<uint16_t *>(blk + 2 * slot) = r16;
+    uint16_t *vp = value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);
+    vp[(2 * lane) * 8] = (uint16_t)(v2 & 0xFFFF);
+    vp[(2 * lane + 1) * 8] = (uint16_t)(v2 >> 16);
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ------------------------------------------------ encode + write one key
 // Called by all 64 lanes of one wavefront: encodes key[128] (fp32) at the
 // page's tier and writes its radius, codes and value (fp16 bits) into slot
@@ -243,42 +292,49 @@ __device__ inline void encode_write_one(const float *key, const uint16_t *value,
         if (lane == 0) set_status(status, ADA_EINTERNAL);
         return;
     }
-    uint32_t *wt = words[0], *ws = words[1];
-    if (lane < 16) {
-        wt[lane] = 0u;
-        ws[lane] = 0u;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    {
-        const int bit = lane * tb;
-        atomicOr(&wt[bit >> 5], tc << (bit & 31));
-        const int bs = lane * sb, sh = bs & 31;
-        atomicOr(&ws[bs >> 5], sc << sh);
-        if (sh + sb > 32) atomicOr(&ws[(bs >> 5) + 1], sc >> (32 - sh));
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    uint8_t *blk = arena + (size_t)meta.y * 16;
-    const int nwt = 2 * tb, nws = 2 * sb;             // 32-bit words per component
-    if (lane < nwt) {
-        const int w = lane;
-        uint8_t *dst = blk + 2 * P + (w >> 2) * 16 * P + slot * 16 + (w & 3) * 4;
-        *reinterpret_cast<uint32_t *>(dst) = wt[w];
-    } else if (lane >= 32 && lane < 32 + nws) {
-        const int w = lane - 32;
-        const int nfull = (8 * sb) / 16;
-        uint8_t *sbase = blk + 2 * P + 8 * tb * P;
-        uint8_t *dst = (w >> 2) < nfull ? sbase + (w >> 2) * 16 * P + slot * 16 + (w & 3) * 4
-                                        : sbase + nfull * 16 * P + slot * 8 + (w - 4 * nfull) * 4;
-        *reinterpret_cast<uint32_t *>(dst) = ws[w];
-    }
-    if (lane == 0) *reinterpret_cast<uint16_t *>(blk + 2 * slot) = f64_to_f16_rne_sat(r);
-    const uint32_t vv = *reinterpret_cast<const uint32_t *>(value + 2 * lane);
-    uint16_t *vp = value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);
-    vp[(2 * lane) * 8] = (uint16_t)(vv & 0xFFFF);
-    vp[(2 * lane + 1) * 8] = (uint16_t)(vv >> 16);
-    __builtin_amdgcn_wave_barrier();
+    const uint32_t v2 = *reinterpret_cast<const uint32_t *>(value + 2 * lane);
+    write_token(tc, sc, f64_to_f16_rne_sat(r), v2, page, slot, meta, arena, value_pool, P, words);
+}
+
+// ------------------------------------------- transcode + write one token
+// Byte `byte` of a component bit string of token `slot` (Bc bytes per
+// token, 16-byte units token-minor, then one 8-byte unit if Bc % 16 == 8).
+__device__ inline const uint8_t *comp_byte(const uint8_t *comp, int Bc, int P, int slot, int byte) {
+    const int u = byte >> 4, within = byte & 15, nfull = Bc >> 4;
+    return u < nfull ? comp + u * 16 * P + slot * 16 + within : comp + nfull * 16 * P + slot * 8 + within;
+}
+
+// code j (b bits) of token `slot` in a component
+__device__ inline uint32_t read_code(const uint8_t *comp, int b, int P, int slot, int j) {
+    const int bit = j * b, Bc = 8 * b;
+    const int b0 = bit >> 3, b1 = (bit + b - 1) >> 3;
+    uint32_t v = *comp_byte(comp, Bc, P, slot, b0);
+    if (b1 != b0) v |= (uint32_t)*comp_byte(comp, Bc, P, slot, b1) << 8;
+    return (v >> (bit & 7)) & ((1u << b) - 1u);
+}
+
+// Called by all 64 lanes of one wavefront: reads token src_slot of the page
+// with code block src_blk (tier src_tier) and value page src_vpage, moves its
+// codes to the destination page's tier in code space (angle: nearest point
+// of the nested coarser grid, half up; magnitude: nearest level, no ties for
+// these tiers; radius and value unchanged) and writes it into (page, slot).
+__device__ inline void transcode_write_one(const uint8_t *src_blk, int src_tier, const uint16_t *src_vpage,
+                                           int src_slot, int page, int slot, uint2 meta, uint8_t *arena,
+                                           uint16_t *value_pool, int P, uint32_t (&words)[2][16]) {
+    const int lane = threadIdx.x & 63;
+    const int tb_o = tier_tb(src_tier), sb_o = tier_sb(src_tier);
+    const int tier = meta.x & 0xFF, tb = tier_tb(tier), sb = tier_sb(tier);
+    const uint8_t *ct = src_blk + 2 * P;
+    const uint32_t th_o = read_code(ct, tb_o, P, src_slot, lane);
+    const uint32_t s_o = read_code(ct + 8 * tb_o * P, sb_o, P, src_slot, lane);
+    const int d = tb_o - tb;
+    const uint32_t tc = (d > 0 ? (th_o + (1u << (d - 1))) >> d : th_o) & ((1u << tb) - 1u);
+    const uint32_t L_o = (1u << sb_o) - 1u, L = (1u << sb) - 1u;
+    const uint32_t sc = (2u * s_o * L + L_o) / (2u * L_o);
+    const uint16_t r16 = *reinterpret_cast<const uint16_t *>(src_blk + 2 * src_slot);
+    const uint16_t *vs = src_vpage + (src_slot >> 3) * 1024 + (src_slot & 7);
+    const uint32_t v2 = (uint32_t)vs[(2 * lane) * 8] | ((uint32_t)vs[(2 * lane + 1) * 8] << 16);
+    write_token(tc, sc, r16, v2, page, slot, meta, arena, value_pool, P, words);
 }
 
 }  // namespace enc

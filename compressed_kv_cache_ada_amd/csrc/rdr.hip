@@ -23,6 +23,11 @@ namespace {
 
 __device__ inline void set_status(int32_t *status, int code) { atomicCAS(status, 0, code); }
 
+// steps item i may take
+__device__ inline int item_steps(const RdrLaunch &a, int64_t i) {
+    return a.cap ? min(a.n_steps, (int)a.cap[i]) : a.n_steps;
+}
+
 __device__ inline unsigned long long prio_key(float w, double c) {
     double p = (double)w * c;
     unsigned long long u;
@@ -65,8 +70,10 @@ __global__ __launch_bounds__(256) void rdr_hist_kernel(RdrLaunch a, int pass) {
         for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
             const int h_ = (int)(it / ctx);
             const int t = (int)(it % ctx);
-            const float w = a.utility[((int64_t)b * a.Hkv + h_) * a.stride + t];
-            for (int k = 0; k < a.n_steps; ++k) {
+            const int64_t i = ((int64_t)b * a.Hkv + h_) * a.stride + t;
+            const float w = a.utility[i];
+            const int nk = item_steps(a, i);
+            for (int k = 0; k < nk; ++k) {
                 const unsigned long long key = prio_key(w, a.c[k]);
                 if (pass > 0 && (key >> shift_hi) != pre) continue;
                 atomicAdd(&h[(key >> shift_dig) & 255ull], (unsigned long long)a.dR[k]);
@@ -126,11 +133,14 @@ __global__ __launch_bounds__(1024) void rdr_tie_kernel(RdrLaunch a) {
         int h_ = 0, t = 0;
         long long bytes = 0;
         float w = 0.f;
+        int nk = 0;
         if (ii < items) {
             t = ctx - 1 - (int)(ii / a.Hkv);
             h_ = (int)(ii % a.Hkv);
-            w = a.utility[((int64_t)b * a.Hkv + h_) * a.stride + t];
-            for (int k = 0; k < a.n_steps; ++k)
+            const int64_t i = ((int64_t)b * a.Hkv + h_) * a.stride + t;
+            w = a.utility[i];
+            nk = item_steps(a, i);
+            for (int k = 0; k < nk; ++k)
                 if (prio_key(w, a.c[k]) == T) bytes += a.dR[k];
         }
         sc[threadIdx.x] = bytes;
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(1024) void rdr_tie_kernel(RdrLaunch a) {
         if (ii < items && bytes > 0) {
             long long cum = carry + sc[threadIdx.x] - bytes;
             int taken = 0;
-            for (int k = 0; k < a.n_steps; ++k) {
+            for (int k = 0; k < nk; ++k) {
                 if (prio_key(w, a.c[k]) != T) continue;
                 if (cum + a.dR[k] > rem) break;
                 cum += a.dR[k];
@@ -171,13 +181,14 @@ __global__ __launch_bounds__(256) void rdr_final_kernel(RdrLaunch a) {
         int8_t out = -1;
         if (t < a.ctx_len_dev[b]) {
             int n;
+            const int nk = item_steps(a, i);
             if (a.all_fit[b]) {
-                n = a.n_steps;
+                n = nk;
             } else {
                 const unsigned long long T = a.prefix[b];
                 const float w = a.utility[i];
                 n = a.tie_sel[i];
-                for (int k = 0; k < a.n_steps; ++k) n += prio_key(w, a.c[k]) > T ? 1 : 0;
+                for (int k = 0; k < nk; ++k) n += prio_key(w, a.c[k]) > T ? 1 : 0;
             }
             out = n ? (int8_t)a.step_tier[n - 1] : (int8_t)-1;
         }
@@ -185,7 +196,37 @@ __global__ __launch_bounds__(256) void rdr_final_kernel(RdrLaunch a) {
     }
 }
 
+__global__ __launch_bounds__(256) void repack_items_kernel(RepackItemsLaunch a) {
+    const int64_t S = (int64_t)a.src_maxp * a.P;
+    const int64_t n = (int64_t)a.B * a.Hkv * S;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t row = i / S, t = i % S;
+        const int ip = (int)(t / a.P), slot = (int)(t % a.P);
+        float u = 0.f;
+        int8_t cap = 0;
+        if (ip < a.num_pages[row]) {
+            const int page = a.page_table[row * a.src_maxp + ip];
+            const ada_page_meta_t m = a.page_meta[page];
+            if (slot < m.count) {
+                u = a.util[(size_t)page * a.P + slot];
+                cap = a.level_of_tier[m.tier];
+            }
+        }
+        a.util_v[i] = u;
+        a.cap_v[i] = cap;
+        if (i < a.B) a.ctx_v[i] = (int32_t)S;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_repack_items(const RepackItemsLaunch &a, hipStream_t s) {
+    const int64_t n = (int64_t)a.B * a.Hkv * a.src_maxp * a.P;
+    int g = (int)((n + 255) / 256);
+    g = g < 1 ? 1 : (g > 8192 ? 8192 : g);
+    hipLaunchKernelGGL(repack_items_kernel, dim3(g), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s) {
     const int64_t total = (int64_t)a.B * a.Hkv * a.stride;

@@ -222,6 +222,32 @@ ada_status_t ada_decode_utility(const ada_config_t *cfg, const ada_cache_t *cach
                                 float scale, float *out, float *lse, float *util, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Workspace bytes for ada_repack of sequences 0..B-1 of `src`. */
+ada_status_t ada_repack_workspace(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, size_t *bytes);
+
+/* RDR re-pack (abstract: retention and precision chosen per token and head
+ * under a fixed budget from estimated future utility; here the budget may
+ * shrink over time and the cache is re-fitted to it).  The items of sequence
+ * b are the kept tokens of its rows in `src`: item (h, t) is slot t % P of
+ * page-list entry t / P of row (b, h), t playing the part of the position in
+ * the RDR order; its utility is util[page * P + slot] (for instance from
+ * ada_decode_utility).  Each item may keep its tier, move to a tier of lower
+ * rate among the enabled ones, or be dropped (the codes hold nothing finer),
+ * under budget[b] bytes with the rate / distortion model of ada_rdr_assign.
+ * Kept items are transcoded in code space -- angle codes to the nearest
+ * point of the nested coarser grid (half up), magnitude codes to the nearest
+ * level (no ties occur between these tiers), radius and value unchanged --
+ * and packed into `dst` exactly as ada_pack lays out a tier map over
+ * positions 0 .. src.max_pages_per_head * P - 1 (tier id ascending, then
+ * position).  dst must be a different cache; its rows of sequences < B are
+ * rewritten and its pages are allocated from its alloc counters.
+ *   util    device fp32 [src.page_capacity][P], finite and >= 0 where kept
+ *   budget  host int64 [B] bytes
+ * Device errors land in dst's status word (bad utility -> ADA_EINVAL,
+ * capacity -> ADA_ENOSPC; then dst is not written). */
+ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, const float *util,
+                        const int64_t *budget, const ada_cache_t *dst, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes for ada_decode_append on sequences 0..B-1. */
 ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
                                          size_t *bytes);
