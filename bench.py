@@ -43,6 +43,8 @@ def parse():
                     help="time decode with per-token utility emission against plain decode")
     ap.add_argument("--append", action="store_true",
                     help="time the fused append + decode step against append then decode")
+    ap.add_argument("--repack", type=float, default=0.0, metavar="FRAC",
+                    help="time ada_repack of the packed cache to FRAC of its current bytes instead")
     ap.add_argument("--queries", type=int, default=1,
                     help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,6 +124,9 @@ def main():
     cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages)
     if args.append:
         append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
+        return
+    if args.repack > 0:
+        repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
         return
     if args.utility:
         utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
@@ -333,6 +338,65 @@ def utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
                    "kept_token_heads": kept_total},
         "utility_ms_per_step": timing["utility"], "decode_ms_per_step": timing["decode"],
         "overhead": timing["utility"] / timing["decode"] - 1.0,
+    }), flush=True)
+
+
+def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
+    """ada_repack of the packed cache into a second cache under budgets of
+    args.repack times each sequence's current bytes, with the utilities of one
+    ada_decode_utility step.  Each timed step resets the destination
+    (ada_cache_init) and re-packs; the destination is checked against the
+    budget afterwards."""
+    P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
+    src = ada.Cache(cfg, B, max_row, n_pages, units)
+    dst = ada.Cache(cfg, B, max_row, n_pages, units)
+    ada.cache_init(src)
+    ada.pack(src, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), torch.from_numpy(w["keys"]).cuda(),
+             torch.from_numpy(w["values"].view(np.int16)).cuda())
+    assert ada.read_status(src.status) == ada.OK
+    torch.cuda.empty_cache()
+    util = torch.zeros((n_pages, P), dtype=torch.float32, device="cuda")
+    ada.decode_utility(src, torch.from_numpy(w["q"]).cuda(), w["scale"], util)
+    rate = {t: ada.block_bytes(t, P) // P + 256 for t in (0, 1, 2)}
+    cur = [sum(rate[t] * int((w["tiers"][b] == t).sum()) for t in (0, 1, 2)) for b in range(B)]
+    budget = [int(args.repack * c) for c in cur]
+    ws = ada.repack_workspace(src, B)
+
+    def step():
+        ada.cache_init(dst)
+        ada.repack(src, B, util, budget, dst, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert ada.read_status(dst.status) == ada.OK
+    h = dst.host()
+    kept_total = sum(kept.values())
+    kept_after = {t: 0 for t in (0, 1, 2)}
+    used = [0] * B
+    for row in range(B * Hkv):
+        for page in h["page_table"][row, : h["num_pages"][row]]:
+            t, c = int(h["page_meta"][page, 0]), int(h["page_meta"][page, 1])
+            kept_after[t] += c
+            used[row // Hkv] += rate[t] * c
+    assert all(u <= bd for u, bd in zip(used, budget))
+    print(json.dumps({
+        "metric": "ADA RDR re-pack of a packed cache",
+        "value": kept_total / (ms * 1e-3), "unit": "source KV token-heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "page_size": P,
+                   "budget_fraction": args.repack, "kept_token_heads_before": kept_total,
+                   "kept_by_tier_before": {str(t): kept[t] for t in (0, 1, 2)},
+                   "kept_by_tier_after": {str(t): kept_after[t] for t in (0, 1, 2)}},
+        "bytes_before": sum(cur), "bytes_after": sum(used), "budget_bytes": sum(budget),
     }), flush=True)
 
 

@@ -294,17 +294,20 @@ def decode_utility(cache, q, scale, util=None, out=None, lse=None, ws=None):
     return out, lse, util
 
 
+def repack_workspace(src, B):
+    n = ctypes.c_size_t(0)
+    _check(lib().ada_repack_workspace(ctypes.byref(src.cfg), ctypes.byref(src.desc), B, ctypes.byref(n)),
+           "ada_repack_workspace")
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=src.page_table.device)
+
+
 def repack(src, B, util, budget, dst, ws=None):
     """RDR re-pack of sequences 0..B-1 of `src` into `dst` from per-slot
     utilities util (device fp32 [page_capacity][P]) under budget (host
     sequence of B byte counts).  Device errors land in dst.status."""
     util = _dev(util, torch.float32, "util")
     bud = (ctypes.c_int64 * B)(*[int(x) for x in budget])
-    if ws is None:
-        n = ctypes.c_size_t(0)
-        _check(lib().ada_repack_workspace(ctypes.byref(src.cfg), ctypes.byref(src.desc), B, ctypes.byref(n)),
-               "ada_repack_workspace")
-        ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=util.device)
+    ws = repack_workspace(src, B) if ws is None else ws
     _check(lib().ada_repack(ctypes.byref(src.cfg), ctypes.byref(src.desc), B, _ptr(util), bud,
                             ctypes.byref(dst.desc), _ptr(ws), ws.numel(), _stream()), "ada_repack")
 
