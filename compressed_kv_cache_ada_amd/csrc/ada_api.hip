@@ -221,6 +221,7 @@ struct RdrWs {
     int32_t *all_fit, *ctx;
     int64_t *budget;
     uint8_t *tie_sel;
+    long long *tie_tile;
     size_t bytes;
 };
 
@@ -234,6 +235,7 @@ RdrWs rdr_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
     w.ctx = c.take<int32_t>(B);
     w.budget = c.take<int64_t>(B);
     w.tie_sel = c.take<uint8_t>((size_t)B * cfg->num_kv_heads * stride);
+    w.tie_tile = c.take<long long>((size_t)B * rdr_tie_tiles((int64_t)cfg->num_kv_heads * stride));
     w.bytes = c.off;
     return w;
 }
@@ -545,6 +547,7 @@ ada_status_t ada_rdr_assign(const ada_config_t *cfg, int32_t B, const int32_t *c
     a.above = w.above;
     a.all_fit = w.all_fit;
     a.tie_sel = w.tie_sel;
+    a.tie_tile = w.tie_tile;
     a.cap = nullptr;
     return hip_status(launch_rdr(a, s));
 }
@@ -608,6 +611,8 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_arena = nullptr;
     a.src_value_pool = nullptr;
     a.src_maxp = 0;
+    a.src_of_slot = nullptr;
+    a.src_of_slot_pages = 0;
     return hip_status(launch_pack(a, s));
 }
 
@@ -618,6 +623,8 @@ struct RepackWs {
     float *util_v;
     int8_t *cap_v, *tier_v;
     void *rdr, *pack;
+    int4 *src_of_slot;
+    int64_t src_of_slot_pages;
     size_t bytes;
 };
 
@@ -633,6 +640,8 @@ static RepackWs repack_layout(const ada_config_t *cfg, const ada_cache_t *src, i
     r.rdr = c.take<char>(rb);
     const size_t pb = pack_layout(cfg, B, S, nullptr).bytes;
     r.pack = c.take<char>(pb);
+    r.src_of_slot_pages = (int64_t)B * cfg->num_kv_heads * repack_pages_per_row(src->max_pages_per_head);
+    r.src_of_slot = c.take<int4>((size_t)r.src_of_slot_pages * cfg->page_size);
     r.bytes = c.off;
     return r;
 }
@@ -702,6 +711,7 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     ra.above = rw.above;
     ra.all_fit = rw.all_fit;
     ra.tie_sel = rw.tie_sel;
+    ra.tie_tile = rw.tie_tile;
     ra.cap = r.cap_v;
     if ((e = launch_rdr(ra, s)) != hipSuccess) return ADA_EHIP;
     // 3. pack the tier map into dst, transcoding each kept token from src
@@ -742,6 +752,8 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_arena = src->code_arena;
     a.src_value_pool = src->value_pool;
     a.src_maxp = src->max_pages_per_head;
+    a.src_of_slot = r.src_of_slot;
+    a.src_of_slot_pages = r.src_of_slot_pages;
     return hip_status(launch_pack(a, s));
 }
 

@@ -147,8 +147,13 @@ struct PackLaunch {
     const uint8_t *src_arena;
     const uint16_t *src_value_pool;
     int32_t src_maxp;
+    int4 *src_of_slot;              // [src_of_slot_pages][P] source {page, slot, tier, code_off16} per new slot
+    int64_t src_of_slot_pages;
 };
 hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
+// pages a re-pack may open per row: sum over three tiers of ceil(n_tau / P)
+// with sum n_tau <= src_maxp * P
+inline int64_t repack_pages_per_row(int32_t src_maxp) { return (int64_t)src_maxp + 2; }
 
 struct AppendLaunch {
     int32_t n, Hkv, P, num_seqs, maxp;
@@ -198,8 +203,11 @@ struct RdrLaunch {
     long long *above;           // [B]
     int32_t *all_fit;           // [B]
     uint8_t *tie_sel;           // [B][Hkv][stride]
+    long long *tie_tile;        // [B][rdr_tie_tiles(Hkv * stride)]: tie bytes per tile, then their prefix
     const int8_t *cap;          // optional [B][Hkv][stride]: steps an item may take
 };
+constexpr int kRdrTieTile = 1024;   // items per tile of the tie scan
+__host__ __device__ inline int64_t rdr_tie_tiles(int64_t items) { return (items + kRdrTieTile - 1) / kRdrTieTile; }
 hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s);
 
 // Re-pack items of a source cache: for B * Hkv rows of S = src_maxp * P

@@ -31,23 +31,170 @@ __global__ __launch_bounds__(256) void encode_write_kernel(EncodeLaunch a) {
 }
 
 // ------------------------------------------------- transcode (re-pack)
-// One wavefront per item of the tier map; item (row, t) comes from slot
-// t % P of page-list entry t / P of the source cache's row.
-__global__ __launch_bounds__(256) void transcode_write_kernel(PackLaunch a) {
-    __shared__ uint32_t words[4][2][16];
-    const int wv = threadIdx.x >> 6;
+// Code-space transcoding of one token from tier TO to tier TN (TN = TO or
+// coarser): angle codes to the nearest point of the nested coarser grid
+// (exactly half-way rounds up, then wraps), magnitude codes to the nearest
+// level c * LN / LO (never a tie for these tiers); radius unchanged.  One
+// thread per token; every bit position is static once the loops unroll.
+template <int B>
+__device__ inline uint32_t get_code(const uint32_t *w, int j) {
+    const int bit = j * B, wi = bit >> 5, sh = bit & 31;
+    uint32_t v = w[wi] >> sh;
+    if (sh + B > 32) v |= w[wi + 1] << (32 - sh);
+    return v & ((1u << B) - 1u);
+}
+
+template <int B>
+__device__ inline void put_code(uint32_t *w, int j, uint32_t c) {
+    const int bit = j * B, wi = bit >> 5, sh = bit & 31;
+    w[wi] |= c << sh;
+    if (sh + B > 32) w[wi + 1] |= c >> (32 - sh);
+}
+
+// component of B bits per code: 8*B bytes per token as 16-byte units
+// (token-minor), then one 8-byte unit when 8*B % 16 == 8
+template <int B>
+__device__ inline void load_comp(const uint8_t *comp, int P, int slot, uint32_t (&w)[2 * B]) {
+#pragma unroll
+    for (int u = 0; u < B / 2; ++u) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(comp + (size_t)u * 16 * P + slot * 16);
+        w[4 * u] = v.x;
+        w[4 * u + 1] = v.y;
+        w[4 * u + 2] = v.z;
+        w[4 * u + 3] = v.w;
+    }
+    if constexpr (B % 2) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(comp + (size_t)(B / 2) * 16 * P + slot * 8);
+        w[2 * B - 2] = v.x;
+        w[2 * B - 1] = v.y;
+    }
+}
+
+template <int B>
+__device__ inline void store_comp(uint8_t *comp, int P, int slot, const uint32_t (&w)[2 * B]) {
+#pragma unroll
+    for (int u = 0; u < B / 2; ++u)
+        *reinterpret_cast<uint4 *>(comp + (size_t)u * 16 * P + slot * 16) =
+            make_uint4(w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]);
+    if constexpr (B % 2)
+        *reinterpret_cast<uint2 *>(comp + (size_t)(B / 2) * 16 * P + slot * 8) = make_uint2(w[2 * B - 2], w[2 * B - 1]);
+}
+
+template <int TO, int TN>
+__device__ inline void transcode_token(const uint8_t *sblk, int sslot, uint8_t *dblk, int slot, int P) {
+    constexpr int BO = tier_tb(TO), SO = tier_sb(TO), BN = tier_tb(TN), SN = tier_sb(TN);
+    {
+        uint32_t wi[2 * BO], wo[2 * BN];
+        load_comp<BO>(sblk + 2 * P, P, sslot, wi);
+#pragma unroll
+        for (int k = 0; k < 2 * BN; ++k) wo[k] = 0u;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+            uint32_t c = get_code<BO>(wi, j);
+            if constexpr (BO > BN) c = ((c + (1u << (BO - BN - 1))) >> (BO - BN)) & ((1u << BN) - 1u);
+            put_code<BN>(wo, j, c);
+        }
+        store_comp<BN>(dblk + 2 * P, P, slot, wo);
+    }
+    {
+        constexpr uint32_t LO = (1u << SO) - 1u, LN = (1u << SN) - 1u;
+        uint32_t wi[2 * SO], wo[2 * SN];
+        load_comp<SO>(sblk + 2 * P + 8 * BO * P, P, sslot, wi);
+#pragma unroll
+        for (int k = 0; k < 2 * SN; ++k) wo[k] = 0u;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+            uint32_t c = get_code<SO>(wi, j);
+            if constexpr (SO != SN) c = (2u * c * LN + LO) / (2u * LO);
+            put_code<SN>(wo, j, c);
+        }
+        store_comp<SN>(dblk + 2 * P + 8 * BN * P, P, slot, wo);
+    }
+    reinterpret_cast<uint16_t *>(dblk)[slot] = reinterpret_cast<const uint16_t *>(sblk)[sslot];
+}
+
+template <int TN>
+__device__ inline void zero_token(uint8_t *dblk, int slot, int P) {
+    constexpr int BN = tier_tb(TN), SN = tier_sb(TN);
+    uint32_t zt[2 * BN], zs[2 * SN];
+#pragma unroll
+    for (int k = 0; k < 2 * BN; ++k) zt[k] = 0u;
+#pragma unroll
+    for (int k = 0; k < 2 * SN; ++k) zs[k] = 0u;
+    store_comp<BN>(dblk + 2 * P, P, slot, zt);
+    store_comp<SN>(dblk + 2 * P + 8 * BN * P, P, slot, zs);
+    reinterpret_cast<uint16_t *>(dblk)[slot] = 0;
+}
+
+// One work-group of 128 threads per new destination page (grid-stride);
+// no LDS and no barrier, so many pages are in flight per compute unit.  Every
+// byte of the page's code block and value page is written, slots past the
+// count as zeros.  Threads 0..P-1 transcode one token each.  The value page
+// is assembled one (8-token group, dimension) 16-byte word per thread: the
+// group's eight source entries are the same for the whole work-group, and
+// each source token's value word for that dimension is one 16-byte load (of
+// which the token's 2 bytes are kept, so source value words shared by pages
+// written far apart in time are fetched again).
+__global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
     if (read_status(a.status) != 0) return;
-    const int64_t n = (int64_t)a.B * a.Hkv * a.stride;
-    for (int64_t item = (int64_t)blockIdx.x * 4 + wv; item < n; item += (int64_t)gridDim.x * 4) {
-        const int page = a.dest_page[item];
-        if (page < 0) continue;
-        const int64_t row = item / a.stride, t = item % a.stride;
-        const int src_page = a.src_page_table[row * a.src_maxp + t / a.P];
-        const ada_page_meta_t sm = a.src_page_meta[src_page];
-        const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + page);
-        enc::transcode_write_one(a.src_arena + (size_t)sm.code_off16 * 16, sm.tier,
-                                 a.src_value_pool + (size_t)src_page * a.P * kD, (int)(t % a.P), page,
-                                 a.dest_slot[item], meta, a.arena, a.value_pool, a.P, words[wv]);
+    const int first = a.n_new[0], n = a.n_new[1];
+    const int P = a.P;
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+        if (i >= a.src_of_slot_pages) break;   // bounded by construction
+        const int page = first + i;
+        const ada_page_meta_t m = a.page_meta[page];
+        const int count = m.count, tier = m.tier;
+        const int4 *ent = a.src_of_slot + (int64_t)i * P;   // {page, slot, tier, code_off16}
+        if (threadIdx.x < P) {
+            uint8_t *dblk = a.arena + (size_t)m.code_off16 * 16;
+            const int k = threadIdx.x;
+            const int4 e = k < count ? ent[k] : make_int4(0, 0, 0, 0);
+            const int st = e.z;
+            if (k >= count || st > tier) {   // past the count; or an upgrade, which the caps rule out
+                if (k < count) set_status(a.status, ADA_EINTERNAL);
+                if (tier == 0) zero_token<0>(dblk, k, P);
+                else if (tier == 1) zero_token<1>(dblk, k, P);
+                else zero_token<2>(dblk, k, P);
+            } else {
+                const uint8_t *sblk = a.src_arena + (size_t)(uint32_t)e.w * 16;
+                const int sslot = e.y;
+                if (tier == 0) transcode_token<0, 0>(sblk, sslot, dblk, k, P);
+                else if (tier == 1 && st == 0) transcode_token<0, 1>(sblk, sslot, dblk, k, P);
+                else if (tier == 1) transcode_token<1, 1>(sblk, sslot, dblk, k, P);
+                else if (st == 0) transcode_token<0, 2>(sblk, sslot, dblk, k, P);
+                else if (st == 1) transcode_token<1, 2>(sblk, sslot, dblk, k, P);
+                else transcode_token<2, 2>(sblk, sslot, dblk, k, P);
+            }
+        }
+        uint16_t *dv = a.value_pool + (size_t)page * P * kD;
+        const int dim = threadIdx.x;
+        for (int g = 0; g < P / 8; ++g) {
+            int2 e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int sl = g * 8 + k;
+                e[k] = sl < count ? make_int2(ent[sl].x, ent[sl].y) : make_int2(-1, 0);
+            }
+            uint4 seg[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                seg[k] = make_uint4(0u, 0u, 0u, 0u);
+                if (e[k].x >= 0)
+                    seg[k] = *reinterpret_cast<const uint4 *>(a.src_value_pool + (size_t)e[k].x * P * kD +
+                                                              (e[k].y >> 3) * 1024 + dim * 8);
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int idx = e[k].y & 7;
+                const int q = idx >> 1;
+                const uint32_t word = q == 0 ? seg[k].x : q == 1 ? seg[k].y : q == 2 ? seg[k].z : seg[k].w;
+                const uint32_t h = (word >> ((idx & 1) * 16)) & 0xFFFFu;
+                if (k & 1) w[k >> 1] |= h << 16;
+                else w[k >> 1] = h;
+            }
+            *reinterpret_cast<uint4 *>(dv + g * 1024 + dim * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -265,6 +412,14 @@ __global__ __launch_bounds__(256) void pack_dest_kernel(PackLaunch a) {
         }
         a.dest_page[rbase + t] = dp;
         a.dest_slot[rbase + t] = ds;
+        if (a.src_of_slot && dp >= 0) {   // re-pack: where the destination slot's token comes from
+            const int64_t j = (int64_t)(dp - a.n_new[0]) * a.P + ds;
+            if (j < a.src_of_slot_pages * a.P) {
+                const int sp = a.src_page_table[(int64_t)row * a.src_maxp + t / a.P];
+                const ada_page_meta_t sm = a.src_page_meta[sp];
+                a.src_of_slot[j] = make_int4(sp, t % a.P, sm.tier, (int)sm.code_off16);
+            }
+        }
     }
 }
 
@@ -651,14 +806,13 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(pack_pages_kernel, dim3(rows), dim3(256), 0, s, a);
     hipLaunchKernelGGL(pack_dest_kernel, dim3(a.n_tiles, rows), dim3(256), 0, s, a);
     const int64_t max_pages = (int64_t)rows * a.maxp;
+    if (a.src_page_table) {   // re-pack: the transcoder writes every byte of each new page
+        hipLaunchKernelGGL(transcode_pages_kernel, dim3(grid_for(a.src_of_slot_pages, 1, 65536)), dim3(128), 0, s, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_pages, 1, 4096)), dim3(256), 0, s,
                        (const int32_t *)nullptr, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
                        a.arena, a.value_pool, a.P, (const int32_t *)a.status);
-    if (a.src_page_table) {
-        hipLaunchKernelGGL(transcode_write_kernel, dim3(grid_for((int64_t)rows * a.stride, 4, 16384)), dim3(256), 0,
-                           s, a);
-        return hipGetLastError();
-    }
     EncodeLaunch e;
     e.keys = a.keys;
     e.values = a.values;

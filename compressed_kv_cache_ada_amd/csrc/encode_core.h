@@ -296,47 +296,6 @@ __device__ inline void encode_write_one(const float *key, const uint16_t *value,
     write_token(tc, sc, f64_to_f16_rne_sat(r), v2, page, slot, meta, arena, value_pool, P, words);
 }
 
-// ------------------------------------------- transcode + write one token
-// Byte `byte` of a component bit string of token `slot` (Bc bytes per
-// token, 16-byte units token-minor, then one 8-byte unit if Bc % 16 == 8).
-__device__ inline const uint8_t *comp_byte(const uint8_t *comp, int Bc, int P, int slot, int byte) {
-    const int u = byte >> 4, within = byte & 15, nfull = Bc >> 4;
-    return u < nfull ? comp + u * 16 * P + slot * 16 + within : comp + nfull * 16 * P + slot * 8 + within;
-}
-
-// code j (b bits) of token `slot` in a component
-__device__ inline uint32_t read_code(const uint8_t *comp, int b, int P, int slot, int j) {
-    const int bit = j * b, Bc = 8 * b;
-    const int b0 = bit >> 3, b1 = (bit + b - 1) >> 3;
-    uint32_t v = *comp_byte(comp, Bc, P, slot, b0);
-    if (b1 != b0) v |= (uint32_t)*comp_byte(comp, Bc, P, slot, b1) << 8;
-    return (v >> (bit & 7)) & ((1u << b) - 1u);
-}
-
-// Called by all 64 lanes of one wavefront: reads token src_slot of the page
-// with code block src_blk (tier src_tier) and value page src_vpage, moves its
-// codes to the destination page's tier in code space (angle: nearest point
-// of the nested coarser grid, half up; magnitude: nearest level, no ties for
-// these tiers; radius and value unchanged) and writes it into (page, slot).
-__device__ inline void transcode_write_one(const uint8_t *src_blk, int src_tier, const uint16_t *src_vpage,
-                                           int src_slot, int page, int slot, uint2 meta, uint8_t *arena,
-                                           uint16_t *value_pool, int P, uint32_t (&words)[2][16]) {
-    const int lane = threadIdx.x & 63;
-    const int tb_o = tier_tb(src_tier), sb_o = tier_sb(src_tier);
-    const int tier = meta.x & 0xFF, tb = tier_tb(tier), sb = tier_sb(tier);
-    const uint8_t *ct = src_blk + 2 * P;
-    const uint32_t th_o = read_code(ct, tb_o, P, src_slot, lane);
-    const uint32_t s_o = read_code(ct + 8 * tb_o * P, sb_o, P, src_slot, lane);
-    const int d = tb_o - tb;
-    const uint32_t tc = (d > 0 ? (th_o + (1u << (d - 1))) >> d : th_o) & ((1u << tb) - 1u);
-    const uint32_t L_o = (1u << sb_o) - 1u, L = (1u << sb) - 1u;
-    const uint32_t sc = (2u * s_o * L + L_o) / (2u * L_o);
-    const uint16_t r16 = *reinterpret_cast<const uint16_t *>(src_blk + 2 * src_slot);
-    const uint16_t *vs = src_vpage + (src_slot >> 3) * 1024 + (src_slot & 7);
-    const uint32_t v2 = (uint32_t)vs[(2 * lane) * 8] | ((uint32_t)vs[(2 * lane + 1) * 8] << 16);
-    write_token(tc, sc, r16, v2, page, slot, meta, arena, value_pool, P, words);
-}
-
 }  // namespace enc
 }  // namespace ada
 

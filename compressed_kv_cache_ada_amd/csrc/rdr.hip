@@ -15,7 +15,7 @@
 // high bytes, and pick the bin where the running byte total crosses the
 // budget.  All byte sums are 64-bit integers, so the result does not depend
 // on summation order.  Steps whose p equals the selected key are then taken
-// in (position desc, head asc, step asc) order by a single work-group scan.
+// in (position desc, head asc, step asc) order by a tiled prefix scan.
 #include "ada_internal.h"
 
 namespace ada {
@@ -66,17 +66,38 @@ __global__ __launch_bounds__(256) void rdr_hist_kernel(RdrLaunch a, int pass) {
     const unsigned long long pre = a.prefix[b];
     const int shift_hi = 64 - 8 * pass, shift_dig = 56 - 8 * pass;
     if (!skip) {
+        // Wavefront-uniform loop.  When every taking lane of a step falls
+        // into one bin (usual in the first pass, where the digit is the
+        // exponent's top bits) one LDS atomic adds them all.
+        const int lane = threadIdx.x & 63;
         const int64_t items = (int64_t)a.Hkv * ctx;
-        for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
-            const int h_ = (int)(it / ctx);
-            const int t = (int)(it % ctx);
-            const int64_t i = ((int64_t)b * a.Hkv + h_) * a.stride + t;
-            const float w = a.utility[i];
-            const int nk = item_steps(a, i);
-            for (int k = 0; k < nk; ++k) {
+        const int64_t stride = (int64_t)gridDim.x * 256;
+        for (int64_t base = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); base < items; base += stride) {
+            const int64_t it = base + lane;
+            float w = 0.f;
+            int nk = 0;
+            if (it < items) {
+                const int h_ = (int)(it / ctx);
+                const int t = (int)(it % ctx);
+                const int64_t i = ((int64_t)b * a.Hkv + h_) * a.stride + t;
+                w = a.utility[i];
+                nk = item_steps(a, i);
+            }
+            for (int k = 0; k < a.n_steps; ++k) {
                 const unsigned long long key = prio_key(w, a.c[k]);
-                if (pass > 0 && (key >> shift_hi) != pre) continue;
-                atomicAdd(&h[(key >> shift_dig) & 255ull], (unsigned long long)a.dR[k]);
+                const bool take = k < nk && (pass == 0 || (key >> shift_hi) == pre);
+                const int bin = (int)((key >> shift_dig) & 255ull);
+                const unsigned long long act = __ballot(take);
+                if (act == 0ull) continue;
+                const int leader = __ffsll((long long)act) - 1;
+                const int lb = __shfl(bin, leader);
+                const unsigned long long same = __ballot(take && bin == lb);
+                if (same == act) {
+                    if (lane == leader)
+                        atomicAdd(&h[lb], (unsigned long long)__popcll(same) * (unsigned long long)a.dR[k]);
+                } else if (take) {
+                    atomicAdd(&h[bin], (unsigned long long)a.dR[k]);
+                }
             }
         }
     }
@@ -84,91 +105,157 @@ __global__ __launch_bounds__(256) void rdr_hist_kernel(RdrLaunch a, int pass) {
     if (!skip && h[threadIdx.x]) atomicAdd(&a.hist[b * 256 + threadIdx.x], h[threadIdx.x]);
 }
 
-__global__ void rdr_select_kernel(RdrLaunch a, int pass) {
-    const int b = blockIdx.x;
-    if (threadIdx.x != 0) return;
+// The cut digit: walking bins from the highest, the first whose bytes no
+// longer fit beside those above it.  Bins' suffix sums grow as the digit
+// falls, so the chosen bin is the highest digit whose inclusive suffix
+// overshoots.  Also clears the histogram for the next pass.
+__global__ __launch_bounds__(256) void rdr_select_kernel(RdrLaunch a, int pass) {
+    __shared__ long long suf[256];
+    __shared__ int n_over;
+    const int b = blockIdx.x, v = threadIdx.x;
     unsigned long long *hb = a.hist + b * 256;
-    if (a.all_fit[b] == 0 && *a.status == 0) {
-        const long long budget = a.budget_dev[b];
-        long long above = a.above[b];
-        int chosen = -1;
-        for (int v = 255; v >= 0; --v) {
-            const long long hv = (long long)hb[v];
-            if (above + hv <= budget) {
-                above += hv;
-            } else {
-                chosen = v;
-                break;
-            }
-        }
+    const bool active = a.all_fit[b] == 0 && *a.status == 0;
+    const long long hv = (long long)hb[v];
+    suf[v] = hv;
+    if (v == 0) n_over = 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {   // suf[v] = sum of bins >= v
+        const long long u = v + off < 256 ? suf[v + off] : 0;
+        __syncthreads();
+        suf[v] += u;
+        __syncthreads();
+    }
+    const long long budget = a.budget_dev[b], above = a.above[b];
+    if (above + suf[v] > budget) atomicAdd(&n_over, 1);
+    __syncthreads();
+    const int chosen = n_over - 1;   // bins 0..chosen overshoot
+    if (active && v == 0) {
         if (chosen < 0) {
             a.all_fit[b] = 1;   // every remaining step fits (possible on the first pass only)
         } else {
-            a.above[b] = above;
+            a.above[b] = above + (chosen < 255 ? suf[chosen + 1] : 0);
             a.prefix[b] = (a.prefix[b] << 8) | (unsigned long long)chosen;
         }
     }
-    for (int v = 0; v < 256; ++v) hb[v] = 0ull;
+    hb[v] = 0ull;
 }
 
-// steps whose key equals the selected key, in (position desc, head asc,
-// step asc) order: longest prefix fitting the remaining budget
-__global__ __launch_bounds__(1024) void rdr_tie_kernel(RdrLaunch a) {
-    __shared__ long long sc[1024];
-    __shared__ long long carry;
-    __shared__ int stop;
-    const int b = blockIdx.x;
-    if (a.all_fit[b] != 0 || *a.status != 0) return;
-    const unsigned long long T = a.prefix[b];
-    const long long rem = a.budget_dev[b] - a.above[b];
+// Steps whose key equals the selected key, taken in (position desc, head
+// asc, step asc) order: the longest prefix of that order fitting the budget
+// left after the steps above the key.  Tie order index ii runs over
+// (t = ctx - 1 - ii / Hkv, h = ii % Hkv); tiles of kRdrTieTile indices, four
+// consecutive indices per thread.  Three passes: tie bytes per tile, an
+// exclusive prefix over the tiles of a sequence, then each tile scans its own
+// items from its prefix.
+__device__ inline long long tie_bytes(const RdrLaunch &a, int b, int ctx, int64_t ii, unsigned long long T,
+                                      float *w_out, int *nk_out, int64_t *i_out) {
+    const int t = ctx - 1 - (int)(ii / a.Hkv), h_ = (int)(ii % a.Hkv);
+    const int64_t i = ((int64_t)b * a.Hkv + h_) * a.stride + t;
+    const float w = a.utility[i];
+    const int nk = item_steps(a, i);
+    long long bytes = 0;
+    for (int k = 0; k < nk; ++k)
+        if (prio_key(w, a.c[k]) == T) bytes += a.dR[k];
+    *w_out = w;
+    *nk_out = nk;
+    *i_out = i;
+    return bytes;
+}
+
+__device__ inline bool tie_active(const RdrLaunch &a, int b) { return a.all_fit[b] == 0 && *a.status == 0; }
+
+__global__ __launch_bounds__(256) void rdr_tie_sum_kernel(RdrLaunch a, int64_t tiles_per_seq) {
+    __shared__ long long red[4];
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    if (!tie_active(a, b)) return;
     const int ctx = a.ctx_len_dev[b];
     const int64_t items = (int64_t)a.Hkv * ctx;
-    if (threadIdx.x == 0) {
-        carry = 0;
-        stop = 0;
+    if (tile * kRdrTieTile >= items) return;
+    const unsigned long long T = a.prefix[b];
+    long long sum = 0;
+    for (int k = 0; k < 4; ++k) {
+        const int64_t ii = tile * kRdrTieTile + threadIdx.x * 4 + k;
+        float w;
+        int nk;
+        int64_t i;
+        if (ii < items) sum += tie_bytes(a, b, ctx, ii, T, &w, &nk, &i);
     }
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sum;
     __syncthreads();
-    for (int64_t base = 0; base < items; base += 1024) {
-        const int64_t ii = base + threadIdx.x;
-        int h_ = 0, t = 0;
-        long long bytes = 0;
-        float w = 0.f;
-        int nk = 0;
-        if (ii < items) {
-            t = ctx - 1 - (int)(ii / a.Hkv);
-            h_ = (int)(ii % a.Hkv);
-            const int64_t i = ((int64_t)b * a.Hkv + h_) * a.stride + t;
-            w = a.utility[i];
-            nk = item_steps(a, i);
-            for (int k = 0; k < nk; ++k)
-                if (prio_key(w, a.c[k]) == T) bytes += a.dR[k];
-        }
-        sc[threadIdx.x] = bytes;
+    if (threadIdx.x == 0) a.tie_tile[b * tiles_per_seq + tile] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(1024) void rdr_tie_scan_kernel(RdrLaunch a, int64_t tiles_per_seq) {
+    __shared__ long long sc[1024];
+    __shared__ long long carry;
+    const int b = blockIdx.x;
+    if (!tie_active(a, b)) return;
+    const int64_t tiles = rdr_tie_tiles((int64_t)a.Hkv * a.ctx_len_dev[b]);
+    long long *tt = a.tie_tile + b * tiles_per_seq;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < tiles; base += 1024) {
+        const int64_t j = base + threadIdx.x;
+        const long long v = j < tiles ? tt[j] : 0;
+        sc[threadIdx.x] = v;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {
-            long long v = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+            const long long u = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
             __syncthreads();
-            sc[threadIdx.x] += v;
+            sc[threadIdx.x] += u;
             __syncthreads();
         }
-        if (ii < items && bytes > 0) {
-            long long cum = carry + sc[threadIdx.x] - bytes;
-            int taken = 0;
-            for (int k = 0; k < nk; ++k) {
-                if (prio_key(w, a.c[k]) != T) continue;
-                if (cum + a.dR[k] > rem) break;
-                cum += a.dR[k];
-                ++taken;
-            }
-            a.tie_sel[((int64_t)b * a.Hkv + h_) * a.stride + t] = (uint8_t)taken;
-        }
+        if (j < tiles) tt[j] = carry + sc[threadIdx.x] - v;
         __syncthreads();
-        if (threadIdx.x == 0) {
-            carry += sc[1023];
-            if (carry > rem) stop = 1;
-        }
+        if (threadIdx.x == 0) carry += sc[1023];
         __syncthreads();
-        if (stop) break;
+    }
+}
+
+__global__ __launch_bounds__(256) void rdr_tie_apply_kernel(RdrLaunch a, int64_t tiles_per_seq) {
+    __shared__ long long sc[256];
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    if (!tie_active(a, b)) return;
+    const int ctx = a.ctx_len_dev[b];
+    const int64_t items = (int64_t)a.Hkv * ctx;
+    if (tile * kRdrTieTile >= items) return;
+    const long long rem = a.budget_dev[b] - a.above[b];
+    const long long off = a.tie_tile[b * tiles_per_seq + tile];
+    if (off >= rem) return;   // every step costs at least one byte: nothing of this tile fits
+    const unsigned long long T = a.prefix[b];
+    float w[4];
+    int nk[4];
+    int64_t idx[4];
+    long long bytes[4], mine = 0;
+    for (int k = 0; k < 4; ++k) {
+        const int64_t ii = tile * kRdrTieTile + threadIdx.x * 4 + k;
+        bytes[k] = ii < items ? tie_bytes(a, b, ctx, ii, T, &w[k], &nk[k], &idx[k]) : 0;
+        mine += bytes[k];
+    }
+    sc[threadIdx.x] = mine;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const long long u = threadIdx.x >= o ? sc[threadIdx.x - o] : 0;
+        __syncthreads();
+        sc[threadIdx.x] += u;
+        __syncthreads();
+    }
+    long long cum = off + sc[threadIdx.x] - mine;
+    for (int k = 0; k < 4; ++k) {
+        if (bytes[k] == 0) continue;
+        long long c = cum;
+        int taken = 0;
+        for (int j = 0; j < nk[k]; ++j) {
+            if (prio_key(w[k], a.c[j]) != T) continue;
+            if (c + a.dR[j] > rem) break;
+            c += a.dR[j];
+            ++taken;
+        }
+        a.tie_sel[idx[k]] = (uint8_t)taken;
+        cum += bytes[k];
     }
 }
 
@@ -234,13 +321,19 @@ hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s) {
     g = g < 1 ? 1 : (g > 8192 ? 8192 : g);
     hipLaunchKernelGGL(rdr_validate_kernel, dim3(g), dim3(256), 0, s, a);
     const int64_t per_seq = (int64_t)a.Hkv * a.stride;
-    int gx = (int)((per_seq + 255) / 256);
-    gx = gx < 1 ? 1 : (gx > 2048 ? 2048 : gx);
+    // about eight items per thread, at most ~4096 work-groups in all: every
+    // work-group adds its non-empty bins to the global histogram atomically
+    const int64_t gcap = 4096 / a.B > 1 ? 4096 / a.B : 1;
+    int64_t gx64 = (per_seq + 2047) / 2048;
+    const int gx = (int)(gx64 < 1 ? 1 : (gx64 > gcap ? gcap : gx64));
     for (int pass = 0; pass < 8; ++pass) {
         hipLaunchKernelGGL(rdr_hist_kernel, dim3(gx, a.B), dim3(256), 0, s, a, pass);
-        hipLaunchKernelGGL(rdr_select_kernel, dim3(a.B), dim3(64), 0, s, a, pass);
+        hipLaunchKernelGGL(rdr_select_kernel, dim3(a.B), dim3(256), 0, s, a, pass);
     }
-    hipLaunchKernelGGL(rdr_tie_kernel, dim3(a.B), dim3(1024), 0, s, a);
+    const int64_t tiles = rdr_tie_tiles(per_seq);
+    hipLaunchKernelGGL(rdr_tie_sum_kernel, dim3((unsigned)tiles, a.B), dim3(256), 0, s, a, tiles);
+    hipLaunchKernelGGL(rdr_tie_scan_kernel, dim3(a.B), dim3(1024), 0, s, a, tiles);
+    hipLaunchKernelGGL(rdr_tie_apply_kernel, dim3((unsigned)tiles, a.B), dim3(256), 0, s, a, tiles);
     hipLaunchKernelGGL(rdr_final_kernel, dim3(g), dim3(256), 0, s, a);
     return hipGetLastError();
 }
