@@ -99,7 +99,9 @@ double orc_f16_to_f64(uint16_t h)
 /* ------------------------------------------------------------------------ */
 /* Encoder.  Key k (fp32, exact in fp64) -> radius r16 (fp16 bits), 64 angle
  * codes, 64 magnitude codes, for angle bits tb and magnitude bits sb.
- *   pairs:    (x_j, y_j) = (k[2j], k[2j+1])
+ *   pairs:    (x_j, y_j) = (k[2j], k[2j+1]) in the adjacent layout, or
+ *             (k[j], k[j+64]) in the half-split layout (the rotate-half
+ *             form of rotary position embeddings pairs these components)
  *   energies: e_j = x_j^2 + y_j^2 (each square exact in fp64)
  *   norm^2:   R2 = fixed pairwise tree over e (strides 32,16,...,1)
  *   radius:   r = sqrt(R2) correctly rounded, r16 = fp16(r)
@@ -154,14 +156,19 @@ static int angle_code(double x, double y, int tb, int *undecidable)
     return (int)(((c % N) + N) % N);
 }
 
+/* Components of key (or query) vector forming pair j, for pair layout
+ * 0 (adjacent) or 1 (half-split). */
+static int pair_x(int layout, int j) { return layout ? j : 2 * j; }
+static int pair_y(int layout, int j) { return layout ? j + ORC_NP : 2 * j + 1; }
+
 /* Returns ORC_OK, ORC_EINVAL (non-finite key) or ORC_EUNDECIDABLE. */
 int orc_encode_key(const float *k, int tb, int sb, uint16_t *r16,
-                   uint16_t *theta, uint16_t *s, double *r_out)
+                   uint16_t *theta, uint16_t *s, double *r_out, int layout)
 {
     double x[ORC_NP], y[ORC_NP], e[ORC_NP], t[ORC_NP];
     for (int j = 0; j < ORC_NP; j++) {
-        x[j] = (double)k[2 * j];
-        y[j] = (double)k[2 * j + 1];
+        x[j] = (double)k[pair_x(layout, j)];
+        y[j] = (double)k[pair_y(layout, j)];
         if (!isfinite(x[j]) || !isfinite(y[j])) return ORC_EINVAL;
         double xx = x[j] * x[j];
         double yy = y[j] * y[j];
@@ -315,6 +322,7 @@ typedef struct {
     uint8_t *th, *sc;       /* [n_pos][64] each, codes <= 8 bits */
     int64_t next;
     int worst;
+    int layout;
     pthread_mutex_t mu;
 } encode_job_t;
 
@@ -334,7 +342,8 @@ static void *encode_worker(void *arg)
             int tau = J->tiers[i];
             if (tau < 0) continue;
             uint16_t th[ORC_NP], sc[ORC_NP];
-            int st = orc_encode_key(J->keys + i * ORC_D, TIER_TB[tau], TIER_SB[tau], &J->r16[i], th, sc, NULL);
+            int st = orc_encode_key(J->keys + i * ORC_D, TIER_TB[tau], TIER_SB[tau], &J->r16[i], th, sc, NULL,
+                                    J->layout);
             if (st > worst) worst = st;
             for (int j = 0; j < ORC_NP; j++) {
                 J->th[i * ORC_NP + j] = (uint8_t)th[j];
@@ -406,7 +415,7 @@ int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
              int32_t max_pages_per_head, int64_t page_capacity, int64_t arena_capacity16,
              int32_t *page_table, int32_t *num_pages, int32_t *open_page,
              uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc,
-             int nthreads)
+             int nthreads, int layout)
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
     /* validation pass */
@@ -452,7 +461,7 @@ int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
     E.r16 = malloc(sizeof(uint16_t) * (n_pos > 0 ? n_pos : 1));
     E.th = malloc((size_t)(n_pos > 0 ? n_pos : 1) * ORC_NP);
     E.sc = malloc((size_t)(n_pos > 0 ? n_pos : 1) * ORC_NP);
-    E.next = 0; E.worst = ORC_OK;
+    E.next = 0; E.worst = ORC_OK; E.layout = layout;
     pthread_mutex_init(&E.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     pthread_t *thr = malloc(sizeof(pthread_t) * nthreads);
@@ -482,7 +491,7 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
                const int32_t *seq, const int32_t *head, const uint8_t *tier,
                const float *keys, const uint16_t *values,
                int32_t *page_table, int32_t *num_pages, int32_t *open_page,
-               uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc)
+               uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc, int layout)
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
     for (int i = 0; i < n; i++) {
@@ -553,7 +562,8 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
             meta_read(page_meta, page, &tr, &cnt, &off16);
         }
         uint16_t r16, th[ORC_NP], sc[ORC_NP];
-        if (orc_encode_key(keys + (int64_t)i * ORC_D, TIER_TB[tau], TIER_SB[tau], &r16, th, sc, NULL) != ORC_OK)
+        if (orc_encode_key(keys + (int64_t)i * ORC_D, TIER_TB[tau], TIER_SB[tau], &r16, th, sc, NULL, layout) !=
+            ORC_OK)
             return ORC_EUNDECIDABLE;
         write_token_codes(arena + (int64_t)off16 * 16, tau, P, cnt, r16, th, sc);
         for (int d = 0; d < ORC_D; d++)
@@ -812,15 +822,16 @@ int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_
 
 /* ------------------------------------------------------------------------ */
 /* Angle lookup table of one query head for angle bits tb:
- *   LUT[j][c] = q[2j] cos(th_c) + q[2j+1] sin(th_c),  th_c = -pi + c*2pi/2^tb
+ *   LUT[j][c] = qx_j cos(th_c) + qy_j sin(th_c),  th_c = -pi + c*2pi/2^tb,
+ * with (qx_j, qy_j) the query's pair j in the same layout as the keys
  * (no softmax scale folded in). */
-void orc_lut(const float *q, int tb, double *lut)
+void orc_lut(const float *q, int tb, double *lut, int layout)
 {
     int N = 1 << tb;
     for (int j = 0; j < ORC_NP; j++)
         for (int c = 0; c < N; c++) {
             double th = -M_PI + (double)c * (2.0 * M_PI / (double)N);
-            lut[j * N + c] = (double)q[2 * j] * cos(th) + (double)q[2 * j + 1] * sin(th);
+            lut[j * N + c] = (double)q[pair_x(layout, j)] * cos(th) + (double)q[pair_y(layout, j)] * sin(th);
         }
 }
 
@@ -841,6 +852,7 @@ typedef struct {
     double scale;
     double *out, *lse;
     int64_t next_row, n_rows;
+    int layout;
     pthread_mutex_t mu;
 } decode_job_t;
 
@@ -851,9 +863,9 @@ static void decode_row(decode_job_t *J, int64_t row_q, double *lut8, double *lut
     int G = J->Hq / J->Hkv;
     int h = hq / G;
     const float *q = J->q + row_q * ORC_D;
-    orc_lut(q, 8, lut8);
-    orc_lut(q, 4, lut4);
-    orc_lut(q, 2, lut2);
+    orc_lut(q, 8, lut8, J->layout);
+    orc_lut(q, 4, lut4, J->layout);
+    orc_lut(q, 2, lut2, J->layout);
     double *luts[3] = {lut8, lut4, lut2};
     int64_t row = (int64_t)b * J->Hkv + h;
     int np = J->num_pages[row];
@@ -924,7 +936,7 @@ static void *decode_worker(void *arg)
 int orc_decode(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
                const int32_t *page_table, const int32_t *num_pages,
                const uint8_t *page_meta, const uint8_t *arena, const uint16_t *value_pool,
-               const float *q, double scale, double *out, double *lse, int nthreads)
+               const float *q, double scale, double *out, double *lse, int nthreads, int layout)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || (P != 16 && P != 32)) return ORC_EINVAL;
     decode_job_t J;
@@ -934,6 +946,7 @@ int orc_decode(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
     J.page_meta = page_meta; J.arena = arena; J.value_pool = value_pool;
     J.q = q; J.scale = scale; J.out = out; J.lse = lse;
     J.next_row = 0; J.n_rows = (int64_t)B * Hq;
+    J.layout = layout;
     pthread_mutex_init(&J.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     pthread_t *th = malloc(sizeof(pthread_t) * nthreads);
@@ -981,9 +994,9 @@ static void *util_worker(void *arg)
         int64_t n = 0;
         for (int g = 0; g < G; g++) {
             const float *q = J->q + ((int64_t)b * J->Hq + (int64_t)h * G + g) * ORC_D;
-            orc_lut(q, 8, lut8);
-            orc_lut(q, 4, lut4);
-            orc_lut(q, 2, lut2);
+            orc_lut(q, 8, lut8, J->layout);
+            orc_lut(q, 4, lut4, J->layout);
+            orc_lut(q, 2, lut2, J->layout);
             double *luts[3] = {lut8, lut4, lut2};
             double m = -INFINITY;
             n = 0;
@@ -1029,7 +1042,7 @@ static void *util_worker(void *arg)
 int orc_decode_utility(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
                        const int32_t *page_table, const int32_t *num_pages,
                        const uint8_t *page_meta, const uint8_t *arena,
-                       const float *q, double scale, double *util, int nthreads)
+                       const float *q, double scale, double *util, int nthreads, int layout)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || (P != 16 && P != 32)) return ORC_EINVAL;
     util_job_t U;
@@ -1040,6 +1053,7 @@ int orc_decode_utility(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head
     J->page_table = page_table; J->num_pages = num_pages;
     J->page_meta = page_meta; J->arena = arena;
     J->q = q; J->scale = scale;
+    J->layout = layout;
     U.util = util;
     U.next_kv = 0; U.n_kv = (int64_t)B * Hkv;
     pthread_mutex_init(&J->mu, NULL);
@@ -1054,15 +1068,16 @@ int orc_decode_utility(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head
 
 /* ------------------------------------------------------------------------ */
 /* Unquantised angle-domain logits (oracle only): r, s_j and theta_j kept as
- * exact fp64 reals, logit = r * sum_j s_j (q_{2j} cos th_j + q_{2j+1} sin th_j).
- * This equals the plain dot product q.k up to rounding. */
-void orc_identity_logits(const float *keys, int64_t n, const float *q, double *logits)
+ * exact fp64 reals, logit = r * sum_j s_j (qx_j cos th_j + qy_j sin th_j)
+ * over the pairs of the given layout.  This equals the plain dot product q.k
+ * up to rounding. */
+void orc_identity_logits(const float *keys, int64_t n, const float *q, double *logits, int layout)
 {
     for (int64_t i = 0; i < n; i++) {
         const float *k = keys + i * ORC_D;
         double e[ORC_NP], t[ORC_NP];
         for (int j = 0; j < ORC_NP; j++) {
-            double x = k[2 * j], y = k[2 * j + 1];
+            double x = k[pair_x(layout, j)], y = k[pair_y(layout, j)];
             e[j] = x * x + y * y;
             t[j] = e[j];
         }
@@ -1072,10 +1087,10 @@ void orc_identity_logits(const float *keys, int64_t n, const float *q, double *l
         double acc = 0.0;
         if (r > 0)
             for (int j = 0; j < ORC_NP; j++) {
-                double x = k[2 * j], y = k[2 * j + 1];
+                double x = k[pair_x(layout, j)], y = k[pair_y(layout, j)];
                 double s = sqrt(e[j]) / r;
                 double th = atan2(y, x);
-                acc += s * ((double)q[2 * j] * cos(th) + (double)q[2 * j + 1] * sin(th));
+                acc += s * ((double)q[pair_x(layout, j)] * cos(th) + (double)q[pair_y(layout, j)] * sin(th));
             }
         logits[i] = r * acc;
     }
@@ -1083,11 +1098,11 @@ void orc_identity_logits(const float *keys, int64_t n, const float *q, double *l
 
 /* encode many keys at once (threads not needed; used by tests) */
 int orc_encode_many(const float *keys, int64_t n, int tb, int sb, uint16_t *r16,
-                    uint16_t *theta, uint16_t *s)
+                    uint16_t *theta, uint16_t *s, int layout)
 {
     int worst = ORC_OK;
     for (int64_t i = 0; i < n; i++) {
-        int st = orc_encode_key(keys + i * ORC_D, tb, sb, r16 + i, theta + i * ORC_NP, s + i * ORC_NP, NULL);
+        int st = orc_encode_key(keys + i * ORC_D, tb, sb, r16 + i, theta + i * ORC_NP, s + i * ORC_NP, NULL, layout);
         if (st > worst) worst = st;
     }
     return worst;

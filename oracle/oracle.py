@@ -19,6 +19,7 @@ SRC = os.path.join(HERE, "ada_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 OK, EINVAL, ENOSPC, EUNSUPPORTED, EUNDECIDABLE = 0, 1, 2, 3, 99
+PAIRS_ADJACENT, PAIRS_HALF = 0, 1   # pair j = (k[2j], k[2j+1]) or (k[j], k[j+64])
 TIER_BITS = {0: (8, 8), 1: (4, 4), 2: (2, 3)}   # tier id -> (angle bits, magnitude bits)
 D = 128
 NP_PAIRS = 64
@@ -54,27 +55,27 @@ def _declare(L):
     L.orc_f64_to_f16_many.argtypes = [vp, i64, vp]
     L.orc_f16_to_f64.restype = dbl
     L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
-    L.orc_encode_key.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
-    L.orc_encode_many.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    L.orc_encode_key.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int]
+    L.orc_encode_many.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_int]
     L.orc_bits_put.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
     L.orc_bits_get.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
     L.orc_block_bytes.restype = i64
     L.orc_block_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
     L.orc_pack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp,
-                           i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+                           i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int]
     L.orc_append.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i64, i64, ctypes.c_int,
-                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     L.orc_rdr_steps.argtypes = [u32, vp, vp, vp, vp]
     L.orc_rdr_assign.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, u32, vp, vp]
     L.orc_transcode.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
     L.orc_repack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp, vp, u32,
                              i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
-    L.orc_lut.argtypes = [vp, ctypes.c_int, vp]
+    L.orc_lut.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
     L.orc_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
-                             vp, vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int]
+                             vp, vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int, ctypes.c_int]
     L.orc_decode_utility.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
-                                     vp, vp, vp, vp, vp, dbl, vp, ctypes.c_int]
-    L.orc_identity_logits.argtypes = [vp, i64, vp, vp]
+                                     vp, vp, vp, vp, vp, dbl, vp, ctypes.c_int, ctypes.c_int]
+    L.orc_identity_logits.argtypes = [vp, i64, vp, vp, ctypes.c_int]
     L.orc_read_token.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp]
     L.orc_value_index.restype = i64
     L.orc_value_index.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -91,14 +92,14 @@ def f16_to_f64(h):
     return lib().orc_f16_to_f64(int(h))
 
 
-def encode(keys, tb, sb):
+def encode(keys, tb, sb, pair_layout=PAIRS_ADJACENT):
     """keys [n,128] fp32 -> (r16 [n] u16 fp16 bits, theta [n,64] u16, s [n,64] u16, status)."""
     keys = np.ascontiguousarray(keys, dtype=np.float32).reshape(-1, D)
     n = keys.shape[0]
     r16 = np.zeros(n, np.uint16)
     th = np.zeros((n, NP_PAIRS), np.uint16)
     s = np.zeros((n, NP_PAIRS), np.uint16)
-    st = lib().orc_encode_many(_p(keys), n, tb, sb, _p(r16), _p(th), _p(s))
+    st = lib().orc_encode_many(_p(keys), n, tb, sb, _p(r16), _p(th), _p(s), pair_layout)
     return r16, th, s, st
 
 
@@ -123,10 +124,13 @@ def block_bytes(tier, P):
 class Cache:
     """Host copy of a paged ADA cache (the same buffers the library keeps on
     the device): page table, page counts, open pages, page metadata, code
-    arena, fp16 value pool and the two allocation counters."""
+    arena, fp16 value pool and the two allocation counters.  pair_layout says
+    which key and query components form the 64 pairs."""
 
-    def __init__(self, P, Hq, Hkv, num_seqs, max_pages_per_head, page_capacity, arena_capacity16):
+    def __init__(self, P, Hq, Hkv, num_seqs, max_pages_per_head, page_capacity, arena_capacity16,
+                 pair_layout=PAIRS_ADJACENT):
         self.P, self.Hq, self.Hkv = P, Hq, Hkv
+        self.pair_layout = pair_layout
         self.num_seqs = num_seqs
         self.max_pages_per_head = max_pages_per_head
         self.page_capacity = page_capacity
@@ -163,7 +167,7 @@ def pack(cache, ctx_len, tiers, keys, values, nthreads=None):
                           cache.max_pages_per_head, cache.page_capacity, cache.arena_capacity16,
                           _p(cache.page_table), _p(cache.num_pages), _p(cache.open_page),
                           _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc),
-                          nthreads)
+                          nthreads, cache.pair_layout)
 
 
 def append(cache, seq, head, tier, keys, values):
@@ -177,7 +181,8 @@ def append(cache, seq, head, tier, keys, values):
                             cache.page_capacity, cache.arena_capacity16, n,
                             _p(seq), _p(head), _p(tier), _p(keys), _p(values),
                             _p(cache.page_table), _p(cache.num_pages), _p(cache.open_page),
-                            _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc))
+                            _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc),
+                            cache.pair_layout)
 
 
 def rdr_steps(tier_mask):
@@ -228,10 +233,10 @@ def repack(src, B, util, budget, dst, tier_mask=0):
     return st, tv
 
 
-def lut(q, tb):
+def lut(q, tb, pair_layout=PAIRS_ADJACENT):
     q = np.ascontiguousarray(q, dtype=np.float32).reshape(D)
     out = np.zeros((NP_PAIRS, 1 << tb), np.float64)
-    lib().orc_lut(_p(q), tb, _p(out))
+    lib().orc_lut(_p(q), tb, _p(out), pair_layout)
     return out
 
 
@@ -246,7 +251,7 @@ def decode(cache, q, scale, nthreads=None):
     st = lib().orc_decode(cache.P, cache.Hq, cache.Hkv, B, cache.max_pages_per_head,
                           _p(cache.page_table), _p(cache.num_pages), _p(cache.page_meta),
                           _p(cache.arena), _p(cache.value_pool), _p(q), float(scale),
-                          _p(out), _p(lse), nthreads)
+                          _p(out), _p(lse), nthreads, cache.pair_layout)
     assert st == OK, st
     return out, lse
 
@@ -264,16 +269,16 @@ def decode_utility(cache, q, scale, util=None, nthreads=None):
     nthreads = nthreads or max(1, len(os.sched_getaffinity(0)))
     st = lib().orc_decode_utility(cache.P, cache.Hq, cache.Hkv, B, cache.max_pages_per_head,
                                   _p(cache.page_table), _p(cache.num_pages), _p(cache.page_meta),
-                                  _p(cache.arena), _p(q), float(scale), _p(util), nthreads)
+                                  _p(cache.arena), _p(q), float(scale), _p(util), nthreads, cache.pair_layout)
     assert st == OK, st
     return util
 
 
-def identity_logits(keys, q):
+def identity_logits(keys, q, pair_layout=PAIRS_ADJACENT):
     keys = np.ascontiguousarray(keys, dtype=np.float32).reshape(-1, D)
     q = np.ascontiguousarray(q, dtype=np.float32).reshape(D)
     out = np.zeros(keys.shape[0], np.float64)
-    lib().orc_identity_logits(_p(keys), keys.shape[0], _p(q), _p(out))
+    lib().orc_identity_logits(_p(keys), keys.shape[0], _p(q), _p(out), pair_layout)
     return out
 
 

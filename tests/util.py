@@ -18,17 +18,19 @@ def dense_attention(keys, values, q, scale):
     return (e[:, None] * values).sum(0) / e.sum(), m + np.log(e.sum())
 
 
-def dequantize(r16, theta, s, tb, sb):
-    """fp64 key from codes: k[2j] = r s_j cos th_j, k[2j+1] = r s_j sin th_j,
-    th_c = -pi + c 2pi/2^tb, s = code/(2^sb - 1)."""
+def dequantize(r16, theta, s, tb, sb, half_split=False):
+    """fp64 key from codes: pair j is (k[2j], k[2j+1]) (or (k[j], k[j+64])
+    when half_split) = r s_j (cos th_j, sin th_j), th_c = -pi + c 2pi/2^tb,
+    s = code/(2^sb - 1)."""
     r = np.asarray(r16, np.uint16).view(np.float16).astype(np.float64)
     N = 1 << tb
     L = (1 << sb) - 1
     th = -np.pi + np.asarray(theta, np.float64) * (2 * np.pi / N)
     sv = np.asarray(s, np.float64) / L
     k = np.zeros(np.shape(theta)[:-1] + (D,))
-    k[..., 0::2] = r[..., None] * sv * np.cos(th)
-    k[..., 1::2] = r[..., None] * sv * np.sin(th)
+    xs, ys = (slice(0, 64), slice(64, 128)) if half_split else (slice(0, None, 2), slice(1, None, 2))
+    k[..., xs] = r[..., None] * sv * np.cos(th)
+    k[..., ys] = r[..., None] * sv * np.sin(th)
     return k
 
 
