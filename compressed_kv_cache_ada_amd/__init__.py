@@ -33,7 +33,8 @@ class AdaError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("rdr_tier_mask", ctypes.c_uint32), ("decode_chunk_pages", ctypes.c_int32)]
+                ("rdr_tier_mask", ctypes.c_uint32), ("decode_chunk_pages", ctypes.c_int32),
+                ("pair_layout", ctypes.c_int32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -140,8 +141,12 @@ def block_bytes(tier, page_size):
     return int(lib().ada_block_bytes(tier, page_size))
 
 
-def make_config(page_size, num_q_heads, num_kv_heads, rdr_tier_mask=0, decode_chunk_pages=0):
-    return Config(D, page_size, num_q_heads, num_kv_heads, rdr_tier_mask, decode_chunk_pages)
+PAIRS_ADJACENT, PAIRS_HALF_SPLIT = 0, 1   # pair j = (x[2j], x[2j+1]) or (x[j], x[j+64])
+
+
+def make_config(page_size, num_q_heads, num_kv_heads, rdr_tier_mask=0, decode_chunk_pages=0,
+                pair_layout=PAIRS_ADJACENT):
+    return Config(D, page_size, num_q_heads, num_kv_heads, rdr_tier_mask, decode_chunk_pages, pair_layout)
 
 
 class Cache:

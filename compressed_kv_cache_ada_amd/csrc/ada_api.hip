@@ -36,6 +36,7 @@ ada_status_t check_cfg(const ada_config_t *cfg) {
     if (G != 1 && G != 2 && G != 4 && G != 8) return ADA_EUNSUPPORTED;
     if (cfg->decode_chunk_pages < 0) return ADA_EINVAL;
     if (cfg->rdr_tier_mask > 7u) return ADA_EINVAL;
+    if (cfg->pair_layout != ADA_PAIRS_ADJACENT && cfg->pair_layout != ADA_PAIRS_HALF_SPLIT) return ADA_EINVAL;
     return ADA_OK;
 }
 
@@ -128,6 +129,7 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.status = cache->status;
     a.logit_buf = nullptr;
     a.util = nullptr;
+    a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     return a;
 }
 
@@ -188,6 +190,7 @@ AppendLaunch make_append(const ada_config_t *cfg, const ada_cache_t *cache, int3
     a.dest_slot = w.dest_slot;
     a.new_pages = w.new_pages;
     a.n_new = w.n_new;
+    a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     return a;
 }
 
@@ -310,7 +313,8 @@ ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, f
     if (st) return st;
     if (B < 0 || (B > 0 && (!q || !lut))) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
-    return hip_status(launch_build_lut(q, B * cfg->num_q_heads, lut, (hipStream_t)stream));
+    return hip_status(launch_build_lut(q, B * cfg->num_q_heads, lut, cfg->pair_layout == ADA_PAIRS_HALF_SPLIT,
+                                       (hipStream_t)stream));
 }
 
 // queries per sequence: a power of two with Q * (Hq / Hkv) <= 8
@@ -613,6 +617,7 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_maxp = 0;
     a.src_of_slot = nullptr;
     a.src_of_slot_pages = 0;
+    a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     return hip_status(launch_pack(a, s));
 }
 
@@ -754,6 +759,7 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_maxp = src->max_pages_per_head;
     a.src_of_slot = r.src_of_slot;
     a.src_of_slot_pages = r.src_of_slot_pages;
+    a.half_pairs = 0;   // codes are transcoded, no key is read
     return hip_status(launch_pack(a, s));
 }
 

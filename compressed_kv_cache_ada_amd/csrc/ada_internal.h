@@ -75,10 +75,11 @@ struct DecodeLaunch {
     // pass turns them into attention mass in util[page * P + slot]
     float *logit_buf;
     float *util;
+    int32_t half_pairs;   // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
 };
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s);
-hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, hipStream_t s);
+hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, bool half_pairs, hipStream_t s);
 // after the reduction (needs lse): util[page * P + slot] for every kept token
 hipError_t launch_decode_utility(const DecodeLaunch &a, hipStream_t s);
 
@@ -107,6 +108,7 @@ struct EncodeLaunch {
     uint16_t *value_pool;
     int32_t P;
     int32_t *status;
+    int32_t half_pairs;   // pair j = (k[j], k[j + 64]) instead of (k[2j], k[2j + 1])
 };
 hipError_t launch_encode_write(const EncodeLaunch &a, hipStream_t s);
 // Zero the code blocks and value pages of new pages listed as
@@ -149,6 +151,7 @@ struct PackLaunch {
     int32_t src_maxp;
     int4 *src_of_slot;              // [src_of_slot_pages][P] source {page, slot, tier, code_off16} per new slot
     int64_t src_of_slot_pages;
+    int32_t half_pairs;             // key pair layout (see EncodeLaunch)
 };
 hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
 // pages a re-pack may open per row: sum over three tiers of ceil(n_tau / P)
@@ -177,6 +180,7 @@ struct AppendLaunch {
     int32_t *dest_page, *dest_slot;   // [n]
     int32_t *new_pages;  // [n]
     int32_t *n_new;      // [1]
+    int32_t half_pairs;  // key pair layout (see EncodeLaunch)
 };
 // append: book destinations, update metadata, zero new pages, then (with
 // encode) encode and write the keys; without encode the caller encodes

@@ -251,6 +251,7 @@ struct AdaPolicy {
     const uint8_t *arena;
     const float *q;
     int32_t Q, Hq, Gr;   // queries per sequence, query heads, query heads per KV head
+    int32_t half;        // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
     float mul;   // softmax scale * log2(e)
     // fused append (APPEND)
     const int32_t *app_page, *app_slot;
@@ -287,7 +288,7 @@ struct AdaPolicy {
             }
             if (w == 0) {
                 enc::encode_write_one(app_keys + (size_t)row * kD, app_values + (size_t)row * kD, dp, slot, m, arena_w,
-                                      value_pool_w, P, status, s.enc_words);
+                                      value_pool_w, P, status, s.enc_words, half != 0);
                 __threadfence_block();
             }
             return true;
@@ -298,12 +299,14 @@ struct AdaPolicy {
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
 
     // phase 1: query pairs and the grid directions.  Virtual head v of the
-    // KV head is query qi = v / Gr, head h * Gr + v % Gr of q [B][Q][Hq][128].
+    // KV head is query qi = v / Gr, head h * Gr + v % Gr of q [B][Q][Hq][128];
+    // component d is x (0) or y (1) of pair j in the cache's pair layout.
     __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
         for (int i = tid; i < G * kD; i += nt) {
             const int v = i >> 7, d = i & 127;
             const int qi = v / Gr, g = v % Gr;
-            s.q8[((d >> 1) * G + v) * 2 + (d & 1)] = q[(((size_t)b * Q + qi) * Hq + (size_t)h * Gr + g) * kD + d];
+            const int j = half ? (d & 63) : (d >> 1), xy = half ? (d >> 6) : (d & 1);
+            s.q8[(j * G + v) * 2 + xy] = q[(((size_t)b * Q + qi) * Hq + (size_t)h * Gr + g) * kD + d];
         }
         for (int c = tid; c < 256; c += nt) {
             const float2 d = grid_dir(c);
@@ -398,6 +401,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.Q = a.Q;
     pol.Hq = a.Hq;
     pol.Gr = a.Hq / a.Hkv;
+    pol.half = a.half_pairs;
     pol.app_page = a.app_page;
     pol.app_slot = a.app_slot;
     pol.app_keys = a.app_keys;
@@ -473,27 +477,28 @@ __global__ __launch_bounds__(256) void decode_utility_kernel(DecodeLaunch a) {
 }
 
 // ---- stand-alone LUT builder --------------------------------------------
-__global__ __launch_bounds__(256) void build_lut_kernel(const float *q, float *lut) {
+// qs holds the query's pairs as [x_0..x_63][y_0..y_63] in either layout.
+__global__ __launch_bounds__(256) void build_lut_kernel(const float *q, float *lut, bool half) {
     __shared__ float2 cs8[256];
     __shared__ float qs[kD];
     const int rowq = blockIdx.x, tid = threadIdx.x;
     cs8[tid] = grid_dir(tid);
-    if (tid < kD) qs[tid] = q[(size_t)rowq * kD + tid];
+    if (tid < kD) qs[half ? tid : (tid & 1) * 64 + (tid >> 1)] = q[(size_t)rowq * kD + tid];
     __syncthreads();
     float *out = lut + (size_t)rowq * (64 * (256 + 16 + 4));
     for (int i = tid; i < 64 * 256; i += 256) {
         const int j = i >> 8, c = i & 255;
-        out[i] = lut_entry(qs[2 * j], qs[2 * j + 1], cs8[c]);
+        out[i] = lut_entry(qs[j], qs[64 + j], cs8[c]);
     }
     out += 64 * 256;
     for (int i = tid; i < 64 * 16; i += 256) {
         const int j = i >> 4, c = i & 15;
-        out[i] = lut_entry(qs[2 * j], qs[2 * j + 1], cs8[c * 16]);
+        out[i] = lut_entry(qs[j], qs[64 + j], cs8[c * 16]);
     }
     out += 64 * 16;
     for (int i = tid; i < 64 * 4; i += 256) {
         const int j = i >> 2, c = i & 3;
-        out[i] = lut_entry(qs[2 * j], qs[2 * j + 1], cs8[c * 64]);
+        out[i] = lut_entry(qs[j], qs[64 + j], cs8[c * 64]);
     }
 }
 
@@ -545,8 +550,8 @@ hipError_t launch_decode_utility(const DecodeLaunch &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, hipStream_t s) {
-    hipLaunchKernelGGL(build_lut_kernel, dim3(rows), dim3(256), 0, s, q, lut);
+hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, bool half_pairs, hipStream_t s) {
+    hipLaunchKernelGGL(build_lut_kernel, dim3(rows), dim3(256), 0, s, q, lut, half_pairs);
     return hipGetLastError();
 }
 

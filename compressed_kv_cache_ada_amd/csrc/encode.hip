@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void encode_write_kernel(EncodeLaunch a) {
         if (page < 0) continue;
         const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + page);
         enc::encode_write_one(a.keys + item * kD, a.values + item * kD, page, a.dest_slot[item], meta, a.arena,
-                              a.value_pool, a.P, a.status, words[wv]);
+                              a.value_pool, a.P, a.status, words[wv], a.half_pairs != 0);
     }
 }
 
@@ -824,6 +824,7 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     e.value_pool = a.value_pool;
     e.P = a.P;
     e.status = a.status;
+    e.half_pairs = a.half_pairs;
     hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(e.n, 4, 16384)), dim3(256), 0, s, e);
     return hipGetLastError();
 }
@@ -848,7 +849,6 @@ hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s) {
                        (const int32_t *)a.new_pages, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
                        a.arena, a.value_pool, a.P, (const int32_t *)a.status);
     if (!encode) return hipGetLastError();
-    if (!encode) return hipGetLastError();
     EncodeLaunch e;
     e.keys = a.keys;
     e.values = a.values;
@@ -860,6 +860,7 @@ hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s) {
     e.value_pool = a.value_pool;
     e.P = a.P;
     e.status = a.status;
+    e.half_pairs = a.half_pairs;
     hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(e.n, 4, 16384)), dim3(256), 0, s, e);
     return hipGetLastError();
 }

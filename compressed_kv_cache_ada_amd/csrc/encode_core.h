@@ -260,19 +260,22 @@ __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint3
 }
 
 // ------------------------------------------------ encode + write one key
-// Called by all 64 lanes of one wavefront: encodes key[128] (fp32) at the
+// Called by all 64 lanes of one wavefront: encodes key[128] (fp32; lane j
+// takes pair j, (key[2j], key[2j+1]) or with half_pairs (key[j], key[j+64])) at the
 // page's tier and writes its radius, codes and value (fp16 bits) into slot
 // `slot` of page `page` (code block at meta.y * 16).  words is the
 // wavefront's LDS scratch for packing the bit strings.  An undecidable code
 // (never expected) sets ADA_EINTERNAL and writes nothing.
 __device__ inline void encode_write_one(const float *key, const uint16_t *value, int page, int slot, uint2 meta,
                                         uint8_t *arena, uint16_t *value_pool, int P, int32_t *status,
-                                        uint32_t (&words)[2][16]) {
+                                        uint32_t (&words)[2][16], bool half_pairs) {
     #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
     const int tier = meta.x & 0xFF;
     const int tb = tier_tb(tier), sb = tier_sb(tier);
-    const float2 kk = *reinterpret_cast<const float2 *>(key + 2 * lane);
+    float2 kk;
+    if (half_pairs) kk = make_float2(key[lane], key[lane + 64]);
+    else kk = *reinterpret_cast<const float2 *>(key + 2 * lane);
     const double x = kk.x, y = kk.y;
     const double xx = x * x;
     const double yy = y * y;

@@ -92,7 +92,15 @@ typedef struct {
                                    max_pages_per_head pages on the current device.  Rounded up to
                                    64 tokens' worth of pages, at most 256.  The same value must be
                                    in effect for the workspace query and the decode calls. */
+    int32_t pair_layout;        /* which components of a key (and of a query) form the 64 pairs
+                                   (abstract: keys as a radius plus per-pair angle codes; the pairing
+                                   is this library's choice): ADA_PAIRS_ADJACENT (k[2j], k[2j+1]) or
+                                   ADA_PAIRS_HALF_SPLIT (k[j], k[j+64]), the pairing of the
+                                   rotate-half form of rotary position embeddings.  A cache must be
+                                   written and read with one layout. */
 } ada_config_t;
+
+enum { ADA_PAIRS_ADJACENT = 0, ADA_PAIRS_HALF_SPLIT = 1 };
 
 /* Metadata of one page, 8 bytes. */
 typedef struct {

@@ -69,7 +69,8 @@ def test_host_validation_without_gpu():
            (ada.Config(128, 16, 48, 8, 0, 0), ada.EUNSUPPORTED),
            (ada.Config(128, 16, 30, 8, 0, 0), ada.EINVAL),
            (ada.Config(128, 16, 32, 0, 0, 0), ada.EINVAL),
-           (ada.Config(128, 16, 32, 8, 9, 0), ada.EINVAL)]
+           (ada.Config(128, 16, 32, 8, 9, 0), ada.EINVAL),
+           (ada.Config(128, 16, 32, 8, 0, 0, 2), ada.EINVAL)]
     for cfg, want in bad[1:]:
         assert _size(L.ada_decode_workspace, ctypes.byref(cfg), ctypes.byref(desc), 2)[0] == want
     # decode refuses a cache with null buffers before touching the device
