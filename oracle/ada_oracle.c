@@ -47,13 +47,29 @@ enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_ENOSPC = 2, ORC_EUNSUPPORTED = 3,
 #define ORC_D 128          /* head dimension                      */
 #define ORC_NP 64          /* pairs per key: head dimension / 2   */
 
-/* Fixed tier table (id order): T8 = 8-bit angle / 8-bit magnitude,
- * T4 = 4 / 4, T2 = 2-bit angle / 3-bit magnitude. */
-static const int TIER_TB[3] = {8, 4, 2};
-static const int TIER_SB[3] = {8, 4, 3};
+/* Fixed tier table (id order).  Keys: T8 = 8-bit angle / 8-bit magnitude,
+ * T4 = 4 / 4, T2 = 2-bit angle / 3-bit magnitude.  Values: fp16 for ids 0-2
+ * (T8, T4, T2); the block-scaled 8-bit value codec V8 (below) for ids 3-5
+ * (T8V8, T4V8, T2V8), whose keys are those of ids 0-2.
+ * Rate per token and head: 2 (radius) + 8 (tb + sb) (codes) + 256 (fp16
+ * values) or 132 (V8 values).  Distortion: 2^-(tb + sb), plus 2^-14 for V8
+ * values (the squared relative step of a 7-bit magnitude); a dropped token
+ * has distortion 1 and rate 0. */
+#define ORC_NT 6
+static const int TIER_TB[ORC_NT] = {8, 4, 2, 8, 4, 2};
+static const int TIER_SB[ORC_NT] = {8, 4, 3, 8, 4, 3};
+static const int TIER_VB[ORC_NT] = {16, 16, 16, 8, 8, 8};
 
-int orc_tier_theta_bits(int tier) { return (tier >= 0 && tier < 3) ? TIER_TB[tier] : -1; }
-int orc_tier_s_bits(int tier) { return (tier >= 0 && tier < 3) ? TIER_SB[tier] : -1; }
+static int64_t tier_rate(int t) { return 2 + 8 * (TIER_TB[t] + TIER_SB[t]) + (TIER_VB[t] == 16 ? 256 : 132); }
+static double tier_dist(int t)
+{
+    return ldexp(1.0, -(TIER_TB[t] + TIER_SB[t])) + (TIER_VB[t] == 16 ? 0.0 : ldexp(1.0, -14));
+}
+
+int orc_tier_theta_bits(int tier) { return (tier >= 0 && tier < ORC_NT) ? TIER_TB[tier] : -1; }
+int orc_tier_s_bits(int tier) { return (tier >= 0 && tier < ORC_NT) ? TIER_SB[tier] : -1; }
+int orc_tier_value_bits(int tier) { return (tier >= 0 && tier < ORC_NT) ? TIER_VB[tier] : -1; }
+int64_t orc_tier_rate(int tier) { return (tier >= 0 && tier < ORC_NT) ? tier_rate(tier) : -1; }
 
 /* ------------------------------------------------------------------------ */
 /* fp16 conversion: round to nearest, ties to even, straight from fp64 (no
@@ -281,6 +297,100 @@ static int64_t value_index(int64_t page, int P, int slot, int d)
     return page * P * ORC_D + (int64_t)(slot / 8) * 1024 + (int64_t)d * 8 + slot % 8;
 }
 
+/* ------------------------------------------------------------------------ */
+/* V8 value codec (value tiers 3-5).  The abstract speaks of precision tiers
+ * per token and head without naming a value format; this one follows the
+ * pattern of the OCP Microscaling formats: blocks of 32 consecutive
+ * dimensions share a power-of-two scale, elements are 8-bit integers with 6
+ * fraction bits.  For block k of a token-head's fp16 values v (exact in
+ * fp64):
+ *   amax = max |v_d|;  e = floor(log2 amax), raised to at least -18
+ *   (e = -18 when amax = 0);
+ *   c_d = clamp(round_half_even(v_d * 2^(6 - e)), -127, 127)   (the product
+ *   is exact);  stored: the byte e + 127 and the int8 codes.
+ *   Decoded value: c_d * 2^(e - 6), exactly an fp16 number (|c| <= 127,
+ *   e - 6 >= -24).
+ * A non-finite value cannot be encoded (EINVAL). */
+int orc_v8_encode(const uint16_t *v, uint8_t *scale_byte, int8_t *codes)
+{
+    for (int k = 0; k < 4; k++) {
+        double amax = 0.0;
+        for (int d = 32 * k; d < 32 * k + 32; d++) {
+            double x = fabs(orc_f16_to_f64(v[d]));
+            if (!isfinite(x)) return ORC_EINVAL;
+            if (x > amax) amax = x;
+        }
+        int e = -18;
+        if (amax > 0) {
+            int ex;
+            frexp(amax, &ex);           /* amax = m 2^ex, m in [0.5, 1) */
+            if (ex - 1 > e) e = ex - 1;
+        }
+        scale_byte[k] = (uint8_t)(e + 127);
+        for (int d = 32 * k; d < 32 * k + 32; d++) {
+            double c = nearbyint(ldexp(orc_f16_to_f64(v[d]), 6 - e));   /* round half to even */
+            if (c > 127) c = 127;
+            if (c < -127) c = -127;
+            codes[d] = (int8_t)c;
+        }
+    }
+    return ORC_OK;
+}
+
+void orc_v8_decode(const uint8_t *scale_byte, const int8_t *codes, double *v)
+{
+    for (int d = 0; d < ORC_D; d++) v[d] = ldexp((double)codes[d], (int)scale_byte[d / 32] - 127 - 6);
+}
+
+/* V8 value page, in the page's value-pool slot viewed as bytes: per 8-token
+ * group g, [4 dimension blocks][8 tokens] scale bytes (32 bytes), then
+ * [128 dims][8 tokens] int8 codes (1024 bytes).  Empty slots are zero. */
+static int64_t v8_scale_off(int slot, int k) { return (int64_t)(slot / 8) * 1056 + k * 8 + slot % 8; }
+static int64_t v8_code_off(int slot, int d) { return (int64_t)(slot / 8) * 1056 + 32 + (int64_t)d * 8 + slot % 8; }
+
+static uint8_t *value_page_bytes(uint16_t *pool, int64_t page, int P) { return (uint8_t *)(pool + page * P * ORC_D); }
+
+/* write token `slot`'s values (fp16 bits) into the page's value slot in the
+ * tier's format; returns EINVAL for a V8 tier and a non-finite value */
+static int value_write(uint16_t *pool, int64_t page, int tier, int P, int slot, const uint16_t *v)
+{
+    if (TIER_VB[tier] == 16) {
+        for (int d = 0; d < ORC_D; d++) pool[value_index(page, P, slot, d)] = v[d];
+        return ORC_OK;
+    }
+    uint8_t sb[4];
+    int8_t c[ORC_D];
+    if (orc_v8_encode(v, sb, c) != ORC_OK) return ORC_EINVAL;
+    uint8_t *pb = value_page_bytes(pool, page, P);
+    for (int k = 0; k < 4; k++) pb[v8_scale_off(slot, k)] = sb[k];
+    for (int d = 0; d < ORC_D; d++) pb[v8_code_off(slot, d)] = (uint8_t)c[d];
+    return ORC_OK;
+}
+
+/* token `slot`'s decoded values, exact in fp64 */
+static void value_read(const uint16_t *pool, int64_t page, int tier, int P, int slot, double *v)
+{
+    if (TIER_VB[tier] == 16) {
+        for (int d = 0; d < ORC_D; d++) v[d] = orc_f16_to_f64(pool[value_index(page, P, slot, d)]);
+        return;
+    }
+    const uint8_t *pb = (const uint8_t *)(pool + page * P * ORC_D);
+    uint8_t sb[4];
+    int8_t c[ORC_D];
+    for (int k = 0; k < 4; k++) sb[k] = pb[v8_scale_off(slot, k)];
+    for (int d = 0; d < ORC_D; d++) c[d] = (int8_t)pb[v8_code_off(slot, d)];
+    orc_v8_decode(sb, c, v);
+}
+
+/* values of a token for an encoder: finite fp16 for V8 tiers */
+static int values_ok(int tier, const uint16_t *v)
+{
+    if (TIER_VB[tier] == 16) return 1;
+    for (int d = 0; d < ORC_D; d++)
+        if (!isfinite(orc_f16_to_f64(v[d]))) return 0;
+    return 1;
+}
+
 static void meta_write(uint8_t *meta, int64_t page, int tier, int count, uint32_t off16)
 {
     uint8_t *m = meta + 8 * page;
@@ -371,8 +481,8 @@ static void pack_layout(int P, int Hkv, int B, const int32_t *ctx_len, int64_t c
         for (int h = 0; h < Hkv; h++) {
             int64_t row = (int64_t)b * Hkv + h;
             int32_t np_row = 0;
-            for (int tau = 0; tau < 3; tau++) {
-                open_page[row * 3 + tau] = -1;
+            for (int tau = 0; tau < ORC_NT; tau++) {
+                open_page[row * ORC_NT + tau] = -1;
                 int64_t page = -1;
                 int slot = P;
                 uint8_t *block = NULL;
@@ -398,12 +508,11 @@ static void pack_layout(int P, int Hkv, int B, const int32_t *ctx_len, int64_t c
                         sc[j] = sc_codes[idx * ORC_NP + j];
                     }
                     write_token_codes(block, tau, P, slot, r16[idx], th, sc);
-                    for (int d = 0; d < ORC_D; d++)
-                        value_pool[value_index(page, P, slot, d)] = values[idx * ORC_D + d];
+                    value_write(value_pool, page, tau, P, slot, values + idx * ORC_D);   /* checked before */
                     slot++;
                     meta_write(page_meta, page, tau, slot, off16);
                 }
-                if (page >= 0 && slot < P) open_page[row * 3 + tau] = (int32_t)page;
+                if (page >= 0 && slot < P) open_page[row * ORC_NT + tau] = (int32_t)page;
             }
             num_pages[row] = np_row;
         }
@@ -424,18 +533,19 @@ int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
         if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride) return ORC_EINVAL;
         for (int h = 0; h < Hkv; h++) {
             int64_t row_pages = 0;
-            int64_t n_tier[3] = {0, 0, 0};
+            int64_t n_tier[ORC_NT] = {0};
             for (int t = 0; t < ctx_len[b]; t++) {
                 int64_t idx = ((int64_t)b * Hkv + h) * ctx_stride + t;
                 int tv = tiers[idx];
-                if (tv < -1 || tv > 2) return ORC_EINVAL;
+                if (tv < -1 || tv >= ORC_NT) return ORC_EINVAL;
                 if (tv < 0) continue;
                 const float *k = keys + idx * ORC_D;
                 for (int d = 0; d < ORC_D; d++)
                     if (!isfinite(k[d])) return ORC_EINVAL;
+                if (!values_ok(tv, values + idx * ORC_D)) return ORC_EINVAL;
                 n_tier[tv]++;
             }
-            for (int tau = 0; tau < 3; tau++) {
+            for (int tau = 0; tau < ORC_NT; tau++) {
                 int64_t pages = (n_tier[tau] + P - 1) / P;
                 row_pages += pages;
                 need_pages += pages;
@@ -495,19 +605,20 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
     for (int i = 0; i < n; i++) {
-        if (seq[i] < 0 || seq[i] >= num_seqs || head[i] < 0 || head[i] >= Hkv || tier[i] > 2)
+        if (seq[i] < 0 || seq[i] >= num_seqs || head[i] < 0 || head[i] >= Hkv || tier[i] >= ORC_NT)
             return ORC_EINVAL;
         for (int d = 0; d < ORC_D; d++)
             if (!isfinite(keys[(int64_t)i * ORC_D + d])) return ORC_EINVAL;
+        if (!values_ok(tier[i], values + (int64_t)i * ORC_D)) return ORC_EINVAL;
     }
     /* dry run on copies of the small state */
     int64_t rows = (int64_t)num_seqs * Hkv;
     int32_t *np_copy = malloc(sizeof(int32_t) * rows);
-    int32_t *open_copy = malloc(sizeof(int32_t) * rows * 3);
-    int32_t *cnt_open = malloc(sizeof(int32_t) * rows * 3);
+    int32_t *open_copy = malloc(sizeof(int32_t) * rows * ORC_NT);
+    int32_t *cnt_open = malloc(sizeof(int32_t) * rows * ORC_NT);
     memcpy(np_copy, num_pages, sizeof(int32_t) * rows);
-    memcpy(open_copy, open_page, sizeof(int32_t) * rows * 3);
-    for (int64_t i = 0; i < rows * 3; i++) {
+    memcpy(open_copy, open_page, sizeof(int32_t) * rows * ORC_NT);
+    for (int64_t i = 0; i < rows * ORC_NT; i++) {
         cnt_open[i] = 0;
         if (open_copy[i] >= 0) {
             int tr, c; uint32_t o;
@@ -519,7 +630,7 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
     int status = ORC_OK;
     for (int i = 0; i < n && status == ORC_OK; i++) {
         int64_t row = (int64_t)seq[i] * Hkv + head[i];
-        int64_t key = row * 3 + tier[i];
+        int64_t key = row * ORC_NT + tier[i];
         if (open_copy[key] < 0) {
             if (a0 + 1 > page_capacity) status = ORC_ENOSPC;
             else if (a1 + orc_block_bytes(tier[i], P) / 16 > arena_capacity16) status = ORC_ENOSPC;
@@ -541,7 +652,7 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
     for (int i = 0; i < n; i++) {
         int64_t row = (int64_t)seq[i] * Hkv + head[i];
         int tau = tier[i];
-        int32_t *op = &open_page[row * 3 + tau];
+        int32_t *op = &open_page[row * ORC_NT + tau];
         int64_t page;
         int cnt;
         uint32_t off16;
@@ -566,8 +677,7 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
             ORC_OK)
             return ORC_EUNDECIDABLE;
         write_token_codes(arena + (int64_t)off16 * 16, tau, P, cnt, r16, th, sc);
-        for (int d = 0; d < ORC_D; d++)
-            value_pool[value_index(page, P, cnt, d)] = values[(int64_t)i * ORC_D + d];
+        value_write(value_pool, page, tau, P, cnt, values + (int64_t)i * ORC_D);   /* checked above */
         cnt++;
         meta_write(page_meta, page, tau, cnt, off16);
         if (cnt == P) *op = -1;
@@ -602,23 +712,22 @@ static int step_cmp(const void *a, const void *b)
 
 int orc_rdr_steps(uint32_t tier_mask, int *n_steps, int *step_tier, int64_t *dR, double *c)
 {
-    int ids[3], n = 0;
-    for (int tau = 0; tau < 3; tau++)
+    int ids[ORC_NT], n = 0;
+    if (tier_mask >> ORC_NT) return ORC_EINVAL;
+    for (int tau = 0; tau < ORC_NT; tau++)
         if (tier_mask & (1u << tau)) ids[n++] = tau;
     if (n == 0) return ORC_EINVAL;
     /* sort enabled tiers by rate ascending */
     for (int i = 0; i < n; i++)
         for (int j = i + 1; j < n; j++) {
-            int64_t ri = 2 + 8 * (TIER_TB[ids[i]] + TIER_SB[ids[i]]) + 256;
-            int64_t rj = 2 + 8 * (TIER_TB[ids[j]] + TIER_SB[ids[j]]) + 256;
-            if (rj < ri) { int tmp = ids[i]; ids[i] = ids[j]; ids[j] = tmp; }
+            if (tier_rate(ids[j]) < tier_rate(ids[i])) { int tmp = ids[i]; ids[i] = ids[j]; ids[j] = tmp; }
         }
     int64_t prevR = 0;
     double prevD = 1.0;
     for (int i = 0; i < n; i++) {
         int tau = ids[i];
-        int64_t R = 2 + 8 * (TIER_TB[tau] + TIER_SB[tau]) + 256;
-        double D = ldexp(1.0, -(TIER_TB[tau] + TIER_SB[tau]));
+        int64_t R = tier_rate(tau);
+        double D = tier_dist(tau);
         if (R <= prevR || D >= prevD) return ORC_EUNSUPPORTED;
         dR[i] = R - prevR;
         c[i] = (prevD - D) / (double)dR[i];
@@ -637,9 +746,9 @@ int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
                    const float *utility, const int64_t *budget, uint32_t tier_mask,
                    const int8_t *cap_level, int8_t *tier_out)
 {
-    int n_steps, step_tier[3];
-    int64_t dR[3];
-    double c[3];
+    int n_steps, step_tier[ORC_NT];
+    int64_t dR[ORC_NT];
+    double c[ORC_NT];
     int st = orc_rdr_steps(tier_mask, &n_steps, step_tier, dR, c);
     if (st) return st;
     for (int b = 0; b < B; b++) {
@@ -692,16 +801,18 @@ int orc_rdr_assign(int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Transcoding a token's codes to a tier of no more bits (tb and sb both not
- * larger), in code space:
+/* Transcoding a token's key codes to a tier of no more bits (tb and sb both
+ * not larger), in code space:
  *   angle:     the grids are nested (grid point c of tb bits is grid point
  *              c * 2^(tb_old - tb) of tb_old bits), so the new code is the
  *              nearest new grid point, c_old / 2^d rounded half up, mod 2^tb
  *              (d = tb_old - tb): the tie rule of the encoder;
  *   magnitude: the nearest of the new levels c / L to c_old / L_old, i.e.
  *              round(c_old * L / L_old); for these tiers no exact tie exists;
- *   radius and value unchanged.
- * This is re-encoding the dequantised key, decided exactly. */
+ *   radius unchanged.
+ * This is re-encoding the dequantised key, decided exactly.  Values are
+ * re-encoded from their decoded fp16 numbers in the new tier's format (an
+ * fp16 -> V8 move quantises them; V8 -> V8 reproduces the codes). */
 void orc_transcode(int tier_old, int tier_new, const uint16_t *th_old, const uint16_t *s_old,
                    uint16_t *th_new, uint16_t *s_new)
 {
@@ -738,11 +849,19 @@ int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
     if (tier_mask == 0) tier_mask = 7;
-    int n_steps, step_tier[3];
-    int64_t dR[3];
-    double c[3];
+    int n_steps, step_tier[ORC_NT];
+    int64_t dR[ORC_NT];
+    double c[ORC_NT];
     int st = orc_rdr_steps(tier_mask, &n_steps, step_tier, dR, c);
     if (st) return st;
+    /* the codes hold nothing finer than they are: each step of the chain must
+     * keep or refine angle, magnitude and value precision, so that the
+     * tiers a token may move to form a prefix of the chain */
+    for (int k = 1; k < n_steps; k++) {
+        int a = step_tier[k - 1], b2 = step_tier[k];
+        if (TIER_TB[a] > TIER_TB[b2] || TIER_SB[a] > TIER_SB[b2] || TIER_VB[a] > TIER_VB[b2])
+            return ORC_EUNSUPPORTED;
+    }
     int64_t S = (int64_t)src_maxp * P;
     int64_t n = (int64_t)B * Hkv * S;
     float *uv = calloc((size_t)(n > 0 ? n : 1), sizeof(float));
@@ -759,9 +878,10 @@ int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_
                 int64_t page = src_page_table[row * src_maxp + i];
                 int tier, count; uint32_t off16;
                 meta_read(src_page_meta, page, &tier, &count, &off16);
-                int64_t rate = 2 + 8 * (TIER_TB[tier] + TIER_SB[tier]) + 256;
-                int lv = 0;   /* steps up to the current tier */
-                while (lv < n_steps && 2 + 8 * (TIER_TB[step_tier[lv]] + TIER_SB[step_tier[lv]]) + 256 <= rate) lv++;
+                int lv = 0;   /* the chain's tiers holding no more than the current one */
+                while (lv < n_steps && TIER_TB[step_tier[lv]] <= TIER_TB[tier] &&
+                       TIER_SB[step_tier[lv]] <= TIER_SB[tier] && TIER_VB[step_tier[lv]] <= TIER_VB[tier])
+                    lv++;
                 for (int slot = 0; slot < count; slot++) {
                     int64_t idx = row * S + (int64_t)i * P + slot;
                     uv[idx] = util[page * P + slot];
@@ -776,10 +896,10 @@ int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_
         /* destination capacity (all-or-nothing) */
         int64_t need_pages = 0, need16 = 0;
         for (int64_t row = 0; row < (int64_t)B * Hkv && st == ORC_OK; row++) {
-            int64_t cnt[3] = {0, 0, 0}, rp = 0;
+            int64_t cnt[ORC_NT] = {0}, rp = 0;
             for (int64_t t = 0; t < S; t++)
                 if (tier_v[row * S + t] >= 0) cnt[tier_v[row * S + t]]++;
-            for (int tau = 0; tau < 3; tau++) {
+            for (int tau = 0; tau < ORC_NT; tau++) {
                 int64_t pg = (cnt[tau] + P - 1) / P;
                 rp += pg;
                 need_pages += pg;
@@ -808,8 +928,9 @@ int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_
                     th[idx * ORC_NP + j] = (uint8_t)th_n[j];
                     sc[idx * ORC_NP + j] = (uint8_t)s_n[j];
                 }
-                for (int dd = 0; dd < ORC_D; dd++)
-                    vals[idx * ORC_D + dd] = src_value_pool[value_index(page, P, slot, dd)];
+                double v[ORC_D];   /* decoded values are fp16 numbers exactly */
+                value_read(src_value_pool, page, tier, P, slot, v);
+                for (int dd = 0; dd < ORC_D; dd++) vals[idx * ORC_D + dd] = orc_f64_to_f16(v[dd]);
             }
         pack_layout(P, Hkv, B, ctx, S, tier_v, r16, th, sc, vals, dst_maxp, page_table, num_pages, open_page,
                     page_meta, arena, value_pool, alloc);
@@ -866,7 +987,6 @@ static void decode_row(decode_job_t *J, int64_t row_q, double *lut8, double *lut
     orc_lut(q, 8, lut8, J->layout);
     orc_lut(q, 4, lut4, J->layout);
     orc_lut(q, 2, lut2, J->layout);
-    double *luts[3] = {lut8, lut4, lut2};
     int64_t row = (int64_t)b * J->Hkv + h;
     int np = J->num_pages[row];
     int64_t n = 0;
@@ -880,12 +1000,13 @@ static void decode_row(decode_job_t *J, int64_t row_q, double *lut8, double *lut
         int tb = TIER_TB[tier], sb = TIER_SB[tier];
         int N = 1 << tb;
         double L = (double)((1 << sb) - 1);
+        const double *lut = tb == 8 ? lut8 : (tb == 4 ? lut4 : lut2);
         for (int slot = 0; slot < count; slot++) {
             uint16_t r16, th[ORC_NP], sc[ORC_NP];
             read_token_codes(block, tier, J->P, slot, &r16, th, sc);
             double acc = 0.0;
             for (int j = 0; j < ORC_NP; j++)
-                acc += ((double)sc[j] / L) * luts[tier][j * N + th[j]];
+                acc += ((double)sc[j] / L) * lut[j * N + th[j]];
             double lg = J->scale * orc_f16_to_f64(r16) * acc;
             if (n < cap) logit[n] = lg;
             n++;
@@ -905,8 +1026,9 @@ static void decode_row(decode_job_t *J, int64_t row_q, double *lut8, double *lut
         meta_read(J->page_meta, page, &tier, &count, &off16);
         for (int slot = 0; slot < count; slot++, t++) {
             double w = exp(logit[t] - m) / sum;
-            for (int d = 0; d < ORC_D; d++)
-                o[d] += w * orc_f16_to_f64(J->value_pool[value_index(page, J->P, slot, d)]);
+            double v[ORC_D];
+            value_read(J->value_pool, page, tier, J->P, slot, v);
+            for (int d = 0; d < ORC_D; d++) o[d] += w * v[d];
         }
     }
     J->lse[row_q] = m + log(sum);
@@ -997,7 +1119,6 @@ static void *util_worker(void *arg)
             orc_lut(q, 8, lut8, J->layout);
             orc_lut(q, 4, lut4, J->layout);
             orc_lut(q, 2, lut2, J->layout);
-            double *luts[3] = {lut8, lut4, lut2};
             double m = -INFINITY;
             n = 0;
             for (int i = 0; i < np; i++) {
@@ -1007,12 +1128,13 @@ static void *util_worker(void *arg)
                 const uint8_t *block = J->arena + (int64_t)off16 * 16;
                 int N = 1 << TIER_TB[tier];
                 double L = (double)((1 << TIER_SB[tier]) - 1);
+                const double *lut = TIER_TB[tier] == 8 ? lut8 : (TIER_TB[tier] == 4 ? lut4 : lut2);
                 for (int slot = 0; slot < count; slot++) {
                     uint16_t r16, th[ORC_NP], sc[ORC_NP];
                     read_token_codes(block, tier, J->P, slot, &r16, th, sc);
                     double acc = 0.0;
                     for (int j = 0; j < ORC_NP; j++)
-                        acc += ((double)sc[j] / L) * luts[tier][j * N + th[j]];
+                        acc += ((double)sc[j] / L) * lut[j * N + th[j]];
                     double lg = J->scale * orc_f16_to_f64(r16) * acc;
                     logit[n++] = lg;
                     if (lg > m) m = lg;
@@ -1117,6 +1239,13 @@ void orc_read_token(const uint8_t *arena, const uint8_t *page_meta, int P, int64
     meta_read(page_meta, page, &tier, &count, &off16);
     read_token_codes(arena + (int64_t)off16 * 16, tier, P, slot, r16, theta, s);
     *tier_out = tier;
+}
+
+void orc_read_values(const uint16_t *value_pool, const uint8_t *page_meta, int P, int64_t page, int slot, double *v)
+{
+    int tier, count; uint32_t off16;
+    meta_read(page_meta, page, &tier, &count, &off16);
+    value_read(value_pool, page, tier, P, slot, v);
 }
 
 void orc_f64_to_f16_many(const double *x, int64_t n, uint16_t *out)

@@ -20,7 +20,9 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 OK, EINVAL, ENOSPC, EUNSUPPORTED, EUNDECIDABLE = 0, 1, 2, 3, 99
 PAIRS_ADJACENT, PAIRS_HALF = 0, 1   # pair j = (k[2j], k[2j+1]) or (k[j], k[j+64])
-TIER_BITS = {0: (8, 8), 1: (4, 4), 2: (2, 3)}   # tier id -> (angle bits, magnitude bits)
+TIER_BITS = {0: (8, 8), 1: (4, 4), 2: (2, 3), 3: (8, 8), 4: (4, 4), 5: (2, 3)}   # tier id -> (angle, magnitude bits)
+VALUE_BITS = {0: 16, 1: 16, 2: 16, 3: 8, 4: 8, 5: 8}   # tier id -> value format (fp16 or V8)
+NUM_TIERS = 6
 D = 128
 NP_PAIRS = 64
 
@@ -77,6 +79,11 @@ def _declare(L):
                                      vp, vp, vp, vp, vp, dbl, vp, ctypes.c_int, ctypes.c_int]
     L.orc_identity_logits.argtypes = [vp, i64, vp, vp, ctypes.c_int]
     L.orc_read_token.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp]
+    L.orc_tier_rate.restype = i64
+    L.orc_tier_rate.argtypes = [ctypes.c_int]
+    L.orc_v8_encode.argtypes = [vp, vp, vp]
+    L.orc_v8_decode.argtypes = [vp, vp, vp]
+    L.orc_read_values.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp]
     L.orc_value_index.restype = i64
     L.orc_value_index.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
 
@@ -138,7 +145,7 @@ class Cache:
         rows = num_seqs * Hkv
         self.page_table = np.zeros((rows, max_pages_per_head), np.int32)
         self.num_pages = np.zeros(rows, np.int32)
-        self.open_page = np.full((rows, 3), -1, np.int32)
+        self.open_page = np.full((rows, NUM_TIERS), -1, np.int32)
         self.page_meta = np.zeros((page_capacity, 8), np.uint8)
         self.arena = np.zeros(arena_capacity16 * 16, np.uint8)
         self.value_pool = np.zeros((page_capacity, P * D), np.uint16)
@@ -187,9 +194,9 @@ def append(cache, seq, head, tier, keys, values):
 
 def rdr_steps(tier_mask):
     n = ctypes.c_int(0)
-    st_tier = np.zeros(3, np.int32)
-    dR = np.zeros(3, np.int64)
-    c = np.zeros(3, np.float64)
+    st_tier = np.zeros(NUM_TIERS, np.int32)
+    dR = np.zeros(NUM_TIERS, np.int64)
+    c = np.zeros(NUM_TIERS, np.float64)
     st = lib().orc_rdr_steps(tier_mask, ctypes.byref(n), _p(st_tier), _p(dR), _p(c))
     return st, st_tier[:n.value], dR[:n.value], c[:n.value]
 
@@ -290,6 +297,34 @@ def read_token(cache, page, slot):
     lib().orc_read_token(_p(cache.arena), _p(cache.page_meta), cache.P, page, slot,
                          _p(r16), _p(th), _p(s), ctypes.byref(tier))
     return int(r16[0]), th, s, tier.value
+
+
+def tier_rate(tier):
+    return lib().orc_tier_rate(tier)
+
+
+def v8_encode(values):
+    """fp16 bits [128] -> (status, scale bytes [4] u8, codes [128] int8)."""
+    v = np.ascontiguousarray(values, dtype=np.uint16).reshape(D)
+    sb = np.zeros(4, np.uint8)
+    c = np.zeros(D, np.int8)
+    st = lib().orc_v8_encode(_p(v), _p(sb), _p(c))
+    return st, sb, c
+
+
+def v8_decode(scale_bytes, codes):
+    sb = np.ascontiguousarray(scale_bytes, dtype=np.uint8).reshape(4)
+    c = np.ascontiguousarray(codes, dtype=np.int8).reshape(D)
+    out = np.zeros(D, np.float64)
+    lib().orc_v8_decode(_p(sb), _p(c), _p(out))
+    return out
+
+
+def read_values(cache, page, slot):
+    """decoded values (fp64 [128]) of a cached token, in its page's format"""
+    out = np.zeros(D, np.float64)
+    lib().orc_read_values(_p(cache.value_pool), _p(cache.page_meta), cache.P, page, slot, _p(out))
+    return out
 
 
 def value_index(page, P, slot, d):

@@ -173,8 +173,14 @@ def test_invalid_inputs_write_nothing():
     c = _cache_for(w)
     before = c.copy()
     bad = w["tiers"].copy()
-    bad[0, 0, 5] = 3
+    bad[0, 0, 5] = O.NUM_TIERS
     assert O.pack(c, w["ctx_len"], bad, w["keys"], w["values"]) == O.EINVAL
+    # a non-finite value cannot be put into a V8 tier (fp16 tiers store it as is)
+    vals = w["values"].copy()
+    kept = np.argwhere(w["tiers"][0, 0] >= 0)[0, 0]
+    vals[0, 0, kept, 7] = np.float16(np.inf).view(np.uint16)
+    v8 = np.where(w["tiers"] >= 0, w["tiers"] + 3, -1).astype(np.int8)
+    assert O.pack(c, w["ctx_len"], v8, w["keys"], vals) == O.EINVAL
     keys = w["keys"].copy()
     kept = np.argwhere(w["tiers"][0, 0] >= 0)[0, 0]
     keys[0, 0, kept, 3] = np.nan
@@ -186,6 +192,6 @@ def test_invalid_inputs_write_nothing():
     keys[0, 0, dropped, :] = np.inf
     assert O.pack(c, w["ctx_len"], w["tiers"], keys, w["values"]) == O.OK
     # append: out-of-range sequence / head / tier
-    for s, h, t in [(1, 0, 0), (0, 8, 0), (0, 0, 3)]:
+    for s, h, t in [(1, 0, 0), (0, 8, 0), (0, 0, O.NUM_TIERS)]:
         c2 = _cache_for(w)
         assert O.append(c2, [s], [h], [t], w["keys"][0, 0, :1], w["values"][0, 0, :1]) == O.EINVAL

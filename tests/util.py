@@ -49,7 +49,7 @@ def kept_tokens(w, b, h):
     (tier id ascending, then position ascending)."""
     t = w["tiers"][b, h, : int(w["ctx_len"][b])]
     out = []
-    for tau in (0, 1, 2):
+    for tau in range(6):
         pos = np.nonzero(t == tau)[0]
         out.extend((int(p), tau) for p in pos)
     return out
