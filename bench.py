@@ -26,7 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-TIER_TOKEN_BYTES = {0: 386, 1: 322, 2: 298}       # radius + codes + fp16 values, head dim 128
+# radius + codes + values per token-head (head dim 128): fp16 values (tiers
+# 0-2) or V8 values, 4 scale bytes + 128 codes (tiers 3-5)
+TIER_TOKEN_BYTES = {0: 386, 1: 322, 2: 298, 3: 262, 4: 198, 5: 174}
+TIERS = range(6)
 DENSE_TOKEN_BYTES = 512
 METRIC = "ADA decode KV-tokens/sec and achieved HBM GB/s (% of peak) at 32k–128k ctx"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -45,6 +48,10 @@ def parse():
                     help="time the fused append + decode step against append then decode")
     ap.add_argument("--repack", type=float, default=0.0, metavar="FRAC",
                     help="time ada_repack of the packed cache to FRAC of its current bytes instead")
+    ap.add_argument("--repack-mask", type=int, default=0,
+                    help="RDR tier mask of the re-pack (0: T8, T4, T2; 56: the V8 tiers)")
+    ap.add_argument("--v8", action="store_true",
+                    help="store every kept token's values in V8 (tiers 3-5: the same keys, 8-bit values)")
     ap.add_argument("--queries", type=int, default=1,
                     help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -102,26 +109,28 @@ def main():
 
     torch.cuda.set_device(0)
     w = build_workload(args.workload, torch, ada, W)
+    if args.v8:
+        w["tiers"] = np.where(w["tiers"] >= 0, w["tiers"] + 3, -1).astype(np.int8)
     P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
     G = Hq // Hkv
     tiers = w["tiers"]
-    kept = {t: int((tiers == t).sum()) for t in (0, 1, 2)}
+    kept = {t: int((tiers == t).sum()) for t in TIERS}
     kept_total = sum(kept.values())
     rows = B * Hkv
-    pages_by_tier = {t: 0 for t in (0, 1, 2)}
+    pages_by_tier = {t: 0 for t in TIERS}
     max_row = 0
     for b in range(B):
         for h in range(Hkv):
             rp = 0
-            for t in (0, 1, 2):
+            for t in TIERS:
                 n = int((tiers[b, h] == t).sum())
                 pages_by_tier[t] += -(-n // P)
                 rp += -(-n // P)
             max_row = max(max_row, rp)
     n_pages = sum(pages_by_tier.values())
-    units = sum(pages_by_tier[t] * ada.block_bytes(t, P) // 16 for t in (0, 1, 2))
+    units = sum(pages_by_tier[t] * ada.block_bytes(t, P) // 16 for t in TIERS)
 
-    cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages)
+    cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages, value_tiers=args.v8)
     if args.append:
         append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
         return
@@ -246,9 +255,9 @@ def main():
         read_gbps[variant] = nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
-    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in (0, 1, 2)) + 12 * n_pages + B * Q * Hq * 128 * 4
+    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in TIERS) + 12 * n_pages + B * Q * Hq * 128 * 4
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload) if Q == 1 else None
+    traffic = measured_traffic(args.workload + ("_v8" if args.v8 else "")) if Q == 1 else None
     value = kept_total / (ms_step * 1e-3)
 
     result = {
@@ -267,8 +276,9 @@ def main():
         "config": {
             "workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
             "context": int(w["ctx_len"].max()), "page_size": P, "kept_token_heads": kept_total,
-            "kept_by_tier_T8_T4_T2": [kept[0], kept[1], kept[2]],
-            "pages_by_tier_T8_T4_T2": [pages_by_tier[0], pages_by_tier[1], pages_by_tier[2]],
+            "kept_by_tier": [kept[t] for t in TIERS],        # tier ids 0-5: T8, T4, T2, T8V8, T4V8, T2V8
+            "pages_by_tier": [pages_by_tier[t] for t in TIERS],
+            "values": "V8" if args.v8 else "fp16",
             "decode_chunk_pages": cfg.decode_chunk_pages, "queries_per_sequence": Q,
         },
         "roofline": {
@@ -346,8 +356,11 @@ def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
     args.repack times each sequence's current bytes, with the utilities of one
     ada_decode_utility step.  Each timed step resets the destination
     (ada_cache_init) and re-packs; the destination is checked against the
-    budget afterwards."""
+    budget afterwards.  With --repack-mask the destination tiers are the
+    mask's (56: fp16 tiers re-packed into V8 tiers)."""
     P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
+    if args.repack_mask:
+        cfg = ada.make_config(P, Hq, Hkv, rdr_tier_mask=args.repack_mask, value_tiers=True)
     src = ada.Cache(cfg, B, max_row, n_pages, units)
     dst = ada.Cache(cfg, B, max_row, n_pages, units)
     ada.cache_init(src)
@@ -357,8 +370,8 @@ def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
     torch.cuda.empty_cache()
     util = torch.zeros((n_pages, P), dtype=torch.float32, device="cuda")
     ada.decode_utility(src, torch.from_numpy(w["q"]).cuda(), w["scale"], util)
-    rate = {t: ada.block_bytes(t, P) // P + 256 for t in (0, 1, 2)}
-    cur = [sum(rate[t] * int((w["tiers"][b] == t).sum()) for t in (0, 1, 2)) for b in range(B)]
+    rate = TIER_TOKEN_BYTES
+    cur = [sum(rate[t] * int((w["tiers"][b] == t).sum()) for t in TIERS) for b in range(B)]
     budget = [int(args.repack * c) for c in cur]
     ws = ada.repack_workspace(src, B)
 
@@ -379,7 +392,7 @@ def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
     assert ada.read_status(dst.status) == ada.OK
     h = dst.host()
     kept_total = sum(kept.values())
-    kept_after = {t: 0 for t in (0, 1, 2)}
+    kept_after = {t: 0 for t in TIERS}
     used = [0] * B
     for row in range(B * Hkv):
         for page in h["page_table"][row, : h["num_pages"][row]]:
@@ -394,8 +407,9 @@ def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "page_size": P,
                    "budget_fraction": args.repack, "kept_token_heads_before": kept_total,
-                   "kept_by_tier_before": {str(t): kept[t] for t in (0, 1, 2)},
-                   "kept_by_tier_after": {str(t): kept_after[t] for t in (0, 1, 2)}},
+                   "rdr_tier_mask": cfg.rdr_tier_mask or 7,
+                   "kept_by_tier_before": {str(t): kept[t] for t in TIERS},
+                   "kept_by_tier_after": {str(t): kept_after[t] for t in TIERS}},
         "bytes_before": sum(cur), "bytes_after": sum(used), "budget_bytes": sum(budget),
     }), flush=True)
 

@@ -34,7 +34,7 @@ class Config(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("rdr_tier_mask", ctypes.c_uint32), ("decode_chunk_pages", ctypes.c_int32),
-                ("pair_layout", ctypes.c_int32)]
+                ("pair_layout", ctypes.c_int32), ("value_tiers", ctypes.c_int32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -141,12 +141,14 @@ def block_bytes(tier, page_size):
     return int(lib().ada_block_bytes(tier, page_size))
 
 
+NUM_TIERS = 6   # T8, T4, T2 (fp16 values), T8V8, T4V8, T2V8 (V8 values)
 PAIRS_ADJACENT, PAIRS_HALF_SPLIT = 0, 1   # pair j = (x[2j], x[2j+1]) or (x[j], x[j+64])
 
 
 def make_config(page_size, num_q_heads, num_kv_heads, rdr_tier_mask=0, decode_chunk_pages=0,
-                pair_layout=PAIRS_ADJACENT):
-    return Config(D, page_size, num_q_heads, num_kv_heads, rdr_tier_mask, decode_chunk_pages, pair_layout)
+                pair_layout=PAIRS_ADJACENT, value_tiers=False):
+    return Config(D, page_size, num_q_heads, num_kv_heads, rdr_tier_mask, decode_chunk_pages, pair_layout,
+                  int(bool(value_tiers)))
 
 
 class Cache:
@@ -159,7 +161,7 @@ class Cache:
         rows = num_seqs * cfg.num_kv_heads
         self.page_table = torch.zeros((rows, max_pages_per_head), dtype=torch.int32, device=device)
         self.num_pages = torch.zeros(rows, dtype=torch.int32, device=device)
-        self.open_page = torch.full((rows, 3), -1, dtype=torch.int32, device=device)
+        self.open_page = torch.full((rows, NUM_TIERS), -1, dtype=torch.int32, device=device)
         self.page_meta = torch.zeros((page_capacity, 8), dtype=torch.uint8, device=device)
         self.code_arena = torch.zeros(arena_capacity16 * 16, dtype=torch.uint8, device=device)
         self.value_pool = torch.zeros((page_capacity, P * D), dtype=torch.int16, device=device)

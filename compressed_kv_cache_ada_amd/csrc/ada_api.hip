@@ -35,8 +35,10 @@ ada_status_t check_cfg(const ada_config_t *cfg) {
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return ADA_EUNSUPPORTED;
     if (cfg->decode_chunk_pages < 0) return ADA_EINVAL;
-    if (cfg->rdr_tier_mask > 7u) return ADA_EINVAL;
+    if (cfg->rdr_tier_mask >> kNumTiers) return ADA_EINVAL;
     if (cfg->pair_layout != ADA_PAIRS_ADJACENT && cfg->pair_layout != ADA_PAIRS_HALF_SPLIT) return ADA_EINVAL;
+    if (cfg->value_tiers != 0 && cfg->value_tiers != 1) return ADA_EINVAL;
+    if (!cfg->value_tiers && (cfg->rdr_tier_mask >> 3)) return ADA_EINVAL;   // V8 tiers need value_tiers
     return ADA_OK;
 }
 
@@ -130,6 +132,7 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.logit_buf = nullptr;
     a.util = nullptr;
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
+    a.value_tiers = cfg->value_tiers;
     return a;
 }
 
@@ -142,7 +145,7 @@ struct AppendWs {
 
 AppendWs append_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, void *ws) {
     AppendWs w;
-    const size_t nkeys = (size_t)cache->num_seqs * cfg->num_kv_heads * 3;
+    const size_t nkeys = (size_t)cache->num_seqs * cfg->num_kv_heads * kNumTiers;
     Carver c(ws);
     w.key_cnt = c.take<int32_t>(nkeys);
     w.key_c0 = c.take<int32_t>(nkeys);
@@ -191,6 +194,7 @@ AppendLaunch make_append(const ada_config_t *cfg, const ada_cache_t *cache, int3
     a.new_pages = w.new_pages;
     a.n_new = w.n_new;
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
+    a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return a;
 }
 
@@ -206,10 +210,10 @@ PackWs pack_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws)
     const size_t rows = (size_t)B * cfg->num_kv_heads;
     w.n_tiles = (int)((stride + 1023) / 1024);
     Carver c(ws);
-    w.tile_counts = c.take<int32_t>(rows * w.n_tiles * 3);
-    w.row_counts = c.take<int32_t>(rows * 3);
-    w.row_base = c.take<int32_t>(rows * 3);
-    w.row_unit = c.take<int64_t>(rows * 3);
+    w.tile_counts = c.take<int32_t>(rows * w.n_tiles * kNumTiers);
+    w.row_counts = c.take<int32_t>(rows * kNumTiers);
+    w.row_base = c.take<int32_t>(rows * kNumTiers);
+    w.row_unit = c.take<int64_t>(rows * kNumTiers);
     w.dest_page = c.take<int32_t>(rows * stride);
     w.dest_slot = c.take<int32_t>(rows * stride);
     w.range = c.take<int32_t>(2);
@@ -244,12 +248,13 @@ RdrWs rdr_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
 }
 
 // RDR upgrade steps of the enabled tiers (rate order); EUNSUPPORTED when the
-// savings per byte do not strictly decrease.
+// savings per byte do not strictly decrease.  Distortion of a tier:
+// 2^-(tb + sb), plus 2^-14 for V8 values.
 ada_status_t rdr_steps(uint32_t mask, int *n_steps, int32_t *step_tier, int64_t *dR, double *c) {
-    int ids[3], n = 0;
-    for (int t = 0; t < 3; ++t)
+    int ids[kNumTiers], n = 0;
+    for (int t = 0; t < kNumTiers; ++t)
         if (mask & (1u << t)) ids[n++] = t;
-    auto rate = [](int t) { return (int64_t)(2 + 8 * (tier_tb(t) + tier_sb(t)) + 256); };
+    auto rate = [](int t) { return tier_rate(t); };
     for (int i = 1; i < n; ++i)   // insertion sort by rate
         for (int j = i; j > 0 && rate(ids[j]) < rate(ids[j - 1]); --j) {
             const int tmp = ids[j];
@@ -261,7 +266,7 @@ ada_status_t rdr_steps(uint32_t mask, int *n_steps, int32_t *step_tier, int64_t 
     for (int i = 0; i < n; ++i) {
         const int t = ids[i];
         const int64_t R = rate(t);
-        const double D = ldexp(1.0, -(tier_tb(t) + tier_sb(t)));
+        const double D = ldexp(1.0, -(tier_tb(t) + tier_sb(t))) + (tier_v8(t) ? ldexp(1.0, -14) : 0.0);
         if (R <= prevR || D >= prevD) return ADA_EUNSUPPORTED;
         dR[i] = R - prevR;
         c[i] = (prevD - D) / (double)dR[i];
@@ -291,7 +296,7 @@ const char *ada_status_str(ada_status_t s) {
 }
 
 int64_t ada_block_bytes(int32_t tier, int32_t page_size) {
-    if (tier < 0 || tier > 2 || (page_size != 16 && page_size != 32)) return -1;
+    if (tier < 0 || tier >= kNumTiers || (page_size != 16 && page_size != 32)) return -1;
     return (int64_t)block16(tier, page_size) * 16;
 }
 
@@ -618,6 +623,7 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_of_slot = nullptr;
     a.src_of_slot_pages = 0;
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
+    a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return hip_status(launch_pack(a, s));
 }
 
@@ -688,10 +694,18 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     it.num_pages = src->num_pages;
     it.page_meta = src->page_meta;
     it.util = util;
-    auto rate = [](int t) { return 2 + 8 * (tier_tb(t) + tier_sb(t)) + 256; };
-    for (int t = 0; t < 3; ++t) {   // steps up to the tier's rate: the tier or cheaper
+    // the codes hold nothing finer than they are: each tier of the chain
+    // must hold no fewer angle, magnitude and value bits than the one
+    // before, and a token may take the chain's tiers holding no more bits
+    // than its own (a prefix of the chain)
+    auto within = [](int a, int b) {
+        return tier_tb(a) <= tier_tb(b) && tier_sb(a) <= tier_sb(b) && tier_vb(a) <= tier_vb(b);
+    };
+    for (int k = 1; k < ra.n_steps; ++k)
+        if (!within(ra.step_tier[k - 1], ra.step_tier[k])) return ADA_EUNSUPPORTED;
+    for (int t = 0; t < kNumTiers; ++t) {
         int lv = 0;
-        while (lv < ra.n_steps && rate(ra.step_tier[lv]) <= rate(t)) ++lv;
+        while (lv < ra.n_steps && within(ra.step_tier[lv], t)) ++lv;
         it.level_of_tier[t] = (int8_t)lv;
     }
     it.util_v = r.util_v;
@@ -760,6 +774,7 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_of_slot = r.src_of_slot;
     a.src_of_slot_pages = r.src_of_slot_pages;
     a.half_pairs = 0;   // codes are transcoded, no key is read
+    a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return hip_status(launch_pack(a, s));
 }
 

@@ -14,11 +14,31 @@ constexpr int kD = 128;       // head dimension
 constexpr int kPairs = 64;    // 2-D pairs per key
 constexpr int kMaxChunkPages = 256;   // page list of a split-K work-group (in LDS)
 
-// Tier table in id order: angle bits, magnitude bits.
-__host__ __device__ constexpr int tier_tb(int t) { return t == 0 ? 8 : (t == 1 ? 4 : 2); }
-__host__ __device__ constexpr int tier_sb(int t) { return t == 0 ? 8 : (t == 1 ? 4 : 3); }
+// Tier table in id order: angle bits, magnitude bits, value format.  Ids
+// 3-5 carry the keys of ids 0-2 with V8 values instead of fp16.
+constexpr int kNumTiers = ADA_NUM_TIERS;
+__host__ __device__ constexpr int key_tier(int t) { return t >= 3 ? t - 3 : t; }
+__host__ __device__ constexpr int tier_tb(int t) { return key_tier(t) == 0 ? 8 : (key_tier(t) == 1 ? 4 : 2); }
+__host__ __device__ constexpr int tier_sb(int t) { return key_tier(t) == 0 ? 8 : (key_tier(t) == 1 ? 4 : 3); }
+__host__ __device__ constexpr bool tier_v8(int t) { return t >= 3; }
+__host__ __device__ constexpr int tier_vb(int t) { return tier_v8(t) ? 8 : 16; }
+// bytes per token and KV head: radius, codes, values (fp16, or V8: 4 scale
+// bytes + 128 codes)
+__host__ __device__ constexpr int64_t tier_rate(int t) {
+    return 2 + 8 * (tier_tb(t) + tier_sb(t)) + (tier_v8(t) ? 132 : 256);
+}
 // code block of one page in 16-byte units: P * (2 + 8 tb + 8 sb) / 16
 __host__ __device__ constexpr int block16(int t, int P) { return P * (2 + 8 * tier_tb(t) + 8 * tier_sb(t)) / 16; }
+// V8 value page (in the page's value-pool slot, as bytes): per 8-token group,
+// [8 tokens][4 dimension blocks] scale bytes (a token's four scales are one
+// 4-byte word), then [128 dims][8 tokens] codes
+constexpr int kV8Group = 1056;
+constexpr int kV8Codes = 32;   // offset of the codes inside a group
+
+// a pair of fp16 values, both finite
+__host__ __device__ inline bool values_finite(uint32_t two_halves) {
+    return (two_halves & 0x7C00u) != 0x7C00u && (two_halves & 0x7C000000u) != 0x7C000000u;
+}
 
 // fp16 bits -> float
 __device__ __forceinline__ float h2f(uint32_t bits16) {
@@ -76,6 +96,7 @@ struct DecodeLaunch {
     float *logit_buf;
     float *util;
     int32_t half_pairs;   // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
+    int32_t value_tiers;  // the cache may hold pages of tiers 3-5 (V8 values)
 };
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s);
@@ -133,10 +154,10 @@ struct PackLaunch {
     int64_t *alloc;
     int32_t *status;
     // workspace
-    int32_t *tile_counts;   // [rows][n_tiles][3]
-    int32_t *row_counts;    // [rows][3]
-    int32_t *row_base;      // [rows][3] first page id of (row, tier)
-    int64_t *row_unit;      // [rows][3] first code unit of (row, tier)
+    int32_t *tile_counts;   // [rows][n_tiles][kNumTiers]
+    int32_t *row_counts;    // [rows][kNumTiers]
+    int32_t *row_base;      // [rows][kNumTiers] first page id of (row, tier)
+    int64_t *row_unit;      // [rows][kNumTiers] first code unit of (row, tier)
     int32_t *dest_page, *dest_slot;   // [B*Hkv*stride]
     int32_t *new_pages;     // [page upper bound] list of allocated pages
     int32_t *n_new;         // [1]
@@ -152,6 +173,7 @@ struct PackLaunch {
     int4 *src_of_slot;              // [src_of_slot_pages][P] source {page, slot, tier, code_off16} per new slot
     int64_t src_of_slot_pages;
     int32_t half_pairs;             // key pair layout (see EncodeLaunch)
+    int32_t n_tiers;                // tier ids below this are accepted (3, or 6 with value tiers)
 };
 hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
 // pages a re-pack may open per row: sum over three tiers of ceil(n_tau / P)
@@ -181,6 +203,7 @@ struct AppendLaunch {
     int32_t *new_pages;  // [n]
     int32_t *n_new;      // [1]
     int32_t half_pairs;  // key pair layout (see EncodeLaunch)
+    int32_t n_tiers;     // tier ids below this are accepted (3, or 6 with value tiers)
 };
 // append: book destinations, update metadata, zero new pages, then (with
 // encode) encode and write the keys; without encode the caller encodes
@@ -198,9 +221,9 @@ struct RdrLaunch {
     const float *utility;
     int8_t *tier_out;
     int32_t *status;
-    int32_t step_tier[3];
-    int64_t dR[3];
-    double c[3];
+    int32_t step_tier[kNumTiers];
+    int64_t dR[kNumTiers];
+    double c[kNumTiers];
     // workspace
     unsigned long long *hist;   // [B][256]
     unsigned long long *prefix; // [B]
@@ -222,7 +245,7 @@ struct RepackItemsLaunch {
     const int32_t *page_table, *num_pages;
     const ada_page_meta_t *page_meta;
     const float *util;          // [page_capacity][P]
-    int8_t level_of_tier[3];    // steps up to and including each tier
+    int8_t level_of_tier[kNumTiers];   // chain tiers holding no more bits than each tier
     float *util_v;
     int8_t *cap_v;
     int32_t *ctx_v;

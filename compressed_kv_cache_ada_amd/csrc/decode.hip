@@ -58,6 +58,7 @@ struct CodeRegs {
     uint2 h;
     uint32_t r;         // fp16 radius bits
     const uint8_t *c;   // the token's first angle unit
+    uint32_t vs;        // V8 pages: the token's four block scales (bytes)
 };
 
 // Per-work-group LUT layout, per pair j with NC codes: slices of SW =
@@ -233,9 +234,10 @@ struct CodeStage {
     uint32_t r[64];
 };
 
-template <int G, int P, int NW, bool APPEND>
+template <int G, int P, int NW, bool APPEND, bool VT>
 struct AdaPolicy {
     static constexpr bool kStaged = true;
+    static constexpr bool kValueTiers = VT;   // the cache may hold pages of tiers 3-5 (V8 values)
     struct Smem {
         float lut4[64 * 16 * G];   // 4-bit angle grid, lut_index<G, 16> layout
         float lut2[64 * 4 * G];    // 2-bit angle grid, lut_index<G, 4> layout
@@ -245,10 +247,13 @@ struct AdaPolicy {
         float q8[64 * G * 2];      // [j][g][x|y] query pairs (T8, factorised)
         CodeStage st[NW];          // the next group's code units, per wavefront
         uint32_t enc_words[2][16]; // bit-string packing of the fused append's key
+        // V8 scale word of each token of the next group (lane = token)
+        uint32_t vs[NW][VT ? 64 : 1];
     };
     const int32_t *num_pages_;
     const ada_page_meta_t *page_meta;
     const uint8_t *arena;
+    const uint16_t *value_pool;
     const float *q;
     int32_t Q, Hq, Gr;   // queries per sequence, query heads, query heads per KV head
     int32_t half;        // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
@@ -332,12 +337,26 @@ struct AdaPolicy {
 
     using Codes = CodeRegs;
 
+    // the scale words of tokens 8 blk .. 8 blk + 7 of the current group,
+    // from the lanes holding those tokens
+    __device__ void scale_words(const Codes &k, int blk, uint32_t (&sd)[8]) const {
+        if constexpr (VT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sd[j] = (uint32_t)__shfl((int)k.vs, 8 * blk + j, 64);
+        }
+    }
+
     // Issues the direct-to-LDS loads of a group's code units into wavefront
     // w's stage (lane = token, wave-uniform destinations).  Branch-free:
-    // every address stays inside the lane's own code block.
-    __device__ void stage(Smem &s, int w, uint2 meta, int slot) const {
+    // every address stays inside the lane's own code block (and, for the
+    // V8 scale word, inside its page's value slot).
+    __device__ void stage(Smem &s, int w, uint2 meta, int page, int slot) const {
+        if constexpr (VT) {
+            const uint8_t *vb = reinterpret_cast<const uint8_t *>(value_pool + (size_t)page * P * kD);
+            __builtin_amdgcn_global_load_lds(vb + (slot >> 3) * kV8Group + (slot & 7) * 4, &s.vs[w][0], 4, 0, 0);
+        }
         const uint8_t *blk = arena + (size_t)meta.y * 16;
-        const int tier = meta.x & 0xFF;
+        const int tier = key_tier(meta.x & 0xFF);
         const uint8_t *c = blk + 2 * P + slot * 16;
         const bool t2 = tier == ADA_TIER_T2;
         const int so = (tier == ADA_TIER_T4) ? 32 * P : 64 * P;   // first magnitude unit
@@ -362,6 +381,7 @@ struct AdaPolicy {
         k.h = (slot & 1) ? make_uint2(hh.z, hh.w) : make_uint2(hh.x, hh.y);
         const uint32_t rr = st.r[lane];
         k.r = (slot & 1) ? rr >> 16 : rr & 0xFFFFu;
+        if constexpr (VT) k.vs = s.vs[w][lane];
         // the slot offset is made opaque here so that arena + slot offset (a
         // 64-bit per-lane value) is not hoisted out of the group loop, where
         // it would hold two more registers for the whole loop
@@ -372,7 +392,7 @@ struct AdaPolicy {
     }
 
     __device__ void logits(const Smem &s, const Codes &k, uint2 meta, bool valid, float (&lg)[G]) const {
-        const int tier = meta.x & 0xFF;
+        const int tier = key_tier(meta.x & 0xFF);
         if (__any(valid && tier == ADA_TIER_T4)) {
             if (valid && tier == ADA_TIER_T4) logits_t4<G>(k, s.lut4, mul, lg);
         }
@@ -386,9 +406,11 @@ struct AdaPolicy {
 };
 
 // MODE: 0 plain, 1 fused append, 2 utility emission
-template <int G, int P, int NW, int WPE, int MODE>
+// VT: the cache may hold V8-value pages (a separate instantiation, so that
+// caches of fp16 tiers only run the kernel without the V8 paths)
+template <int G, int P, int NW, int WPE, int MODE, bool VT>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLaunch a) {
-    using Pol = AdaPolicy<G, P, NW, MODE == 1>;
+    using Pol = AdaPolicy<G, P, NW, MODE == 1, VT>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
     constexpr size_t RAW = sizeof(typename Pol::Smem) > RED ? sizeof(typename Pol::Smem) : RED;
     __shared__ __align__(16) unsigned char raw[RAW];   // policy tables, later the wave-merge buffer
@@ -397,6 +419,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.num_pages_ = a.num_pages;
     pol.page_meta = a.page_meta;
     pol.arena = a.arena;
+    pol.value_pool = a.value_pool;
     pol.q = a.q;
     pol.Q = a.Q;
     pol.Hq = a.Hq;
@@ -502,23 +525,24 @@ __global__ __launch_bounds__(256) void build_lut_kernel(const float *q, float *l
     }
 }
 
-template <int G, int P>
-hipError_t launch_gp(const DecodeLaunch &a, hipStream_t s) {
+template <int G, int P, bool VT>
+hipError_t launch_gpv(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
     constexpr int WPE = decode_waves_per_simd(G);
     const dim3 grid(a.S, a.Hkv, a.B), block(NW * 64);
     if (a.app_page)
-        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 1>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 1, VT>), grid, block, 0, s, a);
     else if (a.logit_buf)
-        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 2>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 2, VT>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 0>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 0, VT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_g(const DecodeLaunch &a, hipStream_t s) {
-    return a.P == 16 ? launch_gp<G, 16>(a, s) : launch_gp<G, 32>(a, s);
+    if (a.value_tiers) return a.P == 16 ? launch_gpv<G, 16, true>(a, s) : launch_gpv<G, 32, true>(a, s);
+    return a.P == 16 ? launch_gpv<G, 16, false>(a, s) : launch_gpv<G, 32, false>(a, s);
 }
 
 }  // namespace

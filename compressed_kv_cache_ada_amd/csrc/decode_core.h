@@ -57,6 +57,30 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// V8 values -> fp16 MFMA operand.  Scale words of 8 tokens (byte k: the
+// token's scale s of dimension block k) -> the half2 factors 2^(s - 133) of
+// token pairs, exact (the fp32 bits (s - 6) << 23 are that power of two; it
+// is an fp16 number since s >= 109).
+__device__ __forceinline__ void v8_scale_pairs(const uint32_t (&sd)[8], int k, uint32_t (&sp)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t b0 = (sd[2 * i] >> (8 * k)) & 0xFFu, b1 = (sd[2 * i + 1] >> (8 * k)) & 0xFFu;
+        const float f0 = __builtin_bit_cast(float, (b0 - 6u) << 23), f1 = __builtin_bit_cast(float, (b1 - 6u) << 23);
+        sp[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1));
+    }
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// two tokens' int8 codes (bytes 0 and 1 of w) times their scale pair: two
+// fp16 values of the MFMA A operand (exact products)
+__device__ __forceinline__ uint32_t v8_pair(uint32_t w, uint32_t scale_pair) {
+    half2_t c;
+    c[0] = (_Float16)(int)(int8_t)w;
+    c[1] = (_Float16)(int)(int8_t)(w >> 8);
+    return __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(half2_t, scale_pair));
+}
+
 // Wavefront sum in the same pattern (a fixed order, identical in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<0xB1>(v);
@@ -155,8 +179,13 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //                                              the chunk is read; returns
 //                                              (uniformly) whether a barrier
 //                                              must follow
+//   kValueTiers: pages of tiers 3-5 hold V8 values (see include/ada.h)
+//     void scale_words(codes, blk, sd[8])     the V8 scale words of the 8
+//                                              tokens of block blk of the
+//                                              current group
 //   kStaged = true:
-//     void stage(smem, w, meta, slot)          request a group's codes into
+//     void stage(smem, w, meta, page, slot)    request a group's codes (and
+//                                              V8 scale words) into
 //                                              wavefront w's LDS stage
 //     Codes unstage(smem, w, meta, slot, lane) read them (after they landed)
 //   kStaged = false:
@@ -208,13 +237,17 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         valid = pvalid && slot < (int)((meta.x >> 8) & 0xFF);
         return meta;
     };
+    auto group_page = [&](int g) {
+        const int gbase = g * TPG;
+        return cs.pages[gbase + pg] >= 0 ? cs.pages[gbase + pg] : cs.pages[gbase];
+    };
     // staged policies: the first group's code units are requested before
     // the tables are built
     if constexpr (Pol::kStaged) {
         if (w < n_groups) {
             bool v;
             const uint2 m0 = group_meta(w, v);
-            pol.stage(ps, w, m0, slot);
+            pol.stage(ps, w, m0, group_page(w), slot);
         }
     }
     pol.build(ps, tid, NT);
@@ -250,7 +283,7 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
             if (grp + NW < n_groups) {
                 bool vn;
                 const uint2 mn = group_meta(grp + NW, vn);
-                pol.stage(ps, w, mn, slot);
+                pol.stage(ps, w, mn, group_page(grp + NW), slot);
             }
         } else {
             const int pidx = gbase + pg;
@@ -279,16 +312,36 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         // 3. values -> MFMA A operands, issued after the logit arithmetic so
         //    they are not held in registers through it (other wavefronts'
         //    work covers their latency).  A block past the row's last page is
-        //    read from the group's first page instead: weight 0.
+        //    read from the group's first page instead: weight 0.  A V8 page
+        //    gives 8 code bytes per dimension (.x, .y) and the block's
+        //    scale dword t (.z of tile t), converted before the MFMAs.
         uint4 va[2][8];
+        bool v8[2] = {false, false};
+        // the lane's place in the MFMA operands, made opaque here so that the
+        // per-lane value offsets are formed in the loop rather than hoisted
+        // out of it (they would hold registers for the whole loop)
+        uint32_t ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int vq = ln >> 4, vh = ln & 15;   // kq, n_head
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            const int blk = 4 * kc + kq;            // 8-token block of the group
-            const int vpage = cs.pages[gbase + blk / KB];
-            const uint16_t *base =
-                a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gbase]) * P * kD + (blk % KB) * 1024 + n_head * 8;
+            const int blk = 4 * kc + vq;            // 8-token block of the group
+            const int pidx = cs.pages[gbase + blk / KB] >= 0 ? gbase + blk / KB : gbase;
+            const uint8_t *vbytes = reinterpret_cast<const uint8_t *>(a.value_pool + (size_t)cs.pages[pidx] * P * kD);
+            if constexpr (Pol::kValueTiers) {
+                // V8 page: 16 bytes from the lane's dimension's 8 code bytes
+                // (the 8 after it belong to the next dimension, unused); the
+                // same instructions as the fp16 loads, other addresses
+                v8[kc] = tier_v8(cs.meta[pidx].x & 0xFF);
+                const uint8_t *b16 = vbytes + (blk % KB) * 2048 + vh * 16;
+                const uint8_t *b8 = vbytes + (blk % KB) * kV8Group + kV8Codes + vh * 8;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
+                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(v8[kc] ? b8 + t * 128 : b16 + t * 256);
+            } else {
+                const uint8_t *base = vbytes + (blk % KB) * 2048 + vh * 16;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 256);
+            }
         }
 
         // 4. online softmax, weights to LDS as fp16 hi + lo
@@ -313,13 +366,36 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         for (int t = 0; t < 8; ++t) acc[t] *= alpha_n;
         wave_lds_sync();
 
-        // 5. O^T += V^T P^T on the matrix cores
+        // 5. O^T += V^T P^T on the matrix cores (V8 lanes: codes x scales ->
+        //    fp16 first, tile t using dimension block t / 2)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             half8_t bh = {}, bl = {};
             if (n_head < G) {
                 bh = *reinterpret_cast<const half8_t *>(&cs.pb[w][0][n_head][32 * kc + 8 * kq]);
                 bl = *reinterpret_cast<const half8_t *>(&cs.pb[w][1][n_head][32 * kc + 8 * kq]);
+            }
+            if constexpr (Pol::kValueTiers) {
+                // codes x scales -> fp16 in place; tiles 2k, 2k+1 use dimension
+                // block k.  The scale words come from other lanes, so they
+                // are gathered with every lane active.
+                uint32_t sd[8];
+                if (__any(v8[kc])) pol.scale_words(codes, 4 * kc + vq, sd);
+                if (v8[kc]) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uint32_t sp[4];
+                        v8_scale_pairs(sd, k, sp);
+#pragma unroll
+                        for (int t = 2 * k; t < 2 * k + 2; ++t) {
+                            const uint32_t lo = va[kc][t].x, hi = va[kc][t].y;
+                            va[kc][t].w = v8_pair(hi >> 16, sp[3]);
+                            va[kc][t].z = v8_pair(hi, sp[2]);
+                            va[kc][t].y = v8_pair(lo >> 16, sp[1]);
+                            va[kc][t].x = v8_pair(lo, sp[0]);
+                        }
+                    }
+                }
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t)

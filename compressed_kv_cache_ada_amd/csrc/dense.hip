@@ -18,6 +18,7 @@ using core::ldg;
 template <int G, int P>
 struct DensePolicy {
     static constexpr bool kStaged = false;
+    static constexpr bool kValueTiers = false;   // fp16 values only
     struct Smem {
         float qd[kD * G];   // [d][g], pre-multiplied by scale * log2(e)
     };

@@ -12,6 +12,7 @@ namespace ada {
 namespace {
 
 using enc::f64_to_f16_rne_sat;
+using enc::v8_value_bits;
 using enc::read_status;
 using enc::set_status;
 
@@ -149,52 +150,97 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
             uint8_t *dblk = a.arena + (size_t)m.code_off16 * 16;
             const int k = threadIdx.x;
             const int4 e = k < count ? ent[k] : make_int4(0, 0, 0, 0);
-            const int st = e.z;
-            if (k >= count || st > tier) {   // past the count; or an upgrade, which the caps rule out
-                if (k < count) set_status(a.status, ADA_EINTERNAL);
-                if (tier == 0) zero_token<0>(dblk, k, P);
-                else if (tier == 1) zero_token<1>(dblk, k, P);
+            // key tiers (0 T8, 1 T4, 2 T2) of source and destination
+            const int st = key_tier(e.z), dt = key_tier(tier);
+            const bool upgrade = k < count && (st > dt || (tier_v8(e.z) && !tier_v8(tier)));
+            if (k >= count || upgrade) {   // past the count; or an upgrade, which the caps rule out
+                if (upgrade) set_status(a.status, ADA_EINTERNAL);
+                if (dt == 0) zero_token<0>(dblk, k, P);
+                else if (dt == 1) zero_token<1>(dblk, k, P);
                 else zero_token<2>(dblk, k, P);
             } else {
                 const uint8_t *sblk = a.src_arena + (size_t)(uint32_t)e.w * 16;
                 const int sslot = e.y;
-                if (tier == 0) transcode_token<0, 0>(sblk, sslot, dblk, k, P);
-                else if (tier == 1 && st == 0) transcode_token<0, 1>(sblk, sslot, dblk, k, P);
-                else if (tier == 1) transcode_token<1, 1>(sblk, sslot, dblk, k, P);
+                if (dt == 0) transcode_token<0, 0>(sblk, sslot, dblk, k, P);
+                else if (dt == 1 && st == 0) transcode_token<0, 1>(sblk, sslot, dblk, k, P);
+                else if (dt == 1) transcode_token<1, 1>(sblk, sslot, dblk, k, P);
                 else if (st == 0) transcode_token<0, 2>(sblk, sslot, dblk, k, P);
                 else if (st == 1) transcode_token<1, 2>(sblk, sslot, dblk, k, P);
                 else transcode_token<2, 2>(sblk, sslot, dblk, k, P);
             }
         }
         uint16_t *dv = a.value_pool + (size_t)page * P * kD;
+        uint8_t *dvb = reinterpret_cast<uint8_t *>(dv);
         const int dim = threadIdx.x;
+        const bool dst_v8 = tier_v8(tier);
         for (int g = 0; g < P / 8; ++g) {
-            int2 e[8];
+            int4 e[8];   // source {page, slot, tier, -} of the group's tokens (page -1: empty slot)
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int sl = g * 8 + k;
-                e[k] = sl < count ? make_int2(ent[sl].x, ent[sl].y) : make_int2(-1, 0);
+                e[k] = sl < count ? ent[sl] : make_int4(-1, 0, 0, 0);
             }
+            // fp16 sources: one 16-byte value word (8 tokens of this dimension) each
             uint4 seg[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 seg[k] = make_uint4(0u, 0u, 0u, 0u);
-                if (e[k].x >= 0)
+                if (e[k].x >= 0 && !tier_v8(e[k].z))
                     seg[k] = *reinterpret_cast<const uint4 *>(a.src_value_pool + (size_t)e[k].x * P * kD +
                                                               (e[k].y >> 3) * 1024 + dim * 8);
             }
-            uint32_t w[4];
+            // each token's value in this dimension as fp16 bits (a V8 source
+            // is decoded: its values are fp16 numbers exactly)
+            uint32_t h[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int idx = e[k].y & 7;
-                const int q = idx >> 1;
-                const uint32_t word = q == 0 ? seg[k].x : q == 1 ? seg[k].y : q == 2 ? seg[k].z : seg[k].w;
-                const uint32_t h = (word >> ((idx & 1) * 16)) & 0xFFFFu;
-                if (k & 1) w[k >> 1] |= h << 16;
-                else w[k >> 1] = h;
+                if (e[k].x < 0) {
+                    h[k] = 0u;
+                } else if (tier_v8(e[k].z)) {
+                    const uint8_t *sb = reinterpret_cast<const uint8_t *>(a.src_value_pool + (size_t)e[k].x * P * kD) +
+                                        (e[k].y >> 3) * kV8Group;
+                    h[k] = v8_value_bits((int8_t)sb[kV8Codes + dim * 8 + idx], sb[idx * 4 + (dim >> 5)]);
+                } else {
+                    const int q = idx >> 1;
+                    const uint32_t word = q == 0 ? seg[k].x : q == 1 ? seg[k].y : q == 2 ? seg[k].z : seg[k].w;
+                    h[k] = (word >> ((idx & 1) * 16)) & 0xFFFFu;
+                }
             }
-            *reinterpret_cast<uint4 *>(dv + g * 1024 + dim * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (!dst_v8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[k] = h[2 * k] | (h[2 * k + 1] << 16);
+                *reinterpret_cast<uint4 *>(dv + g * 1024 + dim * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                // V8: per token, the exponent of its 32-dimension block (32
+                // consecutive lanes), then this dimension's code; empty slots
+                // stay zero
+                uint32_t cw[2] = {0u, 0u};
+                uint8_t sbytes[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    int m = (int)(h[k] & 0x7FFFu);
+                    m = max(m, __shfl_xor(m, 1, 64));
+                    m = max(m, __shfl_xor(m, 2, 64));
+                    m = max(m, __shfl_xor(m, 4, 64));
+                    m = max(m, __shfl_xor(m, 8, 64));
+                    m = max(m, __shfl_xor(m, 16, 64));
+                    const int ex = enc::v8_exponent((uint32_t)m);
+                    const uint32_t c = e[k].x >= 0 ? (uint32_t)(uint8_t)enc::v8_code(h[k], ex) : 0u;
+                    const uint32_t sbyte = e[k].x >= 0 ? (uint32_t)(ex + 127) : 0u;
+                    cw[k >> 2] |= c << (8 * (k & 3));
+                    sbytes[k] = (uint8_t)sbyte;
+                }
+                *reinterpret_cast<uint2 *>(dvb + g * kV8Group + kV8Codes + dim * 8) = make_uint2(cw[0], cw[1]);
+                if ((dim & 31) == 0)   // token k's scale of this block
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) dvb[g * kV8Group + k * 4 + (dim >> 5)] = sbytes[k];
+            }
         }
+        if (dst_v8)   // the rest of the page's value slot is zero
+            for (int i = (P / 8) * kV8Group / 16 + threadIdx.x; i < P * kD * 2 / 16; i += 128)
+                reinterpret_cast<uint4 *>(dvb)[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
@@ -220,13 +266,14 @@ __global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, co
 // ------------------------------------------------------------- pack
 constexpr int kTile = 1024;
 
-// per (row, tile): validate tiers, check kept keys are finite, count per tier
+// per (row, tile): validate tiers, check kept keys (and the values of V8
+// tokens) are finite, count per tier
 __global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
-    __shared__ int cnt[3];
+    __shared__ int cnt[kNumTiers];
     const int tile = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv;
     const int ctx = a.ctx_len_dev[b];
-    if (threadIdx.x < 3) cnt[threadIdx.x] = 0;
+    if (threadIdx.x < kNumTiers) cnt[threadIdx.x] = 0;
     __syncthreads();
     const int64_t rbase = (int64_t)row * a.stride;
     const int t0 = tile * kTile;
@@ -234,7 +281,7 @@ __global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
         const int t = t0 + i;
         if (t >= ctx) break;
         const int tv = a.tier[rbase + t];
-        if (tv < -1 || tv > 2) set_status(a.status, ADA_EINVAL);
+        if (tv < -1 || tv >= a.n_tiers) set_status(a.status, ADA_EINVAL);
         else if (tv >= 0) atomicAdd(&cnt[tv], 1);
     }
     // finiteness of kept keys: one wavefront per position (no keys when
@@ -244,28 +291,32 @@ __global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
     for (int i = wv; a.keys && i < kTile; i += 4) {
         const int t = t0 + i;
         if (t >= ctx) break;
-        if (a.tier[rbase + t] < 0) continue;
+        const int tv = a.tier[rbase + t];
+        if (tv < 0) continue;
         const float2 kk = *reinterpret_cast<const float2 *>(a.keys + (rbase + t) * kD + 2 * lane);
         bad |= !(isfinite(kk.x) && isfinite(kk.y));
+        if (tv < kNumTiers && tier_v8(tv))
+            bad |= !values_finite(*reinterpret_cast<const uint32_t *>(a.values + (rbase + t) * kD + 2 * lane));
     }
     if (__any(bad) && lane == 0) set_status(a.status, ADA_EINVAL);
     __syncthreads();
-    if (threadIdx.x < 3) a.tile_counts[((size_t)row * a.n_tiles + tile) * 3 + threadIdx.x] = cnt[threadIdx.x];
+    if (threadIdx.x < kNumTiers)
+        a.tile_counts[((size_t)row * a.n_tiles + tile) * kNumTiers + threadIdx.x] = cnt[threadIdx.x];
 }
 
 // per row: exclusive scan of tile counts (in place) and row totals
 __global__ __launch_bounds__(256) void pack_rowscan_kernel(PackLaunch a) {
     const int row = blockIdx.x;
-    if (threadIdx.x >= 3) return;
+    if (threadIdx.x >= kNumTiers) return;
     const int tau = threadIdx.x;
     int run = 0;
-    int32_t *tc = a.tile_counts + (size_t)row * a.n_tiles * 3;
+    int32_t *tc = a.tile_counts + (size_t)row * a.n_tiles * kNumTiers;
     for (int tl = 0; tl < a.n_tiles; ++tl) {
-        const int c = tc[tl * 3 + tau];
-        tc[tl * 3 + tau] = run;
+        const int c = tc[tl * kNumTiers + tau];
+        tc[tl * kNumTiers + tau] = run;
         run += c;
     }
-    a.row_counts[row * 3 + tau] = run;
+    a.row_counts[row * kNumTiers + tau] = run;
 }
 
 // single work-group: page and code-unit bases of every (row, tier), capacity
@@ -282,7 +333,7 @@ __global__ __launch_bounds__(1024) void pack_plan_kernel(PackLaunch a, int32_t *
     __syncthreads();
     if (bad) return;
     const int rows = a.B * a.Hkv;
-    const int n_ent = rows * 3;
+    const int n_ent = rows * kNumTiers;
     const int64_t a0 = a.alloc[0], a1 = a.alloc[1];
     for (int base = 0; base < n_ent; base += 1024) {
         const int i = base + threadIdx.x;
@@ -290,7 +341,7 @@ __global__ __launch_bounds__(1024) void pack_plan_kernel(PackLaunch a, int32_t *
         if (i < n_ent) {
             const int n = a.row_counts[i];
             pg = (n + a.P - 1) / a.P;
-            un = pg * block16(i % 3, a.P);
+            un = pg * block16(i % kNumTiers, a.P);
         }
         sp[threadIdx.x] = pg;
         su[threadIdx.x] = un;
@@ -323,18 +374,18 @@ __global__ __launch_bounds__(1024) void pack_plan_kernel(PackLaunch a, int32_t *
     }
     for (int r = threadIdx.x; r < rows; r += 1024) {
         int tot = 0;
-        for (int tau = 0; tau < 3; ++tau) tot += (a.row_counts[r * 3 + tau] + a.P - 1) / a.P;
+        for (int tau = 0; tau < kNumTiers; ++tau) tot += (a.row_counts[r * kNumTiers + tau] + a.P - 1) / a.P;
         if (tot > a.maxp) set_status(a.status, ADA_ENOSPC);
     }
     __syncthreads();
     if (read_status(a.status) != 0) return;
     for (int r = threadIdx.x; r < rows; r += 1024) {
         int tot = 0;
-        for (int tau = 0; tau < 3; ++tau) {
-            const int n = a.row_counts[r * 3 + tau];
+        for (int tau = 0; tau < kNumTiers; ++tau) {
+            const int n = a.row_counts[r * kNumTiers + tau];
             const int pg = (n + a.P - 1) / a.P;
             tot += pg;
-            a.open_page[r * 3 + tau] = (n % a.P != 0) ? a.row_base[r * 3 + tau] + pg - 1 : -1;
+            a.open_page[r * kNumTiers + tau] = (n % a.P != 0) ? a.row_base[r * kNumTiers + tau] + pg - 1 : -1;
         }
         a.num_pages[r] = tot;
     }
@@ -351,11 +402,11 @@ __global__ __launch_bounds__(256) void pack_pages_kernel(PackLaunch a) {
     if (read_status(a.status) != 0) return;
     const int row = blockIdx.x;
     int pos = 0;
-    for (int tau = 0; tau < 3; ++tau) {
-        const int n = a.row_counts[row * 3 + tau];
+    for (int tau = 0; tau < kNumTiers; ++tau) {
+        const int n = a.row_counts[row * kNumTiers + tau];
         const int pg = (n + a.P - 1) / a.P;
-        const int base = a.row_base[row * 3 + tau];
-        const int64_t ubase = a.row_unit[row * 3 + tau];
+        const int base = a.row_base[row * kNumTiers + tau];
+        const int64_t ubase = a.row_unit[row * kNumTiers + tau];
         for (int i = threadIdx.x; i < pg; i += 256) {
             const int page = base + i;
             a.page_table[(size_t)row * a.maxp + pos + i] = page;
@@ -373,33 +424,33 @@ __global__ __launch_bounds__(256) void pack_pages_kernel(PackLaunch a) {
 // per (row, tile): rank of every kept token within its (row, tier) ->
 // destination page and slot
 __global__ __launch_bounds__(256) void pack_dest_kernel(PackLaunch a) {
-    __shared__ int sc[3][256];
+    __shared__ int sc[kNumTiers][256];
     const int tile = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv;
     const int ctx = a.ctx_len_dev[b];
     const int64_t rbase = (int64_t)row * a.stride;
     const int t0 = tile * kTile + threadIdx.x * 4;
     if (read_status(a.status) != 0) return;
-    int tv[4], c[3] = {0, 0, 0};
+    int tv[4], c[kNumTiers] = {};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int t = t0 + k;
         tv[k] = (t < ctx && t < a.stride) ? a.tier[rbase + t] : -1;
         if (tv[k] >= 0) c[tv[k]]++;
     }
-    for (int tau = 0; tau < 3; ++tau) sc[tau][threadIdx.x] = c[tau];
+    for (int tau = 0; tau < kNumTiers; ++tau) sc[tau][threadIdx.x] = c[tau];
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-        int v[3] = {0, 0, 0};
+        int v[kNumTiers] = {};
         if (threadIdx.x >= off)
-            for (int tau = 0; tau < 3; ++tau) v[tau] = sc[tau][threadIdx.x - off];
+            for (int tau = 0; tau < kNumTiers; ++tau) v[tau] = sc[tau][threadIdx.x - off];
         __syncthreads();
-        for (int tau = 0; tau < 3; ++tau) sc[tau][threadIdx.x] += v[tau];
+        for (int tau = 0; tau < kNumTiers; ++tau) sc[tau][threadIdx.x] += v[tau];
         __syncthreads();
     }
-    int run[3];
-    for (int tau = 0; tau < 3; ++tau)
-        run[tau] = sc[tau][threadIdx.x] - c[tau] + a.tile_counts[((size_t)row * a.n_tiles + tile) * 3 + tau];
+    int run[kNumTiers];
+    for (int tau = 0; tau < kNumTiers; ++tau)
+        run[tau] = sc[tau][threadIdx.x] - c[tau] + a.tile_counts[((size_t)row * a.n_tiles + tile) * kNumTiers + tau];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int t = t0 + k;
@@ -407,7 +458,7 @@ __global__ __launch_bounds__(256) void pack_dest_kernel(PackLaunch a) {
         int dp = -1, ds = 0;
         if (tv[k] >= 0) {
             const int r = run[tv[k]]++;
-            dp = a.row_base[row * 3 + tv[k]] + r / a.P;
+            dp = a.row_base[row * kNumTiers + tv[k]] + r / a.P;
             ds = r % a.P;
         }
         a.dest_page[rbase + t] = dp;
@@ -431,7 +482,7 @@ struct AppendKernelArgs {
 
 __global__ __launch_bounds__(256) void append_init_kernel(AppendKernelArgs k) {
     const AppendLaunch &a = k.a;
-    const int nkeys = a.num_seqs * a.Hkv * 3;
+    const int nkeys = a.num_seqs * a.Hkv * kNumTiers;
     for (int i = blockIdx.x * 256 + threadIdx.x; i < nkeys; i += gridDim.x * 256) {
         const int op = a.open_page[i];
         a.key_cnt[i] = 0;
@@ -462,12 +513,15 @@ __global__ __launch_bounds__(256) void append_validate_kernel(AppendLaunch a) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     for (int i = blockIdx.x * 4 + wv; i < a.n; i += gridDim.x * 4) {
         const int s = req_seq(a, i), h = req_head(a, i), tau = a.tier[i];
-        const bool in_range = s >= 0 && s < a.num_seqs && h >= 0 && h < a.Hkv && tau < 3;
+        const bool in_range = s >= 0 && s < a.num_seqs && h >= 0 && h < a.Hkv && tau < a.n_tiers;
         const float2 kk = *reinterpret_cast<const float2 *>(a.keys + (int64_t)i * kD + 2 * lane);
-        const bool bad = __any(!(isfinite(kk.x) && isfinite(kk.y)));
+        bool bad_l = !(isfinite(kk.x) && isfinite(kk.y));
+        if (tau < kNumTiers && tier_v8(tau))
+            bad_l |= !values_finite(*reinterpret_cast<const uint32_t *>(a.values + (int64_t)i * kD + 2 * lane));
+        const bool bad = __any(bad_l);
         if (lane == 0) {
             if (!in_range || bad) set_status(a.status, ADA_EINVAL);
-            else atomicAdd(&a.key_cnt[(s * a.Hkv + h) * 3 + tau], 1);
+            else atomicAdd(&a.key_cnt[(s * a.Hkv + h) * kNumTiers + tau], 1);
         }
     }
 }
@@ -480,8 +534,8 @@ __global__ __launch_bounds__(256) void append_capacity_kernel(AppendLaunch a) {
     for (int r = blockIdx.x * 256 + threadIdx.x; r < rows; r += gridDim.x * 256) {
         int row_new = 0;
         long long units = 0;
-        for (int tau = 0; tau < 3; ++tau) {
-            const int key = r * 3 + tau;
+        for (int tau = 0; tau < kNumTiers; ++tau) {
+            const int key = r * kNumTiers + tau;
             const int cnt = a.key_cnt[key];
             if (cnt == 0) continue;
             const int c0 = a.key_c0[key];
@@ -518,13 +572,22 @@ __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
     }
     __syncthreads();
     const int P = a.P, rows = a.n;
-    // tiers and keys, coalesced: one thread per 16 bytes of key
+    // tiers and keys, coalesced: one thread per 16 bytes of key; then the
+    // values of V8 tokens, one thread per 16 bytes of values
     const float4 *k4 = reinterpret_cast<const float4 *>(a.keys);
     bool ok = true;
     for (int i = tid; i < rows * (kD / 4); i += 1024) {
         const float4 v = k4[i];
         ok &= isfinite(v.x) & isfinite(v.y) & isfinite(v.z) & isfinite(v.w);
-        if ((i & 31) == 0) ok &= a.tier[i >> 5] < 3;
+        if ((i & 31) == 0) ok &= a.tier[i >> 5] < a.n_tiers;
+    }
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(a.values);
+    for (int i = tid; i < rows * (kD / 8); i += 1024) {
+        const int tau = a.tier[i >> 4];
+        if (tau < kNumTiers && tier_v8(tau)) {
+            const uint4 v = v4[i];
+            ok &= values_finite(v.x) & values_finite(v.y) & values_finite(v.z) & values_finite(v.w);
+        }
     }
     if (!ok) atomicOr(&s_bad, 1);
     __syncthreads();
@@ -539,7 +602,7 @@ __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
         long long units = 0;
         if (r < rows) {
             const int tau = a.tier[r];
-            const int open = a.open_page[r * 3 + tau];
+            const int open = a.open_page[r * kNumTiers + tau];
             const int cnt = open >= 0 ? (int)a.page_meta[open].count : P;
             if (cnt < P) {
                 page = open;
@@ -596,10 +659,10 @@ __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
             a.page_meta[page] = m;
             a.page_table[(size_t)r * a.maxp + a.num_pages[r]] = page;
             a.num_pages[r] += 1;
-            a.open_page[r * 3 + tau] = P > 1 ? page : -1;
+            a.open_page[r * kNumTiers + tau] = P > 1 ? page : -1;
         } else {
             a.page_meta[page].count = (uint8_t)(slot + 1);
-            if (slot + 1 == P) a.open_page[r * 3 + tau] = -1;
+            if (slot + 1 == P) a.open_page[r * kNumTiers + tau] = -1;
         }
     }
     if (tid == 0) {
@@ -637,7 +700,7 @@ __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
         if (act) {
             tau = a.tier[i];
             row = req_seq(a, i) * a.Hkv + req_head(a, i);
-            key = row * 3 + tau;
+            key = row * kNumTiers + tau;
         }
         s_key[tid] = key;
         s_row[tid] = row;
@@ -752,7 +815,7 @@ __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
 
 __global__ void cache_init_kernel(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
                                   int32_t *status) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < rows * 3; i += gridDim.x * blockDim.x) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < rows * kNumTiers; i += gridDim.x * blockDim.x) {
         open_page[i] = -1;
         if (i < rows) num_pages[i] = 0;
     }
@@ -793,7 +856,7 @@ hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64
 
 hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc, int32_t *status,
                              hipStream_t s) {
-    hipLaunchKernelGGL(cache_init_kernel, dim3(grid_for((int64_t)rows * 3, 256, 1024)), dim3(256), 0, s, rows,
+    hipLaunchKernelGGL(cache_init_kernel, dim3(grid_for((int64_t)rows * kNumTiers, 256, 1024)), dim3(256), 0, s, rows,
                        num_pages, open_page, alloc, status);
     return hipGetLastError();
 }
@@ -838,7 +901,7 @@ hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s) {
     AppendKernelArgs k;
     k.a = a;
     // key_off lives right after key_page in the workspace (same length)
-    const int nkeys = a.num_seqs * a.Hkv * 3;
+    const int nkeys = a.num_seqs * a.Hkv * kNumTiers;
     k.key_off = a.key_page + nkeys;
     hipLaunchKernelGGL(append_init_kernel, dim3(grid_for(nkeys, 256, 1024)), dim3(256), 0, s, k);
     hipLaunchKernelGGL(append_validate_kernel, dim3(grid_for(a.n, 4, 4096)), dim3(256), 0, s, a);

@@ -210,12 +210,37 @@ __device__ inline int read_status(const int32_t *status) {
     return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------- V8 values
+// V8 value codec (tiers 3-5): blocks of 32 dimensions share the exponent
+// e = floor(log2 max|v|), at least -18; code = round-half-even(v 2^(6-e))
+// clamped to [-127, 127]; decoded value code * 2^(e-6), an fp16 number.
+
+// the shared exponent from the largest magnitude's fp16 bits (finite)
+__device__ inline int v8_exponent(uint32_t amax_bits) {
+    if (amax_bits == 0) return -18;
+    const int E = (int)(amax_bits >> 10);
+    const int e = E > 0 ? E - 15 : (31 - __builtin_clz(amax_bits)) - 24;   // subnormal: bits * 2^-24
+    return e < -18 ? -18 : e;
+}
+
+// code of the fp16 value with bits h under exponent e (the scaling is exact)
+__device__ inline int v8_code(uint32_t h, int e) {
+    const float c = rintf(ldexpf(h2f(h & 0xFFFFu), 6 - e));
+    return (int)fminf(fmaxf(c, -127.f), 127.f);
+}
+
+// fp16 bits of the decoded value code * 2^(scale_byte - 133) (exact)
+__device__ inline uint32_t v8_value_bits(int code, int scale_byte) {
+    return __builtin_bit_cast(uint16_t, (_Float16)ldexpf((float)code, scale_byte - 133));
+}
+
 // --------------------------------------------------- write one token
 // Called by all 64 lanes of one wavefront, lane j holding pair j's angle code
 // tc and magnitude code sc and the token's value dims 2j, 2j+1 (fp16 bits):
 // packs the two bit strings (LSB first) in the wavefront's LDS scratch and
-// writes radius r16, codes and value into slot `slot` of page `page` (tier
-// and code block from meta).
+// writes radius r16, codes and values into slot `slot` of page `page` (tier
+// and code block from meta; values as fp16, or V8-encoded for tiers 3-5:
+// the 16 lanes of a row hold one 32-dimension block).
 __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint32_t v2, int page, int slot,
                                    uint2 meta, uint8_t *arena, uint16_t *value_pool, int P,
                                    uint32_t (&words)[2][16]) {
@@ -253,9 +278,22 @@ __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint3
         *reinterpret_cast<uint32_t *>(dst) = ws[w];
     }
     if (lane == 0) *reinterpret_cast<uint16_t *>(blk + 2 * slot) = r16;
-    uint16_t *vp = value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);
-    vp[(2 * lane) * 8] = (uint16_t)(v2 & 0xFFFF);
-    vp[(2 * lane + 1) * 8] = (uint16_t)(v2 >> 16);
+    if (tier_v8(tier)) {
+        int m = (int)max(v2 & 0x7FFFu, (v2 >> 16) & 0x7FFFu);
+        m = max(m, __shfl_xor(m, 1, 64));
+        m = max(m, __shfl_xor(m, 2, 64));
+        m = max(m, __shfl_xor(m, 4, 64));
+        m = max(m, __shfl_xor(m, 8, 64));
+        const int e = v8_exponent((uint32_t)m);
+        uint8_t *vb = reinterpret_cast<uint8_t *>(value_pool + (size_t)page * P * kD) + (slot >> 3) * kV8Group;
+        vb[kV8Codes + (2 * lane) * 8 + (slot & 7)] = (uint8_t)v8_code(v2, e);
+        vb[kV8Codes + (2 * lane + 1) * 8 + (slot & 7)] = (uint8_t)v8_code(v2 >> 16, e);
+        if ((lane & 15) == 0) vb[(slot & 7) * 4 + (lane >> 4)] = (uint8_t)(e + 127);
+    } else {
+        uint16_t *vp = value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);
+        vp[(2 * lane) * 8] = (uint16_t)(v2 & 0xFFFF);
+        vp[(2 * lane + 1) * 8] = (uint16_t)(v2 >> 16);
+    }
     __builtin_amdgcn_wave_barrier();
 }
 

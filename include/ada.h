@@ -12,7 +12,8 @@
  * budget, producing tier-homogeneous pages with lightweight metadata.  The
  * abstract fixes no bit layout; this header fixes one:
  *
- *  Key codec (head dim 128 -> 64 adjacent pairs (k[2j], k[2j+1])):
+ *  Key codec (head dim 128 -> 64 pairs (k[2j], k[2j+1]); with the half-split
+ *  pair layout of ada_config_t, (k[j], k[j+64]), and the query likewise):
  *   radius     r = |k| (fp64, correctly rounded), stored as fp16 (round to
  *              nearest even straight from fp64, saturating at 65504);
  *   magnitude  s_j = |pair j| / r, code = nearest integer to s_j (2^sb - 1),
@@ -23,7 +24,18 @@
  *   The norm^2 is the fixed pairwise tree sum of the 64 pair energies
  *   (strides 32, 16, ..., 1); codes are decided exactly (not up to rounding).
  *  Tiers (fixed table, id order): ADA_TIER_T8 = (tb 8, sb 8),
- *   ADA_TIER_T4 = (4, 4), ADA_TIER_T2 = (2, 3).
+ *   ADA_TIER_T4 = (4, 4), ADA_TIER_T2 = (2, 3), all with fp16 values;
+ *   ADA_TIER_T8V8, ADA_TIER_T4V8, ADA_TIER_T2V8 = the same keys with V8
+ *   values (the abstract's precision tiers per token and head are not
+ *   restricted to keys; it names no value format, this one is the
+ *   library's):
+ *  V8 value codec, per token and head, blocks k of 32 dimensions:
+ *     e = floor(log2 max |v_d|) over the block, at least -18 (-18 for an
+ *     all-zero block); code c_d = round-half-even(v_d * 2^(6 - e)) clamped
+ *     to [-127, 127]; decoded value c_d * 2^(e - 6), an exact fp16 number.
+ *     (The pattern of the OCP Microscaling formats: a shared power-of-two
+ *     scale per 32 values, 8-bit elements with 6 fraction bits.)  Values of
+ *     a V8 token must be finite.
  *  Logit of a kept token t for query q (per query head):
  *     l_t = scale * r_t * sum_j s_j * LUT[j][theta_code_j],
  *     LUT[j][c] = q[2j] cos(th_c) + q[2j+1] sin(th_c),
@@ -40,7 +52,10 @@
  *     Block bytes: T8 130 P, T4 66 P, T2 42 P.
  *   value page: fp16, element (slot, d) of page p at
  *     value_pool + p*P*128 + (slot/8)*1024 + d*8 + slot%8
- *     (8-token groups, dimension-major inside a group).
+ *     (8-token groups, dimension-major inside a group).  A page of a V8
+ *     tier uses the start of the same slot as bytes: per 8-token group g,
+ *     at byte 1056 g, [8 tokens][4 blocks] scale bytes e + 127, then at
+ *     1056 g + 32, [128 dims][8 tokens] int8 codes; the rest is zero.
  *   Unused slots of a page (slot >= count) are zero in codes and values.
  *
  * Conventions for every call:
@@ -78,7 +93,11 @@ typedef enum {
     ADA_EINTERNAL = 5        /* an exact code decision could not be made (never expected) */
 } ada_status_t;
 
-enum { ADA_TIER_T8 = 0, ADA_TIER_T4 = 1, ADA_TIER_T2 = 2, ADA_NUM_TIERS = 3 };
+enum {
+    ADA_TIER_T8 = 0, ADA_TIER_T4 = 1, ADA_TIER_T2 = 2,           /* fp16 values */
+    ADA_TIER_T8V8 = 3, ADA_TIER_T4V8 = 4, ADA_TIER_T2V8 = 5,     /* V8 values */
+    ADA_NUM_TIERS = 6
+};
 
 /* Shape of one attention layer's cache (host struct). */
 typedef struct {
@@ -86,7 +105,8 @@ typedef struct {
     int32_t page_size;          /* P: 16 or 32 */
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv; Hq / Hkv must be 1, 2, 4 or 8 (query head hq uses KV head hq / (Hq/Hkv)) */
-    uint32_t rdr_tier_mask;     /* tiers RDR may assign (bit i = tier id i); 0 means all three */
+    uint32_t rdr_tier_mask;     /* tiers RDR may assign (bit i = tier id i, i < 6); 0 means
+                                   the three fp16 tiers (0x7) */
     int32_t decode_chunk_pages; /* split-K chunk length in pages for ada_decode; 0 = automatic: about
                                    one round of resident work-groups over B * Hkv rows of
                                    max_pages_per_head pages on the current device.  Rounded up to
@@ -98,6 +118,10 @@ typedef struct {
                                    ADA_PAIRS_HALF_SPLIT (k[j], k[j+64]), the pairing of the
                                    rotate-half form of rotary position embeddings.  A cache must be
                                    written and read with one layout. */
+    int32_t value_tiers;        /* 0: the cache holds tiers 0-2 (fp16 values) only; 1: it may also
+                                   hold tiers 3-5 (V8 values): pack and append accept them, RDR may
+                                   assign them, and the decode runs its V8-capable kernels.  A
+                                   cache must be written and read with one setting. */
 } ada_config_t;
 
 enum { ADA_PAIRS_ADJACENT = 0, ADA_PAIRS_HALF_SPLIT = 1 };
@@ -119,7 +143,7 @@ typedef struct {
     int64_t arena_capacity16;   /* code arena size in 16-byte units */
     int32_t *page_table;        /* [rows][max_pages_per_head] physical page ids */
     int32_t *num_pages;         /* [rows] pages in use per row */
-    int32_t *open_page;         /* [rows][3] last non-full page per tier, -1 = none */
+    int32_t *open_page;         /* [rows][ADA_NUM_TIERS] last non-full page per tier, -1 = none */
     ada_page_meta_t *page_meta; /* [page_capacity] */
     uint8_t *code_arena;        /* [arena_capacity16 * 16], 16-byte aligned */
     uint16_t *value_pool;       /* [page_capacity][P * 128] fp16 bits */
@@ -201,8 +225,9 @@ ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *ca
  * page id, next code block) appended to that row.
  *   seq, kv_head device int32 [n]; tier device uint8 [n]
  *   keys   device fp32 [n][128]; values device fp16 bits [n][128]
- * Device errors: out-of-range seq / head / tier or non-finite key ->
- * ADA_EINVAL; capacity -> ADA_ENOSPC; in both cases nothing is written. */
+ * Device errors: out-of-range seq / head / tier, non-finite key or non-finite
+ * value of a V8 token -> ADA_EINVAL; capacity -> ADA_ENOSPC; in both cases
+ * nothing is written. */
 ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n,
                                const int32_t *seq, const int32_t *kv_head, const uint8_t *tier,
                                const float *keys, const uint16_t *values, void *ws, size_t ws_bytes,
@@ -239,12 +264,15 @@ ada_status_t ada_repack_workspace(const ada_config_t *cfg, const ada_cache_t *sr
  * b are the kept tokens of its rows in `src`: item (h, t) is slot t % P of
  * page-list entry t / P of row (b, h), t playing the part of the position in
  * the RDR order; its utility is util[page * P + slot] (for instance from
- * ada_decode_utility).  Each item may keep its tier, move to a tier of lower
- * rate among the enabled ones, or be dropped (the codes hold nothing finer),
+ * ada_decode_utility).  Each item may keep its tier, move to an enabled tier
+ * holding no more angle, magnitude or value bits, or be dropped (the codes
+ * hold nothing finer); the enabled tiers in rate order must each hold no
+ * fewer bits than the one before (else ADA_EUNSUPPORTED),
  * under budget[b] bytes with the rate / distortion model of ada_rdr_assign.
  * Kept items are transcoded in code space -- angle codes to the nearest
  * point of the nested coarser grid (half up), magnitude codes to the nearest
- * level (no ties occur between these tiers), radius and value unchanged --
+ * level (no ties occur between these tiers), radius unchanged, values
+ * re-encoded from their decoded fp16 numbers in the new tier's format --
  * and packed into `dst` exactly as ada_pack lays out a tier map over
  * positions 0 .. src.max_pages_per_head * P - 1 (tier id ascending, then
  * position).  dst must be a different cache; its rows of sequences < B are
@@ -275,7 +303,8 @@ ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cach
  * The new slots are booked first (metadata updated, new pages zeroed); in the
  * split-K launch the work-group whose context chunk holds a booked slot
  * encodes the key and writes the slot before reading any of its pages.
- * Device errors are the append's (bad tier or non-finite key -> ADA_EINVAL,
+ * Device errors are the append's (bad tier, non-finite key or non-finite
+ * value of a V8 token -> ADA_EINVAL,
  * capacity -> ADA_ENOSPC, in the status word): then nothing is written and
  * out / lse cover the tokens cached before the call. */
 ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
@@ -289,8 +318,9 @@ ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_s
 /* RDR keep/drop + tier choice under a byte budget (abstract: joint
  * keep/drop and precision tiers per token and head under a fixed budget).
  * Items are (KV head, position) of one sequence, all heads sharing the
- * sequence's budget.  Rate of tier (tb, sb): 2 + 8 (tb + sb) + 256 bytes;
- * distortion 2^-(tb + sb); drop: rate 0, distortion 1.  Enabled tiers in
+ * sequence's budget.  Rate of a tier: 2 + 8 (tb + sb) + 256 bytes (fp16
+ * values) or + 132 (V8 values); distortion 2^-(tb + sb), plus 2^-14 for V8
+ * values; drop: rate 0, distortion 1.  Enabled tiers in
  * rate order form upgrade steps drop -> ... with cost dR_k and priority
  * w * (dD_k / dR_k) (fp64); steps are taken in order of priority descending,
  * position descending, head ascending, step ascending, while the byte total
@@ -320,8 +350,9 @@ ada_status_t ada_pack_workspace(const ada_config_t *cfg, const ada_cache_t *cach
  *   ctx_len host int32 [B]
  *   tier    device int8 [B][Hkv][ctx_stride] (-1 = drop)
  *   keys    device fp32 [B][Hkv][ctx_stride][128]; values device fp16 bits, same shape
- * Device errors (tier out of range, non-finite kept key -> ADA_EINVAL;
- * capacity -> ADA_ENOSPC) leave the cache unmodified. */
+ * Device errors (tier out of range, non-finite kept key, non-finite value
+ * of a V8 token -> ADA_EINVAL; capacity -> ADA_ENOSPC) leave the cache
+ * unmodified. */
 ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, const int32_t *ctx_len,
                       int64_t ctx_stride, const int8_t *tier, const float *keys, const uint16_t *values,
                       void *ws, size_t ws_bytes, void *stream);

@@ -343,9 +343,10 @@ void orc_v8_decode(const uint8_t *scale_byte, const int8_t *codes, double *v)
 }
 
 /* V8 value page, in the page's value-pool slot viewed as bytes: per 8-token
- * group g, [4 dimension blocks][8 tokens] scale bytes (32 bytes), then
- * [128 dims][8 tokens] int8 codes (1024 bytes).  Empty slots are zero. */
-static int64_t v8_scale_off(int slot, int k) { return (int64_t)(slot / 8) * 1056 + k * 8 + slot % 8; }
+ * group g, [8 tokens][4 dimension blocks] scale bytes (32 bytes: a token's
+ * four scales are one 4-byte word), then [128 dims][8 tokens] int8 codes
+ * (1024 bytes).  Empty slots and the rest of the slot are zero. */
+static int64_t v8_scale_off(int slot, int k) { return (int64_t)(slot / 8) * 1056 + (slot % 8) * 4 + k; }
 static int64_t v8_code_off(int slot, int d) { return (int64_t)(slot / 8) * 1056 + 32 + (int64_t)d * 8 + slot % 8; }
 
 static uint8_t *value_page_bytes(uint16_t *pool, int64_t page, int P) { return (uint8_t *)(pool + page * P * ORC_D); }

@@ -30,7 +30,8 @@ def test_library_exports_every_declared_symbol():
 def test_block_bytes_and_lut_floats():
     assert [ada.block_bytes(t, 16) for t in (0, 1, 2)] == [2080, 1056, 672]
     assert ada.block_bytes(1, 32) == 2112
-    assert ada.block_bytes(3, 16) == -1 and ada.block_bytes(0, 8) == -1
+    assert [ada.block_bytes(t, 16) for t in (3, 4, 5)] == [2080, 1056, 672]   # V8 tiers: the same keys
+    assert ada.block_bytes(6, 16) == -1 and ada.block_bytes(0, 8) == -1
     assert ada.lut_floats(ada.make_config(16, 32, 8)) == 64 * (256 + 16 + 4)
 
 
@@ -70,7 +71,10 @@ def test_host_validation_without_gpu():
            (ada.Config(128, 16, 30, 8, 0, 0), ada.EINVAL),
            (ada.Config(128, 16, 32, 0, 0, 0), ada.EINVAL),
            (ada.Config(128, 16, 32, 8, 9, 0), ada.EINVAL),
-           (ada.Config(128, 16, 32, 8, 0, 0, 2), ada.EINVAL)]
+           (ada.Config(128, 16, 32, 8, 0, 0, 2), ada.EINVAL),
+           (ada.Config(128, 16, 32, 8, 0b111000, 0, 0, 0), ada.EINVAL),   # V8 tiers without value_tiers
+           (ada.Config(128, 16, 32, 8, 1 << 6, 0, 0, 1), ada.EINVAL),
+           (ada.Config(128, 16, 32, 8, 0, 0, 0, 2), ada.EINVAL)]
     for cfg, want in bad[1:]:
         assert _size(L.ada_decode_workspace, ctypes.byref(cfg), ctypes.byref(desc), 2)[0] == want
     # decode refuses a cache with null buffers before touching the device
