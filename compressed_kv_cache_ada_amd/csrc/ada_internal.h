@@ -31,7 +31,7 @@ __host__ __device__ constexpr int64_t tier_rate(int t) {
 __host__ __device__ constexpr int block16(int t, int P) { return P * (2 + 8 * tier_tb(t) + 8 * tier_sb(t)) / 16; }
 // V8 value page (in the page's value-pool slot, as bytes): per 8-token group,
 // [8 tokens][4 dimension blocks] scale bytes (a token's four scales are one
-// 4-byte word), then [128 dims][8 tokens] codes
+// 4-byte word), then [128 dims][8 tokens] code bytes c + 128 (offset binary)
 constexpr int kV8Group = 1056;
 constexpr int kV8Codes = 32;   // offset of the codes inside a group
 

@@ -58,7 +58,7 @@ struct CodeRegs {
     uint2 h;
     uint32_t r;         // fp16 radius bits
     const uint8_t *c;   // the token's first angle unit
-    uint32_t vs;        // V8 pages: the token's four block scales (bytes)
+    uint2 vs;           // V8 pages: the token's four block scales as fp16 [0|1], [2|3]
 };
 
 // Per-work-group LUT layout, per pair j with NC codes: slices of SW =
@@ -337,12 +337,13 @@ struct AdaPolicy {
 
     using Codes = CodeRegs;
 
-    // the scale words of tokens 8 blk .. 8 blk + 7 of the current group,
-    // from the lanes holding those tokens
-    __device__ void scale_words(const Codes &k, int blk, uint32_t (&sd)[8]) const {
+    // the fp16 scales of dimension blocks 2kp, 2kp + 1 of tokens 8 blk ..
+    // 8 blk + 7 of the current group, from the lanes holding those tokens
+    __device__ void scale_halves(const Codes &k, int blk, int kp, uint32_t (&sh)[8]) const {
         if constexpr (VT) {
+            const int v = (int)(kp ? k.vs.y : k.vs.x);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sd[j] = (uint32_t)__shfl((int)k.vs, 8 * blk + j, 64);
+            for (int j = 0; j < 8; ++j) sh[j] = (uint32_t)__shfl(v, 8 * blk + j, 64);
         }
     }
 
@@ -350,7 +351,13 @@ struct AdaPolicy {
     // w's stage (lane = token, wave-uniform destinations).  Branch-free:
     // every address stays inside the lane's own code block (and, for the
     // V8 scale word, inside its page's value slot).
-    __device__ void stage(Smem &s, int w, uint2 meta, int page, int slot) const {
+    __device__ void stage(Smem &s, int w, uint2 meta, int page, int slot_) const {
+        // slot-derived offsets are formed here, from an opaque copy of the
+        // slot: hoisted out of the group loop they would hold registers
+        // for all of it (and, spilled, their reloads would wait for every
+        // load in flight)
+        uint32_t slot = slot_;
+        if constexpr (VT) asm volatile("" : "+v"(slot));
         if constexpr (VT) {
             const uint8_t *vb = reinterpret_cast<const uint8_t *>(value_pool + (size_t)page * P * kD);
             __builtin_amdgcn_global_load_lds(vb + (slot >> 3) * kV8Group + (slot & 7) * 4, &s.vs[w][0], 4, 0, 0);
@@ -381,7 +388,7 @@ struct AdaPolicy {
         k.h = (slot & 1) ? make_uint2(hh.z, hh.w) : make_uint2(hh.x, hh.y);
         const uint32_t rr = st.r[lane];
         k.r = (slot & 1) ? rr >> 16 : rr & 0xFFFFu;
-        if constexpr (VT) k.vs = s.vs[w][lane];
+        if constexpr (VT) k.vs = core::v8_scale_halves(s.vs[w][lane]);
         // the slot offset is made opaque here so that arena + slot offset (a
         // 64-bit per-lane value) is not hoisted out of the group loop, where
         // it would hold two more registers for the whole loop

@@ -57,27 +57,34 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// V8 values -> fp16 MFMA operand.  Scale words of 8 tokens (byte k: the
-// token's scale s of dimension block k) -> the half2 factors 2^(s - 133) of
-// token pairs, exact (the fp32 bits (s - 6) << 23 are that power of two; it
-// is an fp16 number since s >= 109).
-__device__ __forceinline__ void v8_scale_pairs(const uint32_t (&sd)[8], int k, uint32_t (&sp)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t b0 = (sd[2 * i] >> (8 * k)) & 0xFFu, b1 = (sd[2 * i + 1] >> (8 * k)) & 0xFFu;
-        const float f0 = __builtin_bit_cast(float, (b0 - 6u) << 23), f1 = __builtin_bit_cast(float, (b1 - 6u) << 23);
-        sp[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1));
-    }
-}
-
+// V8 values -> fp16 MFMA operand.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// two tokens' int8 codes (bytes 0 and 1 of w) times their scale pair: two
-// fp16 values of the MFMA A operand (exact products)
+// A token's four scale bytes s (one per dimension block) -> the fp16 factors
+// 2^(s - 133), packed [block 0 | block 1] and [block 2 | block 3]: exact (the
+// fp32 bits (s - 6) << 23 are that power of two, an fp16 number since
+// s >= 109).  The zero byte of an empty slot gives 0, so that its zero code
+// bytes (c = -128) give a zero value.
+__device__ __forceinline__ uint2 v8_scale_halves(uint32_t word) {
+    float f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t b = (word >> (8 * k)) & 0xFFu;
+        f[k] = b ? __builtin_bit_cast(float, (b - 6u) << 23) : 0.f;
+    }
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1])),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2], f[3])));
+}
+
+// two tokens' code bytes u = c + 128 (bytes b and b + 1 of w, b = 0 or 2)
+// times their scale pair: two fp16 values of the MFMA A operand.  The
+// permute forms the halves 0x6400 | u = 1152 + c, so subtracting 1152 gives
+// c exactly; the product with a power of two is exact.
+template <int B>
 __device__ __forceinline__ uint32_t v8_pair(uint32_t w, uint32_t scale_pair) {
-    half2_t c;
-    c[0] = (_Float16)(int)(int8_t)w;
-    c[1] = (_Float16)(int)(int8_t)(w >> 8);
+    constexpr uint32_t sel = B == 0 ? 0x04010400u : 0x04030402u;   // [b, 0x64, b + 1, 0x64]
+    const uint32_t x = __builtin_amdgcn_perm(0x64646464u, w, sel);
+    const half2_t c = __builtin_bit_cast(half2_t, x) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
     return __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(half2_t, scale_pair));
 }
 
@@ -180,7 +187,8 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //                                              (uniformly) whether a barrier
 //                                              must follow
 //   kValueTiers: pages of tiers 3-5 hold V8 values (see include/ada.h)
-//     void scale_words(codes, blk, sd[8])     the V8 scale words of the 8
+//     void scale_halves(codes, blk, kp, sh[8])  fp16 scales of dimension
+//                                              blocks 2kp, 2kp + 1 of the 8
 //                                              tokens of block blk of the
 //                                              current group
 //   kStaged = true:
@@ -377,22 +385,29 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
             }
             if constexpr (Pol::kValueTiers) {
                 // codes x scales -> fp16 in place; tiles 2k, 2k+1 use dimension
-                // block k.  The scale words come from other lanes, so they
-                // are gathered with every lane active.
-                uint32_t sd[8];
-                if (__any(v8[kc])) pol.scale_words(codes, 4 * kc + vq, sd);
-                if (v8[kc]) {
+                // block k.  The scales come from the lanes holding the
+                // tokens, so they are gathered with every lane active.
+                if (__any(v8[kc])) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        uint32_t sp[4];
-                        v8_scale_pairs(sd, k, sp);
+                    for (int kp = 0; kp < 2; ++kp) {   // dimension blocks 2kp, 2kp + 1: tiles 4kp .. 4kp + 3
+                        uint32_t sh[8];   // token j's scale halves of the two blocks
+                        pol.scale_halves(codes, 4 * kc + vq, kp, sh);
+                        if (v8[kc]) {
 #pragma unroll
-                        for (int t = 2 * k; t < 2 * k + 2; ++t) {
-                            const uint32_t lo = va[kc][t].x, hi = va[kc][t].y;
-                            va[kc][t].w = v8_pair(hi >> 16, sp[3]);
-                            va[kc][t].z = v8_pair(hi, sp[2]);
-                            va[kc][t].y = v8_pair(lo >> 16, sp[1]);
-                            va[kc][t].x = v8_pair(lo, sp[0]);
+                            for (int kk = 0; kk < 2; ++kk) {
+                                uint32_t sp[4];   // scale pairs of tokens (2i, 2i + 1), block 2kp + kk
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    sp[i] = __builtin_amdgcn_perm(sh[2 * i + 1], sh[2 * i], kk ? 0x07060302u : 0x05040100u);
+#pragma unroll
+                                for (int t = 4 * kp + 2 * kk; t < 4 * kp + 2 * kk + 2; ++t) {
+                                    const uint32_t lo = va[kc][t].x, hi = va[kc][t].y;
+                                    va[kc][t].w = v8_pair<2>(hi, sp[3]);
+                                    va[kc][t].z = v8_pair<0>(hi, sp[2]);
+                                    va[kc][t].y = v8_pair<2>(lo, sp[1]);
+                                    va[kc][t].x = v8_pair<0>(lo, sp[0]);
+                                }
+                            }
                         }
                     }
                 }

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
                 } else if (tier_v8(e[k].z)) {
                     const uint8_t *sb = reinterpret_cast<const uint8_t *>(a.src_value_pool + (size_t)e[k].x * P * kD) +
                                         (e[k].y >> 3) * kV8Group;
-                    h[k] = v8_value_bits((int8_t)sb[kV8Codes + dim * 8 + idx], sb[idx * 4 + (dim >> 5)]);
+                    h[k] = v8_value_bits((int)sb[kV8Codes + dim * 8 + idx] - 128, sb[idx * 4 + (dim >> 5)]);
                 } else {
                     const int q = idx >> 1;
                     const uint32_t word = q == 0 ? seg[k].x : q == 1 ? seg[k].y : q == 2 ? seg[k].z : seg[k].w;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
                     m = max(m, __shfl_xor(m, 8, 64));
                     m = max(m, __shfl_xor(m, 16, 64));
                     const int ex = enc::v8_exponent((uint32_t)m);
-                    const uint32_t c = e[k].x >= 0 ? (uint32_t)(uint8_t)enc::v8_code(h[k], ex) : 0u;
+                    const uint32_t c = e[k].x >= 0 ? (uint32_t)(enc::v8_code(h[k], ex) + 128) : 0u;
                     const uint32_t sbyte = e[k].x >= 0 ? (uint32_t)(ex + 127) : 0u;
                     cw[k >> 2] |= c << (8 * (k & 3));
                     sbytes[k] = (uint8_t)sbyte;

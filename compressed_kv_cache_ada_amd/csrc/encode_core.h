@@ -286,8 +286,8 @@ __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint3
         m = max(m, __shfl_xor(m, 8, 64));
         const int e = v8_exponent((uint32_t)m);
         uint8_t *vb = reinterpret_cast<uint8_t *>(value_pool + (size_t)page * P * kD) + (slot >> 3) * kV8Group;
-        vb[kV8Codes + (2 * lane) * 8 + (slot & 7)] = (uint8_t)v8_code(v2, e);
-        vb[kV8Codes + (2 * lane + 1) * 8 + (slot & 7)] = (uint8_t)v8_code(v2 >> 16, e);
+        vb[kV8Codes + (2 * lane) * 8 + (slot & 7)] = (uint8_t)(v8_code(v2, e) + 128);
+        vb[kV8Codes + (2 * lane + 1) * 8 + (slot & 7)] = (uint8_t)(v8_code(v2 >> 16, e) + 128);
         if ((lane & 15) == 0) vb[(slot & 7) * 4 + (lane >> 4)] = (uint8_t)(e + 127);
     } else {
         uint16_t *vp = value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);

@@ -55,7 +55,8 @@
  *     (8-token groups, dimension-major inside a group).  A page of a V8
  *     tier uses the start of the same slot as bytes: per 8-token group g,
  *     at byte 1056 g, [8 tokens][4 blocks] scale bytes e + 127, then at
- *     1056 g + 32, [128 dims][8 tokens] int8 codes; the rest is zero.
+ *     1056 g + 32, [128 dims][8 tokens] code bytes c + 128 (offset
+ *     binary); empty slots and the rest of the slot are zero.
  *   Unused slots of a page (slot >= count) are zero in codes and values.
  *
  * Conventions for every call:

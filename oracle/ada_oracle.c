@@ -344,8 +344,9 @@ void orc_v8_decode(const uint8_t *scale_byte, const int8_t *codes, double *v)
 
 /* V8 value page, in the page's value-pool slot viewed as bytes: per 8-token
  * group g, [8 tokens][4 dimension blocks] scale bytes (32 bytes: a token's
- * four scales are one 4-byte word), then [128 dims][8 tokens] int8 codes
- * (1024 bytes).  Empty slots and the rest of the slot are zero. */
+ * four scales are one 4-byte word), then [128 dims][8 tokens] code bytes
+ * c + 128 (offset binary; 1024 bytes).  Empty slots and the rest of the slot
+ * are zero. */
 static int64_t v8_scale_off(int slot, int k) { return (int64_t)(slot / 8) * 1056 + (slot % 8) * 4 + k; }
 static int64_t v8_code_off(int slot, int d) { return (int64_t)(slot / 8) * 1056 + 32 + (int64_t)d * 8 + slot % 8; }
 
@@ -364,7 +365,7 @@ static int value_write(uint16_t *pool, int64_t page, int tier, int P, int slot, 
     if (orc_v8_encode(v, sb, c) != ORC_OK) return ORC_EINVAL;
     uint8_t *pb = value_page_bytes(pool, page, P);
     for (int k = 0; k < 4; k++) pb[v8_scale_off(slot, k)] = sb[k];
-    for (int d = 0; d < ORC_D; d++) pb[v8_code_off(slot, d)] = (uint8_t)c[d];
+    for (int d = 0; d < ORC_D; d++) pb[v8_code_off(slot, d)] = (uint8_t)(c[d] + 128);
     return ORC_OK;
 }
 
@@ -379,7 +380,7 @@ static void value_read(const uint16_t *pool, int64_t page, int tier, int P, int 
     uint8_t sb[4];
     int8_t c[ORC_D];
     for (int k = 0; k < 4; k++) sb[k] = pb[v8_scale_off(slot, k)];
-    for (int d = 0; d < ORC_D; d++) c[d] = (int8_t)pb[v8_code_off(slot, d)];
+    for (int d = 0; d < ORC_D; d++) c[d] = (int8_t)((int)pb[v8_code_off(slot, d)] - 128);
     orc_v8_decode(sb, c, v);
 }
 

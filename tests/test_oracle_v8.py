@@ -128,7 +128,7 @@ def test_v8_page_bytes_follow_the_layout():
                 st, sb, codes = O.v8_encode(w["values"][0, row, pos])
                 g, r = slot // 8, slot % 8
                 assert [raw[g * 1056 + r * 4 + k] for k in range(4)] == list(sb)
-                assert np.array_equal(raw[g * 1056 + 32 + np.arange(128) * 8 + r].view(np.int8), codes)
+                assert np.array_equal(raw[g * 1056 + 32 + np.arange(128) * 8 + r].astype(np.int16) - 128, codes)
             if O.VALUE_BITS[tier] == 8:   # bytes of empty slots and past the V8 layout stay zero
                 used = np.zeros(raw.size, bool)
                 for slot in range(count):
