@@ -325,18 +325,19 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         //    scale dword t (.z of tile t), converted before the MFMAs.
         uint4 va[2][8];
         bool v8[2] = {false, false};
-        // the lane's place in the MFMA operands, made opaque here so that the
-        // per-lane value offsets are formed in the loop rather than hoisted
-        // out of it (they would hold registers for the whole loop)
-        uint32_t ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int vq = ln >> 4, vh = ln & 15;   // kq, n_head
+        if constexpr (Pol::kValueTiers) {
+            // the lane's place in the MFMA operands, made opaque here so that
+            // the per-lane value offsets are formed in the loop rather than
+            // hoisted out of it (they would hold registers for all of it)
+            uint32_t ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int vq = ln >> 4, vh = ln & 15;   // kq, n_head
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int blk = 4 * kc + vq;            // 8-token block of the group
-            const int pidx = cs.pages[gbase + blk / KB] >= 0 ? gbase + blk / KB : gbase;
-            const uint8_t *vbytes = reinterpret_cast<const uint8_t *>(a.value_pool + (size_t)cs.pages[pidx] * P * kD);
-            if constexpr (Pol::kValueTiers) {
+            for (int kc = 0; kc < 2; ++kc) {
+                const int blk = 4 * kc + vq;        // 8-token block of the group
+                const int pidx = cs.pages[gbase + blk / KB] >= 0 ? gbase + blk / KB : gbase;
+                const uint8_t *vbytes =
+                    reinterpret_cast<const uint8_t *>(a.value_pool + (size_t)cs.pages[pidx] * P * kD);
                 // V8 page: 16 bytes from the lane's dimension's 8 code bytes
                 // (the 8 after it belong to the next dimension, unused); the
                 // same instructions as the fp16 loads, other addresses
@@ -345,10 +346,16 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
                 const uint8_t *b8 = vbytes + (blk % KB) * kV8Group + kV8Codes + vh * 8;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(v8[kc] ? b8 + t * 128 : b16 + t * 256);
-            } else {
-                const uint8_t *base = vbytes + (blk % KB) * 2048 + vh * 16;
+            }
+        } else {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 256);
+            for (int kc = 0; kc < 2; ++kc) {
+                const int blk = 4 * kc + kq;        // 8-token block of the group
+                const int vpage = cs.pages[gbase + blk / KB];
+                const uint16_t *base = a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gbase]) * P * kD +
+                                       (blk % KB) * 1024 + n_head * 8;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
             }
         }
 
@@ -391,7 +398,7 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 #pragma unroll
                     for (int kp = 0; kp < 2; ++kp) {   // dimension blocks 2kp, 2kp + 1: tiles 4kp .. 4kp + 3
                         uint32_t sh[8];   // token j's scale halves of the two blocks
-                        pol.scale_halves(codes, 4 * kc + vq, kp, sh);
+                        pol.scale_halves(codes, 4 * kc + kq, kp, sh);
                         if (v8[kc]) {
 #pragma unroll
                             for (int kk = 0; kk < 2; ++kk) {
