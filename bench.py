@@ -56,7 +56,8 @@ def parse():
                     help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=0)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra split-K launches each after 1 GiB of unrelated reads (cold caches), untimed in value")
     return ap.parse_args()
 
 
@@ -191,7 +192,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    k_ms_each = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    k_each = [a.elapsed_time(b) for a, b in evs]
+    k_ms_each = float(np.mean(k_each))
     # dominant kernel alone: K back-to-back split-K launches between two events
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -286,6 +288,8 @@ def main():
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "kernel": "decode_partials_kernel" if Q == 1 else "decode_partials_kernel + decode_reduce_kernel",
             "kernel_ms": k_ms, "kernel_ms_event_per_launch": k_ms_each,
+            "kernel_ms_event_median": float(np.median(k_each)),
+            "frac_of_read_probe": None,
             "reduce_kernel_ms": r_ms,
             "algorithmic_bytes": alg_bytes,
         },
@@ -305,6 +309,7 @@ def main():
         result["dense_fp16_reference"] = dense_reference(w, ada, torch, cfg)
     if not args.no_cpu_baseline and Q == 1:
         result["cpu_baseline"] = cpu_baseline(w, kept_total, max_row, n_pages, units)
+    result["roofline"]["frac_of_read_probe"] = achieved / result["read_probe_gbps"]
     print(json.dumps(result), flush=True)
 
 
@@ -538,10 +543,19 @@ def cpu_baseline(w, kept_total, max_row, n_pages, units, min_seconds=10.0, max_s
         O.decode(oc, w["q"], w["scale"], nthreads=cores)
         dt += time.perf_counter() - t0
         steps += 1
+    # one thread, one decode step of sequence 0 only
+    one = O.Cache(w["P"], w["Hq"], w["Hkv"], 1, max_row, n_pages, units)
+    assert O.pack(one, w["ctx_len"][:1], w["tiers"][:1], w["keys"][:1], w["values"][:1], nthreads=cores) == O.OK
+    kept0 = int((w["tiers"][0, :, : int(w["ctx_len"][0])] >= 0).sum())
+    t0 = time.perf_counter()
+    O.decode(one, w["q"][:1], w["scale"], nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": kept_total * steps / dt, "unit": "KV token-heads/s", "cores": cores, "kind": "oracle",
             "seconds": dt,
             "sample": f"{steps} decode steps over all {B} sequences (all heads, all kept tokens, "
-                      f"{kept_total} token-heads per step), same queries each step"}
+                      f"{kept_total} token-heads per step), same queries each step",
+            "single_thread": {"value": kept0 / dt1, "seconds": dt1,
+                              "sample": f"one decode step of sequence 0 ({kept0} token-heads) on 1 thread"}}
 
 
 if __name__ == "__main__":
