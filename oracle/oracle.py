@@ -37,8 +37,15 @@ _lib = None
 
 
 def lib():
+    """The oracle library; ORACLE_LIB names another build of ada_oracle.c
+    (the sanitizer test loads an instrumented one)."""
     global _lib
     if _lib is None:
+        alt = os.environ.get("ORACLE_LIB")
+        if alt:
+            _lib = ctypes.CDLL(alt)
+            _declare(_lib)
+            return _lib
         if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
             build()
         _lib = ctypes.CDLL(LIB)
