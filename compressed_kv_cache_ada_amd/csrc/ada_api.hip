@@ -13,18 +13,46 @@ namespace {
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
-// carve typed arrays out of a workspace
+// Workspaces larger than this are refused (ADA_EUNSUPPORTED), so no size
+// computed here can wrap around.
+constexpr size_t kMaxWorkspace = size_t(1) << 48;
+
+// a * b, saturating at SIZE_MAX
+inline size_t smul(size_t a, size_t b) {
+    size_t r;
+    return __builtin_mul_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+inline size_t smul(size_t a, size_t b, size_t c) { return smul(smul(a, b), c); }
+inline size_t smul(size_t a, size_t b, size_t c, size_t d) { return smul(smul(a, b, c), d); }
+
+// carve typed arrays out of a workspace; once the running size passes
+// kMaxWorkspace it sticks at SIZE_MAX and the pointers are null
 struct Carver {
     char *base;
     size_t off = 0;
     explicit Carver(void *p) : base(static_cast<char *>(p)) {}
     template <typename T>
     T *take(size_t n) {
+        const size_t bytes = smul(n, sizeof(T));
+        if (off > kMaxWorkspace || bytes > kMaxWorkspace - off) {
+            off = SIZE_MAX;
+            return nullptr;
+        }
         T *p = reinterpret_cast<T *>(base ? base + off : nullptr);
-        off = align_up(off + n * sizeof(T));
+        off = align_up(off + bytes);
         return p;
     }
 };
+
+// a + b for workspace sizes, saturating like the carver
+inline size_t ws_add(size_t a, size_t b) { return (a > kMaxWorkspace || b > kMaxWorkspace) ? SIZE_MAX : a + b; }
+
+// report a workspace size, or refuse one past kMaxWorkspace
+inline ada_status_t ws_out(size_t n, size_t *bytes) {
+    if (n > kMaxWorkspace) return ADA_EUNSUPPORTED;
+    *bytes = n;
+    return ADA_OK;
+}
 
 ada_status_t check_cfg(const ada_config_t *cfg) {
     if (!cfg) return ADA_EINVAL;
@@ -42,11 +70,19 @@ ada_status_t check_cfg(const ada_config_t *cfg) {
     return ADA_OK;
 }
 
-ada_status_t check_cache(const ada_cache_t *c) {
+// Batch and row shapes the kernels index with 32-bit integers: query-head
+// rows B * Hq and token positions max_pages_per_head * P.
+ada_status_t check_dims(const ada_config_t *cfg, int64_t B, int64_t maxp) {
+    if ((int64_t)B * cfg->num_q_heads > INT32_MAX || maxp * cfg->page_size > INT32_MAX) return ADA_EUNSUPPORTED;
+    return ADA_OK;
+}
+
+ada_status_t check_cache(const ada_config_t *cfg, const ada_cache_t *c) {
     if (!c) return ADA_EINVAL;
     if (c->num_seqs <= 0 || c->max_pages_per_head <= 0 || c->page_capacity <= 0 || c->arena_capacity16 <= 0)
         return ADA_EINVAL;
     if (c->page_capacity > INT32_MAX || c->arena_capacity16 > (int64_t)UINT32_MAX) return ADA_EUNSUPPORTED;
+    if (check_dims(cfg, c->num_seqs, c->max_pages_per_head)) return ADA_EUNSUPPORTED;
     if (!c->page_table || !c->num_pages || !c->open_page || !c->page_meta || !c->code_arena || !c->value_pool ||
         !c->alloc || !c->status)
         return ADA_EINVAL;
@@ -69,10 +105,11 @@ int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp, int gv)
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;   // MI355X
-        const int64_t slots = (int64_t)cus * decode_waves_per_simd(gv);
-        const int64_t units = (int64_t)B * cfg->num_kv_heads * maxp;
-        cp = (int)std::min<int64_t>((units + slots - 1) / slots, 1 << 20);
+        const size_t slots = (size_t)cus * decode_waves_per_simd(gv);
+        const size_t units = smul((size_t)B, (size_t)cfg->num_kv_heads, (size_t)maxp);
+        cp = (int)std::min<size_t>(units / slots + (units % slots != 0), 1 << 20);
     }
+    cp = std::min(cp, kMaxChunkPages);
     cp = (cp + tpg - 1) / tpg * tpg;
     if (cp < tpg) cp = tpg;
     if (cp > kMaxChunkPages) cp = kMaxChunkPages;   // page list of a work-group lives in LDS
@@ -89,12 +126,12 @@ struct DecodeWs {
 DecodeWs decode_layout(const ada_config_t *cfg, int32_t B, int32_t Q, int32_t maxp, void *ws) {
     DecodeWs d;
     d.cp = decode_chunk_pages(cfg, B, maxp, Q * (cfg->num_q_heads / cfg->num_kv_heads));
-    d.S = (maxp + d.cp - 1) / d.cp;
-    const size_t rows = (size_t)B * Q * cfg->num_q_heads * d.S;
+    d.S = (int)(((int64_t)maxp + d.cp - 1) / d.cp);
+    const size_t rows = smul((size_t)B, (size_t)Q, (size_t)cfg->num_q_heads, (size_t)d.S);
     Carver c(ws);
     d.pm = c.take<float>(rows);
     d.pl = c.take<float>(rows);
-    d.pacc = c.take<float>(rows * kD);
+    d.pacc = c.take<float>(smul(rows, kD));
     d.bytes = c.off;
     return d;
 }
@@ -145,12 +182,12 @@ struct AppendWs {
 
 AppendWs append_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, void *ws) {
     AppendWs w;
-    const size_t nkeys = (size_t)cache->num_seqs * cfg->num_kv_heads * kNumTiers;
+    const size_t nkeys = smul((size_t)cache->num_seqs, (size_t)cfg->num_kv_heads, kNumTiers);
     Carver c(ws);
     w.key_cnt = c.take<int32_t>(nkeys);
     w.key_c0 = c.take<int32_t>(nkeys);
     w.key_done = c.take<int32_t>(nkeys);
-    w.key_page_and_off = c.take<int32_t>(2 * nkeys);
+    w.key_page_and_off = c.take<int32_t>(smul(2, nkeys));
     w.totals = c.take<int64_t>(2);
     w.dest_page = c.take<int32_t>(n > 0 ? n : 1);
     w.dest_slot = c.take<int32_t>(n > 0 ? n : 1);
@@ -207,15 +244,16 @@ struct PackWs {
 
 PackWs pack_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
     PackWs w;
-    const size_t rows = (size_t)B * cfg->num_kv_heads;
-    w.n_tiles = (int)((stride + 1023) / 1024);
+    const size_t rows = smul((size_t)B, (size_t)cfg->num_kv_heads);
+    const int64_t tiles = stride / 1024 + (stride % 1024 != 0);
+    w.n_tiles = (int)std::min<int64_t>(tiles, INT32_MAX);
     Carver c(ws);
-    w.tile_counts = c.take<int32_t>(rows * w.n_tiles * kNumTiers);
-    w.row_counts = c.take<int32_t>(rows * kNumTiers);
-    w.row_base = c.take<int32_t>(rows * kNumTiers);
-    w.row_unit = c.take<int64_t>(rows * kNumTiers);
-    w.dest_page = c.take<int32_t>(rows * stride);
-    w.dest_slot = c.take<int32_t>(rows * stride);
+    w.tile_counts = c.take<int32_t>(smul(rows, (size_t)tiles, kNumTiers));
+    w.row_counts = c.take<int32_t>(smul(rows, kNumTiers));
+    w.row_base = c.take<int32_t>(smul(rows, kNumTiers));
+    w.row_unit = c.take<int64_t>(smul(rows, kNumTiers));
+    w.dest_page = c.take<int32_t>(smul(rows, (size_t)stride));
+    w.dest_slot = c.take<int32_t>(smul(rows, (size_t)stride));
     w.range = c.take<int32_t>(2);
     w.ctx = c.take<int32_t>(B);
     w.bytes = c.off;
@@ -235,14 +273,15 @@ struct RdrWs {
 RdrWs rdr_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
     RdrWs w;
     Carver c(ws);
-    w.hist = c.take<unsigned long long>((size_t)B * 256);
+    w.hist = c.take<unsigned long long>(smul((size_t)B, 256));
     w.prefix = c.take<unsigned long long>(B);
     w.above = c.take<long long>(B);
     w.all_fit = c.take<int32_t>(B);
     w.ctx = c.take<int32_t>(B);
     w.budget = c.take<int64_t>(B);
-    w.tie_sel = c.take<uint8_t>((size_t)B * cfg->num_kv_heads * stride);
-    w.tie_tile = c.take<long long>((size_t)B * rdr_tie_tiles((int64_t)cfg->num_kv_heads * stride));
+    const size_t row_items = smul((size_t)cfg->num_kv_heads, (size_t)stride);
+    w.tie_sel = c.take<uint8_t>(smul((size_t)B, row_items));
+    w.tie_tile = c.take<long long>(smul((size_t)B, row_items / kRdrTieTile + (row_items % kRdrTieTile != 0)));
     w.bytes = c.off;
     return w;
 }
@@ -284,7 +323,11 @@ ada_status_t rdr_steps(uint32_t mask, int *n_steps, int32_t *step_tier, int64_t 
 extern "C" {
 
 const char *ada_status_str(ada_status_t s) {
-    switch (s) {
+    // a C caller may pass any int; read its bits without an enum load
+    static_assert(sizeof(ada_status_t) == sizeof(int32_t), "status is an int");
+    int32_t v;
+    memcpy(&v, &s, sizeof(v));
+    switch (v) {
         case ADA_OK: return "ADA_OK";
         case ADA_EINVAL: return "ADA_EINVAL: invalid argument or input";
         case ADA_ENOSPC: return "ADA_ENOSPC: cache capacity exceeded";
@@ -308,7 +351,7 @@ size_t ada_lut_floats(const ada_config_t *cfg) {
 ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, void *stream) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
-    if ((st = check_cache(cache))) return st;
+    if ((st = check_cache(cfg, cache))) return st;
     return hip_status(launch_cache_init(cache->num_seqs * cfg->num_kv_heads, cache->num_pages, cache->open_page,
                                         cache->alloc, cache->status, (hipStream_t)stream));
 }
@@ -317,6 +360,7 @@ ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, f
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (B < 0 || (B > 0 && (!q || !lut))) return ADA_EINVAL;
+    if ((st = check_dims(cfg, B, 0))) return st;
     if (B == 0) return ADA_OK;
     return hip_status(launch_build_lut(q, B * cfg->num_q_heads, lut, cfg->pair_layout == ADA_PAIRS_HALF_SPLIT,
                                        (hipStream_t)stream));
@@ -336,8 +380,8 @@ ada_status_t ada_decode_multi_workspace(const ada_config_t *cfg, const ada_cache
     if (st) return st;
     if ((st = check_queries(cfg, Q))) return st;
     if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0) return ADA_EINVAL;
-    *bytes = decode_layout(cfg, B, Q, cache->max_pages_per_head, nullptr).bytes;
-    return ADA_OK;
+    if ((st = check_dims(cfg, B, cache->max_pages_per_head))) return st;
+    return ws_out(decode_layout(cfg, B, Q, cache->max_pages_per_head, nullptr).bytes, bytes);
 }
 
 ada_status_t ada_decode_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, size_t *bytes) {
@@ -349,9 +393,10 @@ static ada_status_t decode_common(const ada_config_t *cfg, const ada_cache_t *ca
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if ((st = check_queries(cfg, Q))) return st;
-    if ((st = check_cache(cache))) return st;
+    if ((st = check_cache(cfg, cache))) return st;
     if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
     *w = decode_layout(cfg, B, Q, cache->max_pages_per_head, ws);
+    if (w->bytes > kMaxWorkspace) return ADA_EUNSUPPORTED;
     if (B > 0 && (!ws || ws_bytes < w->bytes)) return ADA_EINVAL;
     return ADA_OK;
 }
@@ -400,8 +445,7 @@ ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *ca
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!cache || !bytes || n < 0 || cache->num_seqs <= 0) return ADA_EINVAL;
-    *bytes = append_layout(cfg, cache, n, nullptr).bytes;
-    return ADA_OK;
+    return ws_out(append_layout(cfg, cache, n, nullptr).bytes, bytes);
 }
 
 ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, const int32_t *seq,
@@ -409,11 +453,12 @@ ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache
                                void *ws, size_t ws_bytes, void *stream) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
-    if ((st = check_cache(cache))) return st;
+    if ((st = check_cache(cfg, cache))) return st;
     if (n < 0) return ADA_EINVAL;
     if (n == 0) return ADA_OK;
     if (!seq || !kv_head || !tier || !keys || !values) return ADA_EINVAL;
     AppendWs w = append_layout(cfg, cache, n, ws);
+    if (w.bytes > kMaxWorkspace) return ADA_EUNSUPPORTED;
     if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
     AppendLaunch a = make_append(cfg, cache, n, seq, kv_head, tier, keys, values, w);
     return hip_status(launch_append(a, true, (hipStream_t)stream));
@@ -425,8 +470,8 @@ static size_t decode_append_layout(const ada_config_t *cfg, const ada_cache_t *c
                                    DecodeWs *dw, AppendWs *aw) {
     *dw = decode_layout(cfg, B, 1, cache->max_pages_per_head, ws);
     char *ab = ws ? static_cast<char *>(ws) + dw->bytes : nullptr;
-    *aw = append_layout(cfg, cache, B * cfg->num_kv_heads, ab);
-    return dw->bytes + aw->bytes;
+    *aw = append_layout(cfg, cache, (int32_t)std::min<int64_t>((int64_t)B * cfg->num_kv_heads, INT32_MAX), ab);
+    return ws_add(dw->bytes, aw->bytes);
 }
 
 ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
@@ -434,10 +479,10 @@ ada_status_t ada_decode_append_workspace(const ada_config_t *cfg, const ada_cach
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0 || cache->num_seqs <= 0) return ADA_EINVAL;
+    if ((st = check_dims(cfg, B, cache->max_pages_per_head))) return st;
     DecodeWs dw;
     AppendWs aw;
-    *bytes = decode_append_layout(cfg, cache, B, nullptr, &dw, &aw);
-    return ADA_OK;
+    return ws_out(decode_append_layout(cfg, cache, B, nullptr, &dw, &aw), bytes);
 }
 
 ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
@@ -446,13 +491,15 @@ ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache
                                void *stream) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
-    if ((st = check_cache(cache))) return st;
+    if ((st = check_cache(cfg, cache))) return st;
     if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
     if (!q || !out || !new_keys || !new_values || !new_tier || !ws) return ADA_EINVAL;
     DecodeWs dw;
     AppendWs aw;
-    if (ws_bytes < decode_append_layout(cfg, cache, B, ws, &dw, &aw)) return ADA_EINVAL;
+    const size_t need = decode_append_layout(cfg, cache, B, ws, &dw, &aw);
+    if (need > kMaxWorkspace) return ADA_EUNSUPPORTED;
+    if (ws_bytes < need) return ADA_EINVAL;
     const int32_t n = B * cfg->num_kv_heads;
     // 1. book one request per row (row order) and update the metadata
     AppendLaunch ap = make_append(cfg, cache, n, nullptr, nullptr, new_tier, new_keys, new_values, aw);
@@ -473,14 +520,20 @@ ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache
 
 // Utility emission: workspace = decode partials, then the logit buffer
 // [page_capacity * P][G], then an lse buffer [B][Hq] (used when lse is NULL).
+// The split-K pass addresses the logit buffer with 32-bit offsets.
+static ada_status_t check_logit_buf(const ada_config_t *cfg, const ada_cache_t *cache) {
+    const int64_t G = cfg->num_q_heads / cfg->num_kv_heads;
+    return cache->page_capacity > (int64_t)UINT32_MAX / (cfg->page_size * G) ? ADA_EUNSUPPORTED : ADA_OK;
+}
+
 static size_t decode_utility_layout(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *ws,
                                     DecodeWs *dw, float **logit_buf, float **lse_buf) {
     *dw = decode_layout(cfg, B, 1, cache->max_pages_per_head, ws);
     Carver c(ws ? static_cast<char *>(ws) + dw->bytes : nullptr);
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
-    *logit_buf = c.take<float>((size_t)cache->page_capacity * cfg->page_size * G);
-    *lse_buf = c.take<float>((size_t)B * cfg->num_q_heads);
-    return dw->bytes + c.off;
+    *logit_buf = c.take<float>(smul((size_t)cache->page_capacity, (size_t)cfg->page_size, (size_t)G));
+    *lse_buf = c.take<float>(smul((size_t)B, (size_t)cfg->num_q_heads));
+    return ws_add(dw->bytes, c.off);
 }
 
 ada_status_t ada_decode_utility_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
@@ -488,10 +541,10 @@ ada_status_t ada_decode_utility_workspace(const ada_config_t *cfg, const ada_cac
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!cache || !bytes || B < 0 || cache->max_pages_per_head <= 0 || cache->page_capacity <= 0) return ADA_EINVAL;
+    if ((st = check_dims(cfg, B, cache->max_pages_per_head)) || (st = check_logit_buf(cfg, cache))) return st;
     DecodeWs dw;
     float *lb, *sb;
-    *bytes = decode_utility_layout(cfg, cache, B, nullptr, &dw, &lb, &sb);
-    return ADA_OK;
+    return ws_out(decode_utility_layout(cfg, cache, B, nullptr, &dw, &lb, &sb), bytes);
 }
 
 ada_status_t ada_decode_utility(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
@@ -499,13 +552,16 @@ ada_status_t ada_decode_utility(const ada_config_t *cfg, const ada_cache_t *cach
                                 void *stream) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
-    if ((st = check_cache(cache))) return st;
+    if ((st = check_cache(cfg, cache))) return st;
+    if ((st = check_logit_buf(cfg, cache))) return st;
     if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
     if (!q || !out || !util || !ws) return ADA_EINVAL;
     DecodeWs dw;
     float *logit_buf, *lse_buf;
-    if (ws_bytes < decode_utility_layout(cfg, cache, B, ws, &dw, &logit_buf, &lse_buf)) return ADA_EINVAL;
+    const size_t need = decode_utility_layout(cfg, cache, B, ws, &dw, &logit_buf, &lse_buf);
+    if (need > kMaxWorkspace) return ADA_EUNSUPPORTED;
+    if (ws_bytes < need) return ADA_EINVAL;
     DecodeLaunch a = make_decode(cfg, cache, q, B, 1, scale, out, lse ? lse : lse_buf, dw);
     a.logit_buf = logit_buf;
     a.util = util;
@@ -519,8 +575,7 @@ ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_s
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!bytes || B < 0 || ctx_stride < 0) return ADA_EINVAL;
-    *bytes = rdr_layout(cfg, B, ctx_stride, nullptr).bytes;
-    return ADA_OK;
+    return ws_out(rdr_layout(cfg, B, ctx_stride, nullptr).bytes, bytes);
 }
 
 ada_status_t ada_rdr_assign(const ada_config_t *cfg, int32_t B, const int32_t *ctx_len, int64_t ctx_stride,
@@ -531,13 +586,15 @@ ada_status_t ada_rdr_assign(const ada_config_t *cfg, int32_t B, const int32_t *c
     if (B < 0 || ctx_stride <= 0) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
     if (!ctx_len || !utility || !budget || !tier_out || !status) return ADA_EINVAL;
-    if ((int64_t)cfg->num_kv_heads * ctx_stride > INT32_MAX) return ADA_EUNSUPPORTED;
+    if (ctx_stride > INT32_MAX / cfg->num_kv_heads) return ADA_EUNSUPPORTED;
     for (int b = 0; b < B; ++b)
         if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride || budget[b] < 0) return ADA_EINVAL;
     RdrLaunch a;
     const uint32_t mask = cfg->rdr_tier_mask ? cfg->rdr_tier_mask : 7u;
     if ((st = rdr_steps(mask, &a.n_steps, a.step_tier, a.dR, a.c))) return st;
+    if ((int64_t)B * cfg->num_kv_heads > INT32_MAX) return ADA_EUNSUPPORTED;
     RdrWs w = rdr_layout(cfg, B, ctx_stride, ws);
+    if (w.bytes > kMaxWorkspace) return ADA_EUNSUPPORTED;
     if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (hipMemcpyAsync(w.ctx, ctx_len, sizeof(int32_t) * B, hipMemcpyHostToDevice, s) != hipSuccess) return ADA_EHIP;
@@ -566,8 +623,7 @@ ada_status_t ada_pack_workspace(const ada_config_t *cfg, const ada_cache_t *cach
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!cache || !bytes || B < 0 || ctx_stride < 0) return ADA_EINVAL;
-    *bytes = pack_layout(cfg, B, ctx_stride, nullptr).bytes;
-    return ADA_OK;
+    return ws_out(pack_layout(cfg, B, ctx_stride, nullptr).bytes, bytes);
 }
 
 ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, const int32_t *ctx_len,
@@ -575,7 +631,7 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
                       size_t ws_bytes, void *stream) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
-    if ((st = check_cache(cache))) return st;
+    if ((st = check_cache(cfg, cache))) return st;
     if (B < 0 || B > cache->num_seqs || ctx_stride <= 0) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
     if (!ctx_len || !tier || !keys || !values) return ADA_EINVAL;
@@ -583,6 +639,7 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     for (int b = 0; b < B; ++b)
         if (ctx_len[b] < 0 || ctx_len[b] > ctx_stride) return ADA_EINVAL;
     PackWs w = pack_layout(cfg, B, ctx_stride, ws);
+    if (w.bytes > kMaxWorkspace) return ADA_EUNSUPPORTED;
     if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (hipMemcpyAsync(w.ctx, ctx_len, sizeof(int32_t) * B, hipMemcpyHostToDevice, s) != hipSuccess) return ADA_EHIP;
@@ -642,7 +699,7 @@ struct RepackWs {
 static RepackWs repack_layout(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, void *ws) {
     RepackWs r;
     const int64_t S = (int64_t)src->max_pages_per_head * cfg->page_size;
-    const size_t n = (size_t)B * cfg->num_kv_heads * S;
+    const size_t n = smul((size_t)B, (size_t)cfg->num_kv_heads, (size_t)S);
     Carver c(ws);
     r.util_v = c.take<float>(n);
     r.cap_v = c.take<int8_t>(n);
@@ -651,8 +708,10 @@ static RepackWs repack_layout(const ada_config_t *cfg, const ada_cache_t *src, i
     r.rdr = c.take<char>(rb);
     const size_t pb = pack_layout(cfg, B, S, nullptr).bytes;
     r.pack = c.take<char>(pb);
-    r.src_of_slot_pages = (int64_t)B * cfg->num_kv_heads * repack_pages_per_row(src->max_pages_per_head);
-    r.src_of_slot = c.take<int4>((size_t)r.src_of_slot_pages * cfg->page_size);
+    const size_t pages =
+        smul((size_t)B, (size_t)cfg->num_kv_heads, (size_t)repack_pages_per_row(src->max_pages_per_head));
+    r.src_of_slot_pages = (int64_t)std::min<size_t>(pages, INT64_MAX);
+    r.src_of_slot = c.take<int4>(smul(pages, (size_t)cfg->page_size));
     r.bytes = c.off;
     return r;
 }
@@ -661,24 +720,25 @@ ada_status_t ada_repack_workspace(const ada_config_t *cfg, const ada_cache_t *sr
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!src || !bytes || B < 0 || src->max_pages_per_head <= 0) return ADA_EINVAL;
-    *bytes = repack_layout(cfg, src, B, nullptr).bytes;
-    return ADA_OK;
+    if ((st = check_dims(cfg, B, src->max_pages_per_head))) return st;
+    return ws_out(repack_layout(cfg, src, B, nullptr).bytes, bytes);
 }
 
 ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t B, const float *util,
                         const int64_t *budget, const ada_cache_t *dst, void *ws, size_t ws_bytes, void *stream) {
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
-    if ((st = check_cache(src)) || (st = check_cache(dst))) return st;
+    if ((st = check_cache(cfg, src)) || (st = check_cache(cfg, dst))) return st;
     if (B < 0 || B > src->num_seqs || B > dst->num_seqs) return ADA_EINVAL;
     if (B == 0) return ADA_OK;
     if (!util || !budget || !ws) return ADA_EINVAL;
     const int P = cfg->page_size;
     const int64_t S = (int64_t)src->max_pages_per_head * P;
-    if ((int64_t)cfg->num_kv_heads * S > INT32_MAX) return ADA_EUNSUPPORTED;
+    if (S > INT32_MAX / cfg->num_kv_heads) return ADA_EUNSUPPORTED;
     for (int b = 0; b < B; ++b)
         if (budget[b] < 0) return ADA_EINVAL;
     RepackWs r = repack_layout(cfg, src, B, ws);
+    if (r.bytes > kMaxWorkspace) return ADA_EUNSUPPORTED;
     if (ws_bytes < r.bytes) return ADA_EINVAL;
     RdrLaunch ra;
     const uint32_t mask = cfg->rdr_tier_mask ? cfg->rdr_tier_mask : 7u;
@@ -794,8 +854,8 @@ ada_status_t ada_dense_workspace(const ada_config_t *cfg, int32_t B, int32_t max
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (!bytes || B < 0 || max_pages_per_head <= 0) return ADA_EINVAL;
-    *bytes = decode_layout(cfg, B, 1, max_pages_per_head, nullptr).bytes;
-    return ADA_OK;
+    if ((st = check_dims(cfg, B, max_pages_per_head))) return st;
+    return ws_out(decode_layout(cfg, B, 1, max_pages_per_head, nullptr).bytes, bytes);
 }
 
 ada_status_t ada_dense_decode(const ada_config_t *cfg, int32_t B, int32_t max_pages_per_head,
@@ -805,9 +865,11 @@ ada_status_t ada_dense_decode(const ada_config_t *cfg, int32_t B, int32_t max_pa
     ada_status_t st = check_cfg(cfg);
     if (st) return st;
     if (B < 0 || max_pages_per_head <= 0) return ADA_EINVAL;
+    if ((st = check_dims(cfg, B, max_pages_per_head))) return st;
     if (B == 0) return ADA_OK;
     if (!page_table || !ctx_len || !k_pool || !v_pool || !q || !out) return ADA_EINVAL;
     DecodeWs w = decode_layout(cfg, B, 1, max_pages_per_head, ws);
+    if (w.bytes > kMaxWorkspace) return ADA_EUNSUPPORTED;
     if (!ws || ws_bytes < w.bytes) return ADA_EINVAL;
     DenseLaunch a;
     a.page_table = page_table;

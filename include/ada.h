@@ -73,6 +73,10 @@
  *    word; the writing kernels of that call then do nothing (all-or-nothing)
  *    and the caller reads and clears the word with ada_read_status.  Calls
  *    made while the status word is non-zero do not modify the cache.
+ *  - Shape limits, checked on the host (ADA_EUNSUPPORTED): B * num_q_heads
+ *    and max_pages_per_head * page_size fit in int32; a workspace never
+ *    exceeds 2^48 bytes (a query that would need more returns
+ *    ADA_EUNSUPPORTED instead of a wrapped size).
  *  - No C++ exception crosses this boundary.
  */
 #ifndef ADA_H
@@ -235,7 +239,9 @@ ada_status_t ada_encode_append(const ada_config_t *cfg, const ada_cache_t *cache
                                void *stream);
 
 /* Workspace bytes for ada_decode_utility on sequences 0..B-1 (grows with
- * the cache's page_capacity: 4 * P * Hq/Hkv bytes per page). */
+ * the cache's page_capacity: 4 * P * Hq/Hkv bytes per page).  The logit
+ * buffer is addressed with 32-bit offsets: page_capacity * P * Hq/Hkv must
+ * not exceed 2^32 - 1, else ADA_EUNSUPPORTED (here and in the call). */
 ada_status_t ada_decode_utility_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B,
                                           size_t *bytes);
 
