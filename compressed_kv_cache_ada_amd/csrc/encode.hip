@@ -127,29 +127,62 @@ __device__ inline void zero_token(uint8_t *dblk, int slot, int P) {
     reinterpret_cast<uint16_t *>(dblk)[slot] = 0;
 }
 
-// One work-group of 128 threads per new destination page (grid-stride);
-// no LDS and no barrier, so many pages are in flight per compute unit.  Every
-// byte of the page's code block and value page is written, slots past the
-// count as zeros.  Threads 0..P-1 transcode one token each.  The value page
-// is assembled one (8-token group, dimension) 16-byte word per thread: the
-// group's eight source entries are the same for the whole work-group, and
-// each source token's value word for that dimension is one 16-byte load (of
-// which the token's 2 bytes are kept, so source value words shared by pages
-// written far apart in time are fetched again).
+// One work-group of 128 threads per new destination page (grid-stride).
+// Every byte of the page's code block and value page is written, slots past
+// the count as zeros.  The page's source entries {page, slot, tier, code
+// offset} pass through LDS once; then each thread (one dimension) issues the
+// loads of all P source values of its dimension together (the 4-byte word
+// holding a token's fp16 value, or a V8 token's code and scale bytes) while
+// threads 0..P-1 transcode one token's codes each.  A page thus costs three
+// dependent memory steps: its metadata, its entries, its codes and values.
+template <int P>
 __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
-    if (read_status(a.status) != 0) return;
+    __shared__ int4 s_ent[P];
+    __shared__ int s_stop;
+    const int tid = threadIdx.x, dim = tid;
+    // one reading of the status word for the whole work-group: its waves
+    // must agree, since they meet at barriers below
+    if (tid == 0) s_stop = read_status(a.status);
+    __syncthreads();
+    if (s_stop != 0) return;
     const int first = a.n_new[0], n = a.n_new[1];
-    const int P = a.P;
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
         if (i >= a.src_of_slot_pages) break;   // bounded by construction
         const int page = first + i;
         const ada_page_meta_t m = a.page_meta[page];
         const int count = m.count, tier = m.tier;
-        const int4 *ent = a.src_of_slot + (int64_t)i * P;   // {page, slot, tier, code_off16}
-        if (threadIdx.x < P) {
+        int4 e = make_int4(-1, 0, 0, 0);   // page -1: empty slot
+        if (tid < P) {
+            if (tid < count) e = a.src_of_slot[(int64_t)i * P + tid];
+            s_ent[tid] = e;
+        }
+        __syncthreads();
+
+        // 1. this dimension's value of every source token, all loads issued
+        //    before any is used (branch-free: an empty slot reads the pool's
+        //    first word, unused).  fp16 source: the dword holding the value
+        //    (twice); V8 source: the dwords holding its code and scale bytes.
+        uint32_t wa[P], wb[P];
+        const uint8_t *pool = reinterpret_cast<const uint8_t *>(a.src_value_pool);
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int4 ek = s_ent[k];
+            const int idx = ek.y & 7;
+            const size_t grp = (size_t)max(ek.x, 0) * P * kD * 2 + (ek.y >> 3) * (tier_v8(ek.z) ? kV8Group : 2048);
+            size_t oa = grp + dim * 16 + (idx >> 1) * 4, ob = oa;
+            if (tier_v8(ek.z)) {
+                oa = grp + kV8Codes + dim * 8 + (idx & 4);
+                ob = grp + idx * 4;
+            }
+            if (ek.x < 0) oa = ob = 0;
+            wa[k] = *reinterpret_cast<const uint32_t *>(pool + oa);
+            wb[k] = *reinterpret_cast<const uint32_t *>(pool + ob);
+        }
+
+        // 2. threads 0..P-1: token tid's codes
+        if (tid < P) {
             uint8_t *dblk = a.arena + (size_t)m.code_off16 * 16;
-            const int k = threadIdx.x;
-            const int4 e = k < count ? ent[k] : make_int4(0, 0, 0, 0);
+            const int k = tid;
             // key tiers (0 T8, 1 T4, 2 T2) of source and destination
             const int st = key_tier(e.z), dt = key_tier(tier);
             const bool upgrade = k < count && (st > dt || (tier_v8(e.z) && !tier_v8(tier)));
@@ -169,43 +202,27 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
                 else transcode_token<2, 2>(sblk, sslot, dblk, k, P);
             }
         }
+
+        // 3. the value page, one (8-token group, dimension) word per thread
+        //    and group; a V8 source is decoded first (its values are fp16
+        //    numbers exactly)
         uint16_t *dv = a.value_pool + (size_t)page * P * kD;
         uint8_t *dvb = reinterpret_cast<uint8_t *>(dv);
-        const int dim = threadIdx.x;
         const bool dst_v8 = tier_v8(tier);
+#pragma unroll
         for (int g = 0; g < P / 8; ++g) {
-            int4 e[8];   // source {page, slot, tier, -} of the group's tokens (page -1: empty slot)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int sl = g * 8 + k;
-                e[k] = sl < count ? ent[sl] : make_int4(-1, 0, 0, 0);
-            }
-            // fp16 sources: one 16-byte value word (8 tokens of this dimension) each
-            uint4 seg[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                seg[k] = make_uint4(0u, 0u, 0u, 0u);
-                if (e[k].x >= 0 && !tier_v8(e[k].z))
-                    seg[k] = *reinterpret_cast<const uint4 *>(a.src_value_pool + (size_t)e[k].x * P * kD +
-                                                              (e[k].y >> 3) * 1024 + dim * 8);
-            }
-            // each token's value in this dimension as fp16 bits (a V8 source
-            // is decoded: its values are fp16 numbers exactly)
             uint32_t h[8];
+            bool live[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int idx = e[k].y & 7;
-                if (e[k].x < 0) {
-                    h[k] = 0u;
-                } else if (tier_v8(e[k].z)) {
-                    const uint8_t *sb = reinterpret_cast<const uint8_t *>(a.src_value_pool + (size_t)e[k].x * P * kD) +
-                                        (e[k].y >> 3) * kV8Group;
-                    h[k] = v8_value_bits((int)sb[kV8Codes + dim * 8 + idx] - 128, sb[idx * 4 + (dim >> 5)]);
-                } else {
-                    const int q = idx >> 1;
-                    const uint32_t word = q == 0 ? seg[k].x : q == 1 ? seg[k].y : q == 2 ? seg[k].z : seg[k].w;
-                    h[k] = (word >> ((idx & 1) * 16)) & 0xFFFFu;
-                }
+                const int4 ek = s_ent[8 * g + k];
+                const uint32_t ra = wa[8 * g + k], rb = wb[8 * g + k];
+                const int idx = ek.y & 7;
+                live[k] = ek.x >= 0;
+                if (!live[k]) h[k] = 0u;
+                else if (tier_v8(ek.z))
+                    h[k] = v8_value_bits((int)((ra >> (8 * (idx & 3))) & 0xFFu) - 128, (rb >> (8 * (dim >> 5))) & 0xFFu);
+                else h[k] = (ra >> ((idx & 1) * 16)) & 0xFFFFu;
             }
             if (!dst_v8) {
                 uint32_t w[4];
@@ -220,15 +237,15 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
                 uint8_t sbytes[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    int m = (int)(h[k] & 0x7FFFu);
-                    m = max(m, __shfl_xor(m, 1, 64));
-                    m = max(m, __shfl_xor(m, 2, 64));
-                    m = max(m, __shfl_xor(m, 4, 64));
-                    m = max(m, __shfl_xor(m, 8, 64));
-                    m = max(m, __shfl_xor(m, 16, 64));
-                    const int ex = enc::v8_exponent((uint32_t)m);
-                    const uint32_t c = e[k].x >= 0 ? (uint32_t)(enc::v8_code(h[k], ex) + 128) : 0u;
-                    const uint32_t sbyte = e[k].x >= 0 ? (uint32_t)(ex + 127) : 0u;
+                    int mx = (int)(h[k] & 0x7FFFu);
+                    mx = max(mx, __shfl_xor(mx, 1, 64));
+                    mx = max(mx, __shfl_xor(mx, 2, 64));
+                    mx = max(mx, __shfl_xor(mx, 4, 64));
+                    mx = max(mx, __shfl_xor(mx, 8, 64));
+                    mx = max(mx, __shfl_xor(mx, 16, 64));
+                    const int ex = enc::v8_exponent((uint32_t)mx);
+                    const uint32_t c = live[k] ? (uint32_t)(enc::v8_code(h[k], ex) + 128) : 0u;
+                    const uint32_t sbyte = live[k] ? (uint32_t)(ex + 127) : 0u;
                     cw[k >> 2] |= c << (8 * (k & 3));
                     sbytes[k] = (uint8_t)sbyte;
                 }
@@ -239,8 +256,9 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
             }
         }
         if (dst_v8)   // the rest of the page's value slot is zero
-            for (int i = (P / 8) * kV8Group / 16 + threadIdx.x; i < P * kD * 2 / 16; i += 128)
-                reinterpret_cast<uint4 *>(dvb)[i] = make_uint4(0u, 0u, 0u, 0u);
+            for (int j = (P / 8) * kV8Group / 16 + tid; j < P * kD * 2 / 16; j += 128)
+                reinterpret_cast<uint4 *>(dvb)[j] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();   // s_ent is refilled for the next page
     }
 }
 
@@ -870,7 +888,9 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(pack_dest_kernel, dim3(a.n_tiles, rows), dim3(256), 0, s, a);
     const int64_t max_pages = (int64_t)rows * a.maxp;
     if (a.src_page_table) {   // re-pack: the transcoder writes every byte of each new page
-        hipLaunchKernelGGL(transcode_pages_kernel, dim3(grid_for(a.src_of_slot_pages, 1, 65536)), dim3(128), 0, s, a);
+        const dim3 grid(grid_for(a.src_of_slot_pages, 1, 65536));
+        if (a.P == 16) hipLaunchKernelGGL(transcode_pages_kernel<16>, grid, dim3(128), 0, s, a);
+        else hipLaunchKernelGGL(transcode_pages_kernel<32>, grid, dim3(128), 0, s, a);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_pages, 1, 4096)), dim3(256), 0, s,
