@@ -96,3 +96,33 @@ def test_host_validation_without_gpu():
     # RDR: unsupported tier set is caught on the host (T8 + T4 only is fine; 0 = all)
     assert _size(L.ada_rdr_workspace, ctypes.byref(good), 2, 100)[0] == ada.OK
     assert L.ada_probe_copy(None, None, 16, None) == ada.EINVAL
+
+
+def test_shape_limits_and_workspace_ceiling():
+    """Shapes the kernels index with 32-bit integers, and workspaces past
+    2^48 bytes, are refused on the host (ADA_EUNSUPPORTED) rather than
+    reported as a wrapped size."""
+    L = ada.lib()
+    cfg = ada.make_config(16, 32, 8)
+    c = ctypes.byref(cfg)
+    I32 = 2 ** 31 - 1
+    big = ada.CacheDesc(64, 4096, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+    assert _size(L.ada_decode_workspace, c, ctypes.byref(big), 64)[0] == ada.OK
+    # B * Hq past int32
+    assert _size(L.ada_decode_workspace, c, ctypes.byref(big), I32 // 32 + 1)[0] == ada.EUNSUPPORTED
+    assert _size(L.ada_decode_workspace, c, ctypes.byref(big), I32 // 32)[0] == ada.OK
+    # max_pages_per_head * P past int32
+    wide = ada.CacheDesc(1, I32 // 16 + 1, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+    assert _size(L.ada_decode_workspace, c, ctypes.byref(wide), 1)[0] == ada.EUNSUPPORTED
+    assert _size(L.ada_dense_workspace, c, 1, I32 // 16 + 1)[0] == ada.EUNSUPPORTED
+    # the utility logit buffer: page_capacity * P * G within uint32
+    G = 4
+    cap_ok = (2 ** 32 - 1) // (16 * G)
+    for cap, want in ((cap_ok, ada.OK), (cap_ok + 1, ada.EUNSUPPORTED)):
+        d = ada.CacheDesc(2, 64, cap, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+        assert _size(L.ada_decode_utility_workspace, c, ctypes.byref(d), 2)[0] == want
+    # a pack workspace that would pass 2^48 bytes
+    assert _size(L.ada_pack_workspace, c, ctypes.byref(big), 64, 2 ** 40)[0] == ada.EUNSUPPORTED
+    st, n = _size(L.ada_pack_workspace, c, ctypes.byref(big), 64, 1 << 20)
+    assert st == ada.OK and 0 < n <= 2 ** 48
+    assert _size(L.ada_rdr_workspace, c, I32, 2 ** 62)[0] == ada.EUNSUPPORTED
