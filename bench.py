@@ -213,6 +213,28 @@ def main():
         torch.cuda.synchronize()
         r_ms = e0.elapsed_time(e1) / args.steps
 
+    # the same step captured once in a HIP graph and replayed K times (a
+    # serving loop's form: no per-launch host work between the kernels)
+    graph_ms = None
+    if Q == 1:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graph
+
     # cold steps: before each, 1 GiB of another buffer is streamed through the
     # caches with a read kernel (the 256 MB last-level cache then holds clean
     # lines of that buffer, so no write-back is charged to the decode)
@@ -293,6 +315,7 @@ def main():
             "reduce_kernel_ms": r_ms,
             "algorithmic_bytes": alg_bytes,
         },
+        "graph_ms_per_step": graph_ms,
         "step_hbm_gbps": (alg_bytes + B * Q * Hq * 512) / (ms_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w["ctx_len"].sum()) * Hkv / (ms_step * 1e-3),
         "cold_kernel_ms_median": float(np.median(cold)) if cold else None,
