@@ -573,8 +573,14 @@ def cpu_baseline(w, kept_total, max_row, n_pages, units, min_seconds=10.0, max_s
     t0 = time.perf_counter()
     O.decode(one, w["q"][:1], w["scale"], nthreads=1)
     dt1 = time.perf_counter() - t0
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": kept_total * steps / dt, "unit": "KV token-heads/s", "cores": cores, "kind": "oracle",
-            "seconds": dt,
+            "seconds": dt, "cpu_model": cpu_model, "nproc": os.cpu_count(),
             "sample": f"{steps} decode steps over all {B} sequences (all heads, all kept tokens, "
                       f"{kept_total} token-heads per step), same queries each step",
             "single_thread": {"value": kept0 / dt1, "seconds": dt1,
