@@ -464,7 +464,12 @@ __global__ __launch_bounds__(core::kReduceThreads) void decode_reduce_kernel(Dec
     const int b = vr / (a.Hkv * GV), rem = vr % (a.Hkv * GV);
     const int h = rem / GV, v = rem % GV;
     const size_t orow = ((size_t)b * a.Q + v / Gr) * a.Hq + (size_t)h * Gr + v % Gr;
-    const int np = a.num_pages[b * a.Hkv + h];
+    // the page count as a per-lane load (an opaque zero offset): waiting for
+    // a scalar load would also wait for the launch arguments' loads, which
+    // must land before the first partials are requested
+    uint32_t z = 0;
+    asm volatile("" : "+v"(z));
+    const int np = a.num_pages[b * a.Hkv + h + z];
     core::reduce_chunks(a.pm, a.pl, a.pacc, a.S, core::chunks_with_data(np, 64 / a.P, a.S), (size_t)vr, orow,
                         threadIdx.x, a.out, a.lse);
 }

@@ -133,7 +133,10 @@ struct CoreSmem {
 // Reduction pass.  One thread per (sequence, query head, dimension): a
 // running merge over the chunks' partials in tiles of kReduceTile chunks
 // whose loads are all issued before any arithmetic, so a tile costs one
-// memory round trip and no barrier.  The order is fixed: deterministic.
+// memory round trip and no barrier.  The first tile is requested before the
+// row's chunk count nc is known (its slots past nc hold nothing of this
+// launch and are masked), so a row of up to kReduceTile chunks costs one
+// round trip in all.  The order is fixed: deterministic.
 constexpr int kReduceThreads = 128;
 constexpr int kReduceTile = 16;
 
@@ -142,30 +145,50 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
                                               size_t prow, size_t orow, int d, float *out, float *lse) {
     const size_t base = prow * S;
     float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += kReduceTile) {
-        float mv[kReduceTile], lv[kReduceTile], av[kReduceTile];
-#pragma unroll
-        for (int i = 0; i < kReduceTile; ++i) {
-            const int c = min(c0 + i, nc - 1);   // in range; repeats are masked below
-            mv[i] = pm[base + c];
-            lv[i] = pl[base + c];
-            av[i] = pacc[(base + c) * kD + d];
-        }
+    float mv[kReduceTile], lv[kReduceTile], av[kReduceTile];
+    // merges chunks c0 .. c0 + kReduceTile - 1 below nc from mv / lv / av
+    // (branch-free, so the tile's loads are not held back behind a test:
+    // while no chunk had a kept token, M = -inf and L = O = 0 stay so)
+    auto merge = [&](int c0) {
         float Mt = M;
 #pragma unroll
         for (int i = 0; i < kReduceTile; ++i)
             if (c0 + i < nc) Mt = fmaxf(Mt, mv[i]);
-        if (Mt == -INFINITY) continue;       // no kept token so far (uniform)
         const float so = (M == -INFINITY) ? 0.f : exp2f(M - Mt);
         L *= so;
         O *= so;
 #pragma unroll
         for (int i = 0; i < kReduceTile; ++i) {
-            const float f = (c0 + i < nc && mv[i] != -INFINITY) ? exp2f(mv[i] - Mt) : 0.f;
-            L = fmaf(lv[i], f, L);
-            O = fmaf(av[i], f, O);
+            if (c0 + i < nc && mv[i] != -INFINITY) {   // masked slots may hold anything
+                const float f = exp2f(mv[i] - Mt);
+                L = fmaf(lv[i], f, L);
+                O = fmaf(av[i], f, O);
+            }
         }
         M = Mt;
+    };
+    // the chunk scalars as per-lane loads (an opaque zero offset), so that
+    // the whole first tile is in flight before the chunk count arrives
+    uint32_t z = 0;
+    asm volatile("" : "+v"(z));
+#pragma unroll
+    for (int i = 0; i < kReduceTile; ++i) {
+        const int c = min(i, S - 1);   // a slot of the row's S; chunks at or past nc are masked
+        mv[i] = pm[base + c + z];
+        lv[i] = pl[base + c + z];
+        av[i] = pacc[(base + c) * kD + d];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the merge starts
+    merge(0);
+    for (int c0 = kReduceTile; c0 < nc; c0 += kReduceTile) {
+#pragma unroll
+        for (int i = 0; i < kReduceTile; ++i) {
+            const int c = min(c0 + i, nc - 1);   // in range; repeats are masked
+            mv[i] = pm[base + c];
+            lv[i] = pl[base + c];
+            av[i] = pacc[(base + c) * kD + d];
+        }
+        merge(c0);
     }
     if (M == -INFINITY) {
         out[orow * kD + d] = 0.f;
