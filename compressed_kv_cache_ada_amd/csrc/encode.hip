@@ -127,17 +127,19 @@ __device__ inline void zero_token(uint8_t *dblk, int slot, int P) {
     reinterpret_cast<uint16_t *>(dblk)[slot] = 0;
 }
 
-// One work-group of 128 threads per new destination page (grid-stride).
-// Every byte of the page's code block and value page is written, slots past
-// the count as zeros.  The page's source entries {page, slot, tier, code
-// offset} pass through LDS once; then each thread (one dimension) issues the
-// loads of all P source values of its dimension together (the 4-byte word
-// holding a token's fp16 value, or a V8 token's code and scale bytes) while
-// threads 0..P-1 transcode one token's codes each.  A page thus costs three
-// dependent memory steps: its metadata, its entries, its codes and values.
+// About one round of resident 128-thread work-groups, each writing new
+// destination pages in turn (grid-stride).  Every byte of a page's code
+// block and value page is written, slots past the count as zeros.  A page's
+// source entries {page, slot, tier, code offset} pass through LDS once; each
+// thread (one dimension) then issues the loads of all P source values of its
+// dimension together (the 4-byte word holding a token's fp16 value, or a V8
+// token's code and scale bytes) while threads 0..P-1 transcode one token's
+// codes each.  The next page's metadata and entries are requested while the
+// current page is written, so a page costs one dependent memory step of its
+// own (its codes and values) besides the stores.
 template <int P>
 __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
-    __shared__ int4 s_ent[P];
+    __shared__ int4 s_ent[2][P];   // the current page's source entries, and the next page's
     __shared__ int s_stop;
     const int tid = threadIdx.x, dim = tid;
     // one reading of the status word for the whole work-group: its waves
@@ -145,18 +147,33 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
     if (tid == 0) s_stop = read_status(a.status);
     __syncthreads();
     if (s_stop != 0) return;
-    const int first = a.n_new[0], n = a.n_new[1];
-    for (int i = blockIdx.x; i < n; i += gridDim.x) {
-        if (i >= a.src_of_slot_pages) break;   // bounded by construction
+    const int first = a.n_new[0];
+    const int n = (int)min((int64_t)a.n_new[1], a.src_of_slot_pages);   // bounded by construction
+    // the next page's metadata and entries are requested while the current
+    // page is written (entries past a page's count are empty)
+    auto fetch = [&](int i, ada_page_meta_t &m, int4 &e) {
+        m = a.page_meta[first + i];
+        e = tid < P ? a.src_of_slot[(int64_t)i * P + tid] : make_int4(-1, 0, 0, 0);
+    };
+    auto publish = [&](int buf, const ada_page_meta_t &m, const int4 &e) {
+        if (tid < P) s_ent[buf][tid] = tid < (int)m.count ? e : make_int4(-1, 0, 0, 0);
+    };
+    int i = blockIdx.x;
+    if (i >= n) return;
+    ada_page_meta_t m;
+    int4 e_raw;
+    fetch(i, m, e_raw);
+    publish(0, m, e_raw);
+    __syncthreads();
+    for (int buf = 0; i < n; i += gridDim.x, buf ^= 1) {
         const int page = first + i;
-        const ada_page_meta_t m = a.page_meta[page];
         const int count = m.count, tier = m.tier;
-        int4 e = make_int4(-1, 0, 0, 0);   // page -1: empty slot
-        if (tid < P) {
-            if (tid < count) e = a.src_of_slot[(int64_t)i * P + tid];
-            s_ent[tid] = e;
-        }
-        __syncthreads();
+        const int inext = i + gridDim.x;
+        ada_page_meta_t m_next = m;
+        int4 e_next = make_int4(-1, 0, 0, 0);
+        if (inext < n) fetch(inext, m_next, e_next);
+        const int4 (&s_cur)[P] = s_ent[buf];
+        const int4 e = tid < P ? s_cur[tid] : make_int4(-1, 0, 0, 0);
 
         // 1. this dimension's value of every source token, all loads issued
         //    before any is used (branch-free: an empty slot reads the pool's
@@ -166,7 +183,7 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
         const uint8_t *pool = reinterpret_cast<const uint8_t *>(a.src_value_pool);
 #pragma unroll
         for (int k = 0; k < P; ++k) {
-            const int4 ek = s_ent[k];
+            const int4 ek = s_cur[k];
             const int idx = ek.y & 7;
             const size_t grp = (size_t)max(ek.x, 0) * P * kD * 2 + (ek.y >> 3) * (tier_v8(ek.z) ? kV8Group : 2048);
             size_t oa = grp + dim * 16 + (idx >> 1) * 4, ob = oa;
@@ -215,7 +232,7 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
             bool live[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int4 ek = s_ent[8 * g + k];
+                const int4 ek = s_cur[8 * g + k];
                 const uint32_t ra = wa[8 * g + k], rb = wb[8 * g + k];
                 const int idx = ek.y & 7;
                 live[k] = ek.x >= 0;
@@ -258,7 +275,9 @@ __global__ __launch_bounds__(128) void transcode_pages_kernel(PackLaunch a) {
         if (dst_v8)   // the rest of the page's value slot is zero
             for (int j = (P / 8) * kV8Group / 16 + tid; j < P * kD * 2 / 16; j += 128)
                 reinterpret_cast<uint4 *>(dvb)[j] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();   // s_ent is refilled for the next page
+        if (inext < n) publish(buf ^ 1, m_next, e_next);
+        m = m_next;
+        __syncthreads();   // the next page's entries are in place; this page's buffer is refilled after the next barrier
     }
 }
 
@@ -888,7 +907,11 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(pack_dest_kernel, dim3(a.n_tiles, rows), dim3(256), 0, s, a);
     const int64_t max_pages = (int64_t)rows * a.maxp;
     if (a.src_page_table) {   // re-pack: the transcoder writes every byte of each new page
-        const dim3 grid(grid_for(a.src_of_slot_pages, 1, 65536));
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        const dim3 grid(grid_for(a.src_of_slot_pages, 1, 8 * cus));   // about one round of resident work-groups
         if (a.P == 16) hipLaunchKernelGGL(transcode_pages_kernel<16>, grid, dim3(128), 0, s, a);
         else hipLaunchKernelGGL(transcode_pages_kernel<32>, grid, dim3(128), 0, s, a);
         return hipGetLastError();
