@@ -273,10 +273,10 @@ struct RdrWs {
 RdrWs rdr_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws) {
     RdrWs w;
     Carver c(ws);
-    w.hist = c.take<unsigned long long>(smul((size_t)B, 256));
-    w.prefix = c.take<unsigned long long>(B);
-    w.above = c.take<long long>(B);
-    w.all_fit = c.take<int32_t>(B);
+    w.hist = c.take<unsigned long long>(smul((size_t)B, 256 * kRdrPasses));
+    w.prefix = c.take<unsigned long long>(smul((size_t)B, kRdrPasses + 1));
+    w.above = c.take<long long>(smul((size_t)B, kRdrPasses + 1));
+    w.all_fit = c.take<int32_t>(smul((size_t)B, kRdrPasses + 1));
     w.ctx = c.take<int32_t>(B);
     w.budget = c.take<int64_t>(B);
     const size_t row_items = smul((size_t)cfg->num_kv_heads, (size_t)stride);

@@ -224,15 +224,18 @@ struct RdrLaunch {
     int32_t step_tier[kNumTiers];
     int64_t dR[kNumTiers];
     double c[kNumTiers];
-    // workspace
-    unsigned long long *hist;   // [B][256]
-    unsigned long long *prefix; // [B]
-    long long *above;           // [B]
-    int32_t *all_fit;           // [B]
+    // workspace: the radix select's histograms, one per pass, and its state
+    // (chosen key bytes, bytes above them, "everything fits") before each
+    // pass v = 0 .. kRdrPasses - 1 and after the last (v = kRdrPasses)
+    unsigned long long *hist;   // [kRdrPasses][B][256]
+    unsigned long long *prefix; // [kRdrPasses + 1][B]
+    long long *above;           // [kRdrPasses + 1][B]
+    int32_t *all_fit;           // [kRdrPasses + 1][B]
     uint8_t *tie_sel;           // [B][Hkv][stride]
     long long *tie_tile;        // [B][rdr_tie_tiles(Hkv * stride)]: tie bytes per tile, then their prefix
     const int8_t *cap;          // optional [B][Hkv][stride]: steps an item may take
 };
+constexpr int kRdrPasses = 8;       // radix-select passes: one key byte each
 constexpr int kRdrTieTile = 1024;   // items per tile of the tie scan
 __host__ __device__ inline int64_t rdr_tie_tiles(int64_t items) { return (items + kRdrTieTile - 1) / kRdrTieTile; }
 hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s);

@@ -14,8 +14,11 @@
 // 256-bin histogram of step bytes among steps that share the already chosen
 // high bytes, and pick the bin where the running byte total crosses the
 // budget.  All byte sums are 64-bit integers, so the result does not depend
-// on summation order.  Steps whose p equals the selected key are then taken
-// in (position desc, head asc, step asc) order by a tiled prefix scan.
+// on summation order.  Each pass's cut is found at the start of the next
+// pass's histogram kernel, by every work-group from the finished histogram
+// (one launch per pass, plus one for the last cut).  Steps whose p equals
+// the selected key are then taken in (position desc, head asc, step asc)
+// order by a tiled prefix scan.
 #include "ada_internal.h"
 
 namespace ada {
@@ -26,6 +29,25 @@ __device__ inline void set_status(int32_t *status, int code) { atomicCAS(status,
 // steps item i may take
 __device__ inline int item_steps(const RdrLaunch &a, int64_t i) {
     return a.cap ? min(a.n_steps, (int)a.cap[i]) : a.n_steps;
+}
+
+// radix-select state of sequence b after v passes (see RdrLaunch)
+struct SelState {
+    unsigned long long prefix;   // the chosen key bytes
+    long long above;             // bytes of the steps above them
+    int all_fit;                 // every step fits: nothing to select
+};
+
+__device__ inline SelState load_state(const RdrLaunch &a, int v, int b) {
+    const size_t k = (size_t)v * a.B + b;
+    return SelState{a.prefix[k], a.above[k], a.all_fit[k]};
+}
+
+__device__ inline void store_state(const RdrLaunch &a, int v, int b, const SelState &st) {
+    const size_t k = (size_t)v * a.B + b;
+    a.prefix[k] = st.prefix;
+    a.above[k] = st.above;
+    a.all_fit[k] = st.all_fit;
 }
 
 __device__ inline unsigned long long prio_key(float w, double c) {
@@ -46,24 +68,66 @@ __global__ __launch_bounds__(256) void rdr_validate_kernel(RdrLaunch a) {
         if (!(isfinite(w) && w >= 0.f)) set_status(a.status, ADA_EINVAL);
     }
     if (blockIdx.x == 0) {
-        for (int k = threadIdx.x; k < a.B * 256; k += 256) a.hist[k] = 0ull;
-        for (int b = threadIdx.x; b < a.B; b += 256) {
-            a.prefix[b] = 0ull;
-            a.above[b] = 0;
-            a.all_fit[b] = 0;
+        for (int k = threadIdx.x; k < kRdrPasses * a.B * 256; k += 256) a.hist[k] = 0ull;
+        for (int b = threadIdx.x; b < a.B; b += 256) store_state(a, 0, b, SelState{0ull, 0, 0});
+    }
+}
+
+// The cut digit of pass `pass` for sequence b, from that pass's finished
+// histogram: walking bins from the highest, the first whose bytes no longer
+// fit beside those above it.  Bins' suffix sums grow as the digit falls, so
+// the chosen bin is the highest digit whose inclusive suffix overshoots.
+// Run by a whole work-group of 256 threads; every thread gets the state
+// after the pass.
+__device__ SelState select_digit(const RdrLaunch &a, int pass, int b, long long (&suf)[256], int &n_over) {
+    const SelState s0 = load_state(a, pass, b);
+    const int v = threadIdx.x;
+    const bool active = s0.all_fit == 0 && *a.status == 0;
+    suf[v] = (long long)a.hist[((size_t)pass * a.B + b) * 256 + v];
+    if (v == 0) n_over = 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {   // suf[v] = sum of bins >= v
+        const long long u = v + off < 256 ? suf[v + off] : 0;
+        __syncthreads();
+        suf[v] += u;
+        __syncthreads();
+    }
+    if (s0.above + suf[v] > a.budget_dev[b]) atomicAdd(&n_over, 1);
+    __syncthreads();
+    const int chosen = n_over - 1;   // bins 0..chosen overshoot
+    SelState s1 = s0;
+    if (active) {
+        if (chosen < 0) {
+            s1.all_fit = 1;   // every remaining step fits (possible on the first pass only)
+        } else {
+            s1.above = s0.above + (chosen < 255 ? suf[chosen + 1] : 0);
+            s1.prefix = (s0.prefix << 8) | (unsigned long long)chosen;
         }
     }
+    __syncthreads();   // suf and n_over are free again
+    return s1;
 }
 
 // histogram of step bytes per next digit, for steps matching the prefix
 __global__ __launch_bounds__(256) void rdr_hist_kernel(RdrLaunch a, int pass) {
     __shared__ unsigned long long h[256];
+    __shared__ long long suf[256];
+    __shared__ int n_over;
     const int b = blockIdx.y;
+    // the state before this pass: the previous pass's cut, found here from
+    // its histogram by every work-group alike; one of them records it
+    SelState st;
+    if (pass == 0) {
+        st = load_state(a, 0, b);
+    } else {
+        st = select_digit(a, pass - 1, b, suf, n_over);
+        if (blockIdx.x == 0 && threadIdx.x == 0) store_state(a, pass, b, st);
+    }
     h[threadIdx.x] = 0ull;
     __syncthreads();
     const int ctx = a.ctx_len_dev[b];
-    const bool skip = a.all_fit[b] != 0 || *a.status != 0;
-    const unsigned long long pre = a.prefix[b];
+    const bool skip = st.all_fit != 0 || *a.status != 0;
+    const unsigned long long pre = st.prefix;
     const int shift_hi = 64 - 8 * pass, shift_dig = 56 - 8 * pass;
     if (!skip) {
         // Wavefront-uniform loop.  When every taking lane of a step falls
@@ -102,42 +166,16 @@ __global__ __launch_bounds__(256) void rdr_hist_kernel(RdrLaunch a, int pass) {
         }
     }
     __syncthreads();
-    if (!skip && h[threadIdx.x]) atomicAdd(&a.hist[b * 256 + threadIdx.x], h[threadIdx.x]);
+    if (!skip && h[threadIdx.x]) atomicAdd(&a.hist[((size_t)pass * a.B + b) * 256 + threadIdx.x], h[threadIdx.x]);
 }
 
-// The cut digit: walking bins from the highest, the first whose bytes no
-// longer fit beside those above it.  Bins' suffix sums grow as the digit
-// falls, so the chosen bin is the highest digit whose inclusive suffix
-// overshoots.  Also clears the histogram for the next pass.
-__global__ __launch_bounds__(256) void rdr_select_kernel(RdrLaunch a, int pass) {
+// The last pass's cut: the state after every pass (v = kRdrPasses).
+__global__ __launch_bounds__(256) void rdr_select_kernel(RdrLaunch a) {
     __shared__ long long suf[256];
     __shared__ int n_over;
-    const int b = blockIdx.x, v = threadIdx.x;
-    unsigned long long *hb = a.hist + b * 256;
-    const bool active = a.all_fit[b] == 0 && *a.status == 0;
-    const long long hv = (long long)hb[v];
-    suf[v] = hv;
-    if (v == 0) n_over = 0;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {   // suf[v] = sum of bins >= v
-        const long long u = v + off < 256 ? suf[v + off] : 0;
-        __syncthreads();
-        suf[v] += u;
-        __syncthreads();
-    }
-    const long long budget = a.budget_dev[b], above = a.above[b];
-    if (above + suf[v] > budget) atomicAdd(&n_over, 1);
-    __syncthreads();
-    const int chosen = n_over - 1;   // bins 0..chosen overshoot
-    if (active && v == 0) {
-        if (chosen < 0) {
-            a.all_fit[b] = 1;   // every remaining step fits (possible on the first pass only)
-        } else {
-            a.above[b] = above + (chosen < 255 ? suf[chosen + 1] : 0);
-            a.prefix[b] = (a.prefix[b] << 8) | (unsigned long long)chosen;
-        }
-    }
-    hb[v] = 0ull;
+    const int b = blockIdx.x;
+    const SelState st = select_digit(a, kRdrPasses - 1, b, suf, n_over);
+    if (threadIdx.x == 0) store_state(a, kRdrPasses, b, st);
 }
 
 // Steps whose key equals the selected key, taken in (position desc, head
@@ -162,7 +200,9 @@ __device__ inline long long tie_bytes(const RdrLaunch &a, int b, int ctx, int64_
     return bytes;
 }
 
-__device__ inline bool tie_active(const RdrLaunch &a, int b) { return a.all_fit[b] == 0 && *a.status == 0; }
+// the selection after every pass
+__device__ inline SelState final_state(const RdrLaunch &a, int b) { return load_state(a, kRdrPasses, b); }
+__device__ inline bool tie_active(const RdrLaunch &a, int b) { return final_state(a, b).all_fit == 0 && *a.status == 0; }
 
 __global__ __launch_bounds__(256) void rdr_tie_sum_kernel(RdrLaunch a, int64_t tiles_per_seq) {
     __shared__ long long red[4];
@@ -172,7 +212,7 @@ __global__ __launch_bounds__(256) void rdr_tie_sum_kernel(RdrLaunch a, int64_t t
     const int ctx = a.ctx_len_dev[b];
     const int64_t items = (int64_t)a.Hkv * ctx;
     if (tile * kRdrTieTile >= items) return;
-    const unsigned long long T = a.prefix[b];
+    const unsigned long long T = final_state(a, b).prefix;
     long long sum = 0;
     for (int k = 0; k < 4; ++k) {
         const int64_t ii = tile * kRdrTieTile + threadIdx.x * 4 + k;
@@ -222,10 +262,10 @@ __global__ __launch_bounds__(256) void rdr_tie_apply_kernel(RdrLaunch a, int64_t
     const int ctx = a.ctx_len_dev[b];
     const int64_t items = (int64_t)a.Hkv * ctx;
     if (tile * kRdrTieTile >= items) return;
-    const long long rem = a.budget_dev[b] - a.above[b];
+    const long long rem = a.budget_dev[b] - final_state(a, b).above;
     const long long off = a.tie_tile[b * tiles_per_seq + tile];
     if (off >= rem) return;   // every step costs at least one byte: nothing of this tile fits
-    const unsigned long long T = a.prefix[b];
+    const unsigned long long T = final_state(a, b).prefix;
     float w[4];
     int nk[4];
     int64_t idx[4];
@@ -269,10 +309,11 @@ __global__ __launch_bounds__(256) void rdr_final_kernel(RdrLaunch a) {
         if (t < a.ctx_len_dev[b]) {
             int n;
             const int nk = item_steps(a, i);
-            if (a.all_fit[b]) {
+            const SelState st = final_state(a, b);
+            if (st.all_fit) {
                 n = nk;
             } else {
-                const unsigned long long T = a.prefix[b];
+                const unsigned long long T = st.prefix;
                 const float w = a.utility[i];
                 n = a.tie_sel[i];
                 for (int k = 0; k < nk; ++k) n += prio_key(w, a.c[k]) > T ? 1 : 0;
@@ -326,10 +367,9 @@ hipError_t launch_rdr(const RdrLaunch &a, hipStream_t s) {
     const int64_t gcap = 4096 / a.B > 1 ? 4096 / a.B : 1;
     int64_t gx64 = (per_seq + 2047) / 2048;
     const int gx = (int)(gx64 < 1 ? 1 : (gx64 > gcap ? gcap : gx64));
-    for (int pass = 0; pass < 8; ++pass) {
+    for (int pass = 0; pass < kRdrPasses; ++pass)
         hipLaunchKernelGGL(rdr_hist_kernel, dim3(gx, a.B), dim3(256), 0, s, a, pass);
-        hipLaunchKernelGGL(rdr_select_kernel, dim3(a.B), dim3(256), 0, s, a, pass);
-    }
+    hipLaunchKernelGGL(rdr_select_kernel, dim3(a.B), dim3(256), 0, s, a);
     const int64_t tiles = rdr_tie_tiles(per_seq);
     hipLaunchKernelGGL(rdr_tie_sum_kernel, dim3((unsigned)tiles, a.B), dim3(256), 0, s, a, tiles);
     hipLaunchKernelGGL(rdr_tie_scan_kernel, dim3(a.B), dim3(1024), 0, s, a, tiles);
