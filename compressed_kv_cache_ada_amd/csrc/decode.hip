@@ -570,7 +570,7 @@ hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Q * a.Hq), dim3(core::kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.B * a.Q * a.Hq), dim3(kD * core::reduce_groups(a.S)), 0, s, a);
     return hipGetLastError();
 }
 

@@ -130,19 +130,27 @@ struct CoreSmem {
     _Float16 pb[NW][2][G][64];   // [wave][hi|lo][head][token]
 };
 
-// Reduction pass.  One thread per (sequence, query head, dimension): a
-// running merge over the chunks' partials in tiles of kReduceTile chunks
-// whose loads are all issued before any arithmetic, so a tile costs one
-// memory round trip and no barrier.  The first tile is requested before the
-// row's chunk count nc is known (its slots past nc hold nothing of this
-// launch and are masked), so a row of up to kReduceTile chunks costs one
-// round trip in all.  The order is fixed: deterministic.
-constexpr int kReduceThreads = 128;
+// Reduction pass.  A work-group per (sequence, query head): kD threads per
+// group, one per dimension, and up to kReduceGroups groups (blockDim.x / kD,
+// chosen by the launch from the chunk count).  Group q merges the chunk
+// tiles q, q + groups, ... (kReduceTile chunks each) with all of a tile's
+// loads issued before any arithmetic; the groups' results are then merged
+// in group order through LDS.  The first tile of each group is requested
+// before the row's chunk count nc is known (its slots past nc hold nothing
+// of this launch and are masked), so rows of up to groups * kReduceTile
+// chunks cost one round trip in all.  The order is fixed: deterministic.
 constexpr int kReduceTile = 16;
+constexpr int kReduceGroups = 4;
+constexpr int kReduceThreads = kD * kReduceGroups;   // the largest work-group
+__host__ __device__ constexpr int reduce_groups(int S) {
+    return S <= kReduceTile ? 1 : (S <= 2 * kReduceTile ? 2 : kReduceGroups);
+}
 
 // prow: partial row, orow: output row
 __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, const float *pacc, int S, int nc,
-                                              size_t prow, size_t orow, int d, float *out, float *lse) {
+                                              size_t prow, size_t orow, int tid, float *out, float *lse) {
+    __shared__ float gm[kReduceGroups][kD], gl[kReduceGroups][kD], go[kReduceGroups][kD];
+    const int d = tid % kD, q = tid / kD, groups = blockDim.x / kD;
     const size_t base = prow * S;
     float M = -INFINITY, L = 0.f, O = 0.f;
     float mv[kReduceTile], lv[kReduceTile], av[kReduceTile];
@@ -173,22 +181,38 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
     asm volatile("" : "+v"(z));
 #pragma unroll
     for (int i = 0; i < kReduceTile; ++i) {
-        const int c = min(i, S - 1);   // a slot of the row's S; chunks at or past nc are masked
+        const int c = min(q * kReduceTile + i, S - 1);   // a slot of the row's S; chunks at or past nc are masked
         mv[i] = pm[base + c + z];
         lv[i] = pl[base + c + z];
         av[i] = pacc[(base + c) * kD + d];
     }
     __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the merge starts
-    merge(0);
-    for (int c0 = kReduceTile; c0 < nc; c0 += kReduceTile) {
+    merge(q * kReduceTile);
+    for (int c0 = (q + groups) * kReduceTile; c0 < nc; c0 += groups * kReduceTile) {
 #pragma unroll
         for (int i = 0; i < kReduceTile; ++i) {
             const int c = min(c0 + i, nc - 1);   // in range; repeats are masked
-            mv[i] = pm[base + c];
-            lv[i] = pl[base + c];
+            mv[i] = pm[base + c + z];
+            lv[i] = pl[base + c + z];
             av[i] = pacc[(base + c) * kD + d];
         }
         merge(c0);
+    }
+    if (groups > 1) {   // the groups' results, merged in group order by group 0
+        gm[q][d] = M;
+        gl[q][d] = L;
+        go[q][d] = O;
+        __syncthreads();
+        if (q != 0) return;
+        for (int g = 1; g < groups; ++g) {
+            const float Mg = gm[g][d];
+            if (Mg == -INFINITY) continue;
+            const float Mt = fmaxf(M, Mg);
+            const float so = (M == -INFINITY) ? 0.f : exp2f(M - Mt), sg = exp2f(Mg - Mt);
+            L = L * so + gl[g][d] * sg;
+            O = O * so + go[g][d] * sg;
+            M = Mt;
+        }
     }
     if (M == -INFINITY) {
         out[orow * kD + d] = 0.f;

@@ -178,7 +178,7 @@ hipError_t launch_dense_partials(const DenseLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_dense_reduce(const DenseLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL(dense_reduce_kernel, dim3(a.B * a.Hq), dim3(core::kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(dense_reduce_kernel, dim3(a.B * a.Hq), dim3(kD * core::reduce_groups(a.S)), 0, s, a);
     return hipGetLastError();
 }
 
