@@ -595,20 +595,35 @@ __global__ __launch_bounds__(256) void append_capacity_kernel(AppendLaunch a) {
 // requests).  New pages are left to the caller to zero: their booked slot
 // is 0, and new_pages[r] holds their code block offset (16-byte units).
 __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
-    __shared__ int s_need[1024];
-    __shared__ long long s_units[1024];
-    __shared__ int s_bad, s_nospace, c_pages;
+    __shared__ int s_need[16];         // per-wavefront totals of the tile scan
+    __shared__ long long s_units[16];
+    __shared__ int s_bad, s_stop, s_nospace, c_pages;
     __shared__ long long c_units;
     const int tid = threadIdx.x;
-    if (read_status(a.status) != 0) return;
     if (tid == 0) {
         s_bad = 0;
+        s_stop = 0;
         s_nospace = 0;
         c_pages = 0;
         c_units = 0;
     }
-    __syncthreads();
     const int P = a.P, rows = a.n;
+    // The status word, the allocation counters and the first tile's booking
+    // lookups are read together with the keys and values being checked, so
+    // that the checks and the lookups share memory round trips; nothing is
+    // written before every check has passed.
+    const int status0 = read_status(a.status);
+    const long long base_p = a.alloc[0], base_u = a.alloc[1];
+    int tau0 = 0, np0 = 0;
+    if (tid < rows) {
+        tau0 = a.tier[tid];
+        np0 = a.num_pages[tid];
+    }
+    int open0 = -1, cnt0 = P;
+    if (tid < rows && tau0 < a.n_tiers) {   // a tier out of range fails the checks below
+        open0 = a.open_page[tid * kNumTiers + tau0];
+        if (open0 >= 0) cnt0 = (int)a.page_meta[open0].count;
+    }
     // tiers and keys, coalesced: one thread per 16 bytes of key; then the
     // values of V8 tokens, one thread per 16 bytes of values
     const float4 *k4 = reinterpret_cast<const float4 *>(a.keys);
@@ -626,56 +641,86 @@ __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
             ok &= values_finite(v.x) & values_finite(v.y) & values_finite(v.z) & values_finite(v.w);
         }
     }
+    __syncthreads();   // the flags' initial values are in place
+    if (status0 != 0) atomicOr(&s_stop, 1);
     if (!ok) atomicOr(&s_bad, 1);
     __syncthreads();
+    if (s_stop) return;   // an earlier error: leave everything as it is
     if (s_bad) {
         if (tid == 0) set_status(a.status, ADA_EINVAL);
         return;
     }
-    const long long base_p = a.alloc[0], base_u = a.alloc[1];
+    int f_page = -1, f_slot = 0;   // the first tile's booking of row tid, kept for the updates
+    uint32_t f_unit = 0;
     for (int t0 = 0; t0 < rows; t0 += 1024) {
         const int r = t0 + tid;
         int need = 0, page = -1, slot = 0;
         long long units = 0;
         if (r < rows) {
-            const int tau = a.tier[r];
-            const int open = a.open_page[r * kNumTiers + tau];
-            const int cnt = open >= 0 ? (int)a.page_meta[open].count : P;
+            int tau, open, cnt, np;
+            if (t0 == 0) {   // read above
+                tau = tau0;
+                open = open0;
+                cnt = cnt0;
+                np = np0;
+            } else {
+                tau = a.tier[r];
+                open = a.open_page[r * kNumTiers + tau];
+                cnt = open >= 0 ? (int)a.page_meta[open].count : P;
+                np = a.num_pages[r];
+            }
             if (cnt < P) {
                 page = open;
                 slot = cnt;
             } else {
                 need = 1;
                 units = block16(tau, P);
-                if (a.num_pages[r] >= a.maxp) atomicOr(&s_nospace, 1);
+                if (np >= a.maxp) atomicOr(&s_nospace, 1);
             }
         }
-        // inclusive scans of new pages and code units over the tile
-        s_need[tid] = need;
-        s_units[tid] = units;
+        // inclusive scans of new pages and code units over the tile: within
+        // each wavefront by shuffles, then the wavefronts' totals through LDS
+        const int lane = tid & 63, wv = tid >> 6;
+        int need_in = need;
+        long long units_in = units;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(need_in, off, 64);
+            const long long u = __shfl_up(units_in, off, 64);
+            if (lane >= off) {
+                need_in += v;
+                units_in += u;
+            }
+        }
+        if (lane == 63) {
+            s_need[wv] = need_in;
+            s_units[wv] = units_in;
+        }
         __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            const int v = tid >= off ? s_need[tid - off] : 0;
-            const long long u = tid >= off ? s_units[tid - off] : 0;
-            __syncthreads();
-            s_need[tid] += v;
-            s_units[tid] += u;
-            __syncthreads();
+        for (int w = 0; w < wv; ++w) {
+            need_in += s_need[w];
+            units_in += s_units[w];
         }
         if (r < rows) {
+            uint32_t unit = 0;
             if (need) {
-                a.dest_page[r] = (int)(base_p + c_pages + s_need[tid] - 1);
-                a.dest_slot[r] = 0;
-                a.new_pages[r] = (int32_t)(uint32_t)(base_u + c_units + s_units[tid] - units);
-            } else {
-                a.dest_page[r] = page;
-                a.dest_slot[r] = slot;
+                page = (int)(base_p + c_pages + need_in - 1);
+                slot = 0;
+                unit = (uint32_t)(base_u + c_units + units_in - units);
+                a.new_pages[r] = (int32_t)unit;
+            }
+            a.dest_page[r] = page;
+            a.dest_slot[r] = slot;
+            if (t0 == 0) {
+                f_page = page;
+                f_slot = slot;
+                f_unit = unit;
             }
         }
         __syncthreads();
-        if (tid == 1023) {
-            c_pages += s_need[1023];
-            c_units += s_units[1023];
+        if (tid == 1023) {   // the tile's totals
+            c_pages += need_in;
+            c_units += units_in;
         }
         __syncthreads();
     }
@@ -686,16 +731,30 @@ __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
         return;
     }
     for (int r = tid; r < rows; r += 1024) {
-        const int tau = a.tier[r], page = a.dest_page[r], slot = a.dest_slot[r];
+        int tau, page, slot, np;
+        uint32_t unit;
+        if (r == tid) {   // the first tile's row: everything is in registers
+            tau = tau0;
+            page = f_page;
+            slot = f_slot;
+            np = np0;
+            unit = f_unit;
+        } else {
+            tau = a.tier[r];
+            page = a.dest_page[r];
+            slot = a.dest_slot[r];
+            np = a.num_pages[r];
+            unit = (uint32_t)a.new_pages[r];
+        }
         if (slot == 0) {   // a new page (an open page always holds at least one token)
             ada_page_meta_t m;
             m.tier = (uint8_t)tau;
             m.count = 1;
             m.reserved = 0;
-            m.code_off16 = (uint32_t)a.new_pages[r];
+            m.code_off16 = unit;
             a.page_meta[page] = m;
-            a.page_table[(size_t)r * a.maxp + a.num_pages[r]] = page;
-            a.num_pages[r] += 1;
+            a.page_table[(size_t)r * a.maxp + np] = page;
+            a.num_pages[r] = np + 1;
             a.open_page[r * kNumTiers + tau] = P > 1 ? page : -1;
         } else {
             a.page_meta[page].count = (uint8_t)(slot + 1);

@@ -42,7 +42,8 @@ def _rows(w):
 
 
 @pytest.mark.parametrize("name,ctx,batch", [("llama8b", 700, 2), ("tiny", 1000, 2), ("long256k", 900, 1),
-                                            ("ragged", 1500, 3)])
+                                            ("ragged", 1500, 3),
+                                            ("llama8b", 48, 130)])   # 1040 rows: two booking tiles
 def test_decode_append_matches_oracle(name, ctx, batch):
     w = W.config(name, ctx=ctx, batch=batch)
     log(f"decode_append {name} ctx {ctx} batch {batch}")
