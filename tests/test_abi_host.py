@@ -126,3 +126,37 @@ def test_shape_limits_and_workspace_ceiling():
     st, n = _size(L.ada_pack_workspace, c, ctypes.byref(big), 64, 1 << 20)
     assert st == ada.OK and 0 < n <= 2 ** 48
     assert _size(L.ada_rdr_workspace, c, I32, 2 ** 62)[0] == ada.EUNSUPPORTED
+
+
+def test_workspace_sizes_cover_what_the_kernels_write():
+    """Property check of the workspace arithmetic: for explicit chunk lengths,
+    the decode workspace holds the split-K partials (m, l and 128 values per
+    (sequence, query, query head, chunk)), grows with the batch, and the
+    pack and RDR workspaces hold their per-item arrays."""
+    hyp = pytest.importorskip("hypothesis")
+    st = hyp.strategies
+    L = ada.lib()
+
+    @hyp.settings(max_examples=300, deadline=None)
+    @hyp.given(P=st.sampled_from([16, 32]), G=st.sampled_from([1, 2, 4, 8]), Hkv=st.integers(1, 16),
+               B=st.integers(1, 300), maxp=st.integers(1, 20000), chunk=st.integers(1, 400),
+               Q=st.sampled_from([1, 2, 4, 8]), stride=st.integers(1, 1 << 18))
+    def check(P, G, Hkv, B, maxp, chunk, Q, stride):
+        if Q * G > 8:
+            return
+        cfg = ada.make_config(P, G * Hkv, Hkv, decode_chunk_pages=chunk)
+        desc = ada.CacheDesc(B, maxp, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+        s1, n1 = _size(L.ada_decode_multi_workspace, ctypes.byref(cfg), ctypes.byref(desc), B, Q)
+        assert s1 == ada.OK
+        tpg = 64 // P
+        cp = min(-(-chunk // tpg) * tpg, 256)
+        S = -(-maxp // cp)
+        assert n1 >= B * Q * G * Hkv * S * 130 * 4
+        s2, n2 = _size(L.ada_decode_multi_workspace, ctypes.byref(cfg), ctypes.byref(desc), B + 1, Q)
+        assert s2 == ada.OK and n2 >= n1
+        s3, n3 = _size(L.ada_pack_workspace, ctypes.byref(cfg), ctypes.byref(desc), B, stride)
+        assert s3 == ada.OK and n3 >= 2 * 4 * B * Hkv * stride   # destination page and slot per item
+        s4, n4 = _size(L.ada_rdr_workspace, ctypes.byref(cfg), B, stride)
+        assert s4 == ada.OK and n4 >= B * Hkv * stride           # one tie byte per item
+
+    check()
