@@ -771,7 +771,7 @@ __global__ __launch_bounds__(1024) void append_rows_kernel(AppendLaunch a) {
 __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
     const AppendLaunch &a = k.a;
     __shared__ int s_key[1024], s_row[1024], s_rank[1024], s_alloc[1024], s_page[1024], s_off[1024];
-    __shared__ long long s_scan_p[1024], s_scan_u[1024];
+    __shared__ long long s_scan_p[16], s_scan_u[16];   // per-wavefront totals of the tile scan
     __shared__ long long base_p, base_u;
     __shared__ int nnew, bad;
     const int tid = threadIdx.x;
@@ -818,22 +818,29 @@ __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
         }
         s_rank[tid] = rank;
         s_alloc[tid] = alloc;
-        s_scan_p[tid] = alloc;
-        s_scan_u[tid] = alloc ? block16(tau, P) : 0;
-        __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            long long vp = 0, vu = 0;
-            if (tid >= off) {
-                vp = s_scan_p[tid - off];
-                vu = s_scan_u[tid - off];
+        // inclusive scans of new pages and code units over the tile: within
+        // each wavefront by shuffles, then the wavefronts' totals through LDS
+        const int lane = tid & 63, wv = tid >> 6;
+        long long in_p = alloc, in_u = alloc ? block16(tau, P) : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const long long vp = __shfl_up(in_p, o, 64), vu = __shfl_up(in_u, o, 64);
+            if (lane >= o) {
+                in_p += vp;
+                in_u += vu;
             }
-            __syncthreads();
-            s_scan_p[tid] += vp;
-            s_scan_u[tid] += vu;
-            __syncthreads();
         }
-        const long long ex_p = s_scan_p[tid] - alloc;
-        const long long ex_u = s_scan_u[tid] - (alloc ? block16(tau, P) : 0);
+        if (lane == 63) {
+            s_scan_p[wv] = in_p;
+            s_scan_u[wv] = in_u;
+        }
+        __syncthreads();
+        for (int w = 0; w < wv; ++w) {
+            in_p += s_scan_p[w];
+            in_u += s_scan_u[w];
+        }
+        const long long ex_p = in_p - alloc;
+        const long long ex_u = in_u - (alloc ? block16(tau, P) : 0);
         s_page[tid] = alloc ? (int)(base_p + ex_p) : -1;
         s_off[tid] = alloc ? (int)(base_u + ex_u) : -1;
         __syncthreads();
@@ -894,10 +901,10 @@ __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
             if (alloc && last_alloc_of_row) a.num_pages[row] = np_row + rowrank + 1;
         }
         __syncthreads();
-        if (tid == 0) {
-            base_p += s_scan_p[1023];
-            base_u += s_scan_u[1023];
-            nnew += (int)s_scan_p[1023];
+        if (tid == 1023) {   // the tile's totals
+            base_p += in_p;
+            base_u += in_u;
+            nnew += (int)in_p;
         }
         __syncthreads();
     }
