@@ -50,6 +50,9 @@ def parse():
                     help="time ada_repack of the packed cache to FRAC of its current bytes instead")
     ap.add_argument("--repack-mask", type=int, default=0,
                     help="RDR tier mask of the re-pack (0: T8, T4, T2; 56: the V8 tiers)")
+    ap.add_argument("--setup", action="store_true",
+                    help="time the setup path instead: ada_pack (exact encoding and page placement) of the "
+                         "workload, and ada_rdr_assign of the rdr128k utilities")
     ap.add_argument("--v8", action="store_true",
                     help="store every kept token's values in V8 (tiers 3-5: the same keys, 8-bit values)")
     ap.add_argument("--queries", type=int, default=1,
@@ -140,6 +143,9 @@ def main():
         return
     if args.utility:
         utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units)
+        return
+    if args.setup:
+        setup_bench(args, w, ada, torch, W, cfg, kept, max_row, n_pages, units)
         return
     cache = ada.Cache(cfg, B, max_row, n_pages, units)
     ada.cache_init(cache)
@@ -439,6 +445,59 @@ def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
                    "kept_by_tier_before": {str(t): kept[t] for t in TIERS},
                    "kept_by_tier_after": {str(t): kept_after[t] for t in TIERS}},
         "bytes_before": sum(cur), "bytes_after": sum(used), "budget_bytes": sum(budget),
+    }), flush=True)
+
+
+def setup_bench(args, w, ada, torch, W, cfg, kept, max_row, n_pages, units):
+    """The setup path: ada_pack of the workload's tier map into an empty cache
+    (every kept key encoded exactly, pages placed), each timed step resetting
+    the cache first; and ada_rdr_assign on the rdr128k utilities and budgets
+    (the ordered RDR selection over every (head, position) of 4 x 128k)."""
+    P, Hkv, B = w["P"], w["Hkv"], w["B"]
+    cache = ada.Cache(cfg, B, max_row, n_pages, units)
+    keys = torch.from_numpy(w["keys"]).cuda()
+    vals = torch.from_numpy(w["values"].view(np.int16)).cuda()
+    tiers = torch.from_numpy(w["tiers"]).cuda()
+
+    def pack_step():
+        ada.cache_init(cache)
+        ada.pack(cache, w["ctx_len"], tiers, keys, vals)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    pack_ms = timed(pack_step)
+    assert ada.read_status(cache.status) == ada.OK
+    kept_total = sum(kept.values())
+    del cache, keys, vals, tiers
+    torch.cuda.empty_cache()
+
+    r = W.config("rdr128k")
+    rcfg = ada.make_config(r["P"], r["Hq"], r["Hkv"])
+    util = torch.from_numpy(r["utility"]).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t_out = torch.empty(util.shape, dtype=torch.int8, device="cuda")
+    rdr_ms = timed(lambda: ada.rdr_assign(rcfg, r["ctx_len"], util, r["budget"], status, t_out))
+    assert ada.read_status(status) == ada.OK
+    items = int(r["ctx_len"].sum()) * r["Hkv"]
+    print(json.dumps({
+        "metric": "ADA setup path: pack (exact encoding + page placement) and RDR assignment",
+        "value": kept_total / (pack_ms * 1e-3), "unit": "packed KV token-heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": pack_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "page_size": P,
+                   "kept_token_heads": kept_total},
+        "rdr_assign": {"workload": "rdr128k", "ms": rdr_ms, "items": items,
+                       "items_per_s": items / (rdr_ms * 1e-3)},
     }), flush=True)
 
 

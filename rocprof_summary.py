@@ -72,8 +72,9 @@ def cmd_stats(a):
     for name, d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{short(name)}` | {len(d)} | {sum(d) / 1e6:.3f} | {sum(d) / len(d) / 1e3:.2f} | "
                      f"{100 * sum(d) / total:.1f} |")
-    lines += ["", "Split-K decode kernel, per dispatch (us):", ""]
-    for name in pick(agg, DECODE):
+    focus = a.kernel or DECODE
+    lines += ["", f"`{focus}`, per dispatch (us):", ""]
+    for name in pick(agg, focus):
         d = agg[name]
         lines.append(f"- `{short(name)}`: n={len(d)} mean={statistics.mean(d) / 1e3:.2f} "
                      f"median={statistics.median(d) / 1e3:.2f} min={min(d) / 1e3:.2f} max={max(d) / 1e3:.2f}")
@@ -132,6 +133,7 @@ def main():
     s.add_argument("--workload", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", help="summary file name under profiles/")
+    s.add_argument("--kernel", help="kernel whose per-dispatch spread is listed (default: the split-K decode)")
     p = sub.add_parser("pmc")
     p.add_argument("--fetch-db", required=True)
     p.add_argument("--write-db", required=True)
