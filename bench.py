@@ -59,7 +59,7 @@ def parse():
                     help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=20,
+    ap.add_argument("--cold-steps", type=int, default=100,
                     help="extra split-K launches each after 1 GiB of unrelated reads (cold caches), untimed in value")
     return ap.parse_args()
 
