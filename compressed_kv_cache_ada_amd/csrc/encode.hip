@@ -310,6 +310,7 @@ constexpr int kTile = 1024;
 // tokens) are finite, count per tier
 __global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
     __shared__ int cnt[kNumTiers];
+    __shared__ int8_t s_tier[kTile];   // the tile's tiers, for the key checks below
     const int tile = blockIdx.x, row = blockIdx.y;
     const int b = row / a.Hkv;
     const int ctx = a.ctx_len_dev[b];
@@ -319,23 +320,27 @@ __global__ __launch_bounds__(256) void pack_count_kernel(PackLaunch a) {
     const int t0 = tile * kTile;
     for (int i = threadIdx.x; i < kTile; i += 256) {
         const int t = t0 + i;
-        if (t >= ctx) break;
-        const int tv = a.tier[rbase + t];
+        const int tv = t < ctx ? a.tier[rbase + t] : -1;
+        s_tier[i] = (int8_t)tv;
+        if (t >= ctx) continue;
         if (tv < -1 || tv >= a.n_tiers) set_status(a.status, ADA_EINVAL);
         else if (tv >= 0) atomicAdd(&cnt[tv], 1);
     }
+    __syncthreads();
     // finiteness of kept keys: one wavefront per position (no keys when
-    // re-packing from a cache)
+    // re-packing from a cache).  The tiers come from LDS and every position's
+    // key is read (a dropped one is ignored), so the loads of successive
+    // positions do not wait on each other.
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     bool bad = false;
+#pragma unroll 4
     for (int i = wv; a.keys && i < kTile; i += 4) {
         const int t = t0 + i;
         if (t >= ctx) break;
-        const int tv = a.tier[rbase + t];
-        if (tv < 0) continue;
+        const int tv = s_tier[i];
         const float2 kk = *reinterpret_cast<const float2 *>(a.keys + (rbase + t) * kD + 2 * lane);
-        bad |= !(isfinite(kk.x) && isfinite(kk.y));
-        if (tv < kNumTiers && tier_v8(tv))
+        bad |= tv >= 0 && !(isfinite(kk.x) && isfinite(kk.y));
+        if (tv >= 0 && tv < kNumTiers && tier_v8(tv))
             bad |= !values_finite(*reinterpret_cast<const uint32_t *>(a.values + (rbase + t) * kD + 2 * lane));
     }
     if (__any(bad) && lane == 0) set_status(a.status, ADA_EINVAL);
