@@ -38,7 +38,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "rdr128k", "ragged", "long256k", "tiny"])
     ap.add_argument("--chunk-pages", type=int, default=0)
