@@ -226,3 +226,19 @@ def test_errors():
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
         ada.rdr_assign(ada.make_config(w["P"], w["Hq"], w["Hkv"], rdr_tier_mask=0b111000), w["ctx_len"],
                        torch.ones((1, w["Hkv"], 64), dtype=torch.float32, device="cuda"), [1000], status)
+
+
+def test_fullsize_llama8b_all_v8():
+    """The full llama8b layer with every kept token's values in V8 (the
+    configuration `bench.py --v8` times, automatic chunking): pages byte
+    for byte and every output row within the tolerance."""
+    w = _v8(W.config("llama8b"), 1.0)
+    log("v8 full llama8b: pack both")
+    dev = to_dev(w)
+    gc, oc = _pack_both(w, dev)
+    compare_caches(gc, oc, w["P"])
+    log("  decode")
+    out, lse = ada.decode(gc, dev["q"], w["scale"])
+    o_ref, l_ref = O.decode(oc, w["q"], w["scale"])
+    worst = check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref)
+    log(f"  worst row rel err {worst:.2e}")
