@@ -8,7 +8,7 @@ import torch
 import compressed_kv_cache_ada_amd as ada
 import workloads as W
 from oracle import oracle as O
-from tests.gpu_util import check_outputs, compare_caches, gpu_pack, log, oracle_cache, to_dev
+from tests.gpu_util import check_outputs, compare_caches, gpu_cache, gpu_pack, log, oracle_cache, to_dev
 from tests.util import dense_attention
 from workloads import dense_pages
 
@@ -93,3 +93,43 @@ def test_dense_reference_parity(ctx):
                                        w["q"][0, hq], w["scale"])
         err = np.max(np.abs(out[0, hq] - o_ref)) / np.max(np.abs(o_ref))
         assert err <= 2e-3 and abs(lse[0, hq] - l_ref) <= 2e-3, (hq, err)
+
+
+RATE = {-1: 0, 0: 386, 1: 322, 2: 298}
+
+
+def test_fullsize_repack_and_fused_append():
+    """The full llama8b layer through the two measured steps beside the
+    decode: an RDR re-pack to half of each sequence's bytes (seeded
+    utilities) and one fused append + decode step on the re-packed cache,
+    each against the oracle: caches byte for byte, outputs within 2e-3."""
+    w = W.config("llama8b")
+    log("full llama8b: pack both")
+    gsrc, dev = gpu_pack(w)
+    osrc = _oracle_pack(w)
+    util = np.exp(np.random.default_rng(12).standard_normal((osrc.page_capacity, w["P"]))).astype(np.float32)
+    budget = [int(0.5 * sum(RATE[int(x)] for x in w["tiers"][b].ravel())) for b in range(w["B"])]
+    log("  re-pack")
+    gdst = gpu_cache(w)
+    ada.repack(gsrc, w["B"], torch.from_numpy(util).cuda(), budget, gdst)
+    assert ada.read_status(gdst.status) == ada.OK
+    odst = oracle_cache(w)
+    st, _ = O.repack(osrc, w["B"], util, budget, odst)
+    assert st == O.OK
+    compare_caches(gdst, odst, w["P"])
+    del gsrc, osrc
+    log("  fused append + decode")
+    rng = np.random.default_rng(13)
+    B, Hkv = w["B"], w["Hkv"]
+    keys = (rng.standard_normal((B, Hkv, 128)) * 2).astype(np.float32)
+    vals = rng.standard_normal((B, Hkv, 128)).astype(np.float16).view(np.uint16)
+    tiers = rng.integers(0, 3, (B, Hkv)).astype(np.uint8)
+    out, lse = ada.decode_append(gdst, dev["q"], w["scale"], torch.from_numpy(keys).cuda(),
+                                 torch.from_numpy(vals.view(np.int16)).cuda(), torch.from_numpy(tiers).cuda())
+    assert ada.read_status(gdst.status) == ada.OK
+    seq, head = np.repeat(np.arange(B), Hkv), np.tile(np.arange(Hkv), B)
+    assert O.append(odst, seq, head, tiers.ravel(), keys.reshape(-1, 128), vals.reshape(-1, 128)) == O.OK
+    compare_caches(gdst, odst, w["P"])
+    o_ref, l_ref = O.decode(odst, w["q"], w["scale"])
+    worst = check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref)
+    log(f"  worst row rel err {worst:.2e}")
