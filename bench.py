@@ -104,7 +104,7 @@ def build_workload(name, torch, ada, W):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding of the decode is described, not built)"}))
         sys.exit(2)
     import torch
