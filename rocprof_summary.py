@@ -125,6 +125,36 @@ def cmd_pmc(a):
     print(json.dumps(rec, indent=1))
 
 
+def cmd_traffic(a):
+    """HBM bytes per dispatch of every kernel in one command's FETCH_SIZE and
+    WRITE_SIZE passes, scaled by the copy probe's counters from the passes
+    of a decode run on the same box."""
+    cf = statistics.mean(per_kernel_counter(a.calib_fetch_db, "FETCH_SIZE")[
+        pick(per_kernel_counter(a.calib_fetch_db, "FETCH_SIZE"), COPY)[0]])
+    cw = statistics.mean(per_kernel_counter(a.calib_write_db, "WRITE_SIZE")[
+        pick(per_kernel_counter(a.calib_write_db, "WRITE_SIZE"), COPY)[0]])
+    f_scale, w_scale = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    fetch = per_kernel_counter(a.fetch_db, "FETCH_SIZE")
+    write = per_kernel_counter(a.write_db, "WRITE_SIZE")
+    lines = [f"# HBM traffic per dispatch: {a.title}", "", "Commands (from the repository root):", "",
+             "```", a.cmd_fetch, a.cmd_write, a.cmd_calib, "```", "",
+             f"Counter scale from the copy probe of {COPY_BYTES / 2**30:.0f} GiB: FETCH_SIZE x {f_scale:.4f}, "
+             f"WRITE_SIZE x {w_scale:.4f}.", "",
+             "| kernel | dispatches | read MB | write MB |", "|---|---|---|---|"]
+    rows = []
+    for k in fetch:
+        fm = statistics.mean(fetch[k]) * 1024 * f_scale / 1e6
+        wm = statistics.mean(write.get(k, [0.0])) * 1024 * w_scale / 1e6
+        rows.append((fm + wm, short(k), len(fetch[k]), fm, wm))
+    for _, name, n, fm, wm in sorted(rows, reverse=True):
+        lines.append(f"| `{name}` | {n} | {fm:.1f} | {wm:.1f} |")
+    out = os.path.join(PROFILES, a.out)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -134,6 +164,10 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", help="summary file name under profiles/")
     s.add_argument("--kernel", help="kernel whose per-dispatch spread is listed (default: the split-K decode)")
+    t = sub.add_parser("traffic")
+    for k in ("fetch-db", "write-db", "calib-fetch-db", "calib-write-db", "cmd-fetch", "cmd-write", "cmd-calib",
+              "title", "out"):
+        t.add_argument("--" + k, required=True)
     p = sub.add_parser("pmc")
     p.add_argument("--fetch-db", required=True)
     p.add_argument("--write-db", required=True)
@@ -142,7 +176,7 @@ def main():
     p.add_argument("--cmd-write", required=True)
     p.add_argument("--bench-json")
     a = ap.parse_args()
-    (cmd_stats if a.mode == "stats" else cmd_pmc)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "pmc": cmd_pmc}[a.mode](a)
 
 
 if __name__ == "__main__":
