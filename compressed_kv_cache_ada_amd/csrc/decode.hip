@@ -247,6 +247,7 @@ struct AdaPolicy {
         float q8[64 * G * 2];      // [j][g][x|y] query pairs (T8, factorised)
         CodeStage st[NW];          // the next group's code units, per wavefront
         uint32_t enc_words[2][16]; // bit-string packing of the fused append's key
+        int app_status;            // the status word as read once by the work-group (fused append)
         // V8 scale word of each token of the next group (lane = token)
         uint32_t vs[NW][VT ? 64 : 1];
     };
@@ -270,11 +271,15 @@ struct AdaPolicy {
     // row's new token encodes it (wavefront 0) and writes radius, codes and
     // value into its slot before any wavefront reads the chunk's pages.  No
     // other work-group reads that page.  Skipped when the booking failed.
+    // The status word is read once per work-group (thread 0, through LDS),
+    // so that all its wavefronts take the same path through the barriers.
     __device__ bool after_pages(Smem &s, const int *pages, int nch, int row, int w, int lane) const {
         if constexpr (!APPEND) {
             return false;
         } else {
-            if (enc::read_status(status) != 0) return false;
+            if (threadIdx.x == 0) s.app_status = enc::read_status(status);
+            __syncthreads();
+            if (s.app_status != 0) return false;
             const int dp = app_page[row];
             bool own = false;
             for (int i = lane; i < nch; i += 64) own |= pages[i] == dp;

@@ -1,9 +1,9 @@
 // rdr.hip -- Rate-Distortion Retention: keep/drop and tier per (KV head,
 // position) under a per-sequence byte budget, on gfx950.
 //
-// Method: "SPHERICAL KV" (arXiv 2605.18856), Abstract: RDR jointly chooses
-// keep/drop decisions and precision tiers per token and head under a fixed
-// budget.  Rate / distortion model and order (this library's reading):
+// Method: "SPHERICAL KV" (arXiv 2605.18856), Abstract: RDR gives each
+// (token, KV head) either a precision tier or a drop, within a byte budget.
+// Rate / distortion model and order (this library's reading):
 // upgrade steps drop -> tier_1 -> tier_2 ... (tiers in rate order) with cost
 // dR_k bytes and priority p = w * (dD_k / dR_k) in fp64; the steps taken are
 // the longest prefix of the order (p desc, position desc, head asc, step asc)

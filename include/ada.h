@@ -8,9 +8,9 @@
  * abstract states that keys are stored as a scalar radius plus compact angle
  * codes, that attention logits are computed straight from the codes on a
  * paged, block-local decode path, and that Rate-Distortion Retention (RDR)
- * picks keep/drop and a precision tier per token and KV head under a fixed
- * budget, producing tier-homogeneous pages with lightweight metadata.  The
- * abstract fixes no bit layout; this header fixes one:
+ * gives every (token, KV head) a precision tier or a drop within a byte
+ * budget, the result being pages of a single tier described by small
+ * metadata records.  The abstract fixes no bit layout; this header fixes one:
  *
  *  Key codec (head dim 128 -> 64 pairs (k[2j], k[2j+1]); with the half-split
  *  pair layout of ada_config_t, (k[j], k[j+64]), and the query likewise):
@@ -95,7 +95,9 @@ typedef enum {
     ADA_ENOSPC = 2,          /* page / arena / row capacity would be exceeded */
     ADA_EUNSUPPORTED = 3,    /* valid but unsupported shape (head dim, page size, group size) */
     ADA_EHIP = 4,            /* a HIP runtime call failed */
-    ADA_EINTERNAL = 5        /* an exact code decision could not be made (never expected) */
+    ADA_EINTERNAL = 5        /* an exact code decision could not be made (never expected; the
+                                cache is then unspecified: a slot booked by ada_decode_append may
+                                be left unwritten) */
 } ada_status_t;
 
 enum {
@@ -322,8 +324,8 @@ ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache
 /* Workspace bytes for ada_rdr_assign over B sequences of stride ctx_stride. */
 ada_status_t ada_rdr_workspace(const ada_config_t *cfg, int32_t B, int64_t ctx_stride, size_t *bytes);
 
-/* RDR keep/drop + tier choice under a byte budget (abstract: joint
- * keep/drop and precision tiers per token and head under a fixed budget).
+/* RDR keep/drop + tier choice under a byte budget (abstract: RDR gives each
+ * (token, KV head) a precision tier or a drop, within a budget).
  * Items are (KV head, position) of one sequence, all heads sharing the
  * sequence's budget.  Rate of a tier: 2 + 8 (tb + sb) + 256 bytes (fp16
  * values) or + 132 (V8 values); distortion 2^-(tb + sb), plus 2^-14 for V8
