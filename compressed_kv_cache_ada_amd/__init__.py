@@ -73,6 +73,7 @@ def _declare(L):
         "ada_build_lut": (st, [cfgp, vp, i32, vp, vp]),
         "ada_decode_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_decode": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "ada_decode_noalloc": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp]),
         "ada_decode_partials": (st, [cfgp, cachep, vp, i32, f32, vp, sz, vp]),
         "ada_decode_reduce": (st, [cfgp, cachep, i32, vp, vp, vp, sz, vp]),
         "ada_decode_multi_workspace": (st, [cfgp, cachep, i32, i32, ctypes.POINTER(sz)]),
@@ -103,7 +104,7 @@ def _declare(L):
 
 
 ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_build_lut",
-               "ada_decode_workspace", "ada_decode", "ada_decode_partials", "ada_decode_reduce",
+               "ada_decode_workspace", "ada_decode", "ada_decode_noalloc", "ada_decode_partials", "ada_decode_reduce",
                "ada_decode_multi_workspace", "ada_decode_multi", "ada_decode_append_workspace",
                "ada_decode_append", "ada_decode_utility_workspace", "ada_decode_utility", "ada_repack_workspace",
                "ada_repack",
@@ -216,6 +217,19 @@ def decode(cache, q, scale, out=None, lse=None, ws=None):
     ws = decode_workspace(cache, B) if ws is None else ws
     _check(lib().ada_decode(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _ptr(q), B, float(scale),
                             _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()), "ada_decode")
+    return out, lse
+
+
+def decode_noalloc(cache, q, scale, out=None, lse=None):
+    """ada_decode with the library's own per-GPU partials array (no workspace)."""
+    q = _dev(q, torch.float32, "q")
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, cache.cfg.num_q_heads, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, cache.cfg.num_q_heads), dtype=torch.float32, device=q.device)
+    _check(lib().ada_decode_noalloc(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _ptr(q), B, float(scale),
+                                    _ptr(out), _ptr(lse), _stream()), "ada_decode_noalloc")
     return out, lse
 
 

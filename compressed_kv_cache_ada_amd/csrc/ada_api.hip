@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ada_internal.h"
 
@@ -320,6 +321,31 @@ ada_status_t rdr_steps(uint32_t mask, int *n_steps, int32_t *step_tier, int64_t 
 
 }  // namespace
 
+// ---- decode without a caller workspace ----------------------------------
+// The split-K partials of ada_decode_noalloc live in this file-scope device
+// array (one copy per GPU, held until the process ends).  Host code never
+// passes the array's name to a kernel: its device address is looked up once
+// per device with hipGetSymbolAddress and kept in noalloc_ptr[].
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+static std::mutex noalloc_mu;
+static void *noalloc_ptr[kMaxDevices];
+
+// the current device's address of `scratch`, or nullptr if it cannot be had
+static void *noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        noalloc_ptr[dev] = p;
+    }
+    return noalloc_ptr[dev];
+}
+
 extern "C" {
 
 const char *ada_status_str(ada_status_t s) {
@@ -439,6 +465,28 @@ ada_status_t ada_decode_multi(const ada_config_t *cfg, const ada_cache_t *cache,
 ada_status_t ada_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B, float scale,
                         float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
     return ada_decode_multi(cfg, cache, q, B, 1, scale, out, lse, ws, ws_bytes, stream);
+}
+
+ada_status_t ada_decode_noalloc(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                                float scale, float *out, float *lse, void *stream) {
+    ada_status_t st = check_cfg(cfg);
+    if (st) return st;
+    if ((st = check_cache(cfg, cache))) return st;
+    if (B < 0 || B > cache->num_seqs) return ADA_EINVAL;
+    if (B == 0) return ADA_OK;
+    if (!q || !out) return ADA_EINVAL;
+    // sizes first (no device memory touched): the partials must fit the array
+    if (decode_layout(cfg, B, 1, cache->max_pages_per_head, nullptr).bytes > kNoallocScratchBytes)
+        return ADA_EUNSUPPORTED;
+    void *ws = noalloc_scratch();
+    if (!ws) return ADA_EHIP;
+    // every partial the reduction reads is written by the split-K pass of the
+    // same call, so nothing in the array needs clearing first
+    const DecodeWs w = decode_layout(cfg, B, 1, cache->max_pages_per_head, ws);
+    DecodeLaunch a = make_decode(cfg, cache, q, B, 1, scale, out, lse, w);
+    hipError_t e = launch_decode_partials(a, (hipStream_t)stream);
+    if (e != hipSuccess) return ADA_EHIP;
+    return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
 }
 
 ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *cache, int32_t n, size_t *bytes) {

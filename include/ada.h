@@ -63,7 +63,8 @@
  *  - Pointers documented "device" point to HIP device memory owned by the
  *    caller; pointers documented "host" point to host memory read before
  *    the call returns.  The library never allocates or frees memory and
- *    keeps no global state; scratch comes from a caller workspace whose size
+ *    keeps no global state (one exception: ada_decode_noalloc's per-GPU
+ *    device array, below); scratch comes from a caller workspace whose size
  *    the matching *_workspace call returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
  *    calls are asynchronous on that stream except ada_read_status.
@@ -199,6 +200,23 @@ ada_status_t ada_decode_workspace(const ada_config_t *cfg, const ada_cache_t *ca
  * chunk) then the reduction pass.  Page ids are not range-checked. */
 ada_status_t ada_decode(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
                         float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ada_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * allocation-free harnesses).  Same arguments, kernels and results as
+ * ada_decode (bit for bit); the split-K partials go to a device array of
+ * 16 MiB inside the library instead of a caller workspace.  Each GPU the
+ * library runs on holds its own copy of that array until the process ends;
+ * this call allocates and frees nothing.  Limit: the partials of the call,
+ * about 520 bytes per (sequence, query head, split-K chunk) -- the size
+ * ada_decode_workspace reports -- must fit in 16 MiB, else ADA_EUNSUPPORTED
+ * before any launch (llama8b-like layer: 1.6 MB at B = 8, 32k context).
+ * ADA_EHIP if the array's address cannot be obtained.  All calls on one GPU
+ * share the array: calls whose executions overlap on one GPU (other streams,
+ * other host threads) race and give undefined results; calls ordered on one
+ * stream do not. */
+ada_status_t ada_decode_noalloc(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
+                                float scale, float *out, float *lse, void *stream);
 
 /* The two passes of ada_decode, callable separately (same arguments). */
 ada_status_t ada_decode_partials(const ada_config_t *cfg, const ada_cache_t *cache, const float *q, int32_t B,
