@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=100,
                     help="extra split-K launches each after 1 GiB of unrelated reads (cold caches), untimed in value")
+    ap.add_argument("--others", default="rdr128k,ragged,long256k",
+                    help="further workloads measured after the headline one, each reported in `workloads` "
+                         "(comma-separated; empty for none)")
     return ap.parse_args()
 
 
@@ -116,23 +119,7 @@ def main():
     if args.v8:
         w["tiers"] = np.where(w["tiers"] >= 0, w["tiers"] + 3, -1).astype(np.int8)
     P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
-    G = Hq // Hkv
-    tiers = w["tiers"]
-    kept = {t: int((tiers == t).sum()) for t in TIERS}
-    kept_total = sum(kept.values())
-    rows = B * Hkv
-    pages_by_tier = {t: 0 for t in TIERS}
-    max_row = 0
-    for b in range(B):
-        for h in range(Hkv):
-            rp = 0
-            for t in TIERS:
-                n = int((tiers[b, h] == t).sum())
-                pages_by_tier[t] += -(-n // P)
-                rp += -(-n // P)
-            max_row = max(max_row, rp)
-    n_pages = sum(pages_by_tier.values())
-    units = sum(pages_by_tier[t] * ada.block_bytes(t, P) // 16 for t in TIERS)
+    kept, pages_by_tier, max_row, n_pages, units = workload_shape(w, ada)
 
     cfg = ada.make_config(P, Hq, Hkv, decode_chunk_pages=args.chunk_pages, value_tiers=args.v8)
     if args.append:
@@ -147,6 +134,175 @@ def main():
     if args.setup:
         setup_bench(args, w, ada, torch, W, cfg, kept, max_row, n_pages, units)
         return
+    m = measure_decode(args, w, ada, torch, cfg, kept, max_row, n_pages, units, args.steps, args.cold_steps)
+    Q = args.queries
+    # copy probe: streaming ceiling of this box (read + write bytes)
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        ada.probe_copy(src, dst, nb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        ada.probe_copy(src, dst, nb)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # read ceiling: best of the streaming-read variants over 1 GiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    read_gbps = {}
+    for variant in range(5):
+        for _ in range(2):
+            ada.probe_read(src, nb, variant, sink)
+        e0.record()
+        for _ in range(10):
+            ada.probe_read(src, nb, variant, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        read_gbps[variant] = nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
+    alg_bytes = m["alg_bytes"]
+    achieved = alg_bytes / (m["kernel_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload + ("_v8" if args.v8 else "")) if Q == 1 else None
+    ms_step = m["ms_per_step"]
+    value = m["kept"] / (ms_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
+            "context": int(w["ctx_len"].max()), "page_size": P, "kept_token_heads": m["kept"],
+            "kept_by_tier": [kept[t] for t in TIERS],        # tier ids 0-5: T8, T4, T2, T8V8, T4V8, T2V8
+            "pages_by_tier": m["pages_by_tier"],
+            "values": "V8" if args.v8 else "fp16",
+            "decode_chunk_pages": cfg.decode_chunk_pages, "queries_per_sequence": Q,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "kernel": "decode_partials_kernel" if Q == 1 else "decode_partials_kernel + decode_reduce_kernel",
+            "kernel_ms": m["kernel_ms"], "kernel_ms_event_per_launch": m["kernel_ms_event_mean"],
+            "kernel_ms_event_median": m["kernel_ms_event_median"],
+            "frac_of_read_probe": None,
+            "reduce_kernel_ms": m["reduce_kernel_ms"],
+            "algorithmic_bytes": alg_bytes,
+        },
+        # spread of the headline over the individually event-timed steps
+        "value_p10": m["value_p10"], "value_p90": m["value_p90"],
+        "ms_per_step_event_p10": m["ms_per_step_event_p10"], "ms_per_step_event_p90": m["ms_per_step_event_p90"],
+        "graph_ms_per_step": m["graph_ms_per_step"],
+        "ms_per_step_with_events": m["ms_per_step_with_events"],
+        "step_hbm_gbps": m["step_hbm_gbps"],
+        "context_tokens_per_s": m["context_tokens_per_s"],
+        "cold_kernel_ms_median": m["cold_kernel_ms_median"],
+        "cold_gbps": m["cold_gbps"],
+        "copy_probe_gbps": copy_gbps,
+        "read_probe_gbps": max(read_gbps[v] for v in range(4)),
+        "read_probe_variants_gbps": read_gbps,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+
+    if Q > 1:
+        result["query_token_heads_per_s"] = value * Q   # (query, kept token-head) pairs scored per second
+    if not args.no_dense and Q == 1:
+        result["dense_fp16_reference"] = dense_reference(w, ada, torch, cfg)
+    if not args.no_cpu_baseline and Q == 1:
+        result["cpu_baseline"] = cpu_baseline(w, m["kept"], max_row, n_pages, units)
+    result["roofline"]["frac_of_read_probe"] = achieved / result["read_probe_gbps"]
+    # the other workloads of the metric's context range, each timed the same way
+    others = [x for x in args.others.split(",") if x and x != args.workload] if Q == 1 and not args.v8 else []
+    if others:
+        del w
+        result["workloads"] = {}
+        for name in others:
+            result["workloads"][name] = other_workload(name, args, ada, torch, W, result["read_probe_gbps"])
+    print(json.dumps(result), flush=True)
+
+
+def workload_shape(w, ada):
+    """Kept token-heads and pages per tier, the longest row, pages and code
+    units of a packed cache of the workload."""
+    P, Hkv, B = w["P"], w["Hkv"], w["B"]
+    tiers = w["tiers"]
+    kept = {t: int((tiers == t).sum()) for t in TIERS}
+    pages_by_tier = {t: 0 for t in TIERS}
+    max_row = 0
+    for b in range(B):
+        for h in range(Hkv):
+            rp = 0
+            for t in TIERS:
+                n = int((tiers[b, h] == t).sum())
+                pages_by_tier[t] += -(-n // P)
+                rp += -(-n // P)
+            max_row = max(max_row, rp)
+    n_pages = sum(pages_by_tier.values())
+    units = sum(pages_by_tier[t] * ada.block_bytes(t, P) // 16 for t in TIERS)
+    return kept, pages_by_tier, max_row, n_pages, units
+
+
+def other_workload(name, args, ada, torch, W, read_probe_gbps):
+    """One further workload: decode timing as for the headline (fewer cold
+    launches), its roofline fraction and the dense fp16 reference."""
+    w = build_workload(name, torch, ada, W)
+    kept, pages_by_tier, max_row, n_pages, units = workload_shape(w, ada)
+    cfg = ada.make_config(w["P"], w["Hq"], w["Hkv"], decode_chunk_pages=args.chunk_pages)
+    m = measure_decode(args, w, ada, torch, cfg, kept, max_row, n_pages, units, args.steps, min(args.cold_steps, 20))
+    achieved = m["alg_bytes"] / (m["kernel_ms"] * 1e-3) / 1e9
+    rec = {
+        "config": {"batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": 128,
+                   "context_max": int(w["ctx_len"].max()), "context_total": int(w["ctx_len"].sum()),
+                   "page_size": w["P"], "kept_token_heads": m["kept"],
+                   "kept_by_tier": [kept[t] for t in TIERS], "pages_by_tier": m["pages_by_tier"]},
+        "value": m["kept"] / (m["ms_per_step"] * 1e-3), "unit": "KV token-heads/s",
+        "value_p10": m["value_p10"], "value_p90": m["value_p90"],
+        "ms_per_step": m["ms_per_step"],
+        "kernel_ms": m["kernel_ms"], "kernel_ms_event_median": m["kernel_ms_event_median"],
+        "algorithmic_bytes": m["alg_bytes"], "achieved_gbps": achieved, "frac": achieved / PEAK_HBM_GBPS,
+        "frac_of_read_probe": achieved / read_probe_gbps,
+        "traffic": measured_traffic(name),
+        "reduce_kernel_ms": m["reduce_kernel_ms"],
+        "cold_kernel_ms_median": m["cold_kernel_ms_median"],
+        "context_tokens_per_s": m["context_tokens_per_s"],
+        # bytes the decode reads per context token-head (dropped tokens cost nothing)
+        "bytes_per_context_token_head": m["alg_bytes"] / (float(w["ctx_len"].sum()) * w["Hkv"]),
+    }
+    if not args.no_dense:
+        d = dense_reference(w, ada, torch, cfg)
+        d["bytes_per_context_token_head"] = DENSE_TOKEN_BYTES
+        d["frac"] = d["gbps"] / PEAK_HBM_GBPS
+        rec["dense_fp16_reference"] = d
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
+def measure_decode(args, w, ada, torch, cfg, kept, max_row, n_pages, units, steps, cold_steps):
+    """Pack the workload, then time K decode steps back to back (the value),
+    the same K steps with events around each (spread), the split-K kernel
+    alone (roofline), the reduction alone, a graph replay of the step and
+    cold launches."""
+    P, Hq, Hkv, B = w["P"], w["Hq"], w["Hkv"], w["B"]
+    tiers = w["tiers"]
+    kept_total = sum(kept.values())
+    pages_by_tier = {t: 0 for t in TIERS}
+    for t in TIERS:
+        for b in range(B):
+            for h in range(Hkv):
+                pages_by_tier[t] += -(-int((tiers[b, h] == t).sum()) // P)
     cache = ada.Cache(cfg, B, max_row, n_pages, units)
     ada.cache_init(cache)
     keys = torch.from_numpy(w["keys"]).cuda()
@@ -187,6 +343,8 @@ def main():
             ev[1].record()
         if Q == 1:
             ada.decode_reduce(cache, B, out, lse, ws)
+        if ev is not None:
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
@@ -197,38 +355,40 @@ def main():
     # adds about 10 us per step of GPU-side gaps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    # the same K steps again with events bracketing every split-K launch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ms_step = wall * 1e3 / steps
+    # the same K steps again with events bracketing every split-K launch and
+    # every whole step
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    ms_step_events = (time.perf_counter() - t0) * 1e3 / args.steps
-    k_each = [a.elapsed_time(b) for a, b in evs]
+    ms_step_events = (time.perf_counter() - t0) * 1e3 / steps
+    k_each = [e[0].elapsed_time(e[1]) for e in evs]
+    step_each_ms = [e[0].elapsed_time(e[2]) for e in evs]
     k_ms_each = float(np.mean(k_each))
     # dominant kernel alone: K back-to-back split-K launches between two events
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         split_k()
     e1.record()
     torch.cuda.synchronize()
-    k_ms = e0.elapsed_time(e1) / args.steps
+    k_ms = e0.elapsed_time(e1) / steps
     # the reduction pass alone, K back-to-back launches (mostly launch cost:
     # behind a split-K launch it adds about 2 us)
     r_ms = None
     if Q == 1:
         e0.record()
-        for _ in range(args.steps):
+        for _ in range(steps):
             ada.decode_reduce(cache, B, out, lse, ws)
         e1.record()
         torch.cuda.synchronize()
-        r_ms = e0.elapsed_time(e1) / args.steps
+        r_ms = e0.elapsed_time(e1) / steps
 
     # the same step captured once in a HIP graph and replayed K times (a
     # serving loop's form: no per-launch host work between the kernels)
@@ -246,20 +406,20 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             graph.replay()
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
         del graph
 
     # cold steps: before each, 1 GiB of another buffer is streamed through the
     # caches with a read kernel (the 256 MB last-level cache then holds clean
     # lines of that buffer, so no write-back is charged to the decode)
     cold = []
-    if args.cold_steps:
+    if cold_steps:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         fsink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        for _ in range(args.cold_steps):
+        for _ in range(cold_steps):
             ada.probe_read(flush, 1 << 30, 0, fsink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -269,89 +429,26 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del flush
 
-    # copy probe: streaming ceiling of this box (read + write bytes)
-    nb = 1 << 30
-    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    for _ in range(3):
-        ada.probe_copy(src, dst, nb)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        ada.probe_copy(src, dst, nb)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # read ceiling: best of the streaming-read variants over 1 GiB
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    read_gbps = {}
-    for variant in range(5):
-        for _ in range(2):
-            ada.probe_read(src, nb, variant, sink)
-        e0.record()
-        for _ in range(10):
-            ada.probe_read(src, nb, variant, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        read_gbps[variant] = nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
-
-    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in TIERS) + 12 * n_pages + B * Q * Hq * 128 * 4
-    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload + ("_v8" if args.v8 else "")) if Q == 1 else None
-    value = kept_total / (ms_step * 1e-3)
-
-    result = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "KV token-heads/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
-            "context": int(w["ctx_len"].max()), "page_size": P, "kept_token_heads": kept_total,
-            "kept_by_tier": [kept[t] for t in TIERS],        # tier ids 0-5: T8, T4, T2, T8V8, T4V8, T2V8
-            "pages_by_tier": [pages_by_tier[t] for t in TIERS],
-            "values": "V8" if args.v8 else "fp16",
-            "decode_chunk_pages": cfg.decode_chunk_pages, "queries_per_sequence": Q,
-        },
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-            "kernel": "decode_partials_kernel" if Q == 1 else "decode_partials_kernel + decode_reduce_kernel",
-            "kernel_ms": k_ms, "kernel_ms_event_per_launch": k_ms_each,
-            "kernel_ms_event_median": float(np.median(k_each)),
-            "frac_of_read_probe": None,
-            "reduce_kernel_ms": r_ms,
-            "algorithmic_bytes": alg_bytes,
-        },
-        "graph_ms_per_step": graph_ms,
-        "ms_per_step_with_events": ms_step_events,
-        "step_hbm_gbps": (alg_bytes + B * Q * Hq * 512) / (ms_step * 1e-3) / 1e9,
+    # radius + codes + values per kept token-head, page metadata and table
+    # entry per page, the query read and the output written per query row
+    alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in TIERS) + 12 * n_pages + B * Q * Hq * 128 * 4 * 2
+    step_each = np.array(step_each_ms)
+    del cache, ws
+    torch.cuda.empty_cache()
+    return {
+        "kept": kept_total, "pages_by_tier": [pages_by_tier[t] for t in TIERS], "alg_bytes": alg_bytes,
+        "ms_per_step": ms_step, "kernel_ms": k_ms, "kernel_ms_event_mean": k_ms_each,
+        "kernel_ms_event_median": float(np.median(k_each)), "reduce_kernel_ms": r_ms,
+        "value_p10": kept_total / (float(np.percentile(step_each, 90)) * 1e-3),
+        "value_p90": kept_total / (float(np.percentile(step_each, 10)) * 1e-3),
+        "ms_per_step_event_p10": float(np.percentile(step_each, 10)),
+        "ms_per_step_event_p90": float(np.percentile(step_each, 90)),
+        "graph_ms_per_step": graph_ms, "ms_per_step_with_events": ms_step_events,
+        "step_hbm_gbps": alg_bytes / (ms_step * 1e-3) / 1e9,
         "context_tokens_per_s": float(w["ctx_len"].sum()) * Hkv / (ms_step * 1e-3),
         "cold_kernel_ms_median": float(np.median(cold)) if cold else None,
         "cold_gbps": alg_bytes / (np.median(cold) * 1e-3) / 1e9 if cold else None,
-        "copy_probe_gbps": copy_gbps,
-        "read_probe_gbps": max(read_gbps[v] for v in range(4)),
-        "read_probe_variants_gbps": read_gbps,
-        "kernel_source_hash": kernel_source_hash(),
     }
-
-    if Q > 1:
-        result["query_token_heads_per_s"] = value * Q   # (query, kept token-head) pairs scored per second
-    if not args.no_dense and Q == 1:
-        result["dense_fp16_reference"] = dense_reference(w, ada, torch, cfg)
-    if not args.no_cpu_baseline and Q == 1:
-        result["cpu_baseline"] = cpu_baseline(w, kept_total, max_row, n_pages, units)
-    result["roofline"]["frac_of_read_probe"] = achieved / result["read_probe_gbps"]
-    print(json.dumps(result), flush=True)
 
 
 def utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
