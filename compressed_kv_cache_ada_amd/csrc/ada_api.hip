@@ -14,6 +14,9 @@ namespace {
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// Multi-query decode: at most this many virtual heads (Q * Hq / Hkv) per KV head.
+constexpr int kMaxVirtualHeads = 64;
+
 // Workspaces larger than this are refused (ADA_EUNSUPPORTED), so no size
 // computed here can wrap around.
 constexpr size_t kMaxWorkspace = size_t(1) << 48;
@@ -106,7 +109,8 @@ int decode_chunk_pages(const ada_config_t *cfg, int32_t B, int32_t maxp, int gv)
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;   // MI355X
-        const size_t slots = (size_t)cus * decode_waves_per_simd(gv);
+        // work-groups resident at once, per slice of the virtual heads
+        const size_t slots = std::max<size_t>(1, (size_t)cus * decode_waves_per_simd(slice_heads(gv)) / slices(gv));
         const size_t units = smul((size_t)B, (size_t)cfg->num_kv_heads, (size_t)maxp);
         cp = (int)std::min<size_t>(units / slots + (units % slots != 0), 1 << 20);
     }
@@ -171,6 +175,7 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.util = nullptr;
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     a.value_tiers = cfg->value_tiers;
+    a.nslice = slices(Q * (cfg->num_q_heads / cfg->num_kv_heads));
     return a;
 }
 
@@ -396,7 +401,7 @@ ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, f
 static ada_status_t check_queries(const ada_config_t *cfg, int32_t Q) {
     if (Q < 1) return ADA_EINVAL;
     const int gv = Q * (cfg->num_q_heads / cfg->num_kv_heads);
-    if ((Q & (Q - 1)) || gv > 8) return ADA_EUNSUPPORTED;
+    if ((Q & (Q - 1)) || gv > kMaxVirtualHeads) return ADA_EUNSUPPORTED;
     return ADA_OK;
 }
 

@@ -97,7 +97,13 @@ struct DecodeLaunch {
     float *util;
     int32_t half_pairs;   // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
     int32_t value_tiers;  // the cache may hold pages of tiers 3-5 (V8 values)
+    // G' > 8 (several queries per sequence): the virtual heads are cut into
+    // nslice slices of 8, each computed by its own work-group of the chunk
+    int32_t nslice;
 };
+// virtual heads per work-group and slices per chunk for G' virtual heads
+__host__ __device__ constexpr int slice_heads(int gv) { return gv < 8 ? gv : 8; }
+__host__ __device__ constexpr int slices(int gv) { return gv <= 8 ? 1 : gv / 8; }
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeLaunch &a, hipStream_t s);
 hipError_t launch_build_lut(const float *q, int32_t rows, float *lut, bool half_pairs, hipStream_t s);

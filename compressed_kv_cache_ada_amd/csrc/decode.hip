@@ -257,6 +257,7 @@ struct AdaPolicy {
     const uint16_t *value_pool;
     const float *q;
     int32_t Q, Hq, Gr;   // queries per sequence, query heads, query heads per KV head
+    int32_t voff;        // first virtual head of this work-group (slices of 8 when Q * Gr > 8)
     int32_t half;        // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
     float mul;   // softmax scale * log2(e)
     // fused append (APPEND)
@@ -308,13 +309,14 @@ struct AdaPolicy {
     __device__ int num_pages(int row, int) const { return num_pages_[row]; }
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
 
-    // phase 1: query pairs and the grid directions.  Virtual head v of the
-    // KV head is query qi = v / Gr, head h * Gr + v % Gr of q [B][Q][Hq][128];
-    // component d is x (0) or y (1) of pair j in the cache's pair layout.
+    // phase 1: query pairs and the grid directions.  Virtual head voff + v
+    // of the KV head is query qi = (voff + v) / Gr, head h * Gr + (voff + v)
+    // % Gr of q [B][Q][Hq][128]; component d is x (0) or y (1) of pair j in
+    // the cache's pair layout.
     __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
         for (int i = tid; i < G * kD; i += nt) {
             const int v = i >> 7, d = i & 127;
-            const int qi = v / Gr, g = v % Gr;
+            const int qi = (voff + v) / Gr, g = (voff + v) % Gr;
             const int j = half ? (d & 63) : (d >> 1), xy = half ? (d >> 6) : (d & 1);
             s.q8[(j * G + v) * 2 + xy] = q[(((size_t)b * Q + qi) * Hq + (size_t)h * Gr + g) * kD + d];
         }
@@ -436,6 +438,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.Q = a.Q;
     pol.Hq = a.Hq;
     pol.Gr = a.Hq / a.Hkv;
+    // grid x: the chunk, or for nslice > 1 (chunk, slice) with the slices of
+    // a chunk 8 work-groups apart, i.e. on one of the chip's dies (work-groups
+    // go to the dies in turn) and dispatched together: the second slice's
+    // code and value reads can hit that die's L2 / the memory-side cache
+    int chunk = blockIdx.x, slice = 0;
+    if (a.nslice > 1) {
+        const int x = blockIdx.x;
+        chunk = (x / (8 * a.nslice)) * 8 + x % 8;
+        slice = (x / 8) % a.nslice;
+        if (chunk >= a.S) return;
+    }
+    pol.voff = slice * G;
     pol.half = a.half_pairs;
     pol.app_page = a.app_page;
     pol.app_slot = a.app_slot;
@@ -457,8 +471,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
     c.logit_buf = a.logit_buf;
+    c.gv = a.Q * pol.Gr;
+    c.voff = pol.voff;
     core::split_k<G, P, NW, MODE == 2>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
-                            reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
+                            reinterpret_cast<float *>(raw), chunk, blockIdx.y, blockIdx.z);
 }
 
 // one work-group per virtual row (b, h, v); writes query qi = v / Gr, head
@@ -546,7 +562,8 @@ template <int G, int P, bool VT>
 hipError_t launch_gpv(const DecodeLaunch &a, hipStream_t s) {
     constexpr int NW = 4;
     constexpr int WPE = decode_waves_per_simd(G);
-    const dim3 grid(a.S, a.Hkv, a.B), block(NW * 64);
+    const int gx = a.nslice > 1 ? (a.S + 7) / 8 * 8 * a.nslice : a.S;
+    const dim3 grid(gx, a.Hkv, a.B), block(NW * 64);
     if (a.app_page)
         hipLaunchKernelGGL((decode_partials_kernel<G, P, NW, WPE, 1, VT>), grid, block, 0, s, a);
     else if (a.logit_buf)
@@ -565,7 +582,7 @@ hipError_t launch_g(const DecodeLaunch &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_partials(const DecodeLaunch &a, hipStream_t s) {
-    switch (a.Q * (a.Hq / a.Hkv)) {   // virtual heads per KV head
+    switch (slice_heads(a.Q * (a.Hq / a.Hkv))) {   // virtual heads per work-group
         case 1: return launch_g<1>(a, s);
         case 2: return launch_g<2>(a, s);
         case 4: return launch_g<4>(a, s);

@@ -121,6 +121,10 @@ struct CoreArgs {
     float *pm, *pl, *pacc;
     int32_t Hq, Hkv, maxp, chunk_pages, S;
     float *logit_buf;   // EMIT: [page * P + slot][G] base-2 logits of every kept token
+    // virtual heads per KV head (partial rows of a KV head) and the first of
+    // the G this work-group computes (several queries per sequence: slices of
+    // at most 8 virtual heads go to different work-groups)
+    int32_t gv, voff;
 };
 
 template <int G, int NW>
@@ -496,7 +500,7 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         }
     }
     __syncthreads();
-    const size_t bq0 = ((size_t)b * a.Hkv + h) * G;   // first partial row of this KV head
+    const size_t bq0 = ((size_t)b * a.Hkv + h) * a.gv + a.voff;   // first partial row of this work-group
     for (int i = tid; i < G * kD; i += NT) {
         const int g = i >> 7, d = i & 127;
         float M = -INFINITY;

@@ -95,6 +95,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void dense_partials_kernel(DenseLaunc
     c.chunk_pages = a.chunk_pages;
     c.S = a.S;
     c.logit_buf = nullptr;
+    c.gv = G;
+    c.voff = 0;
     core::split_k<G, P, NW, false>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
                             reinterpret_cast<float *>(raw), blockIdx.x, blockIdx.y, blockIdx.z);
 }

@@ -228,7 +228,11 @@ ada_status_t ada_decode_reduce(const ada_config_t *cfg, const ada_cache_t *cache
  * several positions' queries), all attending to the same cached tokens.
  * One pass over the cache serves every query: the Q * G queries of a KV head
  * share each code and value read (G = Hq / Hkv).  Q must be a power of two
- * with Q * G <= 8, else ADA_EUNSUPPORTED.
+ * with Q * G <= 64, else ADA_EUNSUPPORTED.  Up to Q * G = 8 one work-group
+ * computes every query of its chunk; beyond that the Q * G virtual heads are
+ * cut into slices of 8, each computed by its own work-group of the chunk
+ * (placed so that the slices read the chunk's pages at the same time, on one
+ * of the chip's dies).
  *   q     device fp32 [B][Q][Hq][128]
  *   out   device fp32 [B][Q][Hq][128]; lse device fp32 [B][Q][Hq] or NULL
  *   ws    device workspace of at least ada_decode_multi_workspace() bytes

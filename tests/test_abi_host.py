@@ -81,16 +81,17 @@ def test_host_validation_without_gpu():
     null_cache = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
     assert L.ada_decode(ctypes.byref(good), ctypes.byref(null_cache), None, 2, 1.0, None, None, None, 0, None) \
         == ada.EINVAL
-    # multi-query: Q must be a power of two with Q * (Hq / Hkv) <= 8
+    # multi-query: Q must be a power of two with Q * (Hq / Hkv) <= 64
     L_ws = L.ada_decode_multi_workspace
     st2, n2 = _size(L_ws, ctypes.byref(good), ctypes.byref(desc), 2, 2)
     assert st2 == ada.OK and n2 > n   # twice the partial rows
     assert _size(L_ws, ctypes.byref(good), ctypes.byref(desc), 2, 1) == (ada.OK, n)
-    for Q, want in [(0, ada.EINVAL), (-1, ada.EINVAL), (3, ada.EUNSUPPORTED), (4, ada.EUNSUPPORTED)]:
+    for Q, want in [(0, ada.EINVAL), (-1, ada.EINVAL), (3, ada.EUNSUPPORTED), (4, ada.OK), (16, ada.OK),
+                    (32, ada.EUNSUPPORTED)]:
         assert _size(L_ws, ctypes.byref(good), ctypes.byref(desc), 2, Q)[0] == want
     g1 = ada.make_config(16, 8, 8)
-    assert _size(L_ws, ctypes.byref(g1), ctypes.byref(desc), 2, 8)[0] == ada.OK
-    assert _size(L_ws, ctypes.byref(g1), ctypes.byref(desc), 2, 16)[0] == ada.EUNSUPPORTED
+    assert _size(L_ws, ctypes.byref(g1), ctypes.byref(desc), 2, 64)[0] == ada.OK
+    assert _size(L_ws, ctypes.byref(g1), ctypes.byref(desc), 2, 128)[0] == ada.EUNSUPPORTED
     assert L.ada_decode_multi(ctypes.byref(good), ctypes.byref(desc), None, 2, 3, 1.0, None, None, None, 0,
                               None) == ada.EUNSUPPORTED
     # RDR: unsupported tier set is caught on the host (T8 + T4 only is fine; 0 = all)
@@ -140,9 +141,9 @@ def test_workspace_sizes_cover_what_the_kernels_write():
     @hyp.settings(max_examples=300, deadline=None)
     @hyp.given(P=st.sampled_from([16, 32]), G=st.sampled_from([1, 2, 4, 8]), Hkv=st.integers(1, 16),
                B=st.integers(1, 300), maxp=st.integers(1, 20000), chunk=st.integers(1, 400),
-               Q=st.sampled_from([1, 2, 4, 8]), stride=st.integers(1, 1 << 18))
+               Q=st.sampled_from([1, 2, 4, 8, 16]), stride=st.integers(1, 1 << 18))
     def check(P, G, Hkv, B, maxp, chunk, Q, stride):
-        if Q * G > 8:
+        if Q * G > 64:
             return
         cfg = ada.make_config(P, G * Hkv, Hkv, decode_chunk_pages=chunk)
         desc = ada.CacheDesc(B, maxp, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)

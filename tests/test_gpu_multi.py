@@ -1,7 +1,9 @@
 """GPU parity of multi-query decode (ada_decode_multi): Q queries per
-sequence against the same cache.  Each query's output must match the oracle's
-single-query decode of that query (2e-3 per row, as for ada_decode), and
-ada_decode_multi with Q = 1 must equal ada_decode exactly."""
+sequence against the same cache, up to Q * G = 64 virtual heads (beyond 8 the
+heads are cut into slices of 8, one work-group each).  Each query's output
+must match the oracle's single-query decode of that query (2e-3 per row, as
+for ada_decode), and ada_decode_multi with Q = 1 must equal ada_decode
+exactly."""
 import numpy as np
 import pytest
 import torch
@@ -22,7 +24,14 @@ def _queries(w, Q, seed):
 @pytest.mark.parametrize("name,ctx,batch,Q", [("llama8b", 1500, 2, 2),    # G = 4 -> 8 virtual heads
                                               ("tiny", 3000, 2, 8),       # G = 1
                                               ("tiny", 700, 3, 2),
-                                              ("ragged", 2200, 4, 2)])
+                                              ("ragged", 2200, 4, 2),
+                                              # more than 8 virtual heads: slices of 8 per work-group
+                                              ("llama8b", 1300, 2, 4),    # G = 4 -> 16
+                                              ("llama8b", 900, 1, 8),     # G = 4 -> 32
+                                              ("ragged", 1700, 3, 4),
+                                              ("long256k", 2100, 1, 2),   # G = 8 -> 16
+                                              ("long256k", 1500, 1, 4),   # G = 8 -> 32
+                                              ("tiny", 1100, 2, 16)])     # G = 1 -> 16
 def test_multi_query_matches_oracle(name, ctx, batch, Q):
     w = W.config(name, ctx=ctx, batch=batch)
     log(f"multi {name} ctx {ctx} batch {batch} Q {Q}")
@@ -46,8 +55,8 @@ def test_multi_query_q1_is_decode():
 
 
 def test_multi_query_unsupported_shape():
-    w = W.config("long256k", ctx=500)            # G = 8: Q must be 1
+    w = W.config("long256k", ctx=500)            # G = 8: Q * G at most 64
     gc, dev = gpu_pack(w)
-    qs = torch.from_numpy(_queries(w, 2, 1)).cuda()
+    qs = torch.from_numpy(_queries(w, 16, 1)).cuda()
     with pytest.raises(ada.AdaError):
         ada.decode_multi(gc, qs, w["scale"])
