@@ -70,6 +70,7 @@ def _declare(L):
         "ada_block_bytes": (i64, [i32, i32]),
         "ada_lut_floats": (sz, [cfgp]),
         "ada_cache_init": (st, [cfgp, cachep, vp]),
+        "ada_validate_cache": (st, [cfgp, cachep, i32, vp]),
         "ada_build_lut": (st, [cfgp, vp, i32, vp, vp]),
         "ada_decode_workspace": (st, [cfgp, cachep, i32, ctypes.POINTER(sz)]),
         "ada_decode": (st, [cfgp, cachep, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -103,7 +104,8 @@ def _declare(L):
         fn.argtypes = args
 
 
-ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_build_lut",
+ABI_SYMBOLS = ("ada_status_str", "ada_block_bytes", "ada_lut_floats", "ada_cache_init", "ada_validate_cache",
+               "ada_build_lut",
                "ada_decode_workspace", "ada_decode", "ada_decode_noalloc", "ada_decode_partials", "ada_decode_reduce",
                "ada_decode_multi_workspace", "ada_decode_multi", "ada_decode_append_workspace",
                "ada_decode_append", "ada_decode_utility_workspace", "ada_decode_utility", "ada_repack_workspace",
@@ -185,6 +187,13 @@ class Cache:
 
 def cache_init(cache):
     _check(lib().ada_cache_init(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), _stream()), "ada_cache_init")
+
+
+def validate_cache(cache, B):
+    """Range-check the page lists of sequences 0..B-1 on the device; the
+    verdict lands in cache.status (read it with read_status)."""
+    _check(lib().ada_validate_cache(ctypes.byref(cache.cfg), ctypes.byref(cache.desc), B, _stream()),
+           "ada_validate_cache")
 
 
 def lut_floats(cfg):

@@ -939,6 +939,36 @@ __global__ void cache_init_kernel(int32_t rows, int32_t *num_pages, int32_t *ope
     }
 }
 
+// Cache check: every row's page count within the row's table, every listed
+// page id within the pool, and each such page's metadata well formed (a known
+// tier, 1..P tokens, zero reserved field, code block inside the arena).  A
+// page's metadata is read only after its id has been range-checked; nothing
+// outside the buffers is read.  Any failure sets the status word to
+// ADA_EINVAL.  One work-group per row (grid-stride).
+__global__ __launch_bounds__(256) void validate_kernel(int32_t rows, int32_t maxp, int64_t page_capacity,
+                                                       int64_t arena16, int32_t P, int32_t n_tiers,
+                                                       const int32_t *num_pages, const int32_t *page_table,
+                                                       const ada_page_meta_t *page_meta, int32_t *status) {
+    for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+        const int np = num_pages[row];
+        if (np < 0 || np > maxp) {
+            if (threadIdx.x == 0) enc::set_status(status, ADA_EINVAL);
+            continue;
+        }
+        for (int i = threadIdx.x; i < np; i += blockDim.x) {
+            const int pid = page_table[(size_t)row * maxp + i];
+            if (pid < 0 || (int64_t)pid >= page_capacity) {
+                enc::set_status(status, ADA_EINVAL);
+                continue;
+            }
+            const ada_page_meta_t m = page_meta[pid];
+            const bool ok = m.tier < n_tiers && m.count >= 1 && m.count <= P && m.reserved == 0 &&
+                            (int64_t)m.code_off16 + block16(m.tier, P) <= arena16;
+            if (!ok) enc::set_status(status, ADA_EINVAL);
+        }
+    }
+}
+
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -964,6 +994,14 @@ hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64
                              const int32_t *status, hipStream_t s) {
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_n, 1, 4096)), dim3(256), 0, s, pages, n_pages,
                        page_meta, arena, value_pool, P, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_validate(int32_t rows, int32_t maxp, int64_t page_capacity, int64_t arena16, int32_t P,
+                           int32_t n_tiers, const int32_t *num_pages, const int32_t *page_table,
+                           const ada_page_meta_t *page_meta, int32_t *status, hipStream_t s) {
+    hipLaunchKernelGGL(validate_kernel, dim3(grid_for(rows, 1, 4096)), dim3(256), 0, s, rows, maxp, page_capacity,
+                       arena16, P, n_tiers, num_pages, page_table, page_meta, status);
     return hipGetLastError();
 }
 

@@ -175,6 +175,19 @@ size_t ada_lut_floats(const ada_config_t *cfg);
  * they are (pages are zeroed when they are allocated). */
 ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, void *stream);
 
+/* Check the page lists of sequences 0..B-1 before decoding them.  The
+ * decode calls do not range-check page ids on their hot path: a page table
+ * corrupted or filled by hand (restored from a checkpoint, pages permuted
+ * over a shared pool) can make them read outside the buffers.  This call
+ * reads, within the buffers only, every row's page count (must be
+ * 0..max_pages_per_head), every listed page id (must be 0..page_capacity-1)
+ * and that page's metadata (tier id below 3, or below 6 with value_tiers;
+ * count 1..page_size; reserved 0; code block inside the arena).  Any
+ * violation sets the cache's status word to ADA_EINVAL (read and clear it
+ * with ada_read_status); nothing is written otherwise.  Asynchronous on
+ * `stream`; one work-group per row. */
+ada_status_t ada_validate_cache(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *stream);
+
 /* Angle lookup table (the per-query table of the abstract's angle-domain
  * logits): for each query row (b, hq) and each tier, LUT[j][c] =
  * q[2j] cos(th_c) + q[2j+1] sin(th_c), fp32, no softmax scale.
