@@ -189,6 +189,8 @@ def main():
             "kept_by_tier": [kept[t] for t in TIERS],        # tier ids 0-5: T8, T4, T2, T8V8, T4V8, T2V8
             "pages_by_tier": m["pages_by_tier"],
             "values": "V8" if args.v8 else "fp16",
+            # footprint: every page is one arena block (key part, then values)
+            "cache_arena_bytes": units * 16, "cache_arena_bytes_per_kept_token_head": units * 16 / m["kept"],
             "decode_chunk_pages": cfg.decode_chunk_pages, "queries_per_sequence": Q,
         },
         "roofline": {

@@ -42,8 +42,7 @@ class CacheDesc(ctypes.Structure):
                 ("page_capacity", ctypes.c_int64), ("arena_capacity16", ctypes.c_int64),
                 ("page_table", ctypes.c_void_p), ("num_pages", ctypes.c_void_p),
                 ("open_page", ctypes.c_void_p), ("page_meta", ctypes.c_void_p),
-                ("code_arena", ctypes.c_void_p), ("value_pool", ctypes.c_void_p),
-                ("alloc", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("code_arena", ctypes.c_void_p), ("alloc", ctypes.c_void_p), ("status", ctypes.c_void_p)]
 
 
 _lib = None
@@ -160,29 +159,25 @@ class Cache:
 
     def __init__(self, cfg, num_seqs, max_pages_per_head, page_capacity, arena_capacity16, device="cuda"):
         self.cfg = cfg
-        P = cfg.page_size
         rows = num_seqs * cfg.num_kv_heads
         self.page_table = torch.zeros((rows, max_pages_per_head), dtype=torch.int32, device=device)
         self.num_pages = torch.zeros(rows, dtype=torch.int32, device=device)
         self.open_page = torch.full((rows, NUM_TIERS), -1, dtype=torch.int32, device=device)
         self.page_meta = torch.zeros((page_capacity, 8), dtype=torch.uint8, device=device)
         self.code_arena = torch.zeros(arena_capacity16 * 16, dtype=torch.uint8, device=device)
-        self.value_pool = torch.zeros((page_capacity, P * D), dtype=torch.int16, device=device)
         self.alloc = torch.zeros(2, dtype=torch.int64, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.desc = CacheDesc(num_seqs, max_pages_per_head, page_capacity, arena_capacity16,
                               self.page_table.data_ptr(), self.num_pages.data_ptr(), self.open_page.data_ptr(),
-                              self.page_meta.data_ptr(), self.code_arena.data_ptr(), self.value_pool.data_ptr(),
-                              self.alloc.data_ptr(), self.status.data_ptr())
+                              self.page_meta.data_ptr(), self.code_arena.data_ptr(), self.alloc.data_ptr(),
+                              self.status.data_ptr())
 
     def host(self):
         """numpy copies of every buffer (for comparisons)."""
         import numpy as np
         return {"page_table": self.page_table.cpu().numpy(), "num_pages": self.num_pages.cpu().numpy(),
                 "open_page": self.open_page.cpu().numpy(), "page_meta": self.page_meta.cpu().numpy(),
-                "arena": self.code_arena.cpu().numpy(),
-                "value_pool": self.value_pool.cpu().numpy().view(np.uint16),
-                "alloc": self.alloc.cpu().numpy()}
+                "arena": self.code_arena.cpu().numpy(), "alloc": self.alloc.cpu().numpy()}
 
 
 def cache_init(cache):

@@ -87,10 +87,10 @@ ada_status_t check_cache(const ada_config_t *cfg, const ada_cache_t *c) {
         return ADA_EINVAL;
     if (c->page_capacity > INT32_MAX || c->arena_capacity16 > (int64_t)UINT32_MAX) return ADA_EUNSUPPORTED;
     if (check_dims(cfg, c->num_seqs, c->max_pages_per_head)) return ADA_EUNSUPPORTED;
-    if (!c->page_table || !c->num_pages || !c->open_page || !c->page_meta || !c->code_arena || !c->value_pool ||
-        !c->alloc || !c->status)
+    if (!c->page_table || !c->num_pages || !c->open_page || !c->page_meta || !c->code_arena || !c->alloc ||
+        !c->status)
         return ADA_EINVAL;
-    if (((uintptr_t)c->code_arena & 15) || ((uintptr_t)c->value_pool & 15) || ((uintptr_t)c->page_meta & 7))
+    if (((uintptr_t)c->code_arena & 15) || ((uintptr_t)c->page_meta & 7))
         return ADA_EINVAL;
     return ADA_OK;
 }
@@ -149,7 +149,6 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.num_pages = cache->num_pages;
     a.page_meta = cache->page_meta;
     a.arena = cache->code_arena;
-    a.value_pool = cache->value_pool;
     a.q = q;
     a.pm = w.pm;
     a.pl = w.pl;
@@ -169,7 +168,6 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.app_keys = nullptr;
     a.app_values = nullptr;
     a.arena_w = nullptr;
-    a.value_pool_w = nullptr;
     a.status = cache->status;
     a.logit_buf = nullptr;
     a.util = nullptr;
@@ -224,7 +222,6 @@ AppendLaunch make_append(const ada_config_t *cfg, const ada_cache_t *cache, int3
     a.open_page = cache->open_page;
     a.page_meta = cache->page_meta;
     a.arena = cache->code_arena;
-    a.value_pool = cache->value_pool;
     a.alloc = cache->alloc;
     a.status = cache->status;
     a.key_cnt = w.key_cnt;
@@ -577,7 +574,6 @@ ada_status_t ada_decode_append(const ada_config_t *cfg, const ada_cache_t *cache
     a.app_keys = new_keys;
     a.app_values = new_values;
     a.arena_w = cache->code_arena;
-    a.value_pool_w = cache->value_pool;
     if ((e = launch_decode_partials(a, (hipStream_t)stream)) != hipSuccess) return ADA_EHIP;
     // 3. reduction over the chunks
     return hip_status(launch_decode_reduce(a, (hipStream_t)stream));
@@ -725,7 +721,6 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.open_page = cache->open_page;
     a.page_meta = cache->page_meta;
     a.arena = cache->code_arena;
-    a.value_pool = cache->value_pool;
     a.alloc = cache->alloc;
     a.status = cache->status;
     a.tile_counts = w.tile_counts;
@@ -740,7 +735,6 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_page_table = nullptr;
     a.src_page_meta = nullptr;
     a.src_arena = nullptr;
-    a.src_value_pool = nullptr;
     a.src_maxp = 0;
     a.src_of_slot = nullptr;
     a.src_of_slot_pages = 0;
@@ -879,7 +873,6 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.open_page = dst->open_page;
     a.page_meta = dst->page_meta;
     a.arena = dst->code_arena;
-    a.value_pool = dst->value_pool;
     a.alloc = dst->alloc;
     a.status = dst->status;
     a.tile_counts = w.tile_counts;
@@ -894,7 +887,6 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_page_table = src->page_table;
     a.src_page_meta = src->page_meta;
     a.src_arena = src->code_arena;
-    a.src_value_pool = src->value_pool;
     a.src_maxp = src->max_pages_per_head;
     a.src_of_slot = r.src_of_slot;
     a.src_of_slot_pages = r.src_of_slot_pages;

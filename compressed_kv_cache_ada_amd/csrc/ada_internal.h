@@ -27,13 +27,19 @@ __host__ __device__ constexpr int tier_vb(int t) { return tier_v8(t) ? 8 : 16; }
 __host__ __device__ constexpr int64_t tier_rate(int t) {
     return 2 + 8 * (tier_tb(t) + tier_sb(t)) + (tier_v8(t) ? 132 : 256);
 }
-// code block of one page in 16-byte units: P * (2 + 8 tb + 8 sb) / 16
-__host__ __device__ constexpr int block16(int t, int P) { return P * (2 + 8 * tier_tb(t) + 8 * tier_sb(t)) / 16; }
-// V8 value page (in the page's value-pool slot, as bytes): per 8-token group,
-// [8 tokens][4 dimension blocks] scale bytes (a token's four scales are one
-// 4-byte word), then [128 dims][8 tokens] code bytes c + 128 (offset binary)
-constexpr int kV8Group = 1056;
-constexpr int kV8Codes = 32;   // offset of the codes inside a group
+// A page's block in the arena: its key part (radius and codes), then its
+// value part.  Sizes in 16-byte units:
+//   key part   P * (2 + 8 tb + 8 sb) / 16
+//   value part P * 256 / 16 (fp16) or P * 132 / 16 (V8)
+__host__ __device__ constexpr int key16(int t, int P) { return P * (2 + 8 * tier_tb(t) + 8 * tier_sb(t)) / 16; }
+__host__ __device__ constexpr int val16(int t, int P) { return P * (tier_v8(t) ? 132 : 256) / 16; }
+__host__ __device__ constexpr int block16(int t, int P) { return key16(t, P) + val16(t, P); }
+// fp16 value part: 8-token groups of 2048 bytes, [128 dims][8 tokens] fp16.
+// V8 value part: 16-token groups of 2112 bytes, [16 tokens][4 dimension
+// blocks] scale bytes (a token's four scales are one 4-byte word), then
+// [128 dims][16 tokens] code bytes c + 128 (offset binary)
+constexpr int kV8Group = 2112;
+constexpr int kV8Codes = 64;   // offset of the codes inside a group
 
 // a pair of fp16 values, both finite
 __host__ __device__ inline bool values_finite(uint32_t two_halves) {
@@ -74,7 +80,6 @@ struct DecodeLaunch {
     const int32_t *num_pages;
     const ada_page_meta_t *page_meta;
     const uint8_t *arena;
-    const uint16_t *value_pool;
     const float *q;
     float *pm, *pl, *pacc;     // split-K partials
     float *out, *lse;
@@ -88,7 +93,6 @@ struct DecodeLaunch {
     const float *app_keys;        // [B * Hkv][128] fp32
     const uint16_t *app_values;   // [B * Hkv][128] fp16 bits
     uint8_t *arena_w;
-    uint16_t *value_pool_w;
     int32_t *status;
     // utility emission (logit_buf != nullptr): the split-K pass stores every
     // kept token's base-2 logits at [page * P + slot][Hq / Hkv]; the utility
@@ -132,17 +136,16 @@ struct EncodeLaunch {
     const int32_t *dest_slot;   // [n]
     const ada_page_meta_t *page_meta;
     uint8_t *arena;
-    uint16_t *value_pool;
     int32_t P;
     int32_t *status;
     int32_t half_pairs;   // pair j = (k[j], k[j + 64]) instead of (k[2j], k[2j + 1])
 };
 hipError_t launch_encode_write(const EncodeLaunch &a, hipStream_t s);
-// Zero the code blocks and value pages of new pages listed as
-// (page id) in pages[0..*n_pages), upper bound max_n.
+// Zero the blocks of new pages listed as (page id) in pages[0..*n_pages),
+// upper bound max_n.
 hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64_t max_n,
-                             const ada_page_meta_t *page_meta, uint8_t *arena, uint16_t *value_pool,
-                             int32_t P, const int32_t *status, hipStream_t s);
+                             const ada_page_meta_t *page_meta, uint8_t *arena, int32_t P, const int32_t *status,
+                             hipStream_t s);
 // Host-callable copies of device helpers, for CPU tests of the library.
 uint16_t host_f64_to_f16(double x);
 
@@ -156,7 +159,6 @@ struct PackLaunch {
     int32_t *page_table, *num_pages, *open_page;
     ada_page_meta_t *page_meta;
     uint8_t *arena;
-    uint16_t *value_pool;
     int64_t *alloc;
     int32_t *status;
     // workspace
@@ -174,7 +176,6 @@ struct PackLaunch {
     const int32_t *src_page_table;
     const ada_page_meta_t *src_page_meta;
     const uint8_t *src_arena;
-    const uint16_t *src_value_pool;
     int32_t src_maxp;
     int4 *src_of_slot;              // [src_of_slot_pages][P] source {page, slot, tier, code_off16} per new slot
     int64_t src_of_slot_pages;
@@ -196,7 +197,6 @@ struct AppendLaunch {
     int32_t *page_table, *num_pages, *open_page;
     ada_page_meta_t *page_meta;
     uint8_t *arena;
-    uint16_t *value_pool;
     int64_t *alloc;
     int32_t *status;
     // workspace

@@ -132,8 +132,11 @@ __device__ __forceinline__ void logits_t4(const CodeRegs &k, const float *lut4, 
     for (int g = 0; g < G; ++g) lg[g] = acc[g] * m;
 }
 
+// T2 angles are the 4-bit grid's points 4 c (both grids start at -pi), so
+// the T4 table serves T2 codes at index 4 c: the same entries, bit for bit,
+// without a table of their own
 template <int G>
-__device__ __forceinline__ void logits_t2(const CodeRegs &k, const float *lut2, float mul, float (&lg)[G]) {
+__device__ __forceinline__ void logits_t2(const CodeRegs &k, const float *lut4, float mul, float (&lg)[G]) {
     // quarter q covers pairs 16q..16q+15: angle word q (2-bit codes) and
     // magnitude bits [48q, 48q+48) (3-bit codes)
     const uint32_t tw[4] = {k.u[0].x, k.u[0].y, k.u[0].z, k.u[0].w};
@@ -152,14 +155,14 @@ __device__ __forceinline__ void logits_t2(const CodeRegs &k, const float *lut2, 
     for (int q = 0; q < 4; ++q) {
         const uint32_t t = tw[q];
         const uint64_t win = win4[q];
-        const float *lu = lut2 + q * 16 * 4 * G;
+        const float *lu = lut4 + q * 16 * 16 * G;
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {   // 8 pairs at a time
             float e[8][G];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int jj = 8 * h8 + j;
-                lut_load<G, 4>(lu + jj * 4 * G, (t >> (2 * jj)) & 3u, e[j]);
+                lut_load<G, 16>(lu + jj * 16 * G, 4u * ((t >> (2 * jj)) & 3u), e[j]);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -239,11 +242,9 @@ struct AdaPolicy {
     static constexpr bool kStaged = true;
     static constexpr bool kValueTiers = VT;   // the cache may hold pages of tiers 3-5 (V8 values)
     struct Smem {
-        float lut4[64 * 16 * G];   // 4-bit angle grid, lut_index<G, 16> layout
-        float lut2[64 * 4 * G];    // 2-bit angle grid, lut_index<G, 4> layout
+        float lut4[64 * 16 * G];   // 4-bit angle grid (and the 2-bit one), lut_index<G, 16> layout
         float2 cs8[256];           // cos / sin of the 8-bit grid
         float2 cs4[16];            // the 4-bit sub-grid, contiguous (conflict-free reads)
-        float2 cs2[4];             // the 2-bit sub-grid
         float q8[64 * G * 2];      // [j][g][x|y] query pairs (T8, factorised)
         CodeStage st[NW];          // the next group's code units, per wavefront
         uint32_t enc_words[2][16]; // bit-string packing of the fused append's key
@@ -254,7 +255,6 @@ struct AdaPolicy {
     const int32_t *num_pages_;
     const ada_page_meta_t *page_meta;
     const uint8_t *arena;
-    const uint16_t *value_pool;
     const float *q;
     int32_t Q, Hq, Gr;   // queries per sequence, query heads, query heads per KV head
     int32_t voff;        // first virtual head of this work-group (slices of 8 when Q * Gr > 8)
@@ -265,7 +265,6 @@ struct AdaPolicy {
     const float *app_keys;
     const uint16_t *app_values;
     uint8_t *arena_w;
-    uint16_t *value_pool_w;
     int32_t *status;
 
     // Fused append: the work-group whose chunk holds the page booked for the
@@ -288,18 +287,16 @@ struct AdaPolicy {
             if (!own) return false;
             const int slot = app_slot[row];
             const uint2 m = ldg<uint2>(page_meta + dp);
-            if (slot == 0) {   // a new page: zero its code block and value page
+            if (slot == 0) {   // a new page: zero its block (key and value parts)
                 const int tid = threadIdx.x;
                 uint4 *cb = reinterpret_cast<uint4 *>(arena_w + (size_t)m.y * 16);
                 for (int k = tid; k < block16(m.x & 0xFF, P); k += NW * 64) cb[k] = make_uint4(0u, 0u, 0u, 0u);
-                uint4 *vp = reinterpret_cast<uint4 *>(value_pool_w + (size_t)dp * P * kD);
-                for (int k = tid; k < P * kD / 8; k += NW * 64) vp[k] = make_uint4(0u, 0u, 0u, 0u);
                 __threadfence_block();
                 __syncthreads();
             }
             if (w == 0) {
-                enc::encode_write_one(app_keys + (size_t)row * kD, app_values + (size_t)row * kD, dp, slot, m, arena_w,
-                                      value_pool_w, P, status, s.enc_words, half != 0);
+                enc::encode_write_one(app_keys + (size_t)row * kD, app_values + (size_t)row * kD, slot, m, arena_w, P,
+                                      status, s.enc_words, half != 0);
                 __threadfence_block();
             }
             return true;
@@ -308,6 +305,13 @@ struct AdaPolicy {
 
     __device__ int num_pages(int row, int) const { return num_pages_[row]; }
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
+    // a page's value part: its block's bytes after the key part
+    __device__ const uint8_t *value_part(int, uint2 m) const {
+        // key part units per 16 tokens by key tier, one byte each (130, 66, 42)
+        static_assert(key16(0, 16) == 130 && key16(1, 16) == 66 && key16(2, 16) == 42, "key part sizes");
+        const uint32_t k16 = (0x2A4282u >> (8 * key_tier(m.x & 0xFF))) & 0xFFu;
+        return arena + (size_t)(m.y + k16 * (P / 16)) * 16;
+    }
 
     // phase 1: query pairs and the grid directions.  Virtual head voff + v
     // of the KV head is query qi = (voff + v) / Gr, head h * Gr + (voff + v)
@@ -324,21 +328,16 @@ struct AdaPolicy {
             const float2 d = grid_dir(c);
             s.cs8[c] = d;
             if ((c & 15) == 0) s.cs4[c >> 4] = d;
-            if ((c & 63) == 0) s.cs2[c >> 6] = d;
         }
     }
 
-    // phase 2 (after a barrier): the T4 / T2 tables
+    // phase 2 (after a barrier): the T4 table (T2 codes use its entries 4 c)
     __device__ void build(Smem &s, int tid, int nt) const {
         // consecutive threads fill consecutive heads, then codes
         for (int i = tid; i < 64 * 16 * G; i += nt) {
             const int g = i % G, c = (i / G) & 15, j = i / (16 * G);
             s.lut4[lut_index<G, 16>(j, c, g)] =
                 lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs4[c]);
-        }
-        for (int i = tid; i < 64 * 4 * G; i += nt) {
-            const int g = i % G, c = (i / G) & 3, j = i / (4 * G);
-            s.lut2[lut_index<G, 4>(j, c, g)] = lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs2[c]);
         }
     }
 
@@ -366,8 +365,8 @@ struct AdaPolicy {
         uint32_t slot = slot_;
         if constexpr (VT) asm volatile("" : "+v"(slot));
         if constexpr (VT) {
-            const uint8_t *vb = reinterpret_cast<const uint8_t *>(value_pool + (size_t)page * P * kD);
-            __builtin_amdgcn_global_load_lds(vb + (slot >> 3) * kV8Group + (slot & 7) * 4, &s.vs[w][0], 4, 0, 0);
+            const uint8_t *vb = value_part(page, meta);
+            __builtin_amdgcn_global_load_lds(vb + (slot >> 4) * kV8Group + (slot & 15) * 4, &s.vs[w][0], 4, 0, 0);
         }
         const uint8_t *blk = arena + (size_t)meta.y * 16;
         const int tier = key_tier(meta.x & 0xFF);
@@ -411,7 +410,7 @@ struct AdaPolicy {
             if (valid && tier == ADA_TIER_T4) logits_t4<G>(k, s.lut4, mul, lg);
         }
         if (__any(valid && tier == ADA_TIER_T2)) {
-            if (valid && tier == ADA_TIER_T2) logits_t2<G>(k, s.lut2, mul, lg);
+            if (valid && tier == ADA_TIER_T2) logits_t2<G>(k, s.lut4, mul, lg);
         }
         if (__any(valid && tier == ADA_TIER_T8)) {
             if (valid && tier == ADA_TIER_T8) logits_t8<G, P>(k, s.cs8, s.q8, mul, lg);
@@ -433,7 +432,6 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.num_pages_ = a.num_pages;
     pol.page_meta = a.page_meta;
     pol.arena = a.arena;
-    pol.value_pool = a.value_pool;
     pol.q = a.q;
     pol.Q = a.Q;
     pol.Hq = a.Hq;
@@ -456,12 +454,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     pol.app_keys = a.app_keys;
     pol.app_values = a.app_values;
     pol.arena_w = a.arena_w;
-    pol.value_pool_w = a.value_pool_w;
     pol.status = a.status;
     pol.mul = a.scale * core::kLog2e;
     core::CoreArgs c;
     c.page_table = a.page_table;
-    c.value_pool = a.value_pool;
     c.pm = a.pm;
     c.pl = a.pl;
     c.pacc = a.pacc;

@@ -117,7 +117,6 @@ __device__ __forceinline__ T ldg(const void *p) {
 // Shared arguments of a split-K pass.
 struct CoreArgs {
     const int32_t *page_table;
-    const uint16_t *value_pool;
     float *pm, *pl, *pacc;
     int32_t Hq, Hkv, maxp, chunk_pages, S;
     float *logit_buf;   // EMIT: [page * P + slot][G] base-2 logits of every kept token
@@ -231,6 +230,10 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //   Smem                      policy LDS (per-query tables)
 //   int num_pages(row, b)     pages in the row
 //   uint2 meta(page, idx, b)  x = tier | count << 8, y = policy data
+//   const uint8_t *value_part(page, meta)   the page's values: fp16 pages
+//                                           in 8-token groups of [128 dims]
+//                                           [8 tokens]; V8 pages as in
+//                                           ada_internal.h
 //   void prologue(smem, b, h, tid, nthreads)   stores before a barrier
 //   void build(smem, tid, nthreads)            tables after that barrier
 //   bool after_pages(smem, pages, n, row, w, lane)  work before any page of
@@ -239,8 +242,8 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //                                              must follow
 //   kValueTiers: pages of tiers 3-5 hold V8 values (see include/ada.h)
 //     void scale_halves(codes, blk, kp, sh[8])  fp16 scales of dimension
-//                                              blocks 2kp, 2kp + 1 of the 8
-//                                              tokens of block blk of the
+//                                              blocks 2kp, 2kp + 1 of tokens
+//                                              8 blk .. 8 blk + 7 of the
 //                                              current group
 //   kStaged = true:
 //     void stage(smem, w, meta, page, slot)    request a group's codes (and
@@ -370,43 +373,39 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
 
         // 3. values -> MFMA A operands, issued after the logit arithmetic so
         //    they are not held in registers through it (other wavefronts'
-        //    work covers their latency).  A block past the row's last page is
-        //    read from the group's first page instead: weight 0.  A V8 page
-        //    gives 8 code bytes per dimension (.x, .y) and the block's
-        //    scale dword t (.z of tile t), converted before the MFMAs.
+        //    work covers their latency).  The K index of the MFMAs is
+        //    permuted: lane (n_head, kq) takes tokens 16 kq .. 16 kq + 15 of
+        //    the group, the first eight at step kc = 0, the others at kc = 1,
+        //    so that its tokens are consecutive slots of one page.  A lane
+        //    past the row's last page reads the group's first page instead
+        //    (weight 0).  fp16 page: 16 bytes (8 tokens of one dimension) per
+        //    tile and step; V8 page: 8 code bytes per tile and step, converted
+        //    before the MFMAs.
         uint4 va[2][8];
-        bool v8[2] = {false, false};
-        if constexpr (Pol::kValueTiers) {
+        bool v8 = false;
+        {
             // the lane's place in the MFMA operands, made opaque here so that
             // the per-lane value offsets are formed in the loop rather than
             // hoisted out of it (they would hold registers for all of it)
             uint32_t ln = lane;
-            asm volatile("" : "+v"(ln));
+            if constexpr (Pol::kValueTiers) asm volatile("" : "+v"(ln));
             const int vq = ln >> 4, vh = ln & 15;   // kq, n_head
+            const int vslot = gbase + (16 * vq) / P;
+            const int pidx = cs.pages[vslot] >= 0 ? vslot : gbase;
+            const uint2 vmeta = cs.meta[pidx];
+            const uint8_t *vpart = pol.value_part(cs.pages[pidx], vmeta);
+            const int tok = (16 * vq) % P;           // the lane's first slot in that page
+            if constexpr (Pol::kValueTiers) v8 = tier_v8(vmeta.x & 0xFF);
+            // V8 page: the 16 code bytes of the lane's dimension (its 16
+            // tokens) per tile, read at both steps (the second read hits the
+            // cache): the same instructions as the fp16 loads, other addresses
+            const uint8_t *b8 = vpart + (tok / 16) * kV8Group + kV8Codes + vh * 16;
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                const int blk = 4 * kc + vq;        // 8-token block of the group
-                const int pidx = cs.pages[gbase + blk / KB] >= 0 ? gbase + blk / KB : gbase;
-                const uint8_t *vbytes =
-                    reinterpret_cast<const uint8_t *>(a.value_pool + (size_t)cs.pages[pidx] * P * kD);
-                // V8 page: 16 bytes from the lane's dimension's 8 code bytes
-                // (the 8 after it belong to the next dimension, unused); the
-                // same instructions as the fp16 loads, other addresses
-                v8[kc] = tier_v8(cs.meta[pidx].x & 0xFF);
-                const uint8_t *b16 = vbytes + (blk % KB) * 2048 + vh * 16;
-                const uint8_t *b8 = vbytes + (blk % KB) * kV8Group + kV8Codes + vh * 8;
+                const uint8_t *b16 = vpart + (tok / 8 + kc) * 2048 + vh * 16;
+                const uint8_t *base = v8 ? b8 : b16;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(v8[kc] ? b8 + t * 128 : b16 + t * 256);
-            }
-        } else {
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const int blk = 4 * kc + kq;        // 8-token block of the group
-                const int vpage = cs.pages[gbase + blk / KB];
-                const uint16_t *base = a.value_pool + (size_t)(vpage >= 0 ? vpage : cs.pages[gbase]) * P * kD +
-                                       (blk % KB) * 1024 + n_head * 8;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 128);
+                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 256);
             }
         }
 
@@ -438,19 +437,19 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         for (int kc = 0; kc < 2; ++kc) {
             half8_t bh = {}, bl = {};
             if (n_head < G) {
-                bh = *reinterpret_cast<const half8_t *>(&cs.pb[w][0][n_head][32 * kc + 8 * kq]);
-                bl = *reinterpret_cast<const half8_t *>(&cs.pb[w][1][n_head][32 * kc + 8 * kq]);
+                bh = *reinterpret_cast<const half8_t *>(&cs.pb[w][0][n_head][16 * kq + 8 * kc]);
+                bl = *reinterpret_cast<const half8_t *>(&cs.pb[w][1][n_head][16 * kq + 8 * kc]);
             }
             if constexpr (Pol::kValueTiers) {
                 // codes x scales -> fp16 in place; tiles 2k, 2k+1 use dimension
                 // block k.  The scales come from the lanes holding the
                 // tokens, so they are gathered with every lane active.
-                if (__any(v8[kc])) {
+                if (__any(v8)) {
 #pragma unroll
                     for (int kp = 0; kp < 2; ++kp) {   // dimension blocks 2kp, 2kp + 1: tiles 4kp .. 4kp + 3
                         uint32_t sh[8];   // token j's scale halves of the two blocks
-                        pol.scale_halves(codes, 4 * kc + kq, kp, sh);
-                        if (v8[kc]) {
+                        pol.scale_halves(codes, 2 * kq + kc, kp, sh);
+                        if (v8) {
 #pragma unroll
                             for (int kk = 0; kk < 2; ++kk) {
                                 uint32_t sp[4];   // scale pairs of tokens (2i, 2i + 1), block 2kp + kk
@@ -459,7 +458,9 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
                                     sp[i] = __builtin_amdgcn_perm(sh[2 * i + 1], sh[2 * i], kk ? 0x07060302u : 0x05040100u);
 #pragma unroll
                                 for (int t = 4 * kp + 2 * kk; t < 4 * kp + 2 * kk + 2; ++t) {
-                                    const uint32_t lo = va[kc][t].x, hi = va[kc][t].y;
+                                    // step kc's eight tokens: bytes 8 kc .. 8 kc + 7
+                                    const uint32_t lo = kc ? va[kc][t].z : va[kc][t].x;
+                                    const uint32_t hi = kc ? va[kc][t].w : va[kc][t].y;
                                     va[kc][t].w = v8_pair<2>(hi, sp[3]);
                                     va[kc][t].z = v8_pair<0>(hi, sp[2]);
                                     va[kc][t].y = v8_pair<2>(lo, sp[1]);

@@ -23,7 +23,7 @@ struct DensePolicy {
         float qd[kD * G];   // [d][g], pre-multiplied by scale * log2(e)
     };
     const int32_t *ctx_len;
-    const uint16_t *k_pool;
+    const uint16_t *k_pool, *v_pool;
     const float *q;
     int32_t Hq;
     float mul;
@@ -32,6 +32,9 @@ struct DensePolicy {
     __device__ uint2 meta(int, int idx, int b) const {
         const int count = min(P, ctx_len[b] - idx * P);
         return make_uint2((uint32_t)count << 8, 0u);
+    }
+    __device__ const uint8_t *value_part(int page, uint2) const {
+        return reinterpret_cast<const uint8_t *>(v_pool + (size_t)page * P * kD);
     }
     __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
         const float *qrow = q + ((size_t)b * Hq + (size_t)h * G) * kD;
@@ -80,12 +83,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void dense_partials_kernel(DenseLaunc
     Pol pol;
     pol.ctx_len = a.ctx_len;
     pol.k_pool = a.k_pool;
+    pol.v_pool = a.v_pool;
     pol.q = a.q;
     pol.Hq = a.Hq;
     pol.mul = a.scale * core::kLog2e;
     core::CoreArgs c;
     c.page_table = a.page_table;
-    c.value_pool = a.v_pool;
     c.pm = a.pm;
     c.pl = a.pl;
     c.pacc = a.pacc;

@@ -29,8 +29,8 @@ __global__ __launch_bounds__(256, 4) void encode_write_kernel(EncodeLaunch a) {
         const int page = a.dest_page[item];
         if (page < 0) continue;
         const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + page);
-        enc::encode_write_one(a.keys + item * kD, a.values + item * kD, page, a.dest_slot[item], meta, a.arena,
-                              a.value_pool, a.P, a.status, words[wv], a.half_pairs != 0);
+        enc::encode_write_one(a.keys + item * kD, a.values + item * kD, a.dest_slot[item], meta, a.arena, a.P,
+                              a.status, words[wv], a.half_pairs != 0);
     }
 }
 
@@ -181,24 +181,27 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
         const int4 e = tid < P ? s_cur[tid] : make_int4(-1, 0, 0, 0);
 
         // 1. this dimension's value of every source token, all loads issued
-        //    before any is used (branch-free: an empty slot reads the pool's
+        //    before any is used (branch-free: an empty slot reads the arena's
         //    first word, unused).  fp16 source: the dword holding the value
         //    (twice); V8 source: the dwords holding its code and scale bytes.
+        //    A source page's values follow its key part in its block.
         uint32_t wa[P], wb[P];
-        const uint8_t *pool = reinterpret_cast<const uint8_t *>(a.src_value_pool);
 #pragma unroll
         for (int k = 0; k < P; ++k) {
             const int4 ek = s_cur[k];
-            const int idx = ek.y & 7;
-            const size_t grp = (size_t)max(ek.x, 0) * P * kD * 2 + (ek.y >> 3) * (tier_v8(ek.z) ? kV8Group : 2048);
-            size_t oa = grp + dim * 16 + (idx >> 1) * 4, ob = oa;
+            const size_t vpart = ((size_t)(uint32_t)ek.w + key16(ek.z, P)) * 16;
+            size_t oa, ob;
             if (tier_v8(ek.z)) {
-                oa = grp + kV8Codes + dim * 8 + (idx & 4);
-                ob = grp + idx * 4;
+                const size_t grp = vpart + (ek.y >> 4) * kV8Group;
+                oa = grp + kV8Codes + dim * 16 + (ek.y & 12);
+                ob = grp + (ek.y & 15) * 4;
+            } else {
+                oa = vpart + (ek.y >> 3) * 2048 + dim * 16 + ((ek.y & 7) >> 1) * 4;
+                ob = oa;
             }
             if (ek.x < 0) oa = ob = 0;
-            wa[k] = *reinterpret_cast<const uint32_t *>(pool + oa);
-            wb[k] = *reinterpret_cast<const uint32_t *>(pool + ob);
+            wa[k] = *reinterpret_cast<const uint32_t *>(a.src_arena + oa);
+            wb[k] = *reinterpret_cast<const uint32_t *>(a.src_arena + ob);
         }
 
         // 2. threads 0..P-1: token tid's codes
@@ -225,40 +228,41 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
             }
         }
 
-        // 3. the value page, one (8-token group, dimension) word per thread
-        //    and group; a V8 source is decoded first (its values are fp16
+        // 3. the value part, per 16 tokens and dimension: one thread per
+        //    dimension; a V8 source is decoded first (its values are fp16
         //    numbers exactly)
-        uint16_t *dv = a.value_pool + (size_t)page * P * kD;
-        uint8_t *dvb = reinterpret_cast<uint8_t *>(dv);
+        uint8_t *dvb = a.arena + ((size_t)m.code_off16 + key16(tier, P)) * 16;
         const bool dst_v8 = tier_v8(tier);
 #pragma unroll
-        for (int g = 0; g < P / 8; ++g) {
-            uint32_t h[8];
-            bool live[8];
+        for (int g = 0; g < P / 16; ++g) {
+            uint32_t h[16];
+            bool live[16];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int4 ek = s_cur[8 * g + k];
-                const uint32_t ra = wa[8 * g + k], rb = wb[8 * g + k];
-                const int idx = ek.y & 7;
+            for (int k = 0; k < 16; ++k) {
+                const int4 ek = s_cur[16 * g + k];
+                const uint32_t ra = wa[16 * g + k], rb = wb[16 * g + k];
                 live[k] = ek.x >= 0;
                 if (!live[k]) h[k] = 0u;
                 else if (tier_v8(ek.z))
-                    h[k] = v8_value_bits((int)((ra >> (8 * (idx & 3))) & 0xFFu) - 128, (rb >> (8 * (dim >> 5))) & 0xFFu);
-                else h[k] = (ra >> ((idx & 1) * 16)) & 0xFFFFu;
+                    h[k] = v8_value_bits((int)((ra >> (8 * (ek.y & 3))) & 0xFFu) - 128, (rb >> (8 * (dim >> 5))) & 0xFFu);
+                else h[k] = (ra >> ((ek.y & 1) * 16)) & 0xFFFFu;
             }
-            if (!dst_v8) {
-                uint32_t w[4];
+            if (!dst_v8) {   // two 8-token groups, [128 dims][8 tokens] fp16 each
 #pragma unroll
-                for (int k = 0; k < 4; ++k) w[k] = h[2 * k] | (h[2 * k + 1] << 16);
-                *reinterpret_cast<uint4 *>(dv + g * 1024 + dim * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+                for (int hg = 0; hg < 2; ++hg) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w[k] = h[8 * hg + 2 * k] | (h[8 * hg + 2 * k + 1] << 16);
+                    *reinterpret_cast<uint4 *>(dvb + (2 * g + hg) * 2048 + dim * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+                }
             } else {
                 // V8: per token, the exponent of its 32-dimension block (32
                 // consecutive lanes), then this dimension's code; empty slots
-                // stay zero
-                uint32_t cw[2] = {0u, 0u};
-                uint8_t sbytes[8];
+                // are zero
+                uint32_t cw[4] = {0u, 0u, 0u, 0u};
+                uint32_t sw[4] = {0u, 0u, 0u, 0u};   // scale bytes of this block, tokens 4i .. 4i + 3
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
+                for (int k = 0; k < 16; ++k) {
                     int mx = (int)(h[k] & 0x7FFFu);
                     mx = max(mx, __shfl_xor(mx, 1, 64));
                     mx = max(mx, __shfl_xor(mx, 2, 64));
@@ -269,17 +273,15 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
                     const uint32_t c = live[k] ? (uint32_t)(enc::v8_code(h[k], ex) + 128) : 0u;
                     const uint32_t sbyte = live[k] ? (uint32_t)(ex + 127) : 0u;
                     cw[k >> 2] |= c << (8 * (k & 3));
-                    sbytes[k] = (uint8_t)sbyte;
+                    sw[k >> 2] |= sbyte << (8 * (k & 3));
                 }
-                *reinterpret_cast<uint2 *>(dvb + g * kV8Group + kV8Codes + dim * 8) = make_uint2(cw[0], cw[1]);
-                if ((dim & 31) == 0)   // token k's scale of this block
+                uint8_t *grp = dvb + g * kV8Group;
+                *reinterpret_cast<uint4 *>(grp + kV8Codes + dim * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+                if ((dim & 31) == 0)   // token k's scale byte of this block
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) dvb[g * kV8Group + k * 4 + (dim >> 5)] = sbytes[k];
+                    for (int k = 0; k < 16; ++k) grp[k * 4 + (dim >> 5)] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
             }
         }
-        if (dst_v8)   // the rest of the page's value slot is zero
-            for (int j = (P / 8) * kV8Group / 16 + tid; j < P * kD * 2 / 16; j += 128)
-                reinterpret_cast<uint4 *>(dvb)[j] = make_uint4(0u, 0u, 0u, 0u);
         if (inext < n) publish(buf ^ 1, m_next, e_next);
         m = m_next;
         __syncthreads();   // the next page's entries are in place; this page's buffer is refilled after the next barrier
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
 // pages: explicit list, or (when list == nullptr) the range [first, first+n)
 __global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, const int32_t *first_and_n,
                                                          const ada_page_meta_t *page_meta, uint8_t *arena,
-                                                         uint16_t *value_pool, int32_t P, const int32_t *status) {
+                                                         int32_t P, const int32_t *status) {
     if (read_status(status) != 0) return;
     const int n = first_and_n[1];
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
@@ -300,8 +302,6 @@ __global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, co
         uint4 *cb = reinterpret_cast<uint4 *>(arena + (size_t)meta.y * 16);
         const int nb = block16(tier, P);
         for (int k = threadIdx.x; k < nb; k += blockDim.x) cb[k] = make_uint4(0u, 0u, 0u, 0u);
-        uint4 *vp = reinterpret_cast<uint4 *>(value_pool + (size_t)page * P * kD);
-        for (int k = threadIdx.x; k < P * kD / 8; k += blockDim.x) vp[k] = make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
@@ -990,10 +990,10 @@ hipError_t launch_encode_write(const EncodeLaunch &a, hipStream_t s) {
 }
 
 hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64_t max_n,
-                             const ada_page_meta_t *page_meta, uint8_t *arena, uint16_t *value_pool, int32_t P,
-                             const int32_t *status, hipStream_t s) {
+                             const ada_page_meta_t *page_meta, uint8_t *arena, int32_t P, const int32_t *status,
+                             hipStream_t s) {
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_n, 1, 4096)), dim3(256), 0, s, pages, n_pages,
-                       page_meta, arena, value_pool, P, status);
+                       page_meta, arena, P, status);
     return hipGetLastError();
 }
 
@@ -1032,7 +1032,7 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     }
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_pages, 1, 4096)), dim3(256), 0, s,
                        (const int32_t *)nullptr, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
-                       a.arena, a.value_pool, a.P, (const int32_t *)a.status);
+                       a.arena, a.P, (const int32_t *)a.status);
     EncodeLaunch e;
     e.keys = a.keys;
     e.values = a.values;
@@ -1041,7 +1041,6 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     e.dest_slot = a.dest_slot;
     e.page_meta = a.page_meta;
     e.arena = a.arena;
-    e.value_pool = a.value_pool;
     e.P = a.P;
     e.status = a.status;
     e.half_pairs = a.half_pairs;
@@ -1067,7 +1066,7 @@ hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s) {
     hipLaunchKernelGGL(append_book_kernel, dim3(1), dim3(1024), 0, s, k);
     hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(a.n, 1, 4096)), dim3(256), 0, s,
                        (const int32_t *)a.new_pages, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
-                       a.arena, a.value_pool, a.P, (const int32_t *)a.status);
+                       a.arena, a.P, (const int32_t *)a.status);
     if (!encode) return hipGetLastError();
     EncodeLaunch e;
     e.keys = a.keys;
@@ -1077,7 +1076,6 @@ hipError_t launch_append(const AppendLaunch &a, bool encode, hipStream_t s) {
     e.dest_slot = a.dest_slot;
     e.page_meta = a.page_meta;
     e.arena = a.arena;
-    e.value_pool = a.value_pool;
     e.P = a.P;
     e.status = a.status;
     e.half_pairs = a.half_pairs;

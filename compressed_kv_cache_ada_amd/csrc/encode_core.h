@@ -238,12 +238,12 @@ __device__ inline uint32_t v8_value_bits(int code, int scale_byte) {
 // Called by all 64 lanes of one wavefront, lane j holding pair j's angle code
 // tc and magnitude code sc and the token's value dims 2j, 2j+1 (fp16 bits):
 // packs the two bit strings (LSB first) in the wavefront's LDS scratch and
-// writes radius r16, codes and values into slot `slot` of page `page` (tier
-// and code block from meta; values as fp16, or V8-encoded for tiers 3-5:
-// the 16 lanes of a row hold one 32-dimension block).
-__device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint32_t v2, int page, int slot,
-                                   uint2 meta, uint8_t *arena, uint16_t *value_pool, int P,
-                                   uint32_t (&words)[2][16]) {
+// writes radius r16, codes and values into slot `slot` of the page whose
+// metadata is meta (tier, and the block at meta.y * 16: key part, then value
+// part; values as fp16, or V8-encoded for tiers 3-5: the 16 lanes of a row
+// hold one 32-dimension block).
+__device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint32_t v2, int slot, uint2 meta,
+                                   uint8_t *arena, int P, uint32_t (&words)[2][16]) {
     const int lane = threadIdx.x & 63;
     const int tier = meta.x & 0xFF;
     const int tb = tier_tb(tier), sb = tier_sb(tier);
@@ -278,6 +278,7 @@ __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint3
         *reinterpret_cast<uint32_t *>(dst) = ws[w];
     }
     if (lane == 0) *reinterpret_cast<uint16_t *>(blk + 2 * slot) = r16;
+    uint8_t *vpart = blk + key16(tier, P) * 16;
     if (tier_v8(tier)) {
         int m = (int)max(v2 & 0x7FFFu, (v2 >> 16) & 0x7FFFu);
         m = max(m, __shfl_xor(m, 1, 64));
@@ -285,12 +286,12 @@ __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint3
         m = max(m, __shfl_xor(m, 4, 64));
         m = max(m, __shfl_xor(m, 8, 64));
         const int e = v8_exponent((uint32_t)m);
-        uint8_t *vb = reinterpret_cast<uint8_t *>(value_pool + (size_t)page * P * kD) + (slot >> 3) * kV8Group;
-        vb[kV8Codes + (2 * lane) * 8 + (slot & 7)] = (uint8_t)(v8_code(v2, e) + 128);
-        vb[kV8Codes + (2 * lane + 1) * 8 + (slot & 7)] = (uint8_t)(v8_code(v2 >> 16, e) + 128);
-        if ((lane & 15) == 0) vb[(slot & 7) * 4 + (lane >> 4)] = (uint8_t)(e + 127);
+        uint8_t *vb = vpart + (slot >> 4) * kV8Group;
+        vb[kV8Codes + (2 * lane) * 16 + (slot & 15)] = (uint8_t)(v8_code(v2, e) + 128);
+        vb[kV8Codes + (2 * lane + 1) * 16 + (slot & 15)] = (uint8_t)(v8_code(v2 >> 16, e) + 128);
+        if ((lane & 15) == 0) vb[(slot & 15) * 4 + (lane >> 4)] = (uint8_t)(e + 127);
     } else {
-        uint16_t *vp = value_pool + (size_t)page * P * kD + (slot >> 3) * 1024 + (slot & 7);
+        uint16_t *vp = reinterpret_cast<uint16_t *>(vpart) + (slot >> 3) * 1024 + (slot & 7);
         vp[(2 * lane) * 8] = (uint16_t)(v2 & 0xFFFF);
         vp[(2 * lane + 1) * 8] = (uint16_t)(v2 >> 16);
     }
@@ -301,12 +302,12 @@ __device__ inline void write_token(uint32_t tc, uint32_t sc, uint16_t r16, uint3
 // Called by all 64 lanes of one wavefront: encodes key[128] (fp32; lane j
 // takes pair j, (key[2j], key[2j+1]) or with half_pairs (key[j], key[j+64])) at the
 // page's tier and writes its radius, codes and value (fp16 bits) into slot
-// `slot` of page `page` (code block at meta.y * 16).  words is the
+// `slot` of the page whose metadata is meta (block at meta.y * 16).  words is the
 // wavefront's LDS scratch for packing the bit strings.  An undecidable code
 // (never expected) sets ADA_EINTERNAL and writes nothing.
-__device__ inline void encode_write_one(const float *key, const uint16_t *value, int page, int slot, uint2 meta,
-                                        uint8_t *arena, uint16_t *value_pool, int P, int32_t *status,
-                                        uint32_t (&words)[2][16], bool half_pairs) {
+__device__ inline void encode_write_one(const float *key, const uint16_t *value, int slot, uint2 meta,
+                                        uint8_t *arena, int P, int32_t *status, uint32_t (&words)[2][16],
+                                        bool half_pairs) {
     #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
     const int tier = meta.x & 0xFF;
@@ -334,7 +335,7 @@ __device__ inline void encode_write_one(const float *key, const uint16_t *value,
         return;
     }
     const uint32_t v2 = *reinterpret_cast<const uint32_t *>(value + 2 * lane);
-    write_token(tc, sc, f64_to_f16_rne_sat(r), v2, page, slot, meta, arena, value_pool, P, words);
+    write_token(tc, sc, f64_to_f16_rne_sat(r), v2, slot, meta, arena, P, words);
 }
 
 }  // namespace enc

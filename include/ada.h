@@ -40,23 +40,23 @@
  *     l_t = scale * r_t * sum_j s_j * LUT[j][theta_code_j],
  *     LUT[j][c] = q[2j] cos(th_c) + q[2j+1] sin(th_c),
  *   followed by softmax over the kept tokens of the (sequence, KV head) and
- *   a weighted sum of their fp16 values.
+ *   a weighted sum of their values (fp16, or V8 decoded to fp16).
  *
- *  Page layout (page size P in {16, 32}, head dim 128):
- *   code block of a page: 16-byte aligned at code_arena + 16 * code_off16,
- *     [radius: P x u16][angle component][magnitude component]; a component
- *     of Bc = 8*b bytes per token is cut into floor(Bc/16) units of 16 bytes
- *     plus one 8-byte unit when Bc mod 16 == 8; unit u of all P tokens is
- *     stored contiguously (token-minor), units in order; code j of width b
- *     occupies bits [j*b, (j+1)*b) of the token's little-endian bit string.
- *     Block bytes: T8 130 P, T4 66 P, T2 42 P.
- *   value page: fp16, element (slot, d) of page p at
- *     value_pool + p*P*128 + (slot/8)*1024 + d*8 + slot%8
- *     (8-token groups, dimension-major inside a group).  A page of a V8
- *     tier uses the start of the same slot as bytes: per 8-token group g,
- *     at byte 1056 g, [8 tokens][4 blocks] scale bytes e + 127, then at
- *     1056 g + 32, [128 dims][8 tokens] code bytes c + 128 (offset
- *     binary); empty slots and the rest of the slot are zero.
+ *  Page layout (page size P in {16, 32}, head dim 128): a page is one block
+ *   of the arena, 16-byte aligned at code_arena + 16 * code_off16: its key
+ *   part, then its value part (so a page's footprint is exactly its tier's
+ *   bytes per token times P).
+ *   key part: [radius: P x u16][angle component][magnitude component]; a
+ *     component of Bc = 8*b bytes per token is cut into floor(Bc/16) units
+ *     of 16 bytes plus one 8-byte unit when Bc mod 16 == 8; unit u of all P
+ *     tokens is stored contiguously (token-minor), units in order; code j of
+ *     width b occupies bits [j*b, (j+1)*b) of the token's little-endian bit
+ *     string.  Key part bytes: T8 130 P, T4 66 P, T2 42 P.
+ *   value part, fp16 tiers (256 P bytes): u16 element (slot, d) at
+ *     (slot/8)*1024 + d*8 + slot%8 (8-token groups, dimension-major).
+ *   value part, V8 tiers (132 P bytes): per 16-token group g, at byte
+ *     2112 g, [16 tokens][4 blocks] scale bytes e + 127, then at
+ *     2112 g + 64, [128 dims][16 tokens] code bytes c + 128 (offset binary).
  *   Unused slots of a page (slot >= count) are zero in codes and values.
  *
  * Conventions for every call:
@@ -139,7 +139,7 @@ typedef struct {
     uint8_t tier;        /* tier id */
     uint8_t count;       /* filled slots, 1..P */
     uint16_t reserved;   /* zero */
-    uint32_t code_off16; /* code block offset in 16-byte units */
+    uint32_t code_off16; /* offset of the page's block in the arena, 16-byte units */
 } ada_page_meta_t;
 
 /* The cache: every pointer is device memory owned by the caller.  Row r of
@@ -147,14 +147,13 @@ typedef struct {
 typedef struct {
     int32_t num_seqs;           /* rows = num_seqs * Hkv */
     int32_t max_pages_per_head; /* page-table row length */
-    int64_t page_capacity;      /* pages in page_meta / value_pool */
-    int64_t arena_capacity16;   /* code arena size in 16-byte units */
+    int64_t page_capacity;      /* pages in page_meta */
+    int64_t arena_capacity16;   /* arena size in 16-byte units (at most 2^32: 64 GiB) */
     int32_t *page_table;        /* [rows][max_pages_per_head] physical page ids */
     int32_t *num_pages;         /* [rows] pages in use per row */
     int32_t *open_page;         /* [rows][ADA_NUM_TIERS] last non-full page per tier, -1 = none */
     ada_page_meta_t *page_meta; /* [page_capacity] */
-    uint8_t *code_arena;        /* [arena_capacity16 * 16], 16-byte aligned */
-    uint16_t *value_pool;       /* [page_capacity][P * 128] fp16 bits */
+    uint8_t *code_arena;        /* [arena_capacity16 * 16], 16-byte aligned: the pages' blocks */
     int64_t *alloc;             /* [2]: next page id, next code unit */
     int32_t *status;            /* [1] device error word (0 = OK) */
 } ada_cache_t;
@@ -162,8 +161,9 @@ typedef struct {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ada_status_str(ada_status_t s);
 
-/* Bytes of one page's code block for a tier and page size (see layout
- * above); -1 for an invalid tier or page size.  Pure host function. */
+/* Bytes of one page's block (key part and value part) for a tier and page
+ * size (see layout above); -1 for an invalid tier or page size.  Pure host
+ * function. */
 int64_t ada_block_bytes(int32_t tier, int32_t page_size);
 
 /* Floats of the angle LUT of one query head as written by ada_build_lut:
@@ -182,7 +182,7 @@ ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, v
  * reads, within the buffers only, every row's page count (must be
  * 0..max_pages_per_head), every listed page id (must be 0..page_capacity-1)
  * and that page's metadata (tier id below 3, or below 6 with value_tiers;
- * count 1..page_size; reserved 0; code block inside the arena).  Any
+ * count 1..page_size; reserved 0; block inside the arena).  Any
  * violation sets the cache's status word to ADA_EINVAL (read and clear it
  * with ada_read_status); nothing is written otherwise.  Asynchronous on
  * `stream`; one work-group per row. */
@@ -264,7 +264,7 @@ ada_status_t ada_append_workspace(const ada_config_t *cfg, const ada_cache_t *ca
  * (abstract: keys stored as radius + angle codes in tier-homogeneous pages).
  * Sequential semantics in request order: request i fills the open page of
  * (seq[i], kv_head[i], tier[i]) at its next slot, or opens a new page (next
- * page id, next code block) appended to that row.
+ * page id, next block of the arena) appended to that row.
  *   seq, kv_head device int32 [n]; tier device uint8 [n]
  *   keys   device fp32 [n][128]; values device fp16 bits [n][128]
  * Device errors: out-of-range seq / head / tier, non-finite key or non-finite
@@ -388,7 +388,7 @@ ada_status_t ada_pack_workspace(const ada_config_t *cfg, const ada_cache_t *cach
 /* Bulk pack (prefill) of sequences 0..B-1 from a tier map (abstract:
  * tier-homogeneous pages with lightweight metadata).  For each sequence,
  * KV head and tier id ascending, the kept tokens in ascending position are
- * cut into pages of P with consecutive page ids and code blocks taken from
+ * cut into pages of P with consecutive page ids and blocks taken from
  * alloc; the rows of sequences 0..B-1 are (re)initialised; open_page holds
  * each (row, tier)'s last page if it is not full.
  *   ctx_len host int32 [B]

@@ -233,23 +233,25 @@ void orc_bits_get(const uint8_t *src, int b, uint16_t *codes, int n)
 
 /* ------------------------------------------------------------------------ */
 /* Page layout.
- * Code block of a page (tier tau, page size P), 16-byte aligned at
- * arena + 16*code_off16:
- *     [radius: P x u16] [angle component] [magnitude component]
+ * Block of a page (tier tau, page size P), 16-byte aligned at
+ * arena + 16*code_off16: the key part, then the value part.
+ * Key part: [radius: P x u16] [angle component] [magnitude component].
  * A component with Bc = 8*b bytes per token is cut into floor(Bc/16) units of
  * 16 bytes, plus one unit of 8 bytes when Bc mod 16 == 8.  Unit u of all P
  * tokens is stored contiguously (token-minor), units in order.
- * Value page (fp16) for page id p: element (slot, d) at
- *     value_pool + p*P*128 + (slot/8)*1024 + d*8 + slot%8.
+ * Value part of an fp16 tier (256 bytes per token): u16 element (slot, d) at
+ *     (slot/8)*1024 + d*8 + slot%8   (8-token groups, dimension-major).
+ * Value part of a V8 tier (132 bytes per token): see v8_scale_off below.
  * Page metadata (8 bytes): tier (u8), count (u8), reserved (u16, zero),
  * code_off16 (u32), little-endian. */
 
 static int comp_bytes(int b) { return 8 * b; }           /* per token */
 
-int64_t orc_block_bytes(int tier, int P)
-{
-    return (int64_t)P * (2 + comp_bytes(TIER_TB[tier]) + comp_bytes(TIER_SB[tier]));
-}
+/* bytes of a page's key part and value part */
+static int64_t key_bytes(int tier, int P) { return (int64_t)P * (2 + comp_bytes(TIER_TB[tier]) + comp_bytes(TIER_SB[tier])); }
+static int64_t value_bytes(int tier, int P) { return (int64_t)P * (TIER_VB[tier] == 16 ? 256 : 132); }
+
+int64_t orc_block_bytes(int tier, int P) { return key_bytes(tier, P) + value_bytes(tier, P); }
 
 /* byte address (relative to the component start) of byte `byte` of the
  * component bit string of token `slot` */
@@ -292,10 +294,8 @@ static void read_token_codes(const uint8_t *block, int tier, int P, int slot,
     orc_bits_get(bs, sb, sc, ORC_NP);
 }
 
-static int64_t value_index(int64_t page, int P, int slot, int d)
-{
-    return page * P * ORC_D + (int64_t)(slot / 8) * 1024 + (int64_t)d * 8 + slot % 8;
-}
+/* u16 index of fp16 value (slot, d) inside a value part */
+static int64_t value_index(int slot, int d) { return (int64_t)(slot / 8) * 1024 + (int64_t)d * 8 + slot % 8; }
 
 /* ------------------------------------------------------------------------ */
 /* V8 value codec (value tiers 3-5).  The abstract speaks of precision tiers
@@ -342,45 +342,49 @@ void orc_v8_decode(const uint8_t *scale_byte, const int8_t *codes, double *v)
     for (int d = 0; d < ORC_D; d++) v[d] = ldexp((double)codes[d], (int)scale_byte[d / 32] - 127 - 6);
 }
 
-/* V8 value page, in the page's value-pool slot viewed as bytes: per 8-token
- * group g, [8 tokens][4 dimension blocks] scale bytes (32 bytes: a token's
- * four scales are one 4-byte word), then [128 dims][8 tokens] code bytes
- * c + 128 (offset binary; 1024 bytes).  Empty slots and the rest of the slot
- * are zero. */
-static int64_t v8_scale_off(int slot, int k) { return (int64_t)(slot / 8) * 1056 + (slot % 8) * 4 + k; }
-static int64_t v8_code_off(int slot, int d) { return (int64_t)(slot / 8) * 1056 + 32 + (int64_t)d * 8 + slot % 8; }
+/* V8 value part: per 16-token group g, at byte 2112 g, [16 tokens][4
+ * dimension blocks] scale bytes (64 bytes: a token's four scales are one
+ * 4-byte word), then at 2112 g + 64, [128 dims][16 tokens] code bytes c + 128
+ * (offset binary; 2048 bytes).  Empty slots are zero. */
+static int64_t v8_scale_off(int slot, int k) { return (int64_t)(slot / 16) * 2112 + (slot % 16) * 4 + k; }
+static int64_t v8_code_off(int slot, int d) { return (int64_t)(slot / 16) * 2112 + 64 + (int64_t)d * 16 + slot % 16; }
 
-static uint8_t *value_page_bytes(uint16_t *pool, int64_t page, int P) { return (uint8_t *)(pool + page * P * ORC_D); }
-
-/* write token `slot`'s values (fp16 bits) into the page's value slot in the
- * tier's format; returns EINVAL for a V8 tier and a non-finite value */
-static int value_write(uint16_t *pool, int64_t page, int tier, int P, int slot, const uint16_t *v)
+/* write token `slot`'s values (fp16 bits) into the value part of `block` in
+ * the tier's format; returns EINVAL for a V8 tier and a non-finite value */
+static int value_write(uint8_t *block, int tier, int P, int slot, const uint16_t *v)
 {
+    uint8_t *vb = block + key_bytes(tier, P);
     if (TIER_VB[tier] == 16) {
-        for (int d = 0; d < ORC_D; d++) pool[value_index(page, P, slot, d)] = v[d];
+        for (int d = 0; d < ORC_D; d++) {
+            int64_t i = 2 * value_index(slot, d);
+            vb[i] = (uint8_t)(v[d] & 0xFF);
+            vb[i + 1] = (uint8_t)(v[d] >> 8);
+        }
         return ORC_OK;
     }
     uint8_t sb[4];
     int8_t c[ORC_D];
     if (orc_v8_encode(v, sb, c) != ORC_OK) return ORC_EINVAL;
-    uint8_t *pb = value_page_bytes(pool, page, P);
-    for (int k = 0; k < 4; k++) pb[v8_scale_off(slot, k)] = sb[k];
-    for (int d = 0; d < ORC_D; d++) pb[v8_code_off(slot, d)] = (uint8_t)(c[d] + 128);
+    for (int k = 0; k < 4; k++) vb[v8_scale_off(slot, k)] = sb[k];
+    for (int d = 0; d < ORC_D; d++) vb[v8_code_off(slot, d)] = (uint8_t)(c[d] + 128);
     return ORC_OK;
 }
 
-/* token `slot`'s decoded values, exact in fp64 */
-static void value_read(const uint16_t *pool, int64_t page, int tier, int P, int slot, double *v)
+/* token `slot`'s decoded values from the value part of `block`, exact in fp64 */
+static void value_read(const uint8_t *block, int tier, int P, int slot, double *v)
 {
+    const uint8_t *vb = block + key_bytes(tier, P);
     if (TIER_VB[tier] == 16) {
-        for (int d = 0; d < ORC_D; d++) v[d] = orc_f16_to_f64(pool[value_index(page, P, slot, d)]);
+        for (int d = 0; d < ORC_D; d++) {
+            int64_t i = 2 * value_index(slot, d);
+            v[d] = orc_f16_to_f64((uint16_t)(vb[i] | (vb[i + 1] << 8)));
+        }
         return;
     }
-    const uint8_t *pb = (const uint8_t *)(pool + page * P * ORC_D);
     uint8_t sb[4];
     int8_t c[ORC_D];
-    for (int k = 0; k < 4; k++) sb[k] = pb[v8_scale_off(slot, k)];
-    for (int d = 0; d < ORC_D; d++) c[d] = (int8_t)((int)pb[v8_code_off(slot, d)] - 128);
+    for (int k = 0; k < 4; k++) sb[k] = vb[v8_scale_off(slot, k)];
+    for (int d = 0; d < ORC_D; d++) c[d] = (int8_t)((int)vb[v8_code_off(slot, d)] - 128);
     orc_v8_decode(sb, c, v);
 }
 
@@ -477,7 +481,7 @@ static void pack_layout(int P, int Hkv, int B, const int32_t *ctx_len, int64_t c
                         const uint16_t *r16, const uint8_t *th_codes, const uint8_t *sc_codes,
                         const uint16_t *values, int32_t max_pages_per_head, int32_t *page_table,
                         int32_t *num_pages, int32_t *open_page, uint8_t *page_meta, uint8_t *arena,
-                        uint16_t *value_pool, int64_t *alloc)
+                        int64_t *alloc)
 {
     for (int b = 0; b < B; b++) {
         for (int h = 0; h < Hkv; h++) {
@@ -499,7 +503,6 @@ static void pack_layout(int P, int Hkv, int B, const int32_t *ctx_len, int64_t c
                         alloc[1] += bb / 16;
                         block = arena + (int64_t)off16 * 16;
                         memset(block, 0, (size_t)bb);
-                        for (int i = 0; i < P * ORC_D; i++) value_pool[page * P * ORC_D + i] = 0;
                         page_table[row * max_pages_per_head + np_row] = (int32_t)page;
                         np_row++;
                         slot = 0;
@@ -510,7 +513,7 @@ static void pack_layout(int P, int Hkv, int B, const int32_t *ctx_len, int64_t c
                         sc[j] = sc_codes[idx * ORC_NP + j];
                     }
                     write_token_codes(block, tau, P, slot, r16[idx], th, sc);
-                    value_write(value_pool, page, tau, P, slot, values + idx * ORC_D);   /* checked before */
+                    value_write(block, tau, P, slot, values + idx * ORC_D);   /* checked before */
                     slot++;
                     meta_write(page_meta, page, tau, slot, off16);
                 }
@@ -525,7 +528,7 @@ int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
              const int8_t *tiers, const float *keys, const uint16_t *values,
              int32_t max_pages_per_head, int64_t page_capacity, int64_t arena_capacity16,
              int32_t *page_table, int32_t *num_pages, int32_t *open_page,
-             uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc,
+             uint8_t *page_meta, uint8_t *arena, int64_t *alloc,
              int nthreads, int layout)
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
@@ -584,7 +587,7 @@ int orc_pack(int P, int Hkv, int B, const int32_t *ctx_len, int64_t ctx_stride,
     int status = E.worst;
     if (status == ORC_OK)
         pack_layout(P, Hkv, B, ctx_len, ctx_stride, tiers, E.r16, E.th, E.sc, values, max_pages_per_head,
-                    page_table, num_pages, open_page, page_meta, arena, value_pool, alloc);
+                    page_table, num_pages, open_page, page_meta, arena, alloc);
     free(tiers_used); free(E.r16); free(E.th); free(E.sc);
     return status;
 }
@@ -603,7 +606,7 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
                const int32_t *seq, const int32_t *head, const uint8_t *tier,
                const float *keys, const uint16_t *values,
                int32_t *page_table, int32_t *num_pages, int32_t *open_page,
-               uint8_t *page_meta, uint8_t *arena, uint16_t *value_pool, int64_t *alloc, int layout)
+               uint8_t *page_meta, uint8_t *arena, int64_t *alloc, int layout)
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
     for (int i = 0; i < n; i++) {
@@ -664,7 +667,6 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
             int64_t bb = orc_block_bytes(tau, P);
             alloc[1] += bb / 16;
             memset(arena + (int64_t)off16 * 16, 0, (size_t)bb);
-            for (int q = 0; q < P * ORC_D; q++) value_pool[page * P * ORC_D + q] = 0;
             page_table[row * max_pages_per_head + num_pages[row]] = (int32_t)page;
             num_pages[row]++;
             cnt = 0;
@@ -679,7 +681,7 @@ int orc_append(int P, int Hkv, int32_t num_seqs, int32_t max_pages_per_head,
             ORC_OK)
             return ORC_EUNDECIDABLE;
         write_token_codes(arena + (int64_t)off16 * 16, tau, P, cnt, r16, th, sc);
-        value_write(value_pool, page, tau, P, cnt, values + (int64_t)i * ORC_D);   /* checked above */
+        value_write(arena + (int64_t)off16 * 16, tau, P, cnt, values + (int64_t)i * ORC_D);   /* checked above */
         cnt++;
         meta_write(page_meta, page, tau, cnt, off16);
         if (cnt == P) *op = -1;
@@ -844,10 +846,10 @@ void orc_transcode(int tier_old, int tier_new, const uint16_t *th_old, const uin
  * destination is too small (nothing written to it). */
 int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_table,
                const int32_t *src_num_pages, const uint8_t *src_page_meta, const uint8_t *src_arena,
-               const uint16_t *src_value_pool, const float *util, const int64_t *budget, uint32_t tier_mask,
+               const float *util, const int64_t *budget, uint32_t tier_mask,
                int32_t dst_maxp, int64_t dst_page_capacity, int64_t dst_arena_capacity16,
                int32_t *page_table, int32_t *num_pages, int32_t *open_page, uint8_t *page_meta,
-               uint8_t *arena, uint16_t *value_pool, int64_t *alloc, int8_t *tier_v_out)
+               uint8_t *arena, int64_t *alloc, int8_t *tier_v_out)
 {
     if (P != 16 && P != 32) return ORC_EINVAL;
     if (tier_mask == 0) tier_mask = 7;
@@ -931,11 +933,11 @@ int orc_repack(int P, int Hkv, int B, int32_t src_maxp, const int32_t *src_page_
                     sc[idx * ORC_NP + j] = (uint8_t)s_n[j];
                 }
                 double v[ORC_D];   /* decoded values are fp16 numbers exactly */
-                value_read(src_value_pool, page, tier, P, slot, v);
+                value_read(src_arena + (int64_t)off16 * 16, tier, P, slot, v);
                 for (int dd = 0; dd < ORC_D; dd++) vals[idx * ORC_D + dd] = orc_f64_to_f16(v[dd]);
             }
         pack_layout(P, Hkv, B, ctx, S, tier_v, r16, th, sc, vals, dst_maxp, page_table, num_pages, open_page,
-                    page_meta, arena, value_pool, alloc);
+                    page_meta, arena, alloc);
         free(r16); free(th); free(sc); free(vals);
     }
     if (tier_v_out) memcpy(tier_v_out, tier_v, (size_t)n);
@@ -970,7 +972,6 @@ typedef struct {
     int32_t max_pages_per_head;
     const int32_t *page_table, *num_pages;
     const uint8_t *page_meta, *arena;
-    const uint16_t *value_pool;
     const float *q;
     double scale;
     double *out, *lse;
@@ -1029,7 +1030,7 @@ static void decode_row(decode_job_t *J, int64_t row_q, double *lut8, double *lut
         for (int slot = 0; slot < count; slot++, t++) {
             double w = exp(logit[t] - m) / sum;
             double v[ORC_D];
-            value_read(J->value_pool, page, tier, J->P, slot, v);
+            value_read(J->arena + (int64_t)off16 * 16, tier, J->P, slot, v);
             for (int d = 0; d < ORC_D; d++) o[d] += w * v[d];
         }
     }
@@ -1059,7 +1060,7 @@ static void *decode_worker(void *arg)
  * rows == NULL all B*Hq rows are computed.  out/lse are indexed by row. */
 int orc_decode(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
                const int32_t *page_table, const int32_t *num_pages,
-               const uint8_t *page_meta, const uint8_t *arena, const uint16_t *value_pool,
+               const uint8_t *page_meta, const uint8_t *arena,
                const float *q, double scale, double *out, double *lse, int nthreads, int layout)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || (P != 16 && P != 32)) return ORC_EINVAL;
@@ -1067,7 +1068,7 @@ int orc_decode(int P, int Hq, int Hkv, int B, int32_t max_pages_per_head,
     J.P = P; J.Hq = Hq; J.Hkv = Hkv; J.B = B;
     J.max_pages_per_head = max_pages_per_head;
     J.page_table = page_table; J.num_pages = num_pages;
-    J.page_meta = page_meta; J.arena = arena; J.value_pool = value_pool;
+    J.page_meta = page_meta; J.arena = arena;
     J.q = q; J.scale = scale; J.out = out; J.lse = lse;
     J.next_row = 0; J.n_rows = (int64_t)B * Hq;
     J.layout = layout;
@@ -1232,7 +1233,8 @@ int orc_encode_many(const float *keys, int64_t n, int tb, int sb, uint16_t *r16,
     return worst;
 }
 
-int64_t orc_value_index(int64_t page, int P, int slot, int d) { return value_index(page, P, slot, d); }
+int64_t orc_value_index(int slot, int d) { return value_index(slot, d); }
+int64_t orc_key_bytes(int tier, int P) { return key_bytes(tier, P); }
 
 void orc_read_token(const uint8_t *arena, const uint8_t *page_meta, int P, int64_t page, int slot,
                     uint16_t *r16, uint16_t *theta, uint16_t *s, int *tier_out)
@@ -1243,11 +1245,11 @@ void orc_read_token(const uint8_t *arena, const uint8_t *page_meta, int P, int64
     *tier_out = tier;
 }
 
-void orc_read_values(const uint16_t *value_pool, const uint8_t *page_meta, int P, int64_t page, int slot, double *v)
+void orc_read_values(const uint8_t *arena, const uint8_t *page_meta, int P, int64_t page, int slot, double *v)
 {
     int tier, count; uint32_t off16;
     meta_read(page_meta, page, &tier, &count, &off16);
-    value_read(value_pool, page, tier, P, slot, v);
+    value_read(arena + (int64_t)off16 * 16, tier, P, slot, v);
 }
 
 void orc_f64_to_f16_many(const double *x, int64_t n, uint16_t *out)

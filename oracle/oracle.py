@@ -70,18 +70,20 @@ def _declare(L):
     L.orc_bits_get.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
     L.orc_block_bytes.restype = i64
     L.orc_block_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.orc_key_bytes.restype = i64
+    L.orc_key_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
     L.orc_pack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp,
-                           i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int]
+                           i32, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int]
     L.orc_append.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i64, i64, ctypes.c_int,
-                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     L.orc_rdr_steps.argtypes = [u32, vp, vp, vp, vp]
     L.orc_rdr_assign.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, u32, vp, vp]
     L.orc_transcode.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
-    L.orc_repack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp, vp, u32,
-                             i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.orc_repack.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp, u32,
+                             i32, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     L.orc_lut.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int]
     L.orc_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
-                             vp, vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int, ctypes.c_int]
+                             vp, vp, vp, vp, vp, dbl, vp, vp, ctypes.c_int, ctypes.c_int]
     L.orc_decode_utility.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32,
                                      vp, vp, vp, vp, vp, dbl, vp, ctypes.c_int, ctypes.c_int]
     L.orc_identity_logits.argtypes = [vp, i64, vp, vp, ctypes.c_int]
@@ -92,7 +94,7 @@ def _declare(L):
     L.orc_v8_decode.argtypes = [vp, vp, vp]
     L.orc_read_values.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp]
     L.orc_value_index.restype = i64
-    L.orc_value_index.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.orc_value_index.argtypes = [ctypes.c_int, ctypes.c_int]
 
 
 def f64_to_f16(x):
@@ -138,7 +140,8 @@ def block_bytes(tier, P):
 class Cache:
     """Host copy of a paged ADA cache (the same buffers the library keeps on
     the device): page table, page counts, open pages, page metadata, code
-    arena, fp16 value pool and the two allocation counters.  pair_layout says
+    arena (each page's block: its key codes, then its values) and the two
+    allocation counters.  pair_layout says
     which key and query components form the 64 pairs."""
 
     def __init__(self, P, Hq, Hkv, num_seqs, max_pages_per_head, page_capacity, arena_capacity16,
@@ -155,7 +158,6 @@ class Cache:
         self.open_page = np.full((rows, NUM_TIERS), -1, np.int32)
         self.page_meta = np.zeros((page_capacity, 8), np.uint8)
         self.arena = np.zeros(arena_capacity16 * 16, np.uint8)
-        self.value_pool = np.zeros((page_capacity, P * D), np.uint16)
         self.alloc = np.zeros(2, np.int64)
 
     def copy(self):
@@ -180,7 +182,7 @@ def pack(cache, ctx_len, tiers, keys, values, nthreads=None):
     return lib().orc_pack(cache.P, cache.Hkv, B, _p(ctx_len), stride, _p(tiers), _p(keys), _p(values),
                           cache.max_pages_per_head, cache.page_capacity, cache.arena_capacity16,
                           _p(cache.page_table), _p(cache.num_pages), _p(cache.open_page),
-                          _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc),
+                          _p(cache.page_meta), _p(cache.arena), _p(cache.alloc),
                           nthreads, cache.pair_layout)
 
 
@@ -195,7 +197,7 @@ def append(cache, seq, head, tier, keys, values):
                             cache.page_capacity, cache.arena_capacity16, n,
                             _p(seq), _p(head), _p(tier), _p(keys), _p(values),
                             _p(cache.page_table), _p(cache.num_pages), _p(cache.open_page),
-                            _p(cache.page_meta), _p(cache.arena), _p(cache.value_pool), _p(cache.alloc),
+                            _p(cache.page_meta), _p(cache.arena), _p(cache.alloc),
                             cache.pair_layout)
 
 
@@ -240,10 +242,10 @@ def repack(src, B, util, budget, dst, tier_mask=0):
     budget = np.ascontiguousarray(budget, dtype=np.int64)
     tv = np.full((B, src.Hkv, src.max_pages_per_head * src.P), -1, np.int8)
     st = lib().orc_repack(src.P, src.Hkv, B, src.max_pages_per_head, _p(src.page_table), _p(src.num_pages),
-                          _p(src.page_meta), _p(src.arena), _p(src.value_pool), _p(util), _p(budget), tier_mask,
+                          _p(src.page_meta), _p(src.arena), _p(util), _p(budget), tier_mask,
                           dst.max_pages_per_head, dst.page_capacity, dst.arena_capacity16, _p(dst.page_table),
                           _p(dst.num_pages), _p(dst.open_page), _p(dst.page_meta), _p(dst.arena),
-                          _p(dst.value_pool), _p(dst.alloc), _p(tv))
+                          _p(dst.alloc), _p(tv))
     return st, tv
 
 
@@ -264,7 +266,7 @@ def decode(cache, q, scale, nthreads=None):
     nthreads = nthreads or max(1, len(os.sched_getaffinity(0)))
     st = lib().orc_decode(cache.P, cache.Hq, cache.Hkv, B, cache.max_pages_per_head,
                           _p(cache.page_table), _p(cache.num_pages), _p(cache.page_meta),
-                          _p(cache.arena), _p(cache.value_pool), _p(q), float(scale),
+                          _p(cache.arena), _p(q), float(scale),
                           _p(out), _p(lse), nthreads, cache.pair_layout)
     assert st == OK, st
     return out, lse
@@ -330,9 +332,22 @@ def v8_decode(scale_bytes, codes):
 def read_values(cache, page, slot):
     """decoded values (fp64 [128]) of a cached token, in its page's format"""
     out = np.zeros(D, np.float64)
-    lib().orc_read_values(_p(cache.value_pool), _p(cache.page_meta), cache.P, page, slot, _p(out))
+    lib().orc_read_values(_p(cache.arena), _p(cache.page_meta), cache.P, page, slot, _p(out))
     return out
 
 
-def value_index(page, P, slot, d):
-    return lib().orc_value_index(page, P, slot, d)
+def value_index(slot, d):
+    """u16 index of fp16 value (slot, d) inside an fp16 page's value part"""
+    return lib().orc_value_index(slot, d)
+
+
+def key_bytes(tier, P):
+    """bytes of a page's key part (radius and codes); its value part follows"""
+    return lib().orc_key_bytes(tier, P)
+
+
+def value_part(cache, page):
+    """the value part of a page's block, as bytes (a view into the arena)"""
+    tier, _, off16 = cache.meta(page)
+    start = off16 * 16 + key_bytes(tier, cache.P)
+    return cache.arena[start: off16 * 16 + block_bytes(tier, cache.P)]

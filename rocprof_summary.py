@@ -4,6 +4,7 @@ summaries kept under profiles/.
     python rocprof_summary.py stats --db KT.db --workload llama8b --cmd "..." [--out NAME.md]
     python rocprof_summary.py pmc --fetch-db F.db --write-db W.db --workload llama8b \
         --cmd-fetch "..." --cmd-write "..." [--bench-json B.json]
+    python rocprof_summary.py sq --db S1.db --cmd "..." [--db S2.db --cmd "..."] --workload llama8b
 
 `stats` summarises a `--kernel-trace --stats` run: every kernel's call count
 and duration, and the split-K decode kernel's per-dispatch spread.  `pmc`
@@ -11,20 +12,30 @@ turns the FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) into HBM bytes
 per split-K launch, calibrated by the same counters on the copy probe of the
 same run, which moves exactly 1 GiB each way per launch.  The record carries
 the hash of the decode kernel's sources, so bench.py ignores it once the
-kernel has changed.
+kernel has changed.  `sq` records the split-K kernel's SQ counters per
+dispatch (wave cycles, waits, VALU / LDS activity, LDS bank conflicts) and
+their ratios.  Every summary names the rocprofv3 command and this script's
+own invocation.
 """
 import argparse
 import collections
 import json
 import os
+import shlex
 import sqlite3
 import statistics
+import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE = "decode_partials_kernel"
 COPY = "probe_copy_kernel"
 COPY_BYTES = 1 << 30
+
+
+def invocation():
+    """This script's command line, as run from the repository root."""
+    return "python rocprof_summary.py " + shlex.join(sys.argv[1:])
 
 
 def short(name):
@@ -66,8 +77,9 @@ def pick(agg, key):
 def cmd_stats(a):
     agg = per_kernel_durations(a.db)
     total = sum(sum(v) for v in agg.values())
-    lines = [f"# rocprofv3 kernel trace: {a.workload}", "", "Command (from the repository root):", "",
-             "```", a.cmd, "```", "",
+    lines = [f"# rocprofv3 kernel trace: {a.workload}", "", "Commands (from the repository root): the profiled",
+             "run, then the summary of its database:", "",
+             "```", a.cmd, invocation(), "```", "",
              "| kernel | calls | total ms | avg us | % |", "|---|---:|---:|---:|---:|"]
     for name, d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{short(name)}` | {len(d)} | {sum(d) / 1e6:.3f} | {sum(d) / len(d) / 1e3:.2f} | "
@@ -111,6 +123,7 @@ def cmd_pmc(a):
         "hbm_bytes_per_launch": (fk * 1024 * f_scale) + (wk * 1024 * w_scale),
         "cmd_fetch": a.cmd_fetch,
         "cmd_write": a.cmd_write,
+        "summary_cmd": invocation(),
     }
     if a.bench_json:
         with open(a.bench_json) as f:
@@ -136,8 +149,9 @@ def cmd_traffic(a):
     f_scale, w_scale = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
     fetch = per_kernel_counter(a.fetch_db, "FETCH_SIZE")
     write = per_kernel_counter(a.write_db, "WRITE_SIZE")
-    lines = [f"# HBM traffic per dispatch: {a.title}", "", "Commands (from the repository root):", "",
-             "```", a.cmd_fetch, a.cmd_write, a.cmd_calib, "```", "",
+    lines = [f"# HBM traffic per dispatch: {a.title}", "", "Commands (from the repository root): the profiled",
+             "runs, then the summary of their databases:", "",
+             "```", a.cmd_fetch, a.cmd_write, a.cmd_calib, invocation(), "```", "",
              f"Counter scale from the copy probe of {COPY_BYTES / 2**30:.0f} GiB: FETCH_SIZE x {f_scale:.4f}, "
              f"WRITE_SIZE x {w_scale:.4f}.", "",
              "| kernel | dispatches | read MB | write MB |", "|---|---|---|---|"]
@@ -153,6 +167,50 @@ def cmd_traffic(a):
         f.write("\n".join(lines) + "\n")
     print(out)
     print("\n".join(lines))
+
+
+def counter_names(db):
+    con = sqlite3.connect(db)
+    return [r[0] for r in con.execute("select distinct counter_name from counters_collection").fetchall()]
+
+
+def cmd_sq(a):
+    """SQ counters of the split-K kernel, per dispatch, from one or more
+    passes (one database each), and the usual ratios."""
+    import bench
+    rec = {"workload": a.workload, "kernel_source_hash": bench.kernel_source_hash(), "per_dispatch": {}}
+    kn = None
+    for db in a.db:
+        for c in counter_names(db):
+            vals = per_kernel_counter(db, c)
+            kn = pick(vals, DECODE)[0]
+            rec["per_dispatch"][c] = statistics.mean(vals[kn])
+            rec["dispatches"] = len(vals[kn])
+    if kn is None:
+        raise SystemExit("no counters in the databases")
+    rec["kernel"] = short(kn)
+    d = rec["per_dispatch"]
+    cyc = d.get("SQ_WAVE_CYCLES")
+    if cyc:
+        for c, key in (("SQ_WAIT_ANY", "wait_any_over_wave_cycles"),
+                       ("SQ_ACTIVE_INST_VALU", "valu_active_over_wave_cycles"),
+                       ("SQ_ACTIVE_INST_LDS", "lds_active_over_wave_cycles")):
+            if c in d:
+                rec[key] = d[c] / cyc
+    if d.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in d:
+        rec["lds_bank_conflict_cycles_per_lds_inst"] = d["SQ_LDS_BANK_CONFLICT"] / d["SQ_INSTS_LDS"]
+    if d.get("SQ_WAVES"):
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_MFMA"):
+            if c in d:
+                rec[c.lower().replace("sq_insts_", "insts_") + "_per_wave"] = d[c] / d["SQ_WAVES"]
+    rec["cmds"] = a.cmd
+    rec["summary_cmd"] = invocation()
+    out = os.path.join(PROFILES, f"ada_decode_partials_{a.workload}_sq.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(out)
+    print(json.dumps(rec, indent=1))
 
 
 def main():
@@ -175,8 +233,12 @@ def main():
     p.add_argument("--cmd-fetch", required=True)
     p.add_argument("--cmd-write", required=True)
     p.add_argument("--bench-json")
+    q = sub.add_parser("sq")
+    q.add_argument("--db", required=True, action="append", help="one database per counter pass")
+    q.add_argument("--workload", required=True)
+    q.add_argument("--cmd", required=True, action="append", help="the profiled command of each pass")
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "pmc": cmd_pmc}[a.mode](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "pmc": cmd_pmc, "sq": cmd_sq}[a.mode](a)
 
 
 if __name__ == "__main__":

@@ -31,9 +31,10 @@ int main(void) {
     cache.arena_capacity16 = 1 << 24;
 
     /* sizes and strings */
-    CHECK(ada_block_bytes(ADA_TIER_T8, 16) == 2080);
-    CHECK(ada_block_bytes(ADA_TIER_T4, 16) == 1056);
-    CHECK(ada_block_bytes(ADA_TIER_T2, 32) == 1344);
+    CHECK(ada_block_bytes(ADA_TIER_T8, 16) == 16 * (130 + 256));
+    CHECK(ada_block_bytes(ADA_TIER_T4, 16) == 16 * (66 + 256));
+    CHECK(ada_block_bytes(ADA_TIER_T2, 32) == 32 * (42 + 256));
+    CHECK(ada_block_bytes(ADA_TIER_T2V8, 16) == 16 * (42 + 132));
     CHECK(ada_block_bytes(ADA_NUM_TIERS, 16) == -1);
     CHECK(ada_lut_floats(&cfg) == (size_t)64 * (256 + 16 + 4));
     CHECK(strncmp(ada_status_str(ADA_OK), "ADA_OK", 6) == 0);

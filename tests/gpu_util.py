@@ -68,7 +68,6 @@ def compare_caches(gc, oc, P):
     if not np.array_equal(a, b):
         bad = np.nonzero(a != b)[0]
         raise AssertionError(f"arena differs at {bad.size} bytes, first at {bad[:8]}")
-    assert np.array_equal(g["value_pool"][:npg], oc.value_pool[:npg])
 
 
 def check_outputs(out, lse, o_ref, lse_ref, tol=TOL):

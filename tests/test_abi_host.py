@@ -28,9 +28,11 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_block_bytes_and_lut_floats():
-    assert [ada.block_bytes(t, 16) for t in (0, 1, 2)] == [2080, 1056, 672]
-    assert ada.block_bytes(1, 32) == 2112
-    assert [ada.block_bytes(t, 16) for t in (3, 4, 5)] == [2080, 1056, 672]   # V8 tiers: the same keys
+    # a page's block: key part (2 + 8 tb + 8 sb bytes per token), then values
+    # (256 bytes per token for fp16, 132 for V8)
+    assert [ada.block_bytes(t, 16) for t in (0, 1, 2)] == [16 * (130 + 256), 16 * (66 + 256), 16 * (42 + 256)]
+    assert ada.block_bytes(1, 32) == 32 * (66 + 256)
+    assert [ada.block_bytes(t, 16) for t in (3, 4, 5)] == [16 * (130 + 132), 16 * (66 + 132), 16 * (42 + 132)]
     assert ada.block_bytes(6, 16) == -1 and ada.block_bytes(0, 8) == -1
     assert ada.lut_floats(ada.make_config(16, 32, 8)) == 64 * (256 + 16 + 4)
 
@@ -61,7 +63,7 @@ def _size(fn, *args):
 def test_host_validation_without_gpu():
     L = ada.lib()
     good = ada.make_config(16, 32, 8)
-    desc = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
+    desc = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0)
     st, n = _size(L.ada_decode_workspace, ctypes.byref(good), ctypes.byref(desc), 2)
     assert st == ada.OK and n > 0
     bad = [(ada.make_config(16, 32, 8), None),
@@ -78,7 +80,7 @@ def test_host_validation_without_gpu():
     for cfg, want in bad[1:]:
         assert _size(L.ada_decode_workspace, ctypes.byref(cfg), ctypes.byref(desc), 2)[0] == want
     # decode refuses a cache with null buffers before touching the device
-    null_cache = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
+    null_cache = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0)
     assert L.ada_decode(ctypes.byref(good), ctypes.byref(null_cache), None, 2, 1.0, None, None, None, 0, None) \
         == ada.EINVAL
     # multi-query: Q must be a power of two with Q * (Hq / Hkv) <= 64
@@ -107,20 +109,20 @@ def test_shape_limits_and_workspace_ceiling():
     cfg = ada.make_config(16, 32, 8)
     c = ctypes.byref(cfg)
     I32 = 2 ** 31 - 1
-    big = ada.CacheDesc(64, 4096, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+    big = ada.CacheDesc(64, 4096, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0)
     assert _size(L.ada_decode_workspace, c, ctypes.byref(big), 64)[0] == ada.OK
     # B * Hq past int32
     assert _size(L.ada_decode_workspace, c, ctypes.byref(big), I32 // 32 + 1)[0] == ada.EUNSUPPORTED
     assert _size(L.ada_decode_workspace, c, ctypes.byref(big), I32 // 32)[0] == ada.OK
     # max_pages_per_head * P past int32
-    wide = ada.CacheDesc(1, I32 // 16 + 1, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+    wide = ada.CacheDesc(1, I32 // 16 + 1, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0)
     assert _size(L.ada_decode_workspace, c, ctypes.byref(wide), 1)[0] == ada.EUNSUPPORTED
     assert _size(L.ada_dense_workspace, c, 1, I32 // 16 + 1)[0] == ada.EUNSUPPORTED
     # the utility logit buffer: page_capacity * P * G within uint32
     G = 4
     cap_ok = (2 ** 32 - 1) // (16 * G)
     for cap, want in ((cap_ok, ada.OK), (cap_ok + 1, ada.EUNSUPPORTED)):
-        d = ada.CacheDesc(2, 64, cap, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+        d = ada.CacheDesc(2, 64, cap, 1 << 30, 0, 0, 0, 0, 0, 0, 0)
         assert _size(L.ada_decode_utility_workspace, c, ctypes.byref(d), 2)[0] == want
     # a pack workspace that would pass 2^48 bytes
     assert _size(L.ada_pack_workspace, c, ctypes.byref(big), 64, 2 ** 40)[0] == ada.EUNSUPPORTED
@@ -146,7 +148,7 @@ def test_workspace_sizes_cover_what_the_kernels_write():
         if Q * G > 64:
             return
         cfg = ada.make_config(P, G * Hkv, Hkv, decode_chunk_pages=chunk)
-        desc = ada.CacheDesc(B, maxp, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0, 0)
+        desc = ada.CacheDesc(B, maxp, 1 << 20, 1 << 30, 0, 0, 0, 0, 0, 0, 0)
         s1, n1 = _size(L.ada_decode_multi_workspace, ctypes.byref(cfg), ctypes.byref(desc), B, Q)
         assert s1 == ada.OK
         tpg = 64 // P

@@ -64,7 +64,7 @@ ok = 0
 for cfg in configs:
     c = ctypes.byref(cfg)
     for seqs, maxp, cap, arena in shapes:
-        d = ada.CacheDesc(seqs, maxp, cap, arena, 0, 0, 0, 0, 0, 0, 0, 0)
+        d = ada.CacheDesc(seqs, maxp, cap, arena, 0, 0, 0, 0, 0, 0, 0)
         dp = ctypes.byref(d)
         for B in (0, 1, 3, 64, 4096, I32, -1):
             ok += ws(L.ada_decode_workspace, c, dp, B) == ada.OK
@@ -90,7 +90,7 @@ for v in (float("nan"), float("inf"), -float("inf"), 1e308, -1e308, 5e-324, -0.0
     L.ada_host_f64_to_f16(v)
 # compute entry points refuse null buffers on the host
 good = ada.make_config(16, 32, 8)
-null = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0, 0)
+null = ada.CacheDesc(2, 64, 1000, 100000, 0, 0, 0, 0, 0, 0, 0)
 g, n0 = ctypes.byref(good), ctypes.byref(null)
 assert L.ada_cache_init(g, n0, None) == ada.EINVAL
 assert L.ada_decode(g, n0, None, 2, 1.0, None, None, None, 0, None) == ada.EINVAL

@@ -104,7 +104,7 @@ def test_decode_append_into_empty_rows():
 
 def test_decode_append_errors_write_nothing():
     w = W.config("tiny", ctx=64)
-    gc = gpu_cache(w, dims_override=(4, 4, 4 * 66))   # exactly the 4 full T4 pages of the context
+    gc = gpu_cache(w, dims_override=(4, 4, 4 * (66 + 256)))   # exactly the 4 full T4 pages of the context
     ada.pack(gc, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), torch.from_numpy(w["keys"]).cuda(),
              torch.from_numpy(w["values"].view(np.int16)).cuda())
     assert ada.read_status(gc.status) == ada.OK

@@ -74,7 +74,7 @@ def test_checkpoint_round_trip():
     src, dev = gpu_pack(w)
     saved = {k: t.cpu().clone() for k, t in (("page_table", src.page_table), ("num_pages", src.num_pages),
                                               ("open_page", src.open_page), ("page_meta", src.page_meta),
-                                              ("code_arena", src.code_arena), ("value_pool", src.value_pool),
+                                              ("code_arena", src.code_arena),
                                               ("alloc", src.alloc), ("status", src.status))}
     dst = ada.Cache(src.cfg, src.desc.num_seqs, src.desc.max_pages_per_head, src.desc.page_capacity,
                     src.desc.arena_capacity16)

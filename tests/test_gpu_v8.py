@@ -237,6 +237,16 @@ def test_fullsize_llama8b_all_v8():
     dev = to_dev(w)
     gc, oc = _pack_both(w, dev)
     compare_caches(gc, oc, w["P"])
+    # footprint: a V8 page's block is its key part plus 132 value bytes per
+    # slot, so the arena holds exactly that for every page
+    P = w["P"]
+    n_pages = int(gc.alloc[0].item())
+    tiers = gc.page_meta[:n_pages, 0].cpu().numpy()
+    assert (tiers >= 3).all()
+    key_bytes = {3: 130, 4: 66, 5: 42}
+    assert int(gc.alloc[1].item()) * 16 == sum(P * (key_bytes[int(t)] + 132) for t in tiers)
+    kept = int((w["tiers"] >= 0).sum())
+    log(f"  arena bytes per kept token-head {int(gc.alloc[1].item()) * 16 / kept:.1f}")
     log("  decode")
     out, lse = ada.decode(gc, dev["q"], w["scale"])
     o_ref, l_ref = O.decode(oc, w["q"], w["scale"])

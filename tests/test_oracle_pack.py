@@ -16,7 +16,7 @@ from oracle import oracle as O
 from tests.util import kept_tokens, upper_capacity
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-BLOCK16_MAX = {16: 130, 32: 260}
+BLOCK16_MAX = {16: 386, 32: 772}   # T8 key part + fp16 values, in 16-byte units
 
 
 def _cache_for(w, per_row=None, pages=None, units=None):
@@ -25,9 +25,14 @@ def _cache_for(w, per_row=None, pages=None, units=None):
 
 
 def test_block_sizes_closed_form():
-    # radius 2 B + angle 8*tb B + magnitude 8*sb B per token
-    assert [O.block_bytes(t, 16) for t in (0, 1, 2)] == [2080, 1056, 672]
-    assert [O.block_bytes(t, 32) for t in (0, 1, 2)] == [4160, 2112, 1344]
+    # key part: radius 2 B + angle 8*tb B + magnitude 8*sb B per token;
+    # value part: 256 B (fp16) or 132 B (V8) per token
+    assert [O.key_bytes(t, 16) for t in (0, 1, 2)] == [2080, 1056, 672]
+    assert [O.key_bytes(t, 32) for t in (0, 1, 2)] == [4160, 2112, 1344]
+    assert [O.block_bytes(t, 16) for t in (0, 1, 2)] == [2080 + 4096, 1056 + 4096, 672 + 4096]
+    assert [O.block_bytes(t, 32) for t in (0, 1, 2)] == [4160 + 8192, 2112 + 8192, 1344 + 8192]
+    assert [O.block_bytes(t, 16) for t in (3, 4, 5)] == [2080 + 2112, 1056 + 2112, 672 + 2112]
+    assert [O.key_bytes(t, 16) for t in (3, 4, 5)] == [2080, 1056, 672]
 
 
 def test_hand_derived_t2_page():
@@ -100,7 +105,7 @@ def test_pack_structure(name, ctx, batch):
                     assert bt == O.bits_put(th[0], tb).tobytes()
                     assert bs == O.bits_put(s[0], sb).tobytes()
                     # values: element (slot, d) at (slot/8)*1024 + d*8 + slot%8
-                    vp = c.value_pool[page].reshape(P // 8, 128, 8)
+                    vp = O.value_part(c, page).view(np.uint16).reshape(P // 8, 128, 8)
                     assert np.array_equal(vp[slot // 8, :, slot % 8], w["values"][b, h, pos])
                     seen += 1
             assert i == len(toks)                               # each kept token exactly once
@@ -128,7 +133,7 @@ def test_pack_equals_sequential_append():
     n = len(seq)
     for a, z in [(0, n // 3), (n // 3, n // 2), (n // 2, n)]:
         assert O.append(c2, seq[a:z], head[a:z], tier[a:z], np.array(ks[a:z]), np.array(vs[a:z])) == O.OK
-    for name in ("page_table", "num_pages", "open_page", "page_meta", "arena", "value_pool", "alloc"):
+    for name in ("page_table", "num_pages", "open_page", "page_meta", "arena", "alloc"):
         assert np.array_equal(getattr(c1, name), getattr(c2, name)), name
 
 
@@ -153,12 +158,12 @@ def test_append_interleaved_tiers_and_open_pages():
 
 def test_capacity_errors_write_nothing():
     w = W.config("llama8b", ctx=256, batch=1)
-    a, b, u = upper_capacity(w, 130)
+    a, b, u = upper_capacity(w, 386)
     for kw in [dict(pages=5), dict(units=100), dict(per_row=3)]:
         c = _cache_for(w, **kw)
         before = c.copy()
         assert O.pack(c, w["ctx_len"], w["tiers"], w["keys"], w["values"]) == O.ENOSPC
-        for name in ("page_table", "num_pages", "open_page", "page_meta", "arena", "value_pool", "alloc"):
+        for name in ("page_table", "num_pages", "open_page", "page_meta", "arena", "alloc"):
             assert np.array_equal(getattr(c, name), getattr(before, name))
     c = _cache_for(w, pages=2)
     before = c.copy()

@@ -71,7 +71,7 @@ def test_identity_logits_equal_dot_product():
 
 def test_decode_equals_dense_over_half_split_keys():
     w = W.config("ragged", ctx=300, batch=3)
-    per_row, pages, units = upper_capacity(w, 130 * w["P"] // 16)
+    per_row, pages, units = upper_capacity(w, 386 * w["P"] // 16)
     c = O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units, pair_layout=HALF)
     assert O.pack(c, w["ctx_len"], w["tiers"], w["keys"], w["values"]) == O.OK
     out, lse = O.decode(c, w["q"], w["scale"])

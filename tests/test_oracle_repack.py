@@ -99,7 +99,7 @@ def test_capped_rdr_without_binding_caps_is_rdr():
 
 
 def _packed(w):
-    per_row, pages, units = upper_capacity(w, 130 * w["P"] // 16)
+    per_row, pages, units = upper_capacity(w, 386 * w["P"] // 16)
     src = O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units)
     assert O.pack(src, w["ctx_len"], w["tiers"], w["keys"], w["values"]) == O.OK
     dst = O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units)
@@ -112,7 +112,7 @@ def test_repack_unlimited_budget_reproduces_pack():
     util = np.exp(np.random.default_rng(1).standard_normal((src.page_capacity, w["P"]))).astype(np.float32)
     st, tv = O.repack(src, w["B"], util, np.full(w["B"], 1 << 40), dst)
     assert st == O.OK
-    for k in ("page_table", "num_pages", "open_page", "page_meta", "arena", "value_pool", "alloc"):
+    for k in ("page_table", "num_pages", "open_page", "page_meta", "arena", "alloc"):
         assert np.array_equal(getattr(src, k), getattr(dst, k)), k
 
 
@@ -144,7 +144,7 @@ def test_repack_budget_downgrade_and_decode():
                     tb, sb = O.TIER_BITS[tau]
                     keys.append(dequantize(r16, th_n[0], s_n[0], tb, sb))
                     sl = int(t % P)
-                    vals.append(src.value_pool[page][(sl // 8) * 1024 + np.arange(128) * 8 + sl % 8]
+                    vals.append(O.value_part(src, page).view(np.uint16)[(sl // 8) * 1024 + np.arange(128) * 8 + sl % 8]
                                 .view(np.float16).astype(np.float64))
             keys, vals = np.array(keys).reshape(-1, 128), np.array(vals).reshape(-1, 128)
             for g in range(G):

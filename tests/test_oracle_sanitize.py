@@ -28,7 +28,7 @@ from oracle import oracle as O
 from tests.util import upper_capacity
 
 def cache(w, layout=0):
-    per_row, pages, units = upper_capacity(w, 130 * w["P"] // 16, extra_pages_per_row=12)
+    per_row, pages, units = upper_capacity(w, 386 * w["P"] // 16, extra_pages_per_row=12)
     return O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units, pair_layout=layout)
 
 rng = np.random.default_rng(0)

@@ -104,7 +104,7 @@ def _v8_workload(name, ctx, batch):
 
 
 def _pack(w):
-    per_row, pages, units = upper_capacity(w, 130 * w["P"] // 16)
+    per_row, pages, units = upper_capacity(w, 386 * w["P"] // 16)
     c = O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units)
     assert O.pack(c, w["ctx_len"], w["tiers"], w["keys"], w["values"]) == O.OK
     return c
@@ -119,22 +119,25 @@ def test_v8_page_bytes_follow_the_layout():
         for i in range(c.num_pages[row]):
             page = c.page_table[row, i]
             tier, count, _ = c.meta(page)
-            raw = c.value_pool[page].view(np.uint8)
+            raw = O.value_part(c, page)
+            assert raw.size == (256 if O.VALUE_BITS[tier] == 16 else 132) * P   # value bytes per token
             for slot in range(count):
                 pos, tau = next(toks)
                 assert tau == tier
                 if O.VALUE_BITS[tier] == 16:
                     continue
                 st, sb, codes = O.v8_encode(w["values"][0, row, pos])
-                g, r = slot // 8, slot % 8
-                assert [raw[g * 1056 + r * 4 + k] for k in range(4)] == list(sb)
-                assert np.array_equal(raw[g * 1056 + 32 + np.arange(128) * 8 + r].astype(np.int16) - 128, codes)
+                # 16-token groups of 2112 bytes: [16 tokens][4] scale bytes,
+                # then [128 dims][16 tokens] code bytes
+                g, r = slot // 16, slot % 16
+                assert [raw[g * 2112 + r * 4 + k] for k in range(4)] == list(sb)
+                assert np.array_equal(raw[g * 2112 + 64 + np.arange(128) * 16 + r].astype(np.int16) - 128, codes)
             if O.VALUE_BITS[tier] == 8:   # bytes of empty slots and past the V8 layout stay zero
                 used = np.zeros(raw.size, bool)
                 for slot in range(count):
-                    g, r = slot // 8, slot % 8
-                    used[g * 1056 + r * 4 + np.arange(4)] = True
-                    used[g * 1056 + 32 + np.arange(128) * 8 + r] = True
+                    g, r = slot // 16, slot % 16
+                    used[g * 2112 + r * 4 + np.arange(4)] = True
+                    used[g * 2112 + 64 + np.arange(128) * 16 + r] = True
                 assert not raw[~used].any()
 
 
@@ -200,7 +203,7 @@ def test_rdr_v8_chain_brute_force(seed):
 def test_repack_into_v8_chain():
     w = W.config("llama8b", ctx=256, batch=2)
     src = _pack(w)
-    per_row, pages, units = upper_capacity(w, 130 * w["P"] // 16)
+    per_row, pages, units = upper_capacity(w, 386 * w["P"] // 16)
     dst = O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units)
     util = np.exp(np.random.default_rng(5).standard_normal((src.page_capacity, w["P"]))).astype(np.float32)
     cur = [sum(O.tier_rate(int(x)) for x in w["tiers"][b].ravel() if x >= 0) for b in range(w["B"])]
@@ -243,5 +246,5 @@ def test_repack_into_v8_chain():
     dst2 = O.Cache(w["P"], w["Hq"], w["Hkv"], w["B"], per_row, pages, units)
     st, _ = O.repack(dst, w["B"], util, [1 << 40] * w["B"], dst2, tier_mask=0b111000)
     assert st == O.OK
-    for k in ("page_table", "num_pages", "open_page", "page_meta", "arena", "value_pool", "alloc"):
+    for k in ("page_table", "num_pages", "open_page", "page_meta", "arena", "alloc"):
         assert np.array_equal(getattr(dst, k), getattr(dst2, k)), k

@@ -39,7 +39,7 @@ def test_noalloc_decode_twice_second_smaller():
 
 def test_noalloc_refuses_partials_past_the_array():
     cfg = ada.make_config(16, 32, 8, decode_chunk_pages=4)
-    cache = ada.Cache(cfg, 8, 16384, 64, 64 * 130)   # 8 x 32 query heads x 4096 chunks of partials
+    cache = ada.Cache(cfg, 8, 16384, 64, 64 * 386)   # 8 x 32 query heads x 4096 chunks of partials
     ada.cache_init(cache)
     q = torch.zeros((8, 32, 128), dtype=torch.float32, device="cuda")
     with pytest.raises(ada.AdaError) as e:
