@@ -13,14 +13,25 @@
 namespace ada {
 namespace {
 
+using core::floatx4_t;
+using core::half8_t;
 using core::ldg;
 
-template <int G, int P>
+// Logits at eight heads on the matrix cores: for each 16-token tile of the group, the
+// 16 x 128 fp16 keys times the 128 x 16 queries (columns = heads, G used),
+// in four K steps of 32 dimensions.  The queries (times scale * log2 e) go
+// in as fp16 hi + lo, so the products carry about 22 bits of the fp32
+// query; the keys are fp16 numbers exactly; the sums are fp32.
+template <int G, int P, int NW>
 struct DensePolicy {
     static constexpr bool kStaged = false;
     static constexpr bool kValueTiers = false;   // fp16 values only
     struct Smem {
-        float qd[kD * G];   // [d][g], pre-multiplied by scale * log2(e)
+        float qd[kD * G];              // [d][g], pre-multiplied by scale * log2(e)
+        // eight heads: MFMA B operands [hi|lo][K step][lane], and each
+        // wavefront's logits [head][token]
+        half8_t qb[G >= 8 ? 2 : 1][4][G >= 8 ? 64 : 1];
+        float lg[NW][G][G >= 8 ? 64 : 1];
     };
     const int32_t *ctx_len;
     const uint16_t *k_pool, *v_pool;
@@ -40,16 +51,40 @@ struct DensePolicy {
         const float *qrow = q + ((size_t)b * Hq + (size_t)h * G) * kD;
         for (int i = tid; i < G * kD; i += nt) s.qd[(i & 127) * G + (i >> 7)] = qrow[i] * mul;
     }
-    __device__ void build(Smem &, int, int) const {}
+    // B operand of K step ks for lane l: head l % 16 (zero past G),
+    // dimensions 32 ks + 8 (l / 16) .. + 7
+    __device__ void build(Smem &s, int tid, int nt) const {
+        if constexpr (G < 8) return;
+        for (int i = tid; i < 4 * 64; i += nt) {
+            const int ks = i >> 6, l = i & 63, n = l & 15, d0 = 32 * ks + 8 * (l >> 4);
+            half8_t hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = n < G ? s.qd[(d0 + e) * G + (n < G ? n : 0)] : 0.f;
+                const _Float16 vh = (_Float16)v;
+                hi[e] = vh;
+                lo[e] = (_Float16)(v - (float)vh);
+            }
+            s.qb[0][ks][l] = hi;
+            s.qb[1][ks][l] = lo;
+        }
+    }
     __device__ bool after_pages(Smem &, const int *, int, int, int, int) const { return false; }
-    // keys are read inside the logit loop: fetch only records the address
+    // the lane's token's key base; the loads are issued inside the logits
     struct Codes {
         const uint16_t *kp;
     };
     __device__ Codes fetch(int page, uint2, int slot, bool) const {
         return Codes{k_pool + (size_t)page * P * kD + slot * 8};
     }
+    // called by every lane of the wavefront (lane = token of the group).
+    // Eight heads: the matrix cores; fewer: fp32 FMAs per lane, which
+    // measure faster there (the 16 MFMA columns are mostly empty)
     __device__ void logits(const Smem &s, const Codes &c, uint2, bool valid, float (&lg)[G]) const {
+        if constexpr (G >= 8) logits_mfma(s, c, valid, lg);
+        else logits_fma(s, c, valid, lg);
+    }
+    __device__ void logits_fma(const Smem &s, const Codes &c, bool valid, float (&lg)[G]) const {
         if (!valid) return;
         float acc[G];
 #pragma unroll
@@ -71,11 +106,46 @@ struct DensePolicy {
 #pragma unroll
         for (int g = 0; g < G; ++g) lg[g] = acc[g];
     }
+    __device__ void logits_mfma(const Smem &s, const Codes &c, bool valid, float (&lg)[G]) const {
+        const int lane = threadIdx.x & 63;
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        float *buf = const_cast<float *>(&s.lg[w][0][0]);
+        const uintptr_t kp = reinterpret_cast<uintptr_t>(c.kp);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            // token 16 mt + l % 16 of the group: its key base, from the lane holding it
+            const int src = 16 * mt + (lane & 15);
+            const uint32_t lo32 = (uint32_t)__shfl((int)(uint32_t)kp, src, 64);
+            const uint32_t hi32 = (uint32_t)__shfl((int)(uint32_t)(kp >> 32), src, 64);
+            const uint16_t *tk = reinterpret_cast<const uint16_t *>(((uintptr_t)hi32 << 32) | lo32);
+            uint4 a[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) a[ks] = ldg<uint4>(tk + (4 * ks + (lane >> 4)) * P * 8);
+            floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const half8_t av = __builtin_bit_cast(half8_t, a[ks]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, s.qb[0][ks][lane], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, s.qb[1][ks][lane], acc, 0, 0, 0);
+            }
+            // C: row = token 16 mt + 4 (l / 16) + i, column = head l % 16
+            if ((lane & 15) < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) buf[(lane & 15) * 64 + 16 * mt + 4 * (lane >> 4) + i] = acc[i];
+            }
+        }
+        core::wave_lds_sync();
+        if (valid) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) lg[g] = buf[g * 64 + lane];
+        }
+        core::wave_lds_sync();   // read before the next group's logits overwrite it
+    }
 };
 
 template <int G, int P, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void dense_partials_kernel(DenseLaunch a) {
-    using Pol = DensePolicy<G, P>;
+    using Pol = DensePolicy<G, P, NW>;
     constexpr size_t RED = (size_t)NW * G * 130 * sizeof(float);
     constexpr size_t RAW = sizeof(typename Pol::Smem) > RED ? sizeof(typename Pol::Smem) : RED;
     __shared__ __align__(16) unsigned char raw[RAW];

@@ -73,9 +73,14 @@ def test_fullsize_rdr_pack_decode():
     check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
 
 
-@pytest.mark.parametrize("ctx", [1000, 262144])
-def test_dense_reference_parity(ctx):
-    w = W.config("long256k", ctx=ctx)
+@pytest.mark.parametrize("name,ctx,batch", [("long256k", 1000, 1), ("long256k", 262144, 1), ("llama8b", 1500, 2),
+                                            ("ragged", 900, 3), ("tiny", 700, 2)])
+def test_dense_reference_parity(name, ctx, batch):
+    """The dense fp16 reference decode (eight heads per KV head: logits on
+    the matrix cores; fewer: fp32 FMAs) against fp64 softmax attention over
+    the same fp16 keys and values, every query head of every sequence."""
+    w = W.config(name, ctx=ctx, batch=batch)
+    log(f"dense reference {name} ctx {ctx} batch {batch}")
     k16 = w["keys"].astype(np.float16).view(np.uint16)
     kp, vp, pt = dense_pages(k16, w["values"], w["P"])
     cfg = ada.make_config(w["P"], w["Hq"], w["Hkv"])
@@ -85,13 +90,16 @@ def test_dense_reference_parity(ctx):
                                 torch.from_numpy(w["q"]).cuda(), w["scale"])
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     G = w["Hq"] // w["Hkv"]
-    rows = range(w["Hq"]) if ctx < 10000 else range(0, w["Hq"], 9)
-    for hq in rows:
-        h = hq // G
-        o_ref, l_ref = dense_attention(k16[0, h].view(np.float16), w["values"][0, h].view(np.float16),
-                                       w["q"][0, hq], w["scale"])
-        err = np.max(np.abs(out[0, hq] - o_ref)) / np.max(np.abs(o_ref))
-        assert err <= 2e-3 and abs(lse[0, hq] - l_ref) <= 2e-3, (hq, err)
+    for b in range(w["B"]):
+        n = int(w["ctx_len"][b])
+        for h in range(w["Hkv"]):   # the KV head's keys and values converted once
+            kf = k16[b, h, :n].view(np.float16).astype(np.float64)
+            vf = w["values"][b, h, :n].view(np.float16).astype(np.float64)
+            for hq in range(h * G, (h + 1) * G):
+                o_ref, l_ref = dense_attention(kf, vf, w["q"][b, hq], w["scale"])
+                err = np.max(np.abs(out[b, hq] - o_ref)) / np.max(np.abs(o_ref))
+                assert err <= 2e-3 and abs(lse[b, hq] - l_ref) <= 2e-3, (b, hq, err)
+            del kf, vf
 
 
 RATE = {-1: 0, 0: 386, 1: 322, 2: 298}
