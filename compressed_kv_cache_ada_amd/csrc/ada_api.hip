@@ -240,7 +240,8 @@ AppendLaunch make_append(const ada_config_t *cfg, const ada_cache_t *cache, int3
 
 struct PackWs {
     int32_t *tile_counts, *row_counts, *row_base, *dest_page, *dest_slot, *range, *ctx;
-    int64_t *row_unit;
+    int64_t *row_unit, *item_of_slot;
+    int64_t item_slot_pages;
     int n_tiles;
     size_t bytes;
 };
@@ -259,6 +260,11 @@ PackWs pack_layout(const ada_config_t *cfg, int32_t B, int64_t stride, void *ws)
     w.dest_slot = c.take<int32_t>(smul(rows, (size_t)stride));
     w.range = c.take<int32_t>(2);
     w.ctx = c.take<int32_t>(B);
+    // new pages of a pack: at most ceil(stride / P) per row, plus one
+    // partial page per tier
+    const size_t pages = smul(rows, (size_t)(stride / cfg->page_size + 1 + kNumTiers));
+    w.item_slot_pages = (int64_t)std::min<size_t>(pages, INT64_MAX);
+    w.item_of_slot = c.take<int64_t>(smul(pages, (size_t)cfg->page_size));
     w.bytes = c.off;
     return w;
 }
@@ -738,6 +744,8 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_maxp = 0;
     a.src_of_slot = nullptr;
     a.src_of_slot_pages = 0;
+    a.item_of_slot = w.item_of_slot;
+    a.item_slot_pages = w.item_slot_pages;
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return hip_status(launch_pack(a, s));
@@ -890,6 +898,8 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_maxp = src->max_pages_per_head;
     a.src_of_slot = r.src_of_slot;
     a.src_of_slot_pages = r.src_of_slot_pages;
+    a.item_of_slot = nullptr;
+    a.item_slot_pages = 0;
     a.half_pairs = 0;   // codes are transcoded, no key is read
     a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return hip_status(launch_pack(a, s));

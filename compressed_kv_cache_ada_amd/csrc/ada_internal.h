@@ -179,6 +179,10 @@ struct PackLaunch {
     int32_t src_maxp;
     int4 *src_of_slot;              // [src_of_slot_pages][P] source {page, slot, tier, code_off16} per new slot
     int64_t src_of_slot_pages;
+    // pack from keys: the item (row * stride + position) of every new slot,
+    // [item_slot_pages][P], for the page writer
+    int64_t *item_of_slot;
+    int64_t item_slot_pages;
     int32_t half_pairs;             // key pair layout (see EncodeLaunch)
     int32_t n_tiers;                // tier ids below this are accepted (3, or 6 with value tiers)
 };

@@ -305,6 +305,45 @@ __global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, co
     }
 }
 
+// ------------------------------------------------------- pack page writer
+// One work-group (four wavefronts) per new page of a pack, in turn: the
+// page's tokens are encoded one per wavefront into a copy of the page's
+// block in LDS (empty slots stay zero), which is then written out whole in
+// 16-byte stores.  Every byte of the block is written once, by full 16-byte
+// units (the token-by-token writer leaves 1- to 4-byte pieces of each unit
+// to be merged in the caches, and zeroes the page beforehand).
+template <int P>
+__global__ __launch_bounds__(256, 3) void pack_write_pages_kernel(PackLaunch a) {
+    constexpr int kMaxBlock16 = block16(0, P);   // T8 with fp16 values: the largest block
+    __shared__ uint4 blk[kMaxBlock16];
+    __shared__ uint32_t words[4][2][16];
+    __shared__ int s_stop;
+    const int tid = threadIdx.x, wv = tid >> 6;
+    if (tid == 0) s_stop = read_status(a.status);
+    __syncthreads();
+    if (s_stop != 0) return;
+    const int first = a.n_new[0];
+    const int64_t n = min((int64_t)a.n_new[1], a.item_slot_pages);
+    for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
+        const uint2 meta = *reinterpret_cast<const uint2 *>(a.page_meta + first + i);
+        const int tier = meta.x & 0xFF, count = (meta.x >> 8) & 0xFF;
+        const int nb = block16(tier, P);
+        for (int k = tid; k < nb; k += 256) blk[k] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+        // the LDS copy stands in for the arena: block at offset 0
+        const uint2 lmeta = make_uint2(meta.x, 0u);
+        for (int slot = wv; slot < count; slot += 4) {
+            const int64_t item = a.item_of_slot[i * P + slot];
+            enc::encode_write_one(a.keys + item * kD, a.values + item * kD, slot, lmeta,
+                                  reinterpret_cast<uint8_t *>(blk), P, a.status, words[wv], a.half_pairs != 0);
+        }
+        __syncthreads();
+        uint4 *dst = reinterpret_cast<uint4 *>(a.arena + (size_t)meta.y * 16);
+        for (int k = tid; k < nb; k += 256) dst[k] = blk[k];
+        __syncthreads();   // the LDS copy is refilled for the next page
+    }
+}
+
 // ------------------------------------------------------------- pack
 constexpr int kTile = 1024;
 
@@ -510,6 +549,10 @@ __global__ __launch_bounds__(256) void pack_dest_kernel(PackLaunch a) {
         }
         a.dest_page[rbase + t] = dp;
         a.dest_slot[rbase + t] = ds;
+        if (a.item_of_slot && dp >= 0) {   // pack: the item of the destination slot, for the page writer
+            const int64_t j = (int64_t)(dp - a.n_new[0]) * a.P + ds;
+            if (j < a.item_slot_pages * a.P) a.item_of_slot[j] = rbase + t;
+        }
         if (a.src_of_slot && dp >= 0) {   // re-pack: where the destination slot's token comes from
             const int64_t j = (int64_t)(dp - a.n_new[0]) * a.P + ds;
             if (j < a.src_of_slot_pages * a.P) {
@@ -1030,21 +1073,15 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
         else hipLaunchKernelGGL(transcode_pages_kernel<32>, grid, dim3(128), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(zero_pages_kernel, dim3(grid_for(max_pages, 1, 4096)), dim3(256), 0, s,
-                       (const int32_t *)nullptr, (const int32_t *)a.n_new, (const ada_page_meta_t *)a.page_meta,
-                       a.arena, a.P, (const int32_t *)a.status);
-    EncodeLaunch e;
-    e.keys = a.keys;
-    e.values = a.values;
-    e.n = (int64_t)rows * a.stride;
-    e.dest_page = a.dest_page;
-    e.dest_slot = a.dest_slot;
-    e.page_meta = a.page_meta;
-    e.arena = a.arena;
-    e.P = a.P;
-    e.status = a.status;
-    e.half_pairs = a.half_pairs;
-    hipLaunchKernelGGL(encode_write_kernel, dim3(grid_for(e.n, 4, 16384)), dim3(256), 0, s, e);
+    // pack from keys: the page writer encodes and writes every byte of each
+    // new page
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const dim3 grid(grid_for(max_pages < a.item_slot_pages ? max_pages : a.item_slot_pages, 1, 16 * cus));
+    if (a.P == 16) hipLaunchKernelGGL(pack_write_pages_kernel<16>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(pack_write_pages_kernel<32>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
