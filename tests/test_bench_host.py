@@ -30,7 +30,7 @@ def test_tier_token_bytes_follow_the_tier_table():
         assert bench.TIER_TOKEN_BYTES[t] == 2 + 8 * (tb + sb) + (132 if t >= 3 else 256), t
 
 
-@pytest.mark.parametrize("workload", ["llama8b", "llama8b_v8"])
+@pytest.mark.parametrize("workload", ["llama8b", "llama8b_v8", "long256k", "ragged", "rdr128k"])
 def test_committed_counters_match_the_kernel_sources(workload):
     path = os.path.join(ROOT, "profiles", f"ada_decode_partials_{workload}_pmc.json")
     rec = json.load(open(path))
