@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--v8", action="store_true",
                     help="store every kept token's values in V8 (tiers 3-5: the same keys, 8-bit values)")
     ap.add_argument("--queries", type=int, default=1,
-                    help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 8)")
+                    help="queries per sequence (multi-query decode; Q * Hq/Hkv <= 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=100,
