@@ -42,7 +42,8 @@ class CacheDesc(ctypes.Structure):
                 ("page_capacity", ctypes.c_int64), ("arena_capacity16", ctypes.c_int64),
                 ("page_table", ctypes.c_void_p), ("num_pages", ctypes.c_void_p),
                 ("open_page", ctypes.c_void_p), ("page_meta", ctypes.c_void_p),
-                ("code_arena", ctypes.c_void_p), ("alloc", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("code_arena", ctypes.c_void_p), ("alloc", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("row_order", ctypes.c_void_p)]
 
 
 _lib = None
@@ -167,10 +168,11 @@ class Cache:
         self.code_arena = torch.zeros(arena_capacity16 * 16, dtype=torch.uint8, device=device)
         self.alloc = torch.zeros(2, dtype=torch.int64, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.row_order = torch.arange(rows, dtype=torch.int32, device=device)
         self.desc = CacheDesc(num_seqs, max_pages_per_head, page_capacity, arena_capacity16,
                               self.page_table.data_ptr(), self.num_pages.data_ptr(), self.open_page.data_ptr(),
                               self.page_meta.data_ptr(), self.code_arena.data_ptr(), self.alloc.data_ptr(),
-                              self.status.data_ptr())
+                              self.status.data_ptr(), self.row_order.data_ptr())
 
     def host(self):
         """numpy copies of every buffer (for comparisons)."""

@@ -174,6 +174,8 @@ DecodeLaunch make_decode(const ada_config_t *cfg, const ada_cache_t *cache, cons
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     a.value_tiers = cfg->value_tiers;
     a.nslice = slices(Q * (cfg->num_q_heads / cfg->num_kv_heads));
+    // the cache's row order covers all its rows: usable when all are decoded
+    a.row_order = B == cache->num_seqs ? cache->row_order : nullptr;
     return a;
 }
 
@@ -387,7 +389,7 @@ ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, v
     if (st) return st;
     if ((st = check_cache(cfg, cache))) return st;
     return hip_status(launch_cache_init(cache->num_seqs * cfg->num_kv_heads, cache->num_pages, cache->open_page,
-                                        cache->alloc, cache->status, (hipStream_t)stream));
+                                        cache->alloc, cache->status, cache->row_order, (hipStream_t)stream));
 }
 
 ada_status_t ada_validate_cache(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *stream) {
@@ -746,6 +748,8 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_of_slot_pages = 0;
     a.item_of_slot = w.item_of_slot;
     a.item_slot_pages = w.item_slot_pages;
+    a.row_order = cache->row_order;
+    a.rows_total = cache->num_seqs * cfg->num_kv_heads;
     a.half_pairs = cfg->pair_layout == ADA_PAIRS_HALF_SPLIT;
     a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return hip_status(launch_pack(a, s));
@@ -900,6 +904,8 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_of_slot_pages = r.src_of_slot_pages;
     a.item_of_slot = nullptr;
     a.item_slot_pages = 0;
+    a.row_order = dst->row_order;
+    a.rows_total = dst->num_seqs * cfg->num_kv_heads;
     a.half_pairs = 0;   // codes are transcoded, no key is read
     a.n_tiers = cfg->value_tiers ? kNumTiers : 3;
     return hip_status(launch_pack(a, s));

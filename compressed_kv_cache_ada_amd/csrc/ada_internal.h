@@ -101,6 +101,9 @@ struct DecodeLaunch {
     float *util;
     int32_t half_pairs;   // pair j = (x[j], x[j + 64]) instead of (x[2j], x[2j + 1])
     int32_t value_tiers;  // the cache may hold pages of tiers 3-5 (V8 values)
+    // rows in the order their work-groups are dispatched (longest first), or
+    // nullptr for the natural order; only the dispatch order changes
+    const int32_t *row_order;
     // G' > 8 (several queries per sequence): the virtual heads are cut into
     // nslice slices of 8, each computed by its own work-group of the chunk
     int32_t nslice;
@@ -185,6 +188,10 @@ struct PackLaunch {
     int64_t item_slot_pages;
     int32_t half_pairs;             // key pair layout (see EncodeLaunch)
     int32_t n_tiers;                // tier ids below this are accepted (3, or 6 with value tiers)
+    // the cache's row order (see ada_cache_t), re-sorted over all rows_total
+    // rows after the pages are placed; nullptr: none kept
+    int32_t *row_order;
+    int32_t rows_total;
 };
 hipError_t launch_pack(const PackLaunch &a, hipStream_t s);
 // pages a re-pack may open per row: sum over three tiers of ceil(n_tau / P)
@@ -266,7 +273,7 @@ struct RepackItemsLaunch {
 hipError_t launch_repack_items(const RepackItemsLaunch &a, hipStream_t s);
 
 hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
-                             int32_t *status, hipStream_t s);
+                             int32_t *status, int32_t *row_order, hipStream_t s);
 // rows 0..rows-1 of a cache: page counts, page ids and their metadata in range
 hipError_t launch_validate(int32_t rows, int32_t maxp, int64_t page_capacity, int64_t arena16, int32_t P,
                            int32_t n_tiers, const int32_t *num_pages, const int32_t *page_table,

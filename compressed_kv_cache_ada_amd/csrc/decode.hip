@@ -440,6 +440,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     // a chunk 8 work-groups apart, i.e. on one of the chip's dies (work-groups
     // go to the dies in turn) and dispatched together: the second slice's
     // code and value reads can hit that die's L2 / the memory-side cache
+    // the row: in the cache's order (longest rows first) when it is given,
+    // so that the longest rows' work-groups are dispatched first
+    int h = blockIdx.y, b = blockIdx.z;
+    if (a.row_order) {
+        const int r = a.row_order[blockIdx.z * a.Hkv + blockIdx.y];
+        h = r % a.Hkv;
+        b = r / a.Hkv;
+    }
     int chunk = blockIdx.x, slice = 0;
     if (a.nslice > 1) {
         const int x = blockIdx.x;
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_partials_kernel(DecodeLau
     c.gv = a.Q * pol.Gr;
     c.voff = pol.voff;
     core::split_k<G, P, NW, MODE == 2>(c, pol, *reinterpret_cast<typename Pol::Smem *>(raw), cs,
-                            reinterpret_cast<float *>(raw), chunk, blockIdx.y, blockIdx.z);
+                            reinterpret_cast<float *>(raw), chunk, h, b);
 }
 
 // one work-group per virtual row (b, h, v); writes query qi = v / Gr, head

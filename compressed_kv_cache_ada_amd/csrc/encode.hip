@@ -305,6 +305,32 @@ __global__ __launch_bounds__(256) void zero_pages_kernel(const int32_t *list, co
     }
 }
 
+// ------------------------------------------------------------ row order
+// One work-group: the rows by decreasing page count, ties in row order
+// (rank of row r = rows with more pages + rows before r with as many).
+// Up to kMaxOrderRows rows; beyond that the order is left as it is.
+constexpr int kMaxOrderRows = 16384;
+__global__ __launch_bounds__(1024) void row_order_kernel(int32_t rows, const int32_t *num_pages, int32_t *row_order) {
+    __shared__ int32_t tile[4096];
+    if (rows > kMaxOrderRows) return;
+    for (int base_r = 0; base_r < rows; base_r += 1024) {
+        const int r = base_r + threadIdx.x;
+        const int np = r < rows ? num_pages[r] : 0;
+        int rank = 0;
+        for (int base_j = 0; base_j < rows; base_j += 4096) {
+            __syncthreads();
+            for (int k = threadIdx.x; k < 4096 && base_j + k < rows; k += 1024) tile[k] = num_pages[base_j + k];
+            __syncthreads();
+            const int n = rows - base_j < 4096 ? rows - base_j : 4096;
+            for (int k = 0; k < n; ++k) {
+                const int v = tile[k];
+                rank += (v > np) || (v == np && base_j + k < r);
+            }
+        }
+        if (r < rows) row_order[rank] = r;
+    }
+}
+
 // ------------------------------------------------------- pack page writer
 // One work-group (four wavefronts) per new page of a pack, in turn: the
 // page's tokens are encoded one per wavefront into a copy of the page's
@@ -970,10 +996,13 @@ __global__ __launch_bounds__(1024) void append_book_kernel(AppendKernelArgs k) {
 }
 
 __global__ void cache_init_kernel(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc,
-                                  int32_t *status) {
+                                  int32_t *status, int32_t *row_order) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < rows * kNumTiers; i += gridDim.x * blockDim.x) {
         open_page[i] = -1;
-        if (i < rows) num_pages[i] = 0;
+        if (i < rows) {
+            num_pages[i] = 0;
+            if (row_order) row_order[i] = i;
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         alloc[0] = 0;
@@ -1049,9 +1078,9 @@ hipError_t launch_validate(int32_t rows, int32_t maxp, int64_t page_capacity, in
 }
 
 hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_page, int64_t *alloc, int32_t *status,
-                             hipStream_t s) {
+                             int32_t *row_order, hipStream_t s) {
     hipLaunchKernelGGL(cache_init_kernel, dim3(grid_for((int64_t)rows * kNumTiers, 256, 1024)), dim3(256), 0, s, rows,
-                       num_pages, open_page, alloc, status);
+                       num_pages, open_page, alloc, status, row_order);
     return hipGetLastError();
 }
 
@@ -1071,6 +1100,9 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
         const dim3 grid(grid_for(a.src_of_slot_pages, 1, 8 * cus));   // about one round of resident work-groups
         if (a.P == 16) hipLaunchKernelGGL(transcode_pages_kernel<16>, grid, dim3(128), 0, s, a);
         else hipLaunchKernelGGL(transcode_pages_kernel<32>, grid, dim3(128), 0, s, a);
+        if (a.row_order)
+            hipLaunchKernelGGL(row_order_kernel, dim3(1), dim3(1024), 0, s, a.rows_total, (const int32_t *)a.num_pages,
+                               a.row_order);
         return hipGetLastError();
     }
     // pack from keys: the page writer encodes and writes every byte of each
@@ -1082,6 +1114,9 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
     const dim3 grid(grid_for(max_pages < a.item_slot_pages ? max_pages : a.item_slot_pages, 1, 16 * cus));
     if (a.P == 16) hipLaunchKernelGGL(pack_write_pages_kernel<16>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(pack_write_pages_kernel<32>, grid, dim3(256), 0, s, a);
+    if (a.row_order)
+        hipLaunchKernelGGL(row_order_kernel, dim3(1), dim3(1024), 0, s, a.rows_total, (const int32_t *)a.num_pages,
+                           a.row_order);
     return hipGetLastError();
 }
 

@@ -156,6 +156,12 @@ typedef struct {
     uint8_t *code_arena;        /* [arena_capacity16 * 16], 16-byte aligned: the pages' blocks */
     int64_t *alloc;             /* [2]: next page id, next code unit */
     int32_t *status;            /* [1] device error word (0 = OK) */
+    int32_t *row_order;         /* [rows] or NULL: the rows by decreasing page count, a schedule hint
+                                   for the decode (the longest rows are started first).  A
+                                   permutation of 0..rows-1: ada_cache_init writes the identity,
+                                   ada_pack and ada_repack (destination) re-sort it (for up to
+                                   16384 rows; more keep the identity), appends leave it as it
+                                   is.  It changes no result. */
 } ada_cache_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

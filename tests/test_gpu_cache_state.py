@@ -1,5 +1,5 @@
 """Cache state on the device: the page-list check (ada_validate_cache) and a
-checkpoint round trip.
+checkpoint round trip, and the cache's row order (a dispatch hint).
 
 The check must accept packed caches and flag, through the status word, a
 page count past the row's table, a page id outside the pool and malformed
@@ -13,7 +13,7 @@ import torch
 
 import compressed_kv_cache_ada_amd as ada
 import workloads as W
-from tests.gpu_util import gpu_pack, log
+from tests.gpu_util import dims, gpu_pack, log
 
 pytestmark = pytest.mark.gpu
 
@@ -74,8 +74,8 @@ def test_checkpoint_round_trip():
     src, dev = gpu_pack(w)
     saved = {k: t.cpu().clone() for k, t in (("page_table", src.page_table), ("num_pages", src.num_pages),
                                               ("open_page", src.open_page), ("page_meta", src.page_meta),
-                                              ("code_arena", src.code_arena),
-                                              ("alloc", src.alloc), ("status", src.status))}
+                                              ("code_arena", src.code_arena), ("alloc", src.alloc),
+                                              ("status", src.status), ("row_order", src.row_order))}
     dst = ada.Cache(src.cfg, src.desc.num_seqs, src.desc.max_pages_per_head, src.desc.page_capacity,
                     src.desc.arena_capacity16)
     for k, t in saved.items():
@@ -101,3 +101,42 @@ def test_checkpoint_round_trip():
     o1, l1 = ada.decode(src, dev["q"], w["scale"])
     o2, l2 = ada.decode(dst, dev["q"], w["scale"])
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _longest_first(num_pages):
+    return np.argsort(-num_pages.astype(np.int64), kind="stable").astype(np.int32)
+
+
+def test_row_order_sorts_rows_and_changes_no_result():
+    """ada_cache_init writes the identity; pack and re-pack leave the rows
+    sorted by decreasing page count (ties in row order); the decode's result
+    does not depend on the order (every output bit equal under the identity
+    and under a reversed order)."""
+    w = W.config("ragged", ctx=2400, batch=6)
+    log("row order ragged ctx 2400 batch 6")
+    c = ada.Cache(ada.make_config(w["P"], w["Hq"], w["Hkv"]), w["B"], *dims(w))
+    ada.cache_init(c)
+    assert np.array_equal(c.row_order.cpu().numpy(), np.arange(w["B"] * w["Hkv"]))
+    dev = {"keys": torch.from_numpy(w["keys"]).cuda(), "values": torch.from_numpy(w["values"].view(np.int16)).cuda(),
+           "q": torch.from_numpy(w["q"]).cuda()}
+    ada.pack(c, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), dev["keys"], dev["values"])
+    assert ada.read_status(c.status) == ada.OK
+    npg = c.num_pages.cpu().numpy()
+    assert np.array_equal(c.row_order.cpu().numpy(), _longest_first(npg))
+    assert len(set(npg.tolist())) > 1   # the rows differ in length
+    o1, l1 = ada.decode(c, dev["q"], w["scale"])
+    sorted_order = c.row_order.clone()
+    for order in (torch.arange(npg.size, dtype=torch.int32, device="cuda"),
+                  torch.flip(sorted_order, [0]).contiguous()):
+        c.row_order.copy_(order)
+        o2, l2 = ada.decode(c, dev["q"], w["scale"])
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # re-pack: the destination's order follows its own page counts
+    c.row_order.copy_(sorted_order)
+    util = torch.rand((c.desc.page_capacity, w["P"]), device="cuda")
+    dst = ada.Cache(c.cfg, w["B"], c.desc.max_pages_per_head, c.desc.page_capacity, c.desc.arena_capacity16)
+    ada.cache_init(dst)
+    budget = [int(x) for x in np.full(w["B"], 300_000)]
+    ada.repack(c, w["B"], util, budget, dst)
+    assert ada.read_status(dst.status) == ada.OK
+    assert np.array_equal(dst.row_order.cpu().numpy(), _longest_first(dst.num_pages.cpu().numpy()))
