@@ -400,8 +400,8 @@ ada_status_t ada_validate_cache(const ada_config_t *cfg, const ada_cache_t *cach
     if (B == 0) return ADA_OK;
     return hip_status(launch_validate(B * cfg->num_kv_heads, cache->max_pages_per_head, cache->page_capacity,
                                       cache->arena_capacity16, cfg->page_size, cfg->value_tiers ? kNumTiers : 3,
-                                      cache->num_pages, cache->page_table, cache->page_meta, cache->status,
-                                      (hipStream_t)stream));
+                                      cache->num_pages, cache->page_table, cache->page_meta, cache->row_order,
+                                      cache->num_seqs * cfg->num_kv_heads, cache->status, (hipStream_t)stream));
 }
 
 ada_status_t ada_build_lut(const ada_config_t *cfg, const float *q, int32_t B, float *lut, void *stream) {

@@ -277,7 +277,8 @@ hipError_t launch_cache_init(int32_t rows, int32_t *num_pages, int32_t *open_pag
 // rows 0..rows-1 of a cache: page counts, page ids and their metadata in range
 hipError_t launch_validate(int32_t rows, int32_t maxp, int64_t page_capacity, int64_t arena16, int32_t P,
                            int32_t n_tiers, const int32_t *num_pages, const int32_t *page_table,
-                           const ada_page_meta_t *page_meta, int32_t *status, hipStream_t s);
+                           const ada_page_meta_t *page_meta, const int32_t *row_order, int32_t order_rows,
+                           int32_t *status, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 hipError_t launch_probe_read(const void *src, size_t bytes, int variant, uint32_t *out, hipStream_t s);
 

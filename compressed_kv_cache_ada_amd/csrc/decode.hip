@@ -58,7 +58,6 @@ struct CodeRegs {
     uint2 h;
     uint32_t r;         // fp16 radius bits
     const uint8_t *c;   // the token's first angle unit
-    uint2 vs;           // V8 pages: the token's four block scales as fp16 [0|1], [2|3]
 };
 
 // Per-work-group LUT layout, per pair j with NC codes: slices of SW =
@@ -99,6 +98,20 @@ __device__ __forceinline__ void lut_load(const float *pair, uint32_t c, float (&
     }
 }
 
+// lut_load for G >= 4 (16-byte entries), from the code's byte offset c * 16
+template <int G, int NC>
+__device__ __forceinline__ void lut_load16(const float *pair, uint32_t c16, float (&e)[G]) {
+    static_assert(lut_sw<G>() == 4, "16-byte LUT entries");
+#pragma unroll
+    for (int sl = 0; sl < G / 4; ++sl) {
+        const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(pair) + sl * NC * 16 + c16);
+        e[4 * sl] = v.x;
+        e[4 * sl + 1] = v.y;
+        e[4 * sl + 2] = v.z;
+        e[4 * sl + 3] = v.w;
+    }
+}
+
 template <int G>
 __device__ __forceinline__ void logits_t4(const CodeRegs &k, const float *lut4, float mul, float (&lg)[G]) {
     const uint32_t tw[8] = {k.u[0].x, k.u[0].y, k.u[0].z, k.u[0].w, k.u[1].x, k.u[1].y, k.u[1].z, k.u[1].w};
@@ -108,16 +121,27 @@ __device__ __forceinline__ void logits_t4(const CodeRegs &k, const float *lut4, 
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
     // word by word (8 pairs): the 8 gathers are issued together, then the
     // FMAs; a compiler fence keeps the next word's work after this one.
-    // Magnitude nibbles are split into even / odd bytes so each converts
-    // to float with a single byte-select conversion.
+    // Magnitude nibbles are split into even / odd bytes (made opaque, so
+    // that the compiler does not fold the split back into per-nibble field
+    // extractions) and each converts to float with one byte-select
+    // conversion.  With 16-byte table entries (G >= 4) a code's byte offset
+    // c * 16 is a byte's high nibble: in place for odd pairs, in t << 4 for
+    // even ones, one byte-select AND each.
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const uint32_t t = tw[w];
-        const uint32_t se = sw[w] & 0x0F0F0F0Fu, so = (sw[w] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t se = pin(sw[w] & 0x0F0F0F0Fu), so = pin((sw[w] >> 4) & 0x0F0F0F0Fu);
         const float *lu = lut4 + w * 8 * 16 * G;
         float e[8][G];
+        if constexpr (lut_sw<G>() == 4) {
+            const uint32_t te = pin(t << 4);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lut_load<G, 16>(lu + j * 16 * G, (t >> (4 * j)) & 15u, e[j]);
+            for (int j = 0; j < 8; ++j)
+                lut_load16<G, 16>(lu + j * 16 * G, (((j & 1) ? t : te) >> (8 * (j >> 1))) & 0xF0u, e[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lut_load<G, 16>(lu + j * 16 * G, (t >> (4 * j)) & 15u, e[j]);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t sb = (j & 1) ? so : se;
@@ -251,6 +275,9 @@ struct AdaPolicy {
         int app_status;            // the status word as read once by the work-group (fused append)
         // V8 scale word of each token of the next group (lane = token)
         uint32_t vs[NW][VT ? 64 : 1];
+        // the current group's fp16 scales per dimension block (lane = token),
+        // so that a lane reads eight tokens' scales of a block at once
+        alignas(16) uint16_t vsc[NW][VT ? 4 : 1][64];
     };
     const int32_t *num_pages_;
     const ada_page_meta_t *page_meta;
@@ -343,13 +370,15 @@ struct AdaPolicy {
 
     using Codes = CodeRegs;
 
-    // the fp16 scales of dimension blocks 2kp, 2kp + 1 of tokens 8 blk ..
-    // 8 blk + 7 of the current group, from the lanes holding those tokens
-    __device__ void scale_halves(const Codes &k, int blk, int kp, uint32_t (&sh)[8]) const {
+    // fp16 scales of dimension block b for tokens tok .. tok + 7 of the
+    // current group (tok a multiple of 8), as the pairs (tok + 2i, tok + 2i + 1)
+    __device__ void scale_pairs(const Smem &s, int w, int tok, int b, uint32_t (&sp)[4]) const {
         if constexpr (VT) {
-            const int v = (int)(kp ? k.vs.y : k.vs.x);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sh[j] = (uint32_t)__shfl(v, 8 * blk + j, 64);
+            const uint4 v = *reinterpret_cast<const uint4 *>(&s.vsc[w][b][tok]);
+            sp[0] = v.x;
+            sp[1] = v.y;
+            sp[2] = v.z;
+            sp[3] = v.w;
         }
     }
 
@@ -384,8 +413,10 @@ struct AdaPolicy {
         __builtin_amdgcn_global_load_lds(blk + 4 * (slot >> 1), &st.r[0], 4, 0, 0);
     }
 
-    // The lane's code units from wavefront w's stage (after its loads landed).
-    __device__ Codes unstage(const Smem &s, int w, uint2 meta, int slot, int lane) const {
+    // The lane's code units from wavefront w's stage (after its loads
+    // landed); with V8 pages, its token's four block scales go to the
+    // wavefront's scale table, read after the weights' LDS sync.
+    __device__ Codes unstage(Smem &s, int w, uint2 meta, int slot, int lane) const {
         const CodeStage &st = s.st[w];
         CodeRegs k;
 #pragma unroll
@@ -394,7 +425,13 @@ struct AdaPolicy {
         k.h = (slot & 1) ? make_uint2(hh.z, hh.w) : make_uint2(hh.x, hh.y);
         const uint32_t rr = st.r[lane];
         k.r = (slot & 1) ? rr >> 16 : rr & 0xFFFFu;
-        if constexpr (VT) k.vs = core::v8_scale_halves(s.vs[w][lane]);
+        if constexpr (VT) {
+            const uint2 vs = core::v8_scale_halves(s.vs[w][lane]);
+            s.vsc[w][0][lane] = (uint16_t)vs.x;
+            s.vsc[w][1][lane] = (uint16_t)(vs.x >> 16);
+            s.vsc[w][2][lane] = (uint16_t)vs.y;
+            s.vsc[w][3][lane] = (uint16_t)(vs.y >> 16);
+        }
         // the slot offset is made opaque here so that arena + slot offset (a
         // 64-bit per-lane value) is not hoisted out of the group loop, where
         // it would hold two more registers for the whole loop

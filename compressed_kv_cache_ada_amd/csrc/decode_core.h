@@ -42,19 +42,40 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// +inf in a scalar register, hidden from the optimiser (see max2).
+__device__ __forceinline__ float opaque_inf() {
+    float x = INFINITY;
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// max(a, b).  MED3: as the median of a, b and +inf (`inf` from
+// opaque_inf), one v_med3_f32.  fmaxf -- and a median with a literal
+// infinity, which the optimiser turns back into it -- first quiets operands
+// that come from a lane permutation or a readlane (the kernels run in IEEE
+// mode): two more instructions per step.  Measured: the median form is the
+// faster one with eight query heads per KV head, fmaxf with four or fewer.
+// Operands here are logits or -inf, never NaN.
+template <bool MED3>
+__device__ __forceinline__ float max2(float a, float b, float inf) {
+    if constexpr (MED3) return __builtin_amdgcn_fmed3f(a, b, inf);
+    else return fmaxf(a, b);
+}
+
 // Wavefront maximum on the VALU: within each row of 16 lanes by DPP (quad
 // xor 1, quad xor 2, half-row mirror, row mirror), then across the four
 // rows by reading one lane of each.  The result is wave-uniform.
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm(1, 0, 3, 2)
-    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm(2, 3, 0, 1)
-    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+template <bool MED3>
+__device__ __forceinline__ float wave_max(float v, float inf) {
+    v = max2<MED3>(v, dpp_f<0xB1>(v), inf);    // quad_perm(1, 0, 3, 2)
+    v = max2<MED3>(v, dpp_f<0x4E>(v), inf);    // quad_perm(2, 3, 0, 1)
+    v = max2<MED3>(v, dpp_f<0x141>(v), inf);   // row_half_mirror
+    v = max2<MED3>(v, dpp_f<0x140>(v), inf);   // row_mirror
     const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
     const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
     const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
     const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    return max2<MED3>(max2<MED3>(r0, r1, inf), max2<MED3>(r2, r3, inf), inf);
 }
 
 // V8 values -> fp16 MFMA operand.
@@ -241,10 +262,11 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //                                              (uniformly) whether a barrier
 //                                              must follow
 //   kValueTiers: pages of tiers 3-5 hold V8 values (see include/ada.h)
-//     void scale_halves(codes, blk, kp, sh[8])  fp16 scales of dimension
-//                                              blocks 2kp, 2kp + 1 of tokens
-//                                              8 blk .. 8 blk + 7 of the
-//                                              current group
+//     void scale_pairs(smem, w, tok, b, sp[4])  fp16 scales of dimension
+//                                              block b of tokens tok ..
+//                                              tok + 7 of the current group,
+//                                              in pairs of tokens (after the
+//                                              weights' LDS sync)
 //   kStaged = true:
 //     void stage(smem, w, meta, page, slot)    request a group's codes (and
 //                                              V8 scale words) into
@@ -397,24 +419,26 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
             const int tok = (16 * vq) % P;           // the lane's first slot in that page
             if constexpr (Pol::kValueTiers) v8 = tier_v8(vmeta.x & 0xFF);
             // V8 page: the 16 code bytes of the lane's dimension (its 16
-            // tokens) per tile, read at both steps (the second read hits the
-            // cache): the same instructions as the fp16 loads, other addresses
+            // tokens, both steps) per tile, one read into va[0]; va[1] is
+            // formed from it by the conversion
             const uint8_t *b8 = vpart + (tok / 16) * kV8Group + kV8Codes + vh * 16;
+            const uint8_t *b16 = vpart + (tok / 8) * 2048 + vh * 16;
+            const uint8_t *base = v8 ? b8 : b16;
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const uint8_t *b16 = vpart + (tok / 8 + kc) * 2048 + vh * 16;
-                const uint8_t *base = v8 ? b8 : b16;
+            for (int t = 0; t < 8; ++t) va[0][t] = ldg<uint4>(base + t * 256);
+            if (!v8) {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) va[kc][t] = ldg<uint4>(base + t * 256);
+                for (int t = 0; t < 8; ++t) va[1][t] = ldg<uint4>(b16 + 2048 + t * 256);
             }
         }
 
         // 4. online softmax, weights to LDS as fp16 hi + lo
         float alpha_n = 1.f;
+        const float pinf = opaque_inf();
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float mx = wave_max(valid ? lg[g] : -INFINITY);
-            const float mnew = fmaxf(m_run[g], mx);
+            const float mx = wave_max<(G >= 8)>(valid ? lg[g] : -INFINITY, pinf);
+            const float mnew = max2<(G >= 8)>(m_run[g], mx, pinf);
             // v_exp_f32 directly: arguments are <= 0, results below 2^-126
             // flush to zero, far below the weights' resolution
             const float alpha = (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - mnew);
@@ -431,45 +455,35 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         for (int t = 0; t < 8; ++t) acc[t] *= alpha_n;
         wave_lds_sync();
 
-        // 5. O^T += V^T P^T on the matrix cores (V8 lanes: codes x scales ->
-        //    fp16 first, tile t using dimension block t / 2)
+        // 5. O^T += V^T P^T on the matrix cores.  V8 lanes first turn codes
+        //    x scales into fp16: tile t's bytes 0-7 into va[0][t] (step 0),
+        //    bytes 8-15 into va[1][t] (step 1); tiles 2k, 2k + 1 use
+        //    dimension block k, whose scales for a step's eight tokens come
+        //    from the policy's scale table in one read.
+        if constexpr (Pol::kValueTiers) {
+            if (v8) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    uint32_t s0[4], s1[4];   // scale pairs of tokens (2i, 2i + 1), block kb, steps 0 and 1
+                    pol.scale_pairs(ps, w, 16 * kq, kb, s0);
+                    pol.scale_pairs(ps, w, 16 * kq + 8, kb, s1);
+#pragma unroll
+                    for (int t = 2 * kb; t < 2 * kb + 2; ++t) {
+                        const uint4 c = va[0][t];
+                        va[1][t] = make_uint4(v8_pair<0>(c.z, s1[0]), v8_pair<2>(c.z, s1[1]),
+                                              v8_pair<0>(c.w, s1[2]), v8_pair<2>(c.w, s1[3]));
+                        va[0][t] = make_uint4(v8_pair<0>(c.x, s0[0]), v8_pair<2>(c.x, s0[1]),
+                                              v8_pair<0>(c.y, s0[2]), v8_pair<2>(c.y, s0[3]));
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             half8_t bh = {}, bl = {};
             if (n_head < G) {
                 bh = *reinterpret_cast<const half8_t *>(&cs.pb[w][0][n_head][16 * kq + 8 * kc]);
                 bl = *reinterpret_cast<const half8_t *>(&cs.pb[w][1][n_head][16 * kq + 8 * kc]);
-            }
-            if constexpr (Pol::kValueTiers) {
-                // codes x scales -> fp16 in place; tiles 2k, 2k+1 use dimension
-                // block k.  The scales come from the lanes holding the
-                // tokens, so they are gathered with every lane active.
-                if (__any(v8)) {
-#pragma unroll
-                    for (int kp = 0; kp < 2; ++kp) {   // dimension blocks 2kp, 2kp + 1: tiles 4kp .. 4kp + 3
-                        uint32_t sh[8];   // token j's scale halves of the two blocks
-                        pol.scale_halves(codes, 2 * kq + kc, kp, sh);
-                        if (v8) {
-#pragma unroll
-                            for (int kk = 0; kk < 2; ++kk) {
-                                uint32_t sp[4];   // scale pairs of tokens (2i, 2i + 1), block 2kp + kk
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    sp[i] = __builtin_amdgcn_perm(sh[2 * i + 1], sh[2 * i], kk ? 0x07060302u : 0x05040100u);
-#pragma unroll
-                                for (int t = 4 * kp + 2 * kk; t < 4 * kp + 2 * kk + 2; ++t) {
-                                    // step kc's eight tokens: bytes 8 kc .. 8 kc + 7
-                                    const uint32_t lo = kc ? va[kc][t].z : va[kc][t].x;
-                                    const uint32_t hi = kc ? va[kc][t].w : va[kc][t].y;
-                                    va[kc][t].w = v8_pair<2>(hi, sp[3]);
-                                    va[kc][t].z = v8_pair<0>(hi, sp[2]);
-                                    va[kc][t].y = v8_pair<2>(lo, sp[1]);
-                                    va[kc][t].x = v8_pair<0>(lo, sp[0]);
-                                }
-                            }
-                        }
-                    }
-                }
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t)

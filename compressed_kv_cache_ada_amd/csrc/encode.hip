@@ -1041,6 +1041,25 @@ __global__ __launch_bounds__(256) void validate_kernel(int32_t rows, int32_t max
     }
 }
 
+// The row order must be a permutation of 0..rows-1: every entry in range
+// (else the decode would read rows outside the tables), and, for up to
+// 65536 rows, none twice (a bitmap in LDS).  One work-group.
+__global__ __launch_bounds__(1024) void validate_order_kernel(int32_t rows, const int32_t *row_order,
+                                                             int32_t *status) {
+    __shared__ uint32_t seen[2048];
+    const bool dup_check = rows <= 65536;
+    for (int i = threadIdx.x; i < 2048; i += 1024) seen[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows; i += 1024) {
+        const int r = row_order[i];
+        if (r < 0 || r >= rows) {
+            enc::set_status(status, ADA_EINVAL);
+            continue;
+        }
+        if (dup_check && (atomicOr(&seen[r >> 5], 1u << (r & 31)) >> (r & 31)) & 1u) enc::set_status(status, ADA_EINVAL);
+    }
+}
+
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -1071,9 +1090,12 @@ hipError_t launch_zero_pages(const int32_t *pages, const int32_t *n_pages, int64
 
 hipError_t launch_validate(int32_t rows, int32_t maxp, int64_t page_capacity, int64_t arena16, int32_t P,
                            int32_t n_tiers, const int32_t *num_pages, const int32_t *page_table,
-                           const ada_page_meta_t *page_meta, int32_t *status, hipStream_t s) {
+                           const ada_page_meta_t *page_meta, const int32_t *row_order, int32_t order_rows,
+                           int32_t *status, hipStream_t s) {
     hipLaunchKernelGGL(validate_kernel, dim3(grid_for(rows, 1, 4096)), dim3(256), 0, s, rows, maxp, page_capacity,
                        arena16, P, n_tiers, num_pages, page_table, page_meta, status);
+    if (row_order && order_rows > 0)
+        hipLaunchKernelGGL(validate_order_kernel, dim3(1), dim3(1024), 0, s, order_rows, row_order, status);
     return hipGetLastError();
 }
 

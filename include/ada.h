@@ -177,7 +177,8 @@ int64_t ada_block_bytes(int32_t tier, int32_t page_size);
 size_t ada_lut_floats(const ada_config_t *cfg);
 
 /* Reset the rows, counters and status of a cache: num_pages = 0,
- * open_page = -1, alloc = {0, 0}, status = 0.  Page contents are left as
+ * open_page = -1, alloc = {0, 0}, status = 0, row_order = 0..rows-1 (when
+ * not NULL).  Page contents are left as
  * they are (pages are zeroed when they are allocated). */
 ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, void *stream);
 
@@ -190,8 +191,11 @@ ada_status_t ada_cache_init(const ada_config_t *cfg, const ada_cache_t *cache, v
  * and that page's metadata (tier id below 3, or below 6 with value_tiers;
  * count 1..page_size; reserved 0; block inside the arena).  Any
  * violation sets the cache's status word to ADA_EINVAL (read and clear it
- * with ada_read_status); nothing is written otherwise.  Asynchronous on
- * `stream`; one work-group per row. */
+ * with ada_read_status); nothing is written otherwise.  When the cache has
+ * a row_order, it is checked over all num_seqs * num_kv_heads rows too:
+ * every entry must lie in 0..rows-1 and, for up to 65536 rows, no entry may
+ * appear twice.  Asynchronous on `stream`; one work-group per row, and one
+ * more for the row order. */
 ada_status_t ada_validate_cache(const ada_config_t *cfg, const ada_cache_t *cache, int32_t B, void *stream);
 
 /* Angle lookup table (the per-query table of the abstract's angle-domain

@@ -2,8 +2,8 @@
 checkpoint round trip, and the cache's row order (a dispatch hint).
 
 The check must accept packed caches and flag, through the status word, a
-page count past the row's table, a page id outside the pool and malformed
-page metadata.  The decode is never launched on a corrupted table (it does
+page count past the row's table, a page id outside the pool, malformed
+page metadata and a row order that is not a permutation of the rows.  The decode is never launched on a corrupted table (it does
 not range-check page ids).  The round trip copies every caller-owned buffer
 of a packed cache to the host, restores it into a fresh cache and checks
 that decode and append then behave bit for bit as on the original."""
@@ -66,6 +66,14 @@ def test_validate_accepts_packed_and_flags_corruption():
     assert _status_after(gc, B - 1) == ada.OK
     assert _status_after(gc, B) == ada.EINVAL
     gc.num_pages[last] = n_last
+    # the row order: an entry out of range, negative, or repeated
+    order = gc.row_order.clone()
+    rows = order.numel()
+    for i, v in ((2, rows), (0, -1), (1, int(order[3]))):
+        gc.row_order[i] = v
+        assert _status_after(gc, B) == ada.EINVAL, (i, v)
+        gc.row_order.copy_(order)
+    assert _status_after(gc, B) == ada.OK
 
 
 def test_checkpoint_round_trip():
