@@ -39,7 +39,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first (about 30 ms at llama8b; shorter warm-ups measured 3%% slower steps)")
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "rdr128k", "ragged", "long256k", "tiny"])
     ap.add_argument("--chunk-pages", type=int, default=0)
     ap.add_argument("--utility", action="store_true",
