@@ -264,6 +264,7 @@ struct CodeStage {
 template <int G, int P, int NW, bool APPEND, bool VT>
 struct AdaPolicy {
     static constexpr bool kStaged = true;
+    static constexpr bool kEarlyStage = !APPEND;   // the fused append writes before any read
     static constexpr bool kValueTiers = VT;   // the cache may hold pages of tiers 3-5 (V8 values)
     struct Smem {
         float lut4[64 * 16 * G];   // 4-bit angle grid (and the 2-bit one), lut_index<G, 16> layout
@@ -331,6 +332,7 @@ struct AdaPolicy {
     }
 
     __device__ int num_pages(int row, int) const { return num_pages_[row]; }
+    __device__ int num_pages_lane(int row, int, uint32_t z) const { return num_pages_[row + z]; }
     __device__ uint2 meta(int page, int, int) const { return ldg<uint2>(page_meta + page); }
     // a page's value part: its block's bytes after the key part
     __device__ const uint8_t *value_part(int, uint2 m) const {
@@ -345,11 +347,23 @@ struct AdaPolicy {
     // % Gr of q [B][Q][Hq][128]; component d is x (0) or y (1) of pair j in
     // the cache's pair layout.
     __device__ void prologue(Smem &s, int b, int h, int tid, int nt) const {
-        for (int i = tid; i < G * kD; i += nt) {
+        // every query load of the thread is issued before the first store
+        constexpr int NTQ = NW * 64;
+        constexpr int NQ = (G * kD + NTQ - 1) / NTQ;
+        float qv[NQ];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int i = tid + k * NTQ;
             const int v = i >> 7, d = i & 127;
             const int qi = (voff + v) / Gr, g = (voff + v) % Gr;
+            qv[k] = i < G * kD ? q[(((size_t)b * Q + qi) * Hq + (size_t)h * Gr + g) * kD + d] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int i = tid + k * NTQ;
+            const int v = i >> 7, d = i & 127;
             const int j = half ? (d & 63) : (d >> 1), xy = half ? (d >> 6) : (d & 1);
-            s.q8[(j * G + v) * 2 + xy] = q[(((size_t)b * Q + qi) * Hq + (size_t)h * Gr + g) * kD + d];
+            if (i < G * kD) s.q8[(j * G + v) * 2 + xy] = qv[k];
         }
         for (int c = tid; c < 256; c += nt) {
             const float2 d = grid_dir(c);
@@ -360,8 +374,14 @@ struct AdaPolicy {
 
     // phase 2 (after a barrier): the T4 table (T2 codes use its entries 4 c)
     __device__ void build(Smem &s, int tid, int nt) const {
-        // consecutive threads fill consecutive heads, then codes
-        for (int i = tid; i < 64 * 16 * G; i += nt) {
+        // consecutive threads fill consecutive heads, then codes; every
+        // thread fills the same number of entries, a compile-time count, so
+        // that the table reads of four entries are in flight together
+        constexpr int NTB = NW * 64;
+        static_assert((64 * 16 * G) % NTB == 0, "LUT entries per thread");
+#pragma unroll 4
+        for (int k = 0; k < 64 * 16 * G / NTB; ++k) {
+            const int i = tid + k * NTB;
             const int g = i % G, c = (i / G) & 15, j = i / (16 * G);
             s.lut4[lut_index<G, 16>(j, c, g)] =
                 lut_entry(s.q8[(j * G + g) * 2], s.q8[(j * G + g) * 2 + 1], s.cs4[c]);

@@ -4,7 +4,9 @@
 // One work-group = one (context chunk, KV head, sequence).  Prologue: the
 // chunk's page ids and page metadata are staged in LDS (so the per-group
 // critical path has no dependent global loads before the code fetch), and
-// the policy stages its per-query tables.  Then each wavefront walks 64-token
+// the policy stages its per-query tables.  The prologue is two memory round
+// trips (page count, page ids and query; then page metadata), after which
+// each wavefront requests its first group's codes.  Then each wavefront walks 64-token
 // groups (4 pages of 16 / 2 pages of 32):
 //   1. the tokens' codes (lane = token, policy); a staged policy has them
 //      requested into LDS one group ahead;
@@ -250,6 +252,9 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 // Policy interface (see decode.hip / dense.hip):
 //   Smem                      policy LDS (per-query tables)
 //   int num_pages(row, b)     pages in the row
+//   int num_pages_lane(row, b, z)  the same as a per-lane load (z an opaque
+//                             zero), so that it travels with the page-table
+//                             loads of the prologue's first round trip
 //   uint2 meta(page, idx, b)  x = tier | count << 8, y = policy data
 //   const uint8_t *value_part(page, meta)   the page's values: fp16 pages
 //                                           in 8-token groups of [128 dims]
@@ -267,6 +272,9 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //                                              tok + 7 of the current group,
 //                                              in pairs of tokens (after the
 //                                              weights' LDS sync)
+//   kEarlyStage: the first group's codes may be requested before
+//     after_pages (from the registers that fetched its page ids), i.e.
+//     before the prologue's barriers
 //   kStaged = true:
 //     void stage(smem, w, meta, page, slot)    request a group's codes (and
 //                                              V8 scale words) into
@@ -282,35 +290,66 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
     constexpr int KB = P / 8;       // 8-token value blocks per page
     constexpr int NT = NW * 64;
     const int row = b * a.Hkv + h;
-    const int np = pol.num_pages(row, b);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    static_assert(NT >= kMaxChunkPages, "one page-list entry per thread");
+    // an upper bound of the chunk's page slots from the row capacity
+    const int ngr_cap = (a.maxp + TPG - 1) / TPG;
+    if (chunk >= ngr_cap) return;
+    const int nch_cap = (ngr_cap - chunk + a.S - 1) / a.S * TPG;
+    const int32_t *ptab = a.page_table + (size_t)row * a.maxp;
+    // round trip 1: the row's page count (a per-lane load), the page ids of
+    // the chunk's slots up to the capacity bound, the page ids of this
+    // wavefront's first group, and the query
+    uint32_t z = 0;
+    asm volatile("" : "+v"(z));
+    const int np_l = pol.num_pages_lane(row, b, z);
+    const int pslot = (chunk + (tid / TPG) * a.S) * TPG + tid % TPG;   // page index of this thread's slot
+    int praw = -1;
+    if (tid < nch_cap && pslot < a.maxp) praw = ptab[pslot];
+    const int pf = (chunk + w * a.S) * TPG;          // first page of this wavefront's first group
+    const int pl = pf + lane / P;                    // this lane's page of it
+    int pg_own = -1, pg_first = -1;
+    const bool has_first = pf < a.maxp;
+    if (has_first) {
+        pg_first = ptab[pf];
+        if (pl < a.maxp) pg_own = ptab[pl];
+    }
+    pol.prologue(ps, b, h, tid, NT);   // query loads (stored to LDS below their wait)
+    const int np = __builtin_amdgcn_readfirstlane(np_l);
     // chunk c owns the row's 64-token page groups c, c + S, c + 2S, ...: the
     // work-groups running at the same time stream neighbouring pages
     const int ngr_row = (np + TPG - 1) / TPG;
     if (chunk >= ngr_row) return;
     const int ngr = (ngr_row - chunk + a.S - 1) / a.S;   // groups of this chunk
     const int nch = ngr * TPG;                           // page slots of this chunk
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    const int32_t *ptab = a.page_table + (size_t)row * a.maxp;
-    for (int i = tid; i < nch; i += NT) {
-        const int p = (chunk + (i / TPG) * a.S) * TPG + i % TPG;   // page index in the row
-        int page = -1;
-        uint2 m = make_uint2(0u, 0u);
-        if (p < np) {
-            page = ptab[p];
-            m = pol.meta(page, p, b);
-        }
-        cs.pages[i] = page;
-        cs.meta[i] = m;
+    const int n_groups = (nch + TPG - 1) / TPG;
+    const int pg = lane / P, slot = lane % P;
+    // round trip 2: page metadata of the slots and of the first group's pages
+    int page = -1;
+    uint2 m = make_uint2(0u, 0u);
+    if (tid < nch && pslot < np) {
+        page = praw;
+        m = pol.meta(page, pslot, b);
     }
-    pol.prologue(ps, b, h, tid, NT);
+    int fpage = 0;
+    uint2 fmeta = make_uint2(0u, 0u);
+    const bool first = w < n_groups;   // wave-uniform
+    if (first) {
+        fpage = pl < np ? pg_own : pg_first;   // lanes past the row's last page use the group's first page
+        fmeta = pol.meta(fpage, pl, b);
+    }
+    if constexpr (Pol::kStaged && Pol::kEarlyStage) {
+        if (first) pol.stage(ps, w, fmeta, fpage, slot);
+    }
+    if (tid < nch) {
+        cs.pages[tid] = page;
+        cs.meta[tid] = m;
+    }
     __syncthreads();
     // policy work that must precede every code / value read of the chunk
     // (the fused append writes the row's new token into its slot)
     if (pol.after_pages(ps, cs.pages, nch, row, w, lane)) __syncthreads();
-    const int n_groups = (nch + TPG - 1) / TPG;
-    const int pg = lane / P, slot = lane % P;
     // the group's page for this lane (lane = token); lanes past the row's
     // last page use the group's first page (weight 0)
     auto group_meta = [&](int g, bool &valid) {
@@ -325,9 +364,10 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         const int gbase = g * TPG;
         return cs.pages[gbase + pg] >= 0 ? cs.pages[gbase + pg] : cs.pages[gbase];
     };
-    // staged policies: the first group's code units are requested before
-    // the tables are built
-    if constexpr (Pol::kStaged) {
+    // staged policies whose first reads may not start before after_pages:
+    // the first group's code units are requested here, before the tables
+    // are built
+    if constexpr (Pol::kStaged && !Pol::kEarlyStage) {
         if (w < n_groups) {
             bool v;
             const uint2 m0 = group_meta(w, v);

@@ -25,6 +25,7 @@ using core::ldg;
 template <int G, int P, int NW>
 struct DensePolicy {
     static constexpr bool kStaged = false;
+    static constexpr bool kEarlyStage = false;
     static constexpr bool kValueTiers = false;   // fp16 values only
     struct Smem {
         float qd[kD * G];              // [d][g], pre-multiplied by scale * log2(e)
@@ -40,6 +41,7 @@ struct DensePolicy {
     float mul;
 
     __device__ int num_pages(int, int b) const { return (ctx_len[b] + P - 1) / P; }
+    __device__ int num_pages_lane(int, int b, uint32_t z) const { return (ctx_len[b + z] + P - 1) / P; }
     __device__ uint2 meta(int, int idx, int b) const {
         const int count = min(P, ctx_len[b] - idx * P);
         return make_uint2((uint32_t)count << 8, 0u);
