@@ -58,6 +58,7 @@ struct CodeRegs {
     uint2 h;
     uint32_t r;         // fp16 radius bits
     const uint8_t *c;   // the token's first angle unit
+    bool v8_fma;        // V8 values: the group's scales allow the fused conversion
 };
 
 // Per-work-group LUT layout, per pair j with NC codes: slices of SW =
@@ -446,11 +447,21 @@ struct AdaPolicy {
         const uint32_t rr = st.r[lane];
         k.r = (slot & 1) ? rr >> 16 : rr & 0xFFFFu;
         if constexpr (VT) {
-            const uint2 vs = core::v8_scale_halves(s.vs[w][lane]);
+            const uint32_t word = s.vs[w][lane];
+            const uint2 vs = core::v8_scale_halves(word);
             s.vsc[w][0][lane] = (uint16_t)vs.x;
             s.vsc[w][1][lane] = (uint16_t)(vs.x >> 16);
             s.vsc[w][2][lane] = (uint16_t)vs.y;
             s.vsc[w][3][lane] = (uint16_t)(vs.y >> 16);
+            // every scale byte of a V8 token 0 or in the fused conversion's
+            // range (other pages' words are not scales)
+            bool out = false;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint32_t sb = (word >> (8 * kb)) & 0xFFu;
+                out |= sb != 0 && (sb < core::kV8FmaMinScale || sb > core::kV8FmaMaxScale);
+            }
+            k.v8_fma = !__any(out && tier_v8(meta.x & 0xFF));
         }
         // the slot offset is made opaque here so that arena + slot offset (a
         // 64-bit per-lane value) is not hoisted out of the group loop, where

@@ -111,6 +111,27 @@ __device__ __forceinline__ uint32_t v8_pair(uint32_t w, uint32_t scale_pair) {
     return __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(half2_t, scale_pair));
 }
 
+// The fused conversion below needs each block scale 2^(s - 133) as a
+// normal fp16 number at most 2^5: s in [kV8FmaMinScale, kV8FmaMaxScale]
+// (or 0, an empty slot, whose weight is 0).  Its bias -1152 * 2^(s - 133)
+// = -1.125 * 2^(s - 123) then has the scale's fp16 bits plus 0xA880: the
+// sign, ten more in the exponent field, mantissa 0x080 (no carry into the
+// next half, so a scale pair becomes its bias pair in one integer add).
+constexpr uint32_t kV8FmaMinScale = 119, kV8FmaMaxScale = 138;
+constexpr uint32_t kV8BiasAdd = 0xA880A880u;
+
+// v8_pair in one fused multiply-add: (1152 + c) * s + (-1152 * s) is c * s
+// exactly (a small integer times a power of two, rounded once), the same
+// bits as the subtract-then-multiply form, for scales in the range above.
+template <int B>
+__device__ __forceinline__ uint32_t v8_pair_fma(uint32_t w, uint32_t scale_pair, uint32_t bias_pair) {
+    constexpr uint32_t sel = B == 0 ? 0x04010400u : 0x04030402u;   // [b, 0x64, b + 1, 0x64]
+    const uint32_t x = __builtin_amdgcn_perm(0x64646464u, w, sel);
+    const half2_t v = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, x), __builtin_bit_cast(half2_t, scale_pair),
+                                                __builtin_bit_cast(half2_t, bias_pair));
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Wavefront sum in the same pattern (a fixed order, identical in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<0xB1>(v);
@@ -267,6 +288,9 @@ __device__ __forceinline__ void reduce_chunks(const float *pm, const float *pl, 
 //                                              (uniformly) whether a barrier
 //                                              must follow
 //   kValueTiers: pages of tiers 3-5 hold V8 values (see include/ada.h)
+//     codes.v8_fma                              wave-uniform: every V8 token of
+//                                              the group has its block scales
+//                                              in the fused conversion's range
 //     void scale_pairs(smem, w, tok, b, sp[4])  fp16 scales of dimension
 //                                              block b of tokens tok ..
 //                                              tok + 7 of the current group,
@@ -501,7 +525,27 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
         //    dimension block k, whose scales for a step's eight tokens come
         //    from the policy's scale table in one read.
         if constexpr (Pol::kValueTiers) {
-            if (v8) {
+            if (v8 && codes.v8_fma) {   // every block scale of the group's V8 tokens at most 2^5
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    uint32_t s0[4], s1[4], b0[4], b1[4];
+                    pol.scale_pairs(ps, w, 16 * kq, kb, s0);
+                    pol.scale_pairs(ps, w, 16 * kq + 8, kb, s1);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        b0[i] = s0[i] + kV8BiasAdd;
+                        b1[i] = s1[i] + kV8BiasAdd;
+                    }
+#pragma unroll
+                    for (int t = 2 * kb; t < 2 * kb + 2; ++t) {
+                        const uint4 c = va[0][t];
+                        va[1][t] = make_uint4(v8_pair_fma<0>(c.z, s1[0], b1[0]), v8_pair_fma<2>(c.z, s1[1], b1[1]),
+                                              v8_pair_fma<0>(c.w, s1[2], b1[2]), v8_pair_fma<2>(c.w, s1[3], b1[3]));
+                        va[0][t] = make_uint4(v8_pair_fma<0>(c.x, s0[0], b0[0]), v8_pair_fma<2>(c.x, s0[1], b0[1]),
+                                              v8_pair_fma<0>(c.y, s0[2], b0[2]), v8_pair_fma<2>(c.y, s0[3], b0[3]));
+                    }
+                }
+            } else if (v8) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     uint32_t s0[4], s1[4];   // scale pairs of tokens (2i, 2i + 1), block kb, steps 0 and 1

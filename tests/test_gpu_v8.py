@@ -60,6 +60,34 @@ def test_pack_and_decode(name, ctx, batch, frac):
     check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref)
 
 
+@pytest.mark.parametrize("edge", ["inside", "below", "above"])
+def test_fused_conversion_range_edges(edge):
+    """A group whose V8 tokens all have block maxima in [2^-8, 2^12) (scale
+    bytes 119..138) has its codes converted with one fused multiply-add per
+    pair, any other group with a subtract and a multiply; the two give the
+    same fp16 values.  Blocks exactly at the range's edges (maxima 2^-8 and
+    4094), and one token in 37 one step outside it (maxima 0.75 * 2^-8 or
+    4096), decoded against the oracle."""
+    w = _v8(W.config("llama8b", ctx=900, batch=2), 1.0)
+    rng = np.random.default_rng(23)
+    shape = w["values"].shape
+    u = rng.uniform(-1, 1, shape[:-1] + (4, 32))
+    u[..., 0] = np.sign(u[..., 0])                      # each block's maximum is its magnitude
+    mag = np.where(rng.random(shape[:-1] + (4,)) < 0.5, 2.0 ** -8, 4094.0)
+    if edge != "inside":
+        odd = (np.arange(shape[2]) % 37 == 5)[None, None, :, None] & (rng.random(shape[:-1] + (4,)) < 0.5)
+        mag = np.where(odd, 0.75 * 2.0 ** -8 if edge == "below" else 4096.0, mag)
+    v = (u * mag[..., None]).reshape(shape).astype(np.float16)
+    w["values"] = v.view(np.uint16)
+    log(f"v8 fused conversion edges: {edge}")
+    dev = to_dev(w)
+    gc, oc = _pack_both(w, dev)
+    compare_caches(gc, oc, w["P"])
+    out, lse = ada.decode(gc, dev["q"], w["scale"])
+    o_ref, l_ref = O.decode(oc, w["q"], w["scale"])
+    check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref)
+
+
 def test_decode_chunkings_agree():
     w = _v8(W.config("llama8b", ctx=1500, batch=2), 0.5)
     dev = to_dev(w)
