@@ -68,6 +68,18 @@ def parse():
     return ap.parse_args()
 
 
+def release(torch, settle_s=1.5):
+    """Return freed device memory to the driver, then let the device settle
+    before the next timed region.  For a while after several GB are
+    released the driver works on that memory in the background: a decode
+    timed right after freeing the ragged workload's 6.4 GB of input keys and
+    values ran 3% slower (192.8 against 187.3 us after a one-second pause),
+    and rdr128k alternated between 132.6 and 137.7 us."""
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    time.sleep(settle_s)
+
+
 def kernel_source_hash():
     """Hash of the split-K kernel's sources with comments and blank lines
     removed (a comment edit does not change the kernel)."""
@@ -163,7 +175,7 @@ def main():
         torch.cuda.synchronize()
         read_gbps[variant] = nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
-    torch.cuda.empty_cache()
+    release(torch)
 
     alg_bytes = m["alg_bytes"]
     achieved = alg_bytes / (m["kernel_ms"] * 1e-3) / 1e9
@@ -288,7 +300,7 @@ def other_workload(name, args, ada, torch, W, read_probe_gbps):
         d["bytes_per_context_token_head"] = DENSE_TOKEN_BYTES
         rec["dense_fp16_reference"] = d
     del w
-    torch.cuda.empty_cache()
+    release(torch)
     return rec
 
 
@@ -313,7 +325,7 @@ def measure_decode(args, w, ada, torch, cfg, kept, max_row, n_pages, units, step
     st = ada.read_status(cache.status)
     assert st == ada.OK, ada.status_str(st)
     del keys, vals
-    torch.cuda.empty_cache()
+    release(torch)
 
     Q = args.queries
     if Q == 1:
@@ -436,7 +448,7 @@ def measure_decode(args, w, ada, torch, cfg, kept, max_row, n_pages, units, step
     alg_bytes = sum(kept[t] * TIER_TOKEN_BYTES[t] for t in TIERS) + 12 * n_pages + B * Q * Hq * 128 * 4 * 2
     step_each = np.array(step_each_ms)
     del cache, ws
-    torch.cuda.empty_cache()
+    release(torch)
     return {
         "kept": kept_total, "pages_by_tier": [pages_by_tier[t] for t in TIERS], "alg_bytes": alg_bytes,
         "ms_per_step": ms_step, "kernel_ms": k_ms, "kernel_ms_event_mean": k_ms_each,
@@ -462,7 +474,7 @@ def utility_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
     ada.pack(cache, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), torch.from_numpy(w["keys"]).cuda(),
              torch.from_numpy(w["values"].view(np.int16)).cuda())
     assert ada.read_status(cache.status) == ada.OK
-    torch.cuda.empty_cache()
+    release(torch)
     q = torch.from_numpy(w["q"]).cuda()
     out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
@@ -512,7 +524,7 @@ def repack_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
     ada.pack(src, w["ctx_len"], torch.from_numpy(w["tiers"]).cuda(), torch.from_numpy(w["keys"]).cuda(),
              torch.from_numpy(w["values"].view(np.int16)).cuda())
     assert ada.read_status(src.status) == ada.OK
-    torch.cuda.empty_cache()
+    release(torch)
     util = torch.zeros((n_pages, P), dtype=torch.float32, device="cuda")
     ada.decode_utility(src, torch.from_numpy(w["q"]).cuda(), w["scale"], util)
     rate = TIER_TOKEN_BYTES
@@ -590,7 +602,7 @@ def setup_bench(args, w, ada, torch, W, cfg, kept, max_row, n_pages, units):
     assert ada.read_status(cache.status) == ada.OK
     kept_total = sum(kept.values())
     del cache, keys, vals, tiers
-    torch.cuda.empty_cache()
+    release(torch)
 
     r = W.config("rdr128k")
     rcfg = ada.make_config(r["P"], r["Hq"], r["Hkv"])
@@ -632,7 +644,7 @@ def append_bench(args, w, ada, torch, cfg, kept, max_row, n_pages, units):
         assert ada.read_status(c.status) == ada.OK
         caches.append(c)
     del keys, vals
-    torch.cuda.empty_cache()
+    release(torch)
     rng = np.random.default_rng(77)
     nk = torch.from_numpy(rng.standard_normal((n_steps, B, Hkv, 128), dtype=np.float32)).cuda()
     nv = torch.from_numpy(rng.standard_normal((n_steps, B, Hkv, 128)).astype(np.float16).view(np.int16)).cuda()
@@ -713,7 +725,7 @@ def dense_reference(w, ada, torch, cfg):
     token_heads = int(w["ctx_len"].sum()) * w["Hkv"]
     dbytes = token_heads * DENSE_TOKEN_BYTES + B * Hq * 1024
     del kp_d, vp_d
-    torch.cuda.empty_cache()
+    release(torch)
     gbps = dbytes / (ms * 1e-3) / 1e9
     # frac: the dense step's bytes over its time against the 8 TB/s peak,
     # beside the ADA kernel's roofline fraction
