@@ -37,6 +37,9 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy running maximum of the online softmax (base-2 logits): weights are
+// taken against a maximum at most this far below the largest logit seen.
+constexpr float kLazyMax = 8.0f;
 
 // DPP lane permutation of a float (row_mask and bank_mask all on)
 template <int CTRL>
@@ -496,27 +499,52 @@ __device__ __forceinline__ void split_k(const CoreArgs &a, const Pol &pol, typen
             }
         }
 
-        // 4. online softmax, weights to LDS as fp16 hi + lo
-        float alpha_n = 1.f;
-        const float pinf = opaque_inf();
+        // 4. online softmax, weights to LDS as fp16 hi + lo.  A head's
+        //    running maximum moves only when one of the group's logits
+        //    passes it by more than kLazyMax (base 2); otherwise the weights
+        //    are taken against the maximum already held (so at most
+        //    2^kLazyMax, within fp16 and its hi + lo split) and the group
+        //    needs neither wavefront maxima nor a rescale of the sums.
+        bool grow = false;
+        if constexpr (G >= 8) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mx = wave_max<(G >= 8)>(valid ? lg[g] : -INFINITY, pinf);
-            const float mnew = max2<(G >= 8)>(m_run[g], mx, pinf);
-            // v_exp_f32 directly: arguments are <= 0, results below 2^-126
-            // flush to zero, far below the weights' resolution
-            const float alpha = (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - mnew);
-            const float p = valid ? __builtin_amdgcn_exp2f(lg[g] - mnew) : 0.f;
-            l_run[g] = l_run[g] * alpha + p;
-            m_run[g] = mnew;
-            const _Float16 hi = (_Float16)p;
-            const _Float16 lo = (_Float16)(p - (float)hi);
-            cs.pb[w][0][g][lane] = hi;
-            cs.pb[w][1][g][lane] = lo;
-            if (n_head == g) alpha_n = alpha;
+            for (int g = 0; g < G; ++g) grow |= valid && lg[g] > m_run[g] + kLazyMax;
         }
+        // (eight heads: the wavefront maxima are a large share of the VALU work;
+        // at four or fewer the branch costs registers the loop needs)
+        if (G < 8 || __any(grow)) {
+            float alpha_n = 1.f;
+            const float pinf = opaque_inf();
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] *= alpha_n;
+            for (int g = 0; g < G; ++g) {
+                const float mx = wave_max<(G >= 8)>(valid ? lg[g] : -INFINITY, pinf);
+                const float mnew = max2<(G >= 8)>(m_run[g], mx, pinf);
+                // v_exp_f32 directly: arguments are <= 0, results below 2^-126
+                // flush to zero, far below the weights' resolution
+                const float alpha = (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - mnew);
+                const float p = valid ? __builtin_amdgcn_exp2f(lg[g] - mnew) : 0.f;
+                l_run[g] = l_run[g] * alpha + p;
+                m_run[g] = mnew;
+                const _Float16 hi = (_Float16)p;
+                const _Float16 lo = (_Float16)(p - (float)hi);
+                cs.pb[w][0][g][lane] = hi;
+                cs.pb[w][1][g][lane] = lo;
+                if (n_head == g) alpha_n = alpha;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[t] *= alpha_n;
+        } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                // arguments at most kLazyMax; an invalid lane's weight is 0
+                const float p = valid ? __builtin_amdgcn_exp2f(lg[g] - m_run[g]) : 0.f;
+                l_run[g] += p;
+                const _Float16 hi = (_Float16)p;
+                const _Float16 lo = (_Float16)(p - (float)hi);
+                cs.pb[w][0][g][lane] = hi;
+                cs.pb[w][1][g][lane] = lo;
+            }
+        }
         wave_lds_sync();
 
         // 5. O^T += V^T P^T on the matrix cores.  V8 lanes first turn codes
