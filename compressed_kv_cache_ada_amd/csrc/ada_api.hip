@@ -975,7 +975,7 @@ ada_status_t ada_probe_copy(const void *src, void *dst, size_t bytes, void *stre
 }
 
 ada_status_t ada_probe_read(const void *src, size_t bytes, int32_t variant, uint32_t *out, void *stream) {
-    if (!src || !out || (bytes & 15) || variant < 0 || variant > 4) return ADA_EINVAL;
+    if (!src || !out || (bytes & 15) || variant < 0 || variant > 5) return ADA_EINVAL;
     if (bytes == 0) return ADA_OK;
     return hip_status(launch_probe_read(src, bytes, variant, out, (hipStream_t)stream));
 }

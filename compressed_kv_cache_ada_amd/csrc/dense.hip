@@ -228,6 +228,34 @@ __global__ __launch_bounds__(256) void probe_read_blocked_kernel(const uint4 *sr
     if (acc == 0x9E3779B9u) out[0] = acc;
 }
 
+// Random 16 KB chunks: each wavefront reads whole 16 KB chunks (sixteen
+// 16-byte loads per lane in flight, then their fold), the chunks in a
+// scrambled order (chunk c of a power-of-two count n is c * 0x9E3779B1 mod
+// n, a bijection): the access pattern of the split-K decode's value reads,
+// 64-token groups of about 20 KB spread over the arena.  The dynamic LDS
+// only caps residency at three work-groups per compute unit, as the decode.
+constexpr int kChunkProbeLds = 48 * 1024;
+__global__ __launch_bounds__(256) void probe_read_chunks_kernel(const uint4 *src, int64_t nchunks, uint32_t *out) {
+    extern __shared__ uint32_t cap[];
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    uint32_t acc = 0;
+    for (int64_t c = wave; c < nchunks; c += nw) {
+        const int64_t pc = (int64_t)(((uint64_t)c * 0x9E3779B1ull) & (uint64_t)(nchunks - 1));
+        const uint4 *base = src + pc * 1024;
+        uint4 v[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) v[t] = base[t * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc ^= v[t].x ^ v[t].y ^ v[t].z ^ v[t].w;
+    }
+    if (acc == 0x9E3779B9u) {
+        cap[0] = acc;
+        out[0] = cap[0];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_probe_read(const void *src, size_t bytes, int variant, uint32_t *out, hipStream_t s) {
@@ -239,6 +267,13 @@ hipError_t launch_probe_read(const void *src, size_t bytes, int variant, uint32_
         case 1: hipLaunchKernelGGL((probe_read_kernel<4, false>), grid, block, 0, s, p, n, out); break;
         case 2: hipLaunchKernelGGL((probe_read_kernel<4, true>), grid, block, 0, s, p, n, out); break;
         case 3: hipLaunchKernelGGL((probe_read_kernel<8, true>), grid, block, 0, s, p, n, out); break;
+        case 5: {
+            int64_t nc = 1;   // the largest power of two of 16 KB chunks within `bytes`
+            while (nc * 2 * 1024 <= n) nc *= 2;
+            if (n < 1024) return hipSuccess;
+            hipLaunchKernelGGL(probe_read_chunks_kernel, dim3(768), block, kChunkProbeLds, s, p, nc, out);
+            break;
+        }
         default: hipLaunchKernelGGL(probe_read_blocked_kernel, grid, block, 0, s, p, n, out); break;
     }
     return hipGetLastError();

@@ -439,8 +439,12 @@ ada_status_t ada_probe_copy(const void *src, void *dst, size_t bytes, void *stre
  * variant 0: one 16-byte load per lane in flight, grid-stride (the active
  * work-groups read a moving window); 1: four loads; 2: four with the
  * non-temporal hint; 3: eight with the hint; 4: each work-group reads its
- * own contiguous region (many distant streams).  `out` (device, 1 word) is only
- * written when the xor of the data hits a fixed value. */
+ * own contiguous region (many distant streams); 5: each wavefront reads
+ * whole 16 KB chunks (sixteen loads per lane in flight) in a scrambled
+ * order, at most three 256-thread work-groups per compute unit -- the
+ * access pattern of the decode's value reads; it reads the largest
+ * power-of-two number of 16 KB chunks that fits in `bytes`.  `out` (device,
+ * 1 word) is only written when the xor of the data hits a fixed value. */
 ada_status_t ada_probe_read(const void *src, size_t bytes, int32_t variant, uint32_t *out, void *stream);
 
 /* Host-side evaluation of the library's fp64 -> fp16 radius rounding (round
