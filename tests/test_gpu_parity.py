@@ -311,3 +311,35 @@ def test_adversarial_codec_bit_exact(tier):
     st, st_o = _append_both(w, gc, oc, np.zeros(n), np.zeros(n), np.full(n, tier), keys, vals)
     assert st == ada.OK and st_o == O.OK
     compare_caches(gc, oc, w["P"])
+
+
+@pytest.mark.parametrize("name,chunk_pages", [("long256k", 0), ("long256k", 1000), ("llama8b", 1000)])
+def test_decode_late_logit_spikes(name, chunk_pages):
+    """Keys planted late in each row along one query head's direction, each
+    larger than the last, so that a wavefront's running maximum has to move
+    by far more than 2^8 (base 2) in the middle of its groups: the rescale
+    path of the online softmax after groups weighted against an older
+    maximum (eight query heads per KV head), and the per-group maximum
+    (four).  A chunk length of 1000 pages puts one chunk on each row, so
+    every wavefront walks several groups."""
+    w = W.config(name, ctx=2600, batch=1)
+    G = w["Hq"] // w["Hkv"]
+    keys, tiers = w["keys"].copy(), w["tiers"].copy()
+    for h in range(w["Hkv"]):
+        for k, pos in enumerate((1500, 1900, 2300, 2550)):
+            g = h * G + (pos + h) % G
+            keys[0, h, pos] = (1.0 + k) * w["q"][0, g]   # logit about 11 (1 + k) |q|^2 / 128 for head g
+            tiers[0, h, pos] = 1                          # kept, T4
+    w = dict(w, keys=keys, tiers=tiers)
+    log(f"late spikes {name} chunk_pages={chunk_pages}")
+    cfg = ada.make_config(w["P"], w["Hq"], w["Hkv"], decode_chunk_pages=chunk_pages)
+    dev = to_dev(w)
+    gc = gpu_cache(w, cfg=cfg)
+    ada.pack(gc, w["ctx_len"], torch.from_numpy(tiers).cuda(), dev["keys"], dev["values"])
+    assert ada.read_status(gc.status) == ada.OK
+    out, lse = ada.decode(gc, dev["q"], w["scale"])
+    o_ref, lse_ref = O.decode(_oracle_pack(w), w["q"], w["scale"])
+    # the spikes dominate their heads: the largest lse is far above the rest
+    assert np.max(lse_ref) > np.median(lse_ref) + 20
+    worst = check_outputs(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    log(f"  worst row rel err {worst:.2e}")
