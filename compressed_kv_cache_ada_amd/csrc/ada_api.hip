@@ -746,6 +746,8 @@ ada_status_t ada_pack(const ada_config_t *cfg, const ada_cache_t *cache, int32_t
     a.src_maxp = 0;
     a.src_of_slot = nullptr;
     a.src_of_slot_pages = 0;
+    a.first_pos = nullptr;
+    a.page_order = nullptr;
     a.item_of_slot = w.item_of_slot;
     a.item_slot_pages = w.item_slot_pages;
     a.row_order = cache->row_order;
@@ -764,6 +766,7 @@ struct RepackWs {
     void *rdr, *pack;
     int4 *src_of_slot;
     int64_t src_of_slot_pages;
+    int32_t *first_pos, *page_order;
     size_t bytes;
 };
 
@@ -783,6 +786,8 @@ static RepackWs repack_layout(const ada_config_t *cfg, const ada_cache_t *src, i
         smul((size_t)B, (size_t)cfg->num_kv_heads, (size_t)repack_pages_per_row(src->max_pages_per_head));
     r.src_of_slot_pages = (int64_t)std::min<size_t>(pages, INT64_MAX);
     r.src_of_slot = c.take<int4>(smul(pages, (size_t)cfg->page_size));
+    r.first_pos = c.take<int32_t>(pages);
+    r.page_order = c.take<int32_t>(pages);
     r.bytes = c.off;
     return r;
 }
@@ -902,6 +907,8 @@ ada_status_t ada_repack(const ada_config_t *cfg, const ada_cache_t *src, int32_t
     a.src_maxp = src->max_pages_per_head;
     a.src_of_slot = r.src_of_slot;
     a.src_of_slot_pages = r.src_of_slot_pages;
+    a.first_pos = r.first_pos;
+    a.page_order = r.page_order;
     a.item_of_slot = nullptr;
     a.item_slot_pages = 0;
     a.row_order = dst->row_order;

@@ -182,6 +182,10 @@ struct PackLaunch {
     int32_t src_maxp;
     int4 *src_of_slot;              // [src_of_slot_pages][P] source {page, slot, tier, code_off16} per new slot
     int64_t src_of_slot_pages;
+    // re-pack: the source position of each new page's first token, and the
+    // order the transcoder writes the new pages in (per row, all tiers by
+    // that position), both [src_of_slot_pages]
+    int32_t *first_pos, *page_order;
     // pack from keys: the item (row * stride + position) of every new slot,
     // [item_slot_pages][P], for the page writer
     int64_t *item_of_slot;

@@ -130,6 +130,50 @@ __device__ inline void zero_token(uint8_t *dblk, int slot, int P) {
     reinterpret_cast<uint16_t *>(dblk)[slot] = 0;
 }
 
+// Re-pack: the order the transcoder writes the new pages in.  Pages are
+// allocated row by row and, within a row, tier by tier, each tier's pages in
+// the order of their tokens' source positions.  Here a row's pages of all
+// tiers are merged by the source position of their first token (distinct
+// for distinct pages of a row): a page's rank is its index in its tier plus,
+// for every other tier of the row, the number of that tier's pages that
+// start earlier (a binary search in its increasing first positions).  So
+// the pages that draw from one stretch of a source row are written close
+// together in time, and the source value groups they share are read once.
+__global__ __launch_bounds__(256) void repack_order_kernel(PackLaunch a) {
+    if (read_status(a.status) != 0) return;
+    const int first = a.n_new[0];
+    const int n = (int)min((int64_t)a.n_new[1], a.src_of_slot_pages);
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int page = first + i;
+    const int rows = a.B * a.Hkv;
+    // the row: the last one whose first page id is at most this page (an
+    // empty row shares its first page id with the next row)
+    int lo = 0, hi = rows - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (a.row_base[mid * kNumTiers] <= page) lo = mid;
+        else hi = mid - 1;
+    }
+    const int row = lo;
+    const int tier = a.page_meta[page].tier;
+    const int my = a.first_pos[i];
+    int rank = page - a.row_base[row * kNumTiers + tier];
+    for (int t = 0; t < kNumTiers; ++t) {
+        if (t == tier) continue;
+        const int np = (a.row_counts[row * kNumTiers + t] + a.P - 1) / a.P;
+        const int base = a.row_base[row * kNumTiers + t] - first;
+        int l = 0, h = np;   // pages of tier t that start before `my`
+        while (l < h) {
+            const int mid = (l + h) / 2;
+            if (a.first_pos[base + mid] < my) l = mid + 1;
+            else h = mid;
+        }
+        rank += l;
+    }
+    a.page_order[a.row_base[row * kNumTiers] - first + rank] = i;
+}
+
 // About one round of resident 128-thread work-groups, each writing new
 // destination pages in turn (grid-stride).  Every byte of a page's code
 // block and value page is written, slots past the count as zeros.  A page's
@@ -163,20 +207,33 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
     auto publish = [&](int buf, const ada_page_meta_t &m, const int4 &e) {
         if (tid < P) s_ent[buf][tid] = tid < (int)m.count ? e : make_int4(-1, 0, 0, 0);
     };
-    int i = blockIdx.x;
-    if (i >= n) return;
+    // positions j of the write order (page_order[j] is a page): work-groups
+    // go to the chip's 8 dies in turn, and die x = b % 8 takes the x-th
+    // contiguous eighth of the order, so the pages that share source lines
+    // share one L2
+    int lo = 0, hi = n, j = blockIdx.x, step = gridDim.x;
+    if (gridDim.x % 8 == 0) {
+        const int part = (n + 7) / 8, x = blockIdx.x % 8;
+        lo = x * part;
+        hi = min(n, lo + part);
+        step = gridDim.x / 8;
+        j = lo + blockIdx.x / 8;
+    }
+    if (j >= hi) return;
+    int i = a.page_order[j];
     ada_page_meta_t m;
     int4 e_raw;
     fetch(i, m, e_raw);
     publish(0, m, e_raw);
     __syncthreads();
-    for (int buf = 0; i < n; i += gridDim.x, buf ^= 1) {
+    for (int buf = 0; j < hi; buf ^= 1) {
         const int page = first + i;
         const int count = m.count, tier = m.tier;
-        const int inext = i + gridDim.x;
+        const int jnext = j + step;
+        const int inext = jnext < hi ? a.page_order[jnext] : 0;
         ada_page_meta_t m_next = m;
         int4 e_next = make_int4(-1, 0, 0, 0);
-        if (inext < n) fetch(inext, m_next, e_next);
+        if (jnext < hi) fetch(inext, m_next, e_next);
         const int4 (&s_cur)[P] = s_ent[buf];
         const int4 e = tid < P ? s_cur[tid] : make_int4(-1, 0, 0, 0);
 
@@ -282,8 +339,10 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
                     for (int k = 0; k < 16; ++k) grp[k * 4 + (dim >> 5)] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
             }
         }
-        if (inext < n) publish(buf ^ 1, m_next, e_next);
+        if (jnext < hi) publish(buf ^ 1, m_next, e_next);
         m = m_next;
+        j = jnext;
+        i = inext;
         __syncthreads();   // the next page's entries are in place; this page's buffer is refilled after the next barrier
     }
 }
@@ -585,6 +644,7 @@ __global__ __launch_bounds__(256) void pack_dest_kernel(PackLaunch a) {
                 const int sp = a.src_page_table[(int64_t)row * a.src_maxp + t / a.P];
                 const ada_page_meta_t sm = a.src_page_meta[sp];
                 a.src_of_slot[j] = make_int4(sp, t % a.P, sm.tier, (int)sm.code_off16);
+                if (ds == 0) a.first_pos[dp - a.n_new[0]] = t;
             }
         }
     }
@@ -1120,6 +1180,7 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         const dim3 grid(grid_for(a.src_of_slot_pages, 1, 8 * cus));   // about one round of resident work-groups
+        hipLaunchKernelGGL(repack_order_kernel, dim3(grid_for(a.src_of_slot_pages, 256, 1 << 20)), dim3(256), 0, s, a);
         if (a.P == 16) hipLaunchKernelGGL(transcode_pages_kernel<16>, grid, dim3(128), 0, s, a);
         else hipLaunchKernelGGL(transcode_pages_kernel<32>, grid, dim3(128), 0, s, a);
         if (a.row_order)
