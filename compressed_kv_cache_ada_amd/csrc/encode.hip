@@ -130,6 +130,123 @@ __device__ inline void zero_token(uint8_t *dblk, int slot, int P) {
     reinterpret_cast<uint16_t *>(dblk)[slot] = 0;
 }
 
+// The transcoder's three steps for one new page m (metadata) whose source
+// entries s sit in LDS.  Threads are dimensions (dim = thread index).
+template <int P>
+__device__ __forceinline__ void tc_load_values(const PackLaunch &a, const int4 (&s)[P], int dim, uint32_t (&wa)[P],
+                                               uint32_t (&wb)[P]) {
+    // 1. this dimension's value of every source token, all loads issued
+    //    before any is used (branch-free: an empty slot reads the arena's
+    //    first word, unused).  fp16 source: the dword holding the value
+    //    (twice); V8 source: the dwords holding its code and scale bytes.
+    //    A source page's values follow its key part in its block.
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const int4 ek = s[k];
+        const size_t vpart = ((size_t)(uint32_t)ek.w + key16(ek.z, P)) * 16;
+        size_t oa, ob;
+        if (tier_v8(ek.z)) {
+            const size_t grp = vpart + (ek.y >> 4) * kV8Group;
+            oa = grp + kV8Codes + dim * 16 + (ek.y & 12);
+            ob = grp + (ek.y & 15) * 4;
+        } else {
+            oa = vpart + (ek.y >> 3) * 2048 + dim * 16 + ((ek.y & 7) >> 1) * 4;
+            ob = oa;
+        }
+        if (ek.x < 0) oa = ob = 0;
+        wa[k] = *reinterpret_cast<const uint32_t *>(a.src_arena + oa);
+        wb[k] = *reinterpret_cast<const uint32_t *>(a.src_arena + ob);
+    }
+}
+
+template <int P>
+__device__ __forceinline__ void tc_codes(const PackLaunch &a, const ada_page_meta_t &m, int4 e, int tid) {
+    const int count = m.count, tier = m.tier;
+    // 2. threads 0..P-1: token tid's codes
+    if (tid < P) {
+        uint8_t *dblk = a.arena + (size_t)m.code_off16 * 16;
+        const int k = tid;
+        // key tiers (0 T8, 1 T4, 2 T2) of source and destination
+        const int st = key_tier(e.z), dt = key_tier(tier);
+        const bool upgrade = k < count && (st > dt || (tier_v8(e.z) && !tier_v8(tier)));
+        if (k >= count || upgrade) {   // past the count; or an upgrade, which the caps rule out
+            if (upgrade) set_status(a.status, ADA_EINTERNAL);
+            if (dt == 0) zero_token<0>(dblk, k, P);
+            else if (dt == 1) zero_token<1>(dblk, k, P);
+            else zero_token<2>(dblk, k, P);
+        } else {
+            const uint8_t *sblk = a.src_arena + (size_t)(uint32_t)e.w * 16;
+            const int sslot = e.y;
+            if (dt == 0) transcode_token<0, 0>(sblk, sslot, dblk, k, P);
+            else if (dt == 1 && st == 0) transcode_token<0, 1>(sblk, sslot, dblk, k, P);
+            else if (dt == 1) transcode_token<1, 1>(sblk, sslot, dblk, k, P);
+            else if (st == 0) transcode_token<0, 2>(sblk, sslot, dblk, k, P);
+            else if (st == 1) transcode_token<1, 2>(sblk, sslot, dblk, k, P);
+            else transcode_token<2, 2>(sblk, sslot, dblk, k, P);
+        }
+    }
+}
+
+template <int P>
+__device__ __forceinline__ void tc_values(const PackLaunch &a, const ada_page_meta_t &m, const int4 (&s)[P],
+                                          const uint32_t (&wa)[P], const uint32_t (&wb)[P], int dim) {
+    const int tier = m.tier;
+    // 3. the value part, per 16 tokens and dimension: one thread per
+    //    dimension; a V8 source is decoded first (its values are fp16
+    //    numbers exactly)
+    uint8_t *dvb = a.arena + ((size_t)m.code_off16 + key16(tier, P)) * 16;
+    const bool dst_v8 = tier_v8(tier);
+#pragma unroll
+    for (int g = 0; g < P / 16; ++g) {
+        uint32_t h[16];
+        bool live[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int4 ek = s[16 * g + k];
+            const uint32_t ra = wa[16 * g + k], rb = wb[16 * g + k];
+            live[k] = ek.x >= 0;
+            if (!live[k]) h[k] = 0u;
+            else if (tier_v8(ek.z))
+                h[k] = v8_value_bits((int)((ra >> (8 * (ek.y & 3))) & 0xFFu) - 128, (rb >> (8 * (dim >> 5))) & 0xFFu);
+            else h[k] = (ra >> ((ek.y & 1) * 16)) & 0xFFFFu;
+        }
+        if (!dst_v8) {   // two 8-token groups, [128 dims][8 tokens] fp16 each
+#pragma unroll
+            for (int hg = 0; hg < 2; ++hg) {
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[k] = h[8 * hg + 2 * k] | (h[8 * hg + 2 * k + 1] << 16);
+                *reinterpret_cast<uint4 *>(dvb + (2 * g + hg) * 2048 + dim * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        } else {
+            // V8: per token, the exponent of its 32-dimension block (32
+            // consecutive lanes), then this dimension's code; empty slots
+            // are zero
+            uint32_t cw[4] = {0u, 0u, 0u, 0u};
+            uint32_t sw[4] = {0u, 0u, 0u, 0u};   // scale bytes of this block, tokens 4i .. 4i + 3
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                int mx = (int)(h[k] & 0x7FFFu);
+                mx = max(mx, __shfl_xor(mx, 1, 64));
+                mx = max(mx, __shfl_xor(mx, 2, 64));
+                mx = max(mx, __shfl_xor(mx, 4, 64));
+                mx = max(mx, __shfl_xor(mx, 8, 64));
+                mx = max(mx, __shfl_xor(mx, 16, 64));
+                const int ex = enc::v8_exponent((uint32_t)mx);
+                const uint32_t c = live[k] ? (uint32_t)(enc::v8_code(h[k], ex) + 128) : 0u;
+                const uint32_t sbyte = live[k] ? (uint32_t)(ex + 127) : 0u;
+                cw[k >> 2] |= c << (8 * (k & 3));
+                sw[k >> 2] |= sbyte << (8 * (k & 3));
+            }
+            uint8_t *grp = dvb + g * kV8Group;
+            *reinterpret_cast<uint4 *>(grp + kV8Codes + dim * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            if ((dim & 31) == 0)   // token k's scale byte of this block
+#pragma unroll
+                for (int k = 0; k < 16; ++k) grp[k * 4 + (dim >> 5)] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
+        }
+    }
+}
+
 // Re-pack: the order the transcoder writes the new pages in.  Pages are
 // allocated row by row and, within a row, tier by tier, each tier's pages in
 // the order of their tokens' source positions.  Here a row's pages of all
@@ -227,8 +344,6 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
     publish(0, m, e_raw);
     __syncthreads();
     for (int buf = 0; j < hi; buf ^= 1) {
-        const int page = first + i;
-        const int count = m.count, tier = m.tier;
         const int jnext = j + step;
         const int inext = jnext < hi ? a.page_order[jnext] : 0;
         ada_page_meta_t m_next = m;
@@ -237,113 +352,103 @@ __global__ __launch_bounds__(128, 4) void transcode_pages_kernel(PackLaunch a) {
         const int4 (&s_cur)[P] = s_ent[buf];
         const int4 e = tid < P ? s_cur[tid] : make_int4(-1, 0, 0, 0);
 
-        // 1. this dimension's value of every source token, all loads issued
-        //    before any is used (branch-free: an empty slot reads the arena's
-        //    first word, unused).  fp16 source: the dword holding the value
-        //    (twice); V8 source: the dwords holding its code and scale bytes.
-        //    A source page's values follow its key part in its block.
         uint32_t wa[P], wb[P];
-#pragma unroll
-        for (int k = 0; k < P; ++k) {
-            const int4 ek = s_cur[k];
-            const size_t vpart = ((size_t)(uint32_t)ek.w + key16(ek.z, P)) * 16;
-            size_t oa, ob;
-            if (tier_v8(ek.z)) {
-                const size_t grp = vpart + (ek.y >> 4) * kV8Group;
-                oa = grp + kV8Codes + dim * 16 + (ek.y & 12);
-                ob = grp + (ek.y & 15) * 4;
-            } else {
-                oa = vpart + (ek.y >> 3) * 2048 + dim * 16 + ((ek.y & 7) >> 1) * 4;
-                ob = oa;
-            }
-            if (ek.x < 0) oa = ob = 0;
-            wa[k] = *reinterpret_cast<const uint32_t *>(a.src_arena + oa);
-            wb[k] = *reinterpret_cast<const uint32_t *>(a.src_arena + ob);
-        }
-
-        // 2. threads 0..P-1: token tid's codes
-        if (tid < P) {
-            uint8_t *dblk = a.arena + (size_t)m.code_off16 * 16;
-            const int k = tid;
-            // key tiers (0 T8, 1 T4, 2 T2) of source and destination
-            const int st = key_tier(e.z), dt = key_tier(tier);
-            const bool upgrade = k < count && (st > dt || (tier_v8(e.z) && !tier_v8(tier)));
-            if (k >= count || upgrade) {   // past the count; or an upgrade, which the caps rule out
-                if (upgrade) set_status(a.status, ADA_EINTERNAL);
-                if (dt == 0) zero_token<0>(dblk, k, P);
-                else if (dt == 1) zero_token<1>(dblk, k, P);
-                else zero_token<2>(dblk, k, P);
-            } else {
-                const uint8_t *sblk = a.src_arena + (size_t)(uint32_t)e.w * 16;
-                const int sslot = e.y;
-                if (dt == 0) transcode_token<0, 0>(sblk, sslot, dblk, k, P);
-                else if (dt == 1 && st == 0) transcode_token<0, 1>(sblk, sslot, dblk, k, P);
-                else if (dt == 1) transcode_token<1, 1>(sblk, sslot, dblk, k, P);
-                else if (st == 0) transcode_token<0, 2>(sblk, sslot, dblk, k, P);
-                else if (st == 1) transcode_token<1, 2>(sblk, sslot, dblk, k, P);
-                else transcode_token<2, 2>(sblk, sslot, dblk, k, P);
-            }
-        }
-
-        // 3. the value part, per 16 tokens and dimension: one thread per
-        //    dimension; a V8 source is decoded first (its values are fp16
-        //    numbers exactly)
-        uint8_t *dvb = a.arena + ((size_t)m.code_off16 + key16(tier, P)) * 16;
-        const bool dst_v8 = tier_v8(tier);
-#pragma unroll
-        for (int g = 0; g < P / 16; ++g) {
-            uint32_t h[16];
-            bool live[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int4 ek = s_cur[16 * g + k];
-                const uint32_t ra = wa[16 * g + k], rb = wb[16 * g + k];
-                live[k] = ek.x >= 0;
-                if (!live[k]) h[k] = 0u;
-                else if (tier_v8(ek.z))
-                    h[k] = v8_value_bits((int)((ra >> (8 * (ek.y & 3))) & 0xFFu) - 128, (rb >> (8 * (dim >> 5))) & 0xFFu);
-                else h[k] = (ra >> ((ek.y & 1) * 16)) & 0xFFFFu;
-            }
-            if (!dst_v8) {   // two 8-token groups, [128 dims][8 tokens] fp16 each
-#pragma unroll
-                for (int hg = 0; hg < 2; ++hg) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) w[k] = h[8 * hg + 2 * k] | (h[8 * hg + 2 * k + 1] << 16);
-                    *reinterpret_cast<uint4 *>(dvb + (2 * g + hg) * 2048 + dim * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            } else {
-                // V8: per token, the exponent of its 32-dimension block (32
-                // consecutive lanes), then this dimension's code; empty slots
-                // are zero
-                uint32_t cw[4] = {0u, 0u, 0u, 0u};
-                uint32_t sw[4] = {0u, 0u, 0u, 0u};   // scale bytes of this block, tokens 4i .. 4i + 3
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    int mx = (int)(h[k] & 0x7FFFu);
-                    mx = max(mx, __shfl_xor(mx, 1, 64));
-                    mx = max(mx, __shfl_xor(mx, 2, 64));
-                    mx = max(mx, __shfl_xor(mx, 4, 64));
-                    mx = max(mx, __shfl_xor(mx, 8, 64));
-                    mx = max(mx, __shfl_xor(mx, 16, 64));
-                    const int ex = enc::v8_exponent((uint32_t)mx);
-                    const uint32_t c = live[k] ? (uint32_t)(enc::v8_code(h[k], ex) + 128) : 0u;
-                    const uint32_t sbyte = live[k] ? (uint32_t)(ex + 127) : 0u;
-                    cw[k >> 2] |= c << (8 * (k & 3));
-                    sw[k >> 2] |= sbyte << (8 * (k & 3));
-                }
-                uint8_t *grp = dvb + g * kV8Group;
-                *reinterpret_cast<uint4 *>(grp + kV8Codes + dim * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-                if ((dim & 31) == 0)   // token k's scale byte of this block
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) grp[k * 4 + (dim >> 5)] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
-            }
-        }
+        tc_load_values<P>(a, s_cur, dim, wa, wb);
+        tc_codes<P>(a, m, e, tid);
+        tc_values<P>(a, m, s_cur, wa, wb, dim);
         if (jnext < hi) publish(buf ^ 1, m_next, e_next);
         m = m_next;
         j = jnext;
         i = inext;
         __syncthreads();   // the next page's entries are in place; this page's buffer is refilled after the next barrier
+    }
+}
+
+// The same transcoder with each page's value loads issued one page ahead
+// (16-token pages: two pages' values fit the registers).  The entries of the
+// next page are in LDS while the current page is written: after this page's
+// code loads, the next page's value loads are issued, and this page's values
+// (loaded one iteration earlier) are assembled and written while they are in
+// flight.  The barriers wait for LDS work only (s_waitcnt lgkmcnt(0), then
+// s_barrier): a full __syncthreads would also wait for the loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int P>
+__global__ __launch_bounds__(128, 4) void transcode_pages_pipe_kernel(PackLaunch a) {
+    __shared__ int4 s_ent[2][P];   // the current page's source entries, and the next page's
+    __shared__ int s_stop;
+    const int tid = threadIdx.x, dim = tid;
+    if (tid == 0) s_stop = read_status(a.status);
+    __syncthreads();
+    if (s_stop != 0) return;
+    const int first = a.n_new[0];
+    const int n = (int)min((int64_t)a.n_new[1], a.src_of_slot_pages);   // bounded by construction
+    auto fetch = [&](int i, ada_page_meta_t &m, int4 &e) {
+        m = a.page_meta[first + i];
+        e = tid < P ? a.src_of_slot[(int64_t)i * P + tid] : make_int4(-1, 0, 0, 0);
+    };
+    auto publish = [&](int buf, const ada_page_meta_t &m, const int4 &e) {
+        if (tid < P) s_ent[buf][tid] = tid < (int)m.count ? e : make_int4(-1, 0, 0, 0);
+    };
+    // die x = b % 8 takes the x-th contiguous eighth of the write order
+    int lo = 0, hi = n, j = blockIdx.x, step = gridDim.x;
+    if (gridDim.x % 8 == 0) {
+        const int part = (n + 7) / 8, x = blockIdx.x % 8;
+        lo = x * part;
+        hi = min(n, lo + part);
+        step = gridDim.x / 8;
+        j = lo + blockIdx.x / 8;
+    }
+    if (j >= hi) return;
+    // pages at write positions j (current), j1, j2: entries of j and j1 in
+    // LDS, of j2 in registers; the page of j3 is requested one iteration
+    // before its entries are
+    int j1 = j + step, j2 = j1 + step;
+    const int i0 = a.page_order[j];
+    const int i1 = j1 < hi ? a.page_order[j1] : 0;
+    int i2 = j2 < hi ? a.page_order[j2] : 0;
+    ada_page_meta_t m, m1;
+    int4 e0, e1 = make_int4(-1, 0, 0, 0);
+    fetch(i0, m, e0);
+    m1 = m;
+    if (j1 < hi) fetch(i1, m1, e1);
+    publish(0, m, e0);
+    lds_barrier();
+    uint32_t wa[P], wb[P];
+    tc_load_values<P>(a, s_ent[0], dim, wa, wb);
+    if (j1 < hi) publish(1, m1, e1);
+    lds_barrier();
+    for (int buf = 0; j < hi; buf ^= 1) {
+        ada_page_meta_t m2 = m1;
+        int4 e2 = make_int4(-1, 0, 0, 0);
+        if (j2 < hi) fetch(i2, m2, e2);
+        const int j3 = j2 + step;
+        const int i3 = j3 < hi ? a.page_order[j3] : 0;
+        const int4 e = tid < P ? s_ent[buf][tid] : make_int4(-1, 0, 0, 0);
+        tc_codes<P>(a, m, e, tid);
+        uint32_t wa1[P], wb1[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k) wa1[k] = wb1[k] = 0u;
+        if (j1 < hi) tc_load_values<P>(a, s_ent[buf ^ 1], dim, wa1, wb1);
+        tc_values<P>(a, m, s_ent[buf], wa, wb, dim);
+        lds_barrier();   // every thread is done with this page's entries
+        if (j2 < hi) publish(buf, m2, e2);
+        lds_barrier();   // the entries of the page after the next one are in place
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            wa[k] = wa1[k];
+            wb[k] = wb1[k];
+        }
+        m = m1;
+        m1 = m2;
+        j = j1;
+        j1 = j2;
+        j2 = j3;
+        i2 = i3;
     }
 }
 
@@ -1181,7 +1286,7 @@ hipError_t launch_pack(const PackLaunch &a, hipStream_t s) {
             cus = 256;
         const dim3 grid(grid_for(a.src_of_slot_pages, 1, 8 * cus));   // about one round of resident work-groups
         hipLaunchKernelGGL(repack_order_kernel, dim3(grid_for(a.src_of_slot_pages, 256, 1 << 20)), dim3(256), 0, s, a);
-        if (a.P == 16) hipLaunchKernelGGL(transcode_pages_kernel<16>, grid, dim3(128), 0, s, a);
+        if (a.P == 16) hipLaunchKernelGGL(transcode_pages_pipe_kernel<16>, grid, dim3(128), 0, s, a);
         else hipLaunchKernelGGL(transcode_pages_kernel<32>, grid, dim3(128), 0, s, a);
         if (a.row_order)
             hipLaunchKernelGGL(row_order_kernel, dim3(1), dim3(1024), 0, s, a.rows_total, (const int32_t *)a.num_pages,
